@@ -1,0 +1,475 @@
+/*
+ * kvq oracle: plain CPU reference. TEST INFRASTRUCTURE ONLY (see kvq_oracle.h).
+ *
+ * Build: gcc -std=c11 -O2 -ffp-contract=off -fno-fast-math -fPIC -shared kvq_oracle.c -lm
+ * -ffp-contract=off keeps every fp32 operation a separate IEEE rounding, which the
+ * arithmetic contract in kvq_oracle.h requires.
+ */
+#include "kvq_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------- */
+/* Number formats, written from the IEEE 754 binary16 and bfloat16 definitions. */
+
+float orc_bf16_to_f32(uint16_t b) {
+  /* bfloat16 is the top half of a binary32 pattern: widening is exact. */
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+static int bit_length_u32(uint32_t m) {
+  int n = 0;
+  while (m) {
+    ++n;
+    m >>= 1;
+  }
+  return n;
+}
+
+uint16_t orc_f32_to_f16(float x) {
+  uint32_t u;
+  memcpy(&u, &x, 4);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  uint32_t ex = (u >> 23) & 0xFFu;
+  uint32_t man = u & 0x7FFFFFu;
+  if (ex == 0xFFu) {
+    if (man == 0) return sign | 0x7C00u;                      /* infinity */
+    return (uint16_t)(sign | 0x7E00u | (man >> 13));          /* quiet NaN */
+  }
+  /* |x| = m * 2^e with m an integer of at most 24 bits */
+  uint32_t m;
+  int e;
+  if (ex == 0) {
+    m = man;
+    e = -149;
+  } else {
+    m = man | 0x800000u;
+    e = (int)ex - 150;
+  }
+  if (m == 0) return sign; /* signed zero */
+  /* binary16 keeps 11 significant bits; its smallest quantum is 2^-24 */
+  int top = bit_length_u32(m) - 1 + e; /* floor(log2 |x|) */
+  int q = top - 10;
+  if (q < -24) q = -24;
+  /* N = round_half_even(m * 2^(e - q)) */
+  uint64_t N;
+  int sh = q - e;
+  if (sh <= 0) {
+    N = (uint64_t)m << (-sh); /* exact; only when the value is already coarse */
+  } else if (sh > 40) {
+    N = 0;
+  } else {
+    uint64_t mm = m;
+    uint64_t whole = mm >> sh;
+    uint64_t rem = mm - (whole << sh);
+    uint64_t half = (uint64_t)1 << (sh - 1);
+    if (rem > half || (rem == half && (whole & 1u))) whole += 1;
+    N = whole;
+  }
+  if (N == 0) return sign;
+  /* re-normalise: a round-up can carry into the next binade */
+  while (N >= 2048) {
+    N >>= 1; /* N is even here: 2048 exactly */
+    q += 1;
+  }
+  if (N >= 1024) {
+    int biased = q + 25; /* value = N * 2^q = (N/1024) * 2^(q+10), exponent field q+10+15 */
+    if (biased >= 31) return sign | 0x7C00u;
+    return (uint16_t)(sign | ((uint32_t)biased << 10) | (uint32_t)(N - 1024));
+  }
+  /* subnormal: q == -24 */
+  return (uint16_t)(sign | (uint32_t)N);
+}
+
+float orc_f16_to_f32(uint16_t h) {
+  uint32_t sign = (h & 0x8000u) ? 1u : 0u;
+  uint32_t ex = (h >> 10) & 31u;
+  uint32_t f = h & 1023u;
+  float v;
+  if (ex == 0) {
+    v = ldexpf((float)f, -24);
+  } else if (ex == 31) {
+    if (f == 0) {
+      v = INFINITY;
+    } else {
+      uint32_t u = 0x7FC00000u | (f << 13);
+      memcpy(&v, &u, 4);
+      return sign ? -v : v;
+    }
+  } else {
+    v = ldexpf((float)(1024u + f), (int)ex - 25);
+  }
+  return sign ? -v : v;
+}
+
+void orc_f32_to_f16_array(const float* x, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_f16(x[i]);
+}
+
+void orc_f16_to_f32_array(const uint16_t* h, float* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f16_to_f32(h[i]);
+}
+
+float orc_fmaf(float a, float b, float c) { return fmaf(a, b, c); }
+
+/* ------------------------------------------------------------------------- */
+/* Walsh-Hadamard rotation (SAW-INT4, Abstract: block-diagonal Hadamard rotation;
+   Dual-QK, Abstract: the same orthogonal transform on queries and keys). */
+
+static int popcount_u32(uint32_t v) {
+  int c = 0;
+  while (v) {
+    c += (int)(v & 1u);
+    v >>= 1;
+  }
+  return c;
+}
+
+void orc_hadamard_sylvester(int n, int32_t* H) {
+  for (int i = 0; i < n; ++i)
+    for (int j = 0; j < n; ++j) H[i * n + j] = (popcount_u32((uint32_t)(i & j)) & 1) ? -1 : 1;
+}
+
+void orc_fwht_unnormalized(float* x, int n) {
+  for (int h = 1; h < n; h <<= 1)
+    for (int i = 0; i < n; ++i)
+      if (!(i & h)) {
+        float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+}
+
+float orc_rotation_constant(int n) {
+  /* 1/sqrt(2^k) = 2^(-k/2); for odd k it is sqrt(2) * 2^(-(k+1)/2), and scaling the
+     correctly rounded sqrt(2) by a power of two keeps it the nearest float. */
+  int k = 0;
+  while ((1 << k) < n) ++k;
+  if ((k & 1) == 0) return ldexpf(1.0f, -k / 2);
+  return ldexpf(sqrtf(2.0f), -(k + 1) / 2);
+}
+
+void orc_rotate(float* x, int d, int block) {
+  if (block <= 0) return;
+  float c = orc_rotation_constant(block);
+  for (int b = 0; b < d; b += block) {
+    orc_fwht_unnormalized(x + b, block);
+    for (int i = 0; i < block; ++i) x[b + i] = x[b + i] * c;
+  }
+}
+
+void orc_rotate_dense_f64(const double* x, double* y, int d, int block) {
+  if (block <= 0) {
+    for (int i = 0; i < d; ++i) y[i] = x[i];
+    return;
+  }
+  int32_t* H = (int32_t*)malloc(sizeof(int32_t) * (size_t)block * (size_t)block);
+  orc_hadamard_sylvester(block, H);
+  double inv = 1.0 / sqrt((double)block);
+  for (int b = 0; b < d; b += block)
+    for (int i = 0; i < block; ++i) {
+      double acc = 0.0;
+      for (int k = 0; k < block; ++k) acc += (double)H[i * block + k] * x[b + k];
+      y[b + i] = acc * inv;
+    }
+  free(H);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Asymmetric min/max group quantizer (InnerQ, Abstract: group-wise quantization with
+   asymmetric groups; SAW-INT4, Abstract: token-wise groups; the fp32 formula itself is
+   this library's reading, spelled out in kvq_oracle.h). */
+
+void orc_quantize_row(const float* x, int d, int bits, int group, uint8_t* codes, uint16_t* scale,
+                      uint16_t* zero) {
+  const int qmax = (1 << bits) - 1;
+  for (int g = 0; g < d / group; ++g) {
+    const float* xg = x + g * group;
+    float mn = xg[0], mx = xg[0];
+    for (int i = 1; i < group; ++i) {
+      if (xg[i] < mn) mn = xg[i];
+      if (xg[i] > mx) mx = xg[i];
+    }
+    float range = mx - mn;
+    float s32 = range / (float)qmax;
+    uint16_t s16 = orc_f32_to_f16(s32);
+    uint16_t z16 = orc_f32_to_f16(mn + 0.0f); /* +0.0f turns -0 into +0 */
+    scale[g] = s16;
+    zero[g] = z16;
+    float s = orc_f16_to_f32(s16), z = orc_f16_to_f32(z16);
+    if (s == 0.0f) {
+      for (int i = 0; i < group; ++i) codes[g * group + i] = 0;
+      continue;
+    }
+    float inv = 1.0f / s;
+    for (int i = 0; i < group; ++i) {
+      float diff = xg[i] - z;
+      float u = diff * inv;
+      float r = rintf(u);
+      int c = (int)r;
+      if (r < 0.0f) c = 0;
+      if (r > (float)qmax) c = qmax;
+      codes[g * group + i] = (uint8_t)c;
+    }
+  }
+}
+
+void orc_pack_row(const uint8_t* codes, int d, int bits, uint8_t* packed) {
+  int per_byte = 8 / bits;
+  memset(packed, 0, (size_t)(d * bits / 8));
+  for (int k = 0; k < d; ++k) packed[k / per_byte] |= (uint8_t)(codes[k] << (bits * (k % per_byte)));
+}
+
+void orc_unpack_row(const uint8_t* packed, int d, int bits, uint8_t* codes) {
+  int per_byte = 8 / bits;
+  uint8_t mask = (uint8_t)((1 << bits) - 1);
+  for (int k = 0; k < d; ++k) codes[k] = (packed[k / per_byte] >> (bits * (k % per_byte))) & mask;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Cache layout (SAW-INT4, Abstract: quantized rows go straight into a paged KV layout;
+   the byte layout itself is this library's reading, spelled out in kvq_oracle.h). */
+
+static int64_t row_bytes(const orc_cache* c) { return (int64_t)c->head_dim * c->bits / 8; }
+static int64_t n_groups(const orc_cache* c) { return c->head_dim / c->group_size; }
+
+int64_t orc_plane_bytes(const orc_cache* c, int plane) {
+  int64_t tokens = c->num_pages * c->num_kv_heads * (int64_t)c->page_size;
+  if (plane == 0 || plane == 2) return tokens * row_bytes(c);
+  return tokens * n_groups(c) * 4;
+}
+
+int orc_check_cache(const orc_cache* c) {
+  if (c->head_dim <= 0 || c->head_dim > 4096 || c->num_kv_heads <= 0 || c->num_pages <= 0) return 1;
+  if (c->bits != 2 && c->bits != 4) return 2;
+  if (c->group_size <= 0 || c->head_dim % c->group_size) return 3;
+  if (c->hadamard_block < 0) return 4;
+  if (c->hadamard_block > 0) {
+    if (c->hadamard_block & (c->hadamard_block - 1)) return 4;
+    if (c->head_dim % c->hadamard_block) return 4;
+  }
+  if (c->page_size <= 0 || c->page_size % 16) return 5;
+  if ((c->head_dim * c->bits) % 16) return 6;
+  return 0;
+}
+
+static int64_t k_code_off(const orc_cache* c, int64_t page, int h, int off) {
+  return ((page * c->num_kv_heads + h) * c->page_size + off) * row_bytes(c);
+}
+static int64_t k_meta_off(const orc_cache* c, int64_t page, int h, int off, int g) {
+  return (((page * c->num_kv_heads + h) * c->page_size + off) * n_groups(c) + g) * 4;
+}
+static int64_t v_word_off(const orc_cache* c, int64_t page, int h, int off, int w) {
+  int64_t base = (page * c->num_kv_heads + h) * c->page_size * row_bytes(c);
+  int64_t tile = (off / 16) * 16 * row_bytes(c);
+  return base + tile + ((int64_t)w * 16 + off % 16) * 2;
+}
+static int64_t v_meta_off(const orc_cache* c, int64_t page, int h, int off, int g) {
+  int64_t tiles = c->page_size / 16;
+  int64_t t = (page * c->num_kv_heads + h) * tiles + off / 16;
+  return ((t * n_groups(c) + g) * 16 + off % 16) * 4;
+}
+
+static void put_u16(uint8_t* p, uint16_t v) {
+  p[0] = (uint8_t)(v & 0xFF);
+  p[1] = (uint8_t)(v >> 8);
+}
+static uint16_t get_u16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+static void store_row(const orc_cache* c, int which, int64_t page, int h, int off, const uint8_t* packed,
+                      const uint16_t* scale, const uint16_t* zero) {
+  int64_t rb = row_bytes(c);
+  if (which == 0) {
+    memcpy(c->k_codes + k_code_off(c, page, h, off), packed, (size_t)rb);
+    for (int g = 0; g < n_groups(c); ++g) {
+      uint8_t* m = c->k_meta + k_meta_off(c, page, h, off, g);
+      put_u16(m, scale[g]);
+      put_u16(m + 2, zero[g]);
+    }
+  } else {
+    for (int w = 0; w < rb / 2; ++w) {
+      uint8_t* p = c->v_codes + v_word_off(c, page, h, off, w);
+      p[0] = packed[2 * w];
+      p[1] = packed[2 * w + 1];
+    }
+    for (int g = 0; g < n_groups(c); ++g) {
+      uint8_t* m = c->v_meta + v_meta_off(c, page, h, off, g);
+      put_u16(m, scale[g]);
+      put_u16(m + 2, zero[g]);
+    }
+  }
+}
+
+static void load_row(const orc_cache* c, int which, int64_t page, int h, int off, uint8_t* packed,
+                     uint16_t* scale, uint16_t* zero) {
+  int64_t rb = row_bytes(c);
+  if (which == 0) {
+    memcpy(packed, c->k_codes + k_code_off(c, page, h, off), (size_t)rb);
+    for (int g = 0; g < n_groups(c); ++g) {
+      const uint8_t* m = c->k_meta + k_meta_off(c, page, h, off, g);
+      scale[g] = get_u16(m);
+      zero[g] = get_u16(m + 2);
+    }
+  } else {
+    for (int w = 0; w < rb / 2; ++w) {
+      const uint8_t* p = c->v_codes + v_word_off(c, page, h, off, w);
+      packed[2 * w] = p[0];
+      packed[2 * w + 1] = p[1];
+    }
+    for (int g = 0; g < n_groups(c); ++g) {
+      const uint8_t* m = c->v_meta + v_meta_off(c, page, h, off, g);
+      scale[g] = get_u16(m);
+      zero[g] = get_u16(m + 2);
+    }
+  }
+}
+
+/* Dequantize one stored row into fp32: xhat = fmaf(code, scale, zero). */
+static void dequant_row(const orc_cache* c, int which, int64_t page, int h, int off, float* out) {
+  int d = c->head_dim;
+  int G = c->group_size;
+  uint8_t packed[4096];
+  uint8_t codes[4096];
+  uint16_t sc[4096], ze[4096];
+  load_row(c, which, page, h, off, packed, sc, ze);
+  orc_unpack_row(packed, d, c->bits, codes);
+  for (int i = 0; i < d; ++i) {
+    float s = orc_f16_to_f32(sc[i / G]);
+    float z = orc_f16_to_f32(ze[i / G]);
+    out[i] = fmaf((float)codes[i], s, z);
+  }
+}
+
+void orc_quantize_append(const orc_cache* c, const uint16_t* k_new, const uint16_t* v_new,
+                         const int64_t* slots, int64_t n) {
+  int d = c->head_dim;
+  float* x = (float*)malloc(sizeof(float) * (size_t)d);
+  uint8_t* codes = (uint8_t*)malloc((size_t)d);
+  uint8_t* packed = (uint8_t*)malloc((size_t)d);
+  uint16_t* sc = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)d);
+  uint16_t* ze = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)d);
+  for (int64_t r = 0; r < n; ++r) {
+    int64_t page = slots[r] / c->page_size;
+    int off = (int)(slots[r] % c->page_size);
+    for (int h = 0; h < c->num_kv_heads; ++h) {
+      for (int which = 0; which < 2; ++which) {
+        const uint16_t* src = (which == 0 ? k_new : v_new) + (r * c->num_kv_heads + h) * d;
+        for (int i = 0; i < d; ++i) x[i] = orc_bf16_to_f32(src[i]);
+        if (which == 0) orc_rotate(x, d, c->hadamard_block); /* keys only */
+        orc_quantize_row(x, d, c->bits, c->group_size, codes, sc, ze);
+        orc_pack_row(codes, d, c->bits, packed);
+        store_row(c, which, page, h, off, packed, sc, ze);
+      }
+    }
+  }
+  free(x);
+  free(codes);
+  free(packed);
+  free(sc);
+  free(ze);
+}
+
+void orc_dequantize(const orc_cache* c, int which, const int64_t* slots, int64_t n, float* out) {
+  int d = c->head_dim;
+  for (int64_t r = 0; r < n; ++r) {
+    int64_t page = slots[r] / c->page_size;
+    int off = (int)(slots[r] % c->page_size);
+    for (int h = 0; h < c->num_kv_heads; ++h)
+      dequant_row(c, which, page, h, off, out + (r * c->num_kv_heads + h) * d);
+  }
+}
+
+/* ------------------------------------------------------------------------- */
+/* Decode attention over the quantized cache, in fp64 (SAW-INT4, Abstract: attention runs
+   over the INT4 paged cache; Dual-QK, Abstract: queries get the keys' rotation so q.k is
+   preserved). Query head j reads KV head j / (Hq / Hkv). */
+
+void orc_decode_attention(const orc_cache* c, const uint16_t* q, int32_t batch, int32_t num_q_heads,
+                          const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                          double softmax_scale, double* out) {
+  int d = c->head_dim;
+  int P = c->page_size;
+  int ratio = num_q_heads / c->num_kv_heads;
+  double sigma = softmax_scale > 0.0 ? softmax_scale : 1.0 / sqrt((double)d);
+  double* qv = (double*)malloc(sizeof(double) * (size_t)d);
+  double* qr = (double*)malloc(sizeof(double) * (size_t)d);
+  float* row = (float*)malloc(sizeof(float) * (size_t)d);
+  double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int b = 0; b < batch; ++b) {
+    int T = seq_lens[b];
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    for (int j = 0; j < num_q_heads; ++j) {
+      int h = j / ratio;
+      double* o = out + ((int64_t)b * num_q_heads + j) * d;
+      if (T <= 0) {
+        for (int i = 0; i < d; ++i) o[i] = 0.0;
+        continue;
+      }
+      for (int i = 0; i < d; ++i) qv[i] = (double)orc_bf16_to_f32(q[((int64_t)b * num_q_heads + j) * d + i]);
+      orc_rotate_dense_f64(qv, qr, d, c->hadamard_block);
+      double m = -INFINITY;
+      for (int t = 0; t < T; ++t) {
+        int64_t page = block_table[(int64_t)b * max_pages + t / P];
+        dequant_row(c, 0, page, h, t % P, row);
+        double dot = 0.0;
+        for (int i = 0; i < d; ++i) dot += qr[i] * (double)row[i];
+        logit[t] = sigma * dot;
+        if (logit[t] > m) m = logit[t];
+      }
+      double den = 0.0;
+      for (int i = 0; i < d; ++i) acc[i] = 0.0;
+      for (int t = 0; t < T; ++t) {
+        double w = exp(logit[t] - m);
+        den += w;
+        int64_t page = block_table[(int64_t)b * max_pages + t / P];
+        dequant_row(c, 1, page, h, t % P, row);
+        for (int i = 0; i < d; ++i) acc[i] += w * (double)row[i];
+      }
+      for (int i = 0; i < d; ++i) o[i] = acc[i] / den;
+    }
+    free(logit);
+  }
+  free(qv);
+  free(qr);
+  free(row);
+  free(acc);
+}
+
+void orc_attention_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int32_t batch,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t seq_len,
+                        double softmax_scale, double* out) {
+  int d = head_dim;
+  int ratio = num_q_heads / num_kv_heads;
+  double sigma = softmax_scale > 0.0 ? softmax_scale : 1.0 / sqrt((double)d);
+  double* logit = (double*)malloc(sizeof(double) * (size_t)(seq_len > 0 ? seq_len : 1));
+  for (int b = 0; b < batch; ++b)
+    for (int j = 0; j < num_q_heads; ++j) {
+      int h = j / ratio;
+      double* o = out + ((int64_t)b * num_q_heads + j) * d;
+      const uint16_t* qq = q + ((int64_t)b * num_q_heads + j) * d;
+      for (int i = 0; i < d; ++i) o[i] = 0.0;
+      if (seq_len <= 0) continue;
+      double m = -INFINITY;
+      for (int t = 0; t < seq_len; ++t) {
+        const uint16_t* kk = k + (((int64_t)b * seq_len + t) * num_kv_heads + h) * d;
+        double dot = 0.0;
+        for (int i = 0; i < d; ++i) dot += (double)orc_bf16_to_f32(qq[i]) * (double)orc_bf16_to_f32(kk[i]);
+        logit[t] = sigma * dot;
+        if (logit[t] > m) m = logit[t];
+      }
+      double den = 0.0;
+      for (int t = 0; t < seq_len; ++t) {
+        double w = exp(logit[t] - m);
+        den += w;
+        const uint16_t* vv = v + (((int64_t)b * seq_len + t) * num_kv_heads + h) * d;
+        for (int i = 0; i < d; ++i) o[i] += w * (double)orc_bf16_to_f32(vv[i]);
+      }
+      for (int i = 0; i < d; ++i) o[i] /= den;
+    }
+  free(logit);
+}

@@ -1,0 +1,116 @@
+/*
+ * kvq oracle: a plain, slow, obviously-correct CPU reference for rotated low-bit
+ * KV-cache quantization and decode attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this library. The product path
+ * (libkvq.so and its Python binding) never links, imports or executes it, and it
+ * shares no code, header, table or constant with that path.
+ *
+ * What it follows (no page prints formulas or code; the readings are fixed here):
+ *  - SAW-INT4: System-Aware 4-Bit KV-Cache Quantization for Real-World LLM Serving,
+ *    Abstract: keys and values are quantized token-wise to 4 bits after a
+ *    block-diagonal Hadamard rotation, written straight into a paged KV layout.
+ *  - Dual-QK: Sharp Queries and Flat Keys for Prunable 2-bit KV Caches, Abstract:
+ *    the orthogonal transform applied to keys is applied to queries too, so
+ *    query-key dot products are unchanged; 2-bit caches are in scope.
+ *  - InnerQ: Hardware-Aware Tuning-Free Quantization of KV Cache for Large
+ *    Language Models, Abstract: group-wise quantization with asymmetric
+ *    (scale + zero) groups.
+ *  - "Is QuaRot superseded?" (scholarfeed), critique quotes: INT2 has four levels;
+ *    the INT2 methods compared sit at about 2.25 bits per element with group 128.
+ *
+ * Arithmetic contract (fp32, round-to-nearest-even everywhere, no fused ops
+ * except the single fmaf of dequantization):
+ *   rotate  : per block of n channels, butterfly with strides 1,2,4,..,n/2 in that
+ *             order, (a,b) -> (a+b, a-b); then multiply by c_n = fp32 nearest 1/sqrt(n).
+ *   group   : mn = min, mx = max; s32 = (mx - mn) / (2^bits - 1);
+ *             scale = fp16(s32); zero = fp16(mn + 0.0f).
+ *   codes   : s = float(scale), z = float(zero); s == 0 -> all 0; else
+ *             inv = 1/s; u = (x - z) * inv (two roundings); code = clamp(rint(u), 0, 2^bits-1).
+ *   dequant : xhat = fmaf(code, s, z).
+ *   attention (fp64): qr = dense (H/sqrt(n)) q per block; logit_t = sigma * qr . khat_t;
+ *             o = sum_t exp(logit_t - max) vhat_t / sum_t exp(logit_t - max).
+ *
+ * Cache layout (all byte offsets; RB = head_dim*bits/8 bytes per token row,
+ * NG = head_dim/group_size groups, P = page_size, a multiple of 16):
+ *   row base      u = page*Hkv + h
+ *   K codes       [u][P][RB]                  token-major; byte k holds channels
+ *                                             (INT4) 2k at bits 0-3, 2k+1 at 4-7;
+ *                                             (INT2) 4k+e at bits 2e.
+ *   K meta        [u][P][NG] x {u16 scale, u16 zero}  (scale in the low half)
+ *   V codes       [u][P/16][RB/2][16][2 bytes] the same packed row cut into 16-bit
+ *                                             words; word w of token o of a 16-token
+ *                                             tile sits at (w*16 + o)*2.
+ *   V meta        [u][P/16][NG][16] x {u16 scale, u16 zero}
+ */
+#ifndef KVQ_ORACLE_H
+#define KVQ_ORACLE_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- number formats (IEEE 754 binary16 / bfloat16, written from the definitions) ---- */
+float orc_bf16_to_f32(uint16_t b);
+uint16_t orc_f32_to_f16(float x); /* round to nearest, ties to even; subnormals; inf; nan */
+float orc_f16_to_f32(uint16_t h);
+void orc_f32_to_f16_array(const float* x, uint16_t* out, int64_t n);
+void orc_f16_to_f32_array(const uint16_t* h, float* out, int64_t n);
+float orc_fmaf(float a, float b, float c);
+
+/* ---- Walsh-Hadamard ---- */
+void orc_hadamard_sylvester(int n, int32_t* H);      /* H[i*n+j] = (-1)^popcount(i&j) */
+void orc_fwht_unnormalized(float* x, int n);         /* butterfly, ascending strides */
+float orc_rotation_constant(int n);                  /* fp32 nearest to 1/sqrt(n) */
+void orc_rotate(float* x, int d, int block);         /* block-diagonal rotation of d channels */
+void orc_rotate_dense_f64(const double* x, double* y, int d, int block);
+
+/* ---- quantizer (one token row of d channels, already rotated when needed) ---- */
+void orc_quantize_row(const float* x, int d, int bits, int group,
+                      uint8_t* codes, uint16_t* scale, uint16_t* zero);
+void orc_pack_row(const uint8_t* codes, int d, int bits, uint8_t* packed);
+void orc_unpack_row(const uint8_t* packed, int d, int bits, uint8_t* codes);
+
+/* ---- cache ---- */
+typedef struct {
+  int32_t head_dim;
+  int32_t num_kv_heads;
+  int32_t bits;
+  int32_t group_size;
+  int32_t hadamard_block; /* 0 = none */
+  int32_t page_size;
+  int64_t num_pages;
+  uint8_t* k_codes;
+  uint8_t* k_meta;
+  uint8_t* v_codes;
+  uint8_t* v_meta;
+} orc_cache;
+
+/* bytes of each plane: 0 = K codes, 1 = K meta, 2 = V codes, 3 = V meta */
+int64_t orc_plane_bytes(const orc_cache* c, int plane);
+/* returns 0 on success, nonzero when the description is outside the oracle's domain */
+int orc_check_cache(const orc_cache* c);
+
+/* k_new, v_new: bf16 [n][Hkv][d]; slots[r] = page*P + offset */
+void orc_quantize_append(const orc_cache* c, const uint16_t* k_new, const uint16_t* v_new,
+                         const int64_t* slots, int64_t n);
+/* which: 0 = K, 1 = V; out: float [n][Hkv][d] */
+void orc_dequantize(const orc_cache* c, int which, const int64_t* slots, int64_t n, float* out);
+/* q: bf16 [B][Hq][d]; block_table [B][max_pages]; out: double [B][Hq][d].
+   softmax_scale <= 0 means 1/sqrt(d). */
+void orc_decode_attention(const orc_cache* c, const uint16_t* q, int32_t batch, int32_t num_q_heads,
+                          const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                          double softmax_scale, double* out);
+/* fp64 attention over unquantized bf16 K/V ([B][T][Hkv][d] contiguous), no rotation:
+   the loss-free reference the quantized cache approximates (information only). */
+void orc_attention_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int32_t batch,
+                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t seq_len,
+                        double softmax_scale, double* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

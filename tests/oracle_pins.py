@@ -1,0 +1,458 @@
+"""Pins of the oracle: checks against facts fixed outside the oracle itself.
+
+Each ``check_*`` function raises AssertionError on failure. They run against the real
+oracle (tests/test_oracle_pins.py) and against deliberately broken copies of it
+(tests/test_oracle_mutants.py), which must each fail at least one check.
+
+What pins what (the pages print no worked example, so the pins are mathematics,
+IEEE definitions, library routines and hand derivations):
+  Hadamard           scipy.linalg.hadamard (Sylvester construction); H H^T = n I;
+                     butterfly == dense product exactly on small integers; involution.
+  rotation constant  nearest-float property of 1/sqrt(n), checked with exact rationals.
+  one-hot key        a single outlier channel spreads to +-A/sqrt(n) in every channel.
+  q.k invariance     (Rq).(Rk) == q.k (Dual-QK, Abstract: paired transform preserves q.k).
+  fp16 conversion    x86 F16C instruction (exhaustive over the finite range) and numpy.
+  fmaf               exact rational arithmetic rounded to nearest-even binary32.
+  quantizer          hand-derived worked examples (tests/golden); code range; round-trip
+                     bound |x - xhat| <= scale/2 (+ zero rounding + ulps).
+  packing            documented nibble/crumb order; the documented cache byte layout.
+  storage            bits per element = b + 32/G (2.25 at INT2 g128, as the QuaRot page's
+                     "BPE ~2.25" for INT2 group 128).
+  attention          torch scaled_dot_product_attention in fp64 on the oracle's own
+                     dequantized K/V with a scipy-rotated query; T=1 gives v0; q=0 or
+                     identical keys give the mean of V; page-permutation invariance.
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+import scipy.linalg
+import torch
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden", "quantizer_worked_examples.json")
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def nearest_f32(fr: Fraction) -> np.float32:
+    """Round an exact rational to the nearest binary32, ties to even (normal range)."""
+    f = np.float32(float(fr))  # candidate; may be off by one ulp through double rounding
+    best = None
+    for cand in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        err = abs(Fraction(float(cand)) - fr)
+        key = (err, int(np.array(cand, np.float32).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, cand)
+    return best[1]
+
+
+def _f16c_lib():
+    src = os.path.join(HERE, "native", "f16_check.c")
+    out = os.path.join(HERE, "native", "libf16_check.so")
+    if not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        subprocess.run(["gcc", "-O2", "-mf16c", "-fPIC", "-shared", src, "-o", out], check=True)
+    lib = ctypes.CDLL(out)
+    lib.f16_check_range.restype = ctypes.c_int64
+    lib.f16_check_range.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32,
+                                    ctypes.POINTER(ctypes.c_uint32)]
+    return lib
+
+
+# ----------------------------------------------------------------------------- Hadamard
+
+def check_hadamard_is_sylvester():
+    for n in (2, 4, 8, 16, 32, 64, 128, 256):
+        H = oracle.hadamard(n)
+        assert np.array_equal(H, scipy.linalg.hadamard(n)), n
+
+
+def check_hadamard_orthogonal():
+    for n in (2, 4, 8, 16, 32, 64, 128, 256):
+        H = oracle.hadamard(n).astype(np.int64)
+        assert np.array_equal(H @ H.T, n * np.eye(n, dtype=np.int64)), n
+
+
+def check_fwht_equals_dense_on_integers():
+    rng = np.random.default_rng(1)
+    for n in (2, 8, 32, 128):
+        Hs = scipy.linalg.hadamard(n).astype(np.int64)
+        for _ in range(20):
+            x = rng.integers(-(1 << 16), (1 << 16) + 1, n)
+            got = oracle.fwht_unnormalized(x.astype(np.float32)).astype(np.float64)
+            assert np.array_equal(got, (Hs @ x).astype(np.float64)), n
+
+
+def check_fwht_involution():
+    rng = np.random.default_rng(2)
+    for n in (4, 64, 128):
+        x = rng.integers(-1000, 1001, n).astype(np.float32)
+        y = oracle.fwht_unnormalized(oracle.fwht_unnormalized(x))
+        assert np.array_equal(y, n * x)
+
+
+def check_rotation_constant():
+    for k in range(1, 9):
+        n = 1 << k
+        c = np.float32(oracle.rotation_constant(n))
+        # c is the float nearest 1/sqrt(n): |c^2 n - 1| is minimal among c and its neighbours
+        def err(v):
+            return abs(Fraction(float(v)) ** 2 * n - 1)
+        for nb in (np.nextafter(c, np.float32(0)), np.nextafter(c, np.float32(1))):
+            assert err(c) < err(nb), (n, c)
+    assert np.array(np.float32(oracle.rotation_constant(128))).view(np.uint32) == 0x3DB504F3
+
+
+def check_rotate_one_hot():
+    n = 128
+    H = scipy.linalg.hadamard(n)
+    for c in (0, 5, 77, 127):
+        for A in (10.0, -3.5):
+            x = np.zeros(n, np.float32)
+            x[c] = A
+            y = oracle.rotate(x, n)
+            mag = np.float32(A) * np.float32(oracle.rotation_constant(n))
+            assert np.array_equal(y, (H[:, c] * mag).astype(np.float32)), (c, A)
+
+
+def check_rotate_matches_dense():
+    rng = np.random.default_rng(3)
+    n = 128
+    R = scipy.linalg.hadamard(n) / np.sqrt(n)
+    for block in (32, 64, 128):
+        Rb = np.kron(np.eye(n // block), scipy.linalg.hadamard(block) / np.sqrt(block))
+        for _ in range(10):
+            x = rng.standard_normal(n).astype(np.float32)
+            y32 = oracle.rotate(x, block).astype(np.float64)
+            y64 = oracle.rotate_dense_f64(x.astype(np.float64), block)
+            ref = Rb @ x.astype(np.float64)
+            assert np.max(np.abs(y64 - ref)) < 1e-13
+            assert np.max(np.abs(y32 - ref)) < 1e-5 * np.max(np.abs(ref)) + 1e-6
+    assert R.shape == (n, n)
+
+
+def check_qk_invariance():
+    rng = np.random.default_rng(4)
+    for _ in range(20):
+        q = rng.standard_normal(128)
+        k = rng.standard_normal(128) * np.where(rng.random(128) < 0.03, 10.0, 1.0)
+        rq = oracle.rotate_dense_f64(q, 128)
+        rk = oracle.rotate_dense_f64(k, 128)
+        assert abs(rq @ rk - q @ k) <= 1e-12 * np.linalg.norm(q) * np.linalg.norm(k)
+        rq32 = oracle.rotate(q.astype(np.float32), 128).astype(np.float64)
+        rk32 = oracle.rotate(k.astype(np.float32), 128).astype(np.float64)
+        q32, k32 = q.astype(np.float32).astype(np.float64), k.astype(np.float32).astype(np.float64)
+        assert abs(rq32 @ rk32 - q32 @ k32) <= 1e-5 * np.linalg.norm(q) * np.linalg.norm(k)
+
+
+# ----------------------------------------------------------------------------- formats
+
+def check_f16_conversion_f16c(full: bool = True):
+    """Every binary32 whose binary16 rounding is not trivially 0 or inf, against F16C."""
+    lib = _f16c_lib()
+    fn = ctypes.cast(oracle.load().orc_f32_to_f16, ctypes.c_void_p)
+    first = ctypes.c_uint32(0)
+    if full:
+        ranges = [(0x33000000, 0x47800000)]   # [2^-25, 2^16]: every rounding case
+    else:
+        ranges = [(0x33000000 + i * 0x100000, 0x33000000 + i * 0x100000 + 0x3FFF) for i in range(0x148)]
+    # below 2^-25 everything rounds to zero, above 2^16 to infinity: check the edges
+    ranges += [(0x0, 0x2000), (0x32FF0000, 0x33000000), (0x47800000, 0x47810000),
+               (0x7F7FF000, 0x7F800010), (0x7FC00000, 0x7FC00010)]
+    for lo, hi in ranges:
+        bad = lib.f16_check_range(fn, lo, hi, ctypes.byref(first))
+        assert bad == 0, f"{bad} mismatches, first 0x{first.value:08x}"
+
+
+def check_f16_conversion_numpy():
+    rng = np.random.default_rng(5)
+    u = rng.integers(0, 1 << 32, 1 << 22, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32)
+    finite = np.isfinite(x)
+    got = oracle.f32_to_f16_bits(x[finite])
+    with np.errstate(over="ignore"):
+        ref = x[finite].astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, ref)
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    back = oracle.f16_bits_to_f32(h)
+    ref32 = h.view(np.float16).astype(np.float32)
+    nan = np.isnan(ref32)
+    assert np.array_equal(np.isnan(back), nan)
+    assert np.array_equal(back[~nan].view(np.uint32), ref32[~nan].view(np.uint32))
+
+
+def check_fmaf_exact():
+    rng = np.random.default_rng(6)
+    for _ in range(3000):
+        c = float(rng.integers(0, 16))
+        s = float(np.float16(abs(rng.standard_normal()) * 0.3))
+        z = float(np.float16(rng.standard_normal() * 2))
+        got = np.float32(oracle.fmaf(c, s, z))
+        ref = nearest_f32(Fraction(c) * Fraction(s) + Fraction(z))
+        assert got == ref or (got == 0 and ref == 0), (c, s, z, got, ref)
+    # a case where fma and multiply-then-add differ
+    a, b, cc = np.float32(1 + 2 ** -12), np.float32(1 + 2 ** -12), np.float32(-1)
+    exact = Fraction(float(a)) * Fraction(float(b)) + Fraction(float(cc))
+    assert np.float32(oracle.fmaf(float(a), float(b), float(cc))) == nearest_f32(exact)
+
+
+# ----------------------------------------------------------------------------- quantizer
+
+def _golden_cases():
+    with open(GOLDEN) as f:
+        data = json.load(f)
+    for c in data["cases"]:
+        if "x_rule" in c:
+            pat_x = [0, 3, 1, 2, 0.5, 1.5, 2.5, 2.4]
+            pat_c = [0, 3, 1, 2, 0, 2, 2, 2]
+            x = [pat_x[i % 8] for i in range(c["group"])]
+            codes = [pat_c[i % 8] for i in range(c["group"])]
+        else:
+            x, codes = c["x"], c["codes"]
+        yield c["name"], c["bits"], c["group"], np.array(x, np.float32), np.array(codes, np.uint8), \
+            int(c["scale_bits"], 16), int(c["zero_bits"], 16)
+
+
+def check_quantizer_worked_examples():
+    for name, bits, group, x, codes, sb, zb in _golden_cases():
+        got_c, got_s, got_z = oracle.quantize_row(x, bits, group)
+        assert got_s[0] == sb, (name, hex(got_s[0]), hex(sb))
+        assert got_z[0] == zb, (name, hex(got_z[0]), hex(zb))
+        assert np.array_equal(got_c, codes), (name, got_c, codes)
+
+
+def check_codes_in_range_and_extremes():
+    rng = np.random.default_rng(7)
+    for bits in (2, 4):
+        for group in (32, 64, 128):
+            for _ in range(50):
+                x = (rng.standard_normal(128) * np.exp(rng.standard_normal())).astype(np.float32)
+                codes, sc, ze = oracle.quantize_row(x, bits, group)
+                assert codes.max() <= (1 << bits) - 1
+                for g in range(128 // group):
+                    cg = codes[g * group:(g + 1) * group]
+                    xg = x[g * group:(g + 1) * group]
+                    # the group minimum maps to code 0 and the maximum to the top code
+                    # unless fp16 rounding of scale/zero moves them by one level
+                    assert cg[np.argmin(xg)] <= 1 and cg[np.argmax(xg)] >= (1 << bits) - 2
+
+
+def check_codes_in_range_offset_groups():
+    """Large mean, small range: the fp16 zero can land above the minimum, so the
+    unclamped code would be negative; codes must still lie in [0, 2^bits-1] and the
+    round trip obey the bound with the zero's rounding included."""
+    rng = np.random.default_rng(17)
+    for bits in (2, 4):
+        for base in (1000.1, -777.7, 3.3e4):
+            x = (base + rng.random(128) * 0.9).astype(np.float32)
+            codes, sc, ze = oracle.quantize_row(x, bits, 32)
+            assert codes.max() <= (1 << bits) - 1
+            s = sc.view(np.float16).astype(np.float64)
+            z = ze.view(np.float16).astype(np.float64)
+            for g in range(4):
+                xg = x[g * 32:(g + 1) * 32].astype(np.float64)
+                xh = np.array([oracle.fmaf(float(c), float(s[g]), float(z[g])) for c in codes[g * 32:(g + 1) * 32]])
+                ulp = float(np.spacing(np.float32(np.max(np.abs(xg)))))
+                assert np.all(np.abs(xg - xh) <= s[g] / 2 + abs(xg.min() - z[g]) + 4 * ulp)
+
+
+def check_round_trip_bound():
+    """|x - xhat| <= scale/2 + |min - zero| + 4 ulp(max|x|), per element."""
+    rng = np.random.default_rng(8)
+    for bits in (2, 4):
+        for group in (32, 64, 128):
+            for trial in range(100):
+                x = rng.standard_normal(128).astype(np.float32)
+                if trial % 3 == 0:
+                    x[rng.integers(0, 128, 3)] *= 10
+                codes, sc, ze = oracle.quantize_row(x, bits, group)
+                s = sc.view(np.float16).astype(np.float64)
+                z = ze.view(np.float16).astype(np.float64)
+                for g in range(128 // group):
+                    xg = x[g * group:(g + 1) * group].astype(np.float64)
+                    xh = np.array([oracle.fmaf(float(c), float(s[g]), float(z[g]))
+                                   for c in codes[g * group:(g + 1) * group]])
+                    ulp = np.spacing(np.float32(np.max(np.abs(xg)))).astype(np.float64)
+                    bound = s[g] / 2 + abs(xg.min() - z[g]) + 4 * ulp
+                    assert np.all(np.abs(xg - xh) <= bound), (bits, group, trial)
+
+
+def check_packing_order():
+    codes4 = np.arange(16, dtype=np.uint8)
+    assert list(oracle.pack_row(codes4, 4)) == [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]
+    codes2 = np.array([0, 1, 2, 3, 3, 2, 1, 0], np.uint8)
+    assert list(oracle.pack_row(codes2, 2)) == [0b11100100, 0b00011011]
+    rng = np.random.default_rng(9)
+    for bits in (2, 4):
+        c = rng.integers(0, 1 << bits, 128).astype(np.uint8)
+        assert np.array_equal(oracle.unpack_row(oracle.pack_row(c, bits), 128, bits), c)
+
+
+def check_storage_bits_per_element():
+    assert oracle.bits_per_element(128, 2, 128) == 2.25
+    assert oracle.bits_per_element(128, 4, 32) == 5.0
+    assert oracle.bits_per_element(128, 4, 64) == 4.5
+
+
+def _bf16(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def check_cache_layout_bytes():
+    """One token with known codes lands at the documented byte offsets."""
+    d, Hkv, P = 128, 2, 32
+    c = oracle.Cache(d, Hkv, 4, 32, 0, P, 3)
+    # K row for kv head 1: group g holds values 0..15,15..0 -> scale 1, zero 0
+    ramp = np.concatenate([np.arange(16), np.arange(15, -1, -1)]).astype(np.float32)
+    x = np.tile(ramp, 4)
+    k = np.zeros((1, Hkv, d), np.float32)
+    v = np.zeros((1, Hkv, d), np.float32)
+    k[0, 1] = x
+    v[0, 1] = x
+    page, off = 2, 21
+    c.append(_bf16(k), _bf16(v), np.array([page * P + off]))
+    packed = oracle.pack_row(x.astype(np.uint8), 4)
+    rb = d * 4 // 8
+    kbase = ((page * Hkv + 1) * P + off) * rb
+    assert np.array_equal(c.k_codes[kbase:kbase + rb], packed)
+    kmeta = ((page * Hkv + 1) * P + off) * 4 * 4
+    assert list(c.k_meta[kmeta:kmeta + 4]) == [0x00, 0x3C, 0x00, 0x00]  # scale 1.0, zero 0.0
+    vbase = (page * Hkv + 1) * P * rb + (off // 16) * 16 * rb
+    for w in range(rb // 2):
+        o = vbase + (w * 16 + off % 16) * 2
+        assert list(c.v_codes[o:o + 2]) == list(packed[2 * w:2 * w + 2]), w
+    vmeta = (((page * Hkv + 1) * (P // 16) + off // 16) * 4 + 3) * 16 + off % 16
+    assert list(c.v_meta[vmeta * 4:vmeta * 4 + 4]) == [0x00, 0x3C, 0x00, 0x00]
+
+
+def check_v_not_rotated_and_k_rotated():
+    """Dequantized V is within the round-trip bound of raw V; dequantized K of R k."""
+    rng = np.random.default_rng(10)
+    d, Hkv, n = 128, 2, 8
+    c = oracle.Cache(d, Hkv, 4, 32, 128, 16, 1)
+    k = _bf16(rng.standard_normal((n, Hkv, d)))
+    v = _bf16(rng.standard_normal((n, Hkv, d)))
+    slots = np.arange(n)
+    c.append(k, v, slots)
+    R = scipy.linalg.hadamard(d) / np.sqrt(d)
+    kh, vh = c.dequantize(0, slots), c.dequantize(1, slots)
+    kf, vf = oracle.bf16_to_f32(k).astype(np.float64), oracle.bf16_to_f32(v).astype(np.float64)
+    krot = kf @ R.T
+    for ref, got in ((krot, kh), (vf, vh)):
+        for g in range(4):
+            sl = slice(32 * g, 32 * (g + 1))
+            rng_g = ref[..., sl].max(-1) - ref[..., sl].min(-1)
+            assert np.all(np.abs(ref[..., sl] - got[..., sl]).max(-1) <= rng_g / 15 * 0.5 * 1.01 + 1e-3)
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _rand_cache(rng, d=128, Hkv=2, T=40, bits=4, G=32, hb=128, P=16, paged_perm=None, B=2):
+    pages_per = (T + P - 1) // P
+    num_pages = B * pages_per
+    c = oracle.Cache(d, Hkv, bits, G, hb, P, num_pages)
+    perm = np.arange(num_pages) if paged_perm is None else paged_perm
+    bt = perm.reshape(B, pages_per).astype(np.int32)
+    k = _bf16(rng.standard_normal((B, T, Hkv, d)))
+    v = _bf16(rng.standard_normal((B, T, Hkv, d)))
+    for b in range(B):
+        t = np.arange(T)
+        slots = bt[b][t // P].astype(np.int64) * P + t % P
+        c.append(k[b], v[b], slots)
+    return c, bt, k, v
+
+
+def check_attention_matches_sdpa():
+    rng = np.random.default_rng(11)
+    for hb, bits, G in ((128, 4, 32), (0, 4, 64), (128, 2, 128), (64, 4, 32)):
+        B, Hq, Hkv, d, T, P = 2, 8, 2, 128, 45, 16
+        c, bt, k, v = _rand_cache(rng, d, Hkv, T, bits, G, hb, P, B=B)
+        q = _bf16(rng.standard_normal((B, Hq, d)))
+        lens = np.array([T, 17], np.int32)
+        out = c.decode(q, bt, lens, 0.0)
+        # independent: scipy Hadamard, oracle-free dequant via page table, torch SDPA in fp64
+        blk = hb if hb else d
+        R = np.kron(np.eye(d // blk), scipy.linalg.hadamard(blk) / np.sqrt(blk)) if hb else np.eye(d)
+        for b in range(B):
+            t = np.arange(lens[b])
+            slots = bt[b][t // P].astype(np.int64) * P + t % P
+            kh = torch.from_numpy(c.dequantize(0, slots).astype(np.float64))  # [T][Hkv][d]
+            vh = torch.from_numpy(c.dequantize(1, slots).astype(np.float64))
+            qf = oracle.bf16_to_f32(q[b]).astype(np.float64) @ R.T            # [Hq][d]
+            qt = torch.from_numpy(qf).reshape(Hkv, Hq // Hkv, 1, d)
+            kt = kh.permute(1, 0, 2).reshape(Hkv, 1, -1, d).contiguous()
+            vt = vh.permute(1, 0, 2).reshape(Hkv, 1, -1, d).contiguous()
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)  # scale 1/sqrt(d)
+            ref = ref.reshape(Hq, d).numpy()
+            assert np.max(np.abs(out[b] - ref)) < 1e-12, (hb, bits, G, b)
+
+
+def check_attention_special_cases():
+    rng = np.random.default_rng(12)
+    B, Hq, Hkv, d, P = 1, 4, 1, 128, 16
+    c, bt, k, v = _rand_cache(rng, d, Hkv, 32, 4, 32, 128, P, B=B)
+    q = _bf16(rng.standard_normal((B, Hq, d)))
+    # T = 1: output is the first dequantized value row exactly
+    out = c.decode(q, bt, np.array([1], np.int32))
+    v0 = c.dequantize(1, np.array([bt[0][0] * P]))[0, 0].astype(np.float64)
+    assert np.all(out[0] == v0)
+    # q = 0: uniform weights -> mean of dequantized V
+    out = c.decode(np.zeros_like(q), bt, np.array([32], np.int32))
+    slots = bt[0][np.arange(32) // P].astype(np.int64) * P + np.arange(32) % P
+    vm = c.dequantize(1, slots)[:, 0].astype(np.float64).mean(0)
+    assert np.max(np.abs(out[0] - vm)) < 1e-12
+    # seq_len 0: zeros
+    out = c.decode(q, bt, np.array([0], np.int32))
+    assert np.all(out == 0)
+    # identical keys: uniform weights again
+    c2 = oracle.Cache(d, 1, 4, 32, 128, P, 2)
+    kk = np.repeat(_bf16(rng.standard_normal((1, 1, d))), 32, axis=0)
+    vv = _bf16(rng.standard_normal((32, 1, d)))
+    c2.append(kk, vv, np.arange(32))
+    out = c2.decode(q, np.array([[0, 1]], np.int32), np.array([32], np.int32))
+    vm = c2.dequantize(1, np.arange(32))[:, 0].astype(np.float64).mean(0)
+    assert np.max(np.abs(out[0] - vm)) < 1e-12
+
+
+def check_attention_page_permutation():
+    B, T, P = 2, 64, 16
+    pages = B * T // P
+    outs = []
+    for perm in (np.arange(pages), np.random.default_rng(13).permutation(pages)):
+        rng = np.random.default_rng(14)
+        c, bt, k, v = _rand_cache(rng, 128, 2, T, 4, 32, 128, P, paged_perm=perm, B=B)
+        q = _bf16(np.random.default_rng(15).standard_normal((B, 8, 128)))
+        outs.append(c.decode(q, bt, np.array([T, T - 5], np.int32)))
+    assert np.array_equal(outs[0], outs[1])
+
+
+ALL_CHECKS = [
+    check_hadamard_is_sylvester,
+    check_hadamard_orthogonal,
+    check_fwht_equals_dense_on_integers,
+    check_fwht_involution,
+    check_rotation_constant,
+    check_rotate_one_hot,
+    check_rotate_matches_dense,
+    check_qk_invariance,
+    check_f16_conversion_numpy,
+    check_fmaf_exact,
+    check_quantizer_worked_examples,
+    check_codes_in_range_and_extremes,
+    check_codes_in_range_offset_groups,
+    check_round_trip_bound,
+    check_packing_order,
+    check_storage_bits_per_element,
+    check_cache_layout_bytes,
+    check_v_not_rotated_and_k_rotated,
+    check_attention_matches_sdpa,
+    check_attention_special_cases,
+    check_attention_page_permutation,
+]
