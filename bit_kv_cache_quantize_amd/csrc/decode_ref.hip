@@ -1,0 +1,199 @@
+// Split-K decode attention, plain VALU formulation, and the split combine.
+//
+// SAW-INT4 (Abstract): attention runs directly over the paged low-bit cache.
+// Dual-QK (Abstract): the query gets the keys' rotation so q.k is unchanged.
+// The split-K / log-sum-exp combine structure is the standard flash-decoding
+// arrangement; partials are (unnormalised o[d], running max m, running sum l) with
+// logits in the exp2 domain (the query is pre-scaled by softmax_scale * log2 e).
+//
+// This kernel is the straightforward one: one workgroup per (sequence, kv head,
+// partition), fp32 dequantization fma(code, scale, zero) per element, fp32 dot
+// products, scores staged in LDS. It is kept as an independent GPU formulation that
+// the tests compare the MFMA kernel against; the library's decode call uses the MFMA
+// kernel for every supported configuration.
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kMaxSplit = 2048;  // tokens per partition this kernel stages in LDS
+constexpr int kThreads = 256;
+
+template <int BITS, int G>
+__global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(DecodeArgs a) {
+  constexpr int kD = 128;
+  constexpr int kMask = (1 << BITS) - 1;
+  const DevCache& c = a.c;
+  const int unit = blockIdx.x;
+  const int split = unit % a.num_splits;
+  const int bh = unit / a.num_splits;
+  const int h = bh % c.hkv;
+  const int b = bh / c.hkv;
+  const int T = a.seq_lens[b];
+  const int start = split * a.split_len;
+  if (start >= T) return;
+  const int end = min(T, start + a.split_len);
+  const int n = end - start;
+  const int R = a.ratio;
+  const int tid = threadIdx.x;
+
+  __shared__ float qs[4][kD];
+  __shared__ float sc[4][kMaxSplit];
+  __shared__ float red[4][kThreads];
+  __shared__ float stat[2][4];
+
+  for (int idx = tid; idx < R * kD; idx += kThreads) {
+    const int j = idx / kD, i = idx % kD;
+    const uint16_t bits = a.q[(static_cast<int64_t>(b) * a.num_q_heads + h * R + j) * kD + i];
+    qs[j][i] = __uint_as_float(static_cast<uint32_t>(bits) << 16);
+  }
+  __syncthreads();
+  if (a.hblock > 0) {
+    for (int s = 1; s < a.hblock; s <<= 1) {
+      for (int idx = tid; idx < R * (kD / 2); idx += kThreads) {
+        const int j = idx / (kD / 2), p = idx % (kD / 2);
+        const int i = (p / s) * 2 * s + (p % s);
+        const float x0 = qs[j][i], x1 = qs[j][i + s];
+        qs[j][i] = x0 + x1;
+        qs[j][i + s] = x0 - x1;
+      }
+      __syncthreads();
+    }
+  }
+  for (int idx = tid; idx < R * kD; idx += kThreads) {
+    const int j = idx / kD, i = idx % kD;
+    qs[j][i] = qs[j][i] * (a.hblock > 0 ? a.rot_c : 1.0f) * a.qscale;
+  }
+  __syncthreads();
+
+  // scores: one token per thread
+  for (int t = start + tid; t < end; t += kThreads) {
+    const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + t / c.page];
+    const int off = t % c.page;
+    const int64_t u = page * c.hkv + h;
+    const uint8_t* codes = c.kc + (u * c.page + off) * c.row_bytes;
+    const uint32_t* meta = c.km + (u * c.page + off) * c.ngroups;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kD; ++i) {
+      const uint32_t byte = codes[i * BITS / 8];
+      const uint32_t code = (byte >> ((i * BITS) % 8)) & kMask;
+      const uint32_t m = meta[i / G];
+      const float khat = __builtin_fmaf(static_cast<float>(code), f16_bits_to_float(m & 0xFFFFu),
+                                        f16_bits_to_float(m >> 16));
+      for (int j = 0; j < R; ++j) acc[j] = __builtin_fmaf(qs[j][i], khat, acc[j]);
+    }
+    for (int j = 0; j < R; ++j) sc[j][t - start] = acc[j];
+  }
+  __syncthreads();
+
+  // max and sum per head
+  for (int j = 0; j < R; ++j) {
+    float m = -INFINITY;
+    for (int t = tid; t < n; t += kThreads) m = fmaxf(m, sc[j][t]);
+    red[j][tid] = m;
+  }
+  __syncthreads();
+  if (tid < R) {
+    float m = -INFINITY;
+    for (int k = 0; k < kThreads; ++k) m = fmaxf(m, red[tid][k]);
+    stat[0][tid] = m;
+  }
+  __syncthreads();
+  for (int j = 0; j < R; ++j) {
+    float l = 0.f;
+    for (int t = tid; t < n; t += kThreads) {
+      const float p = exp2f(sc[j][t] - stat[0][j]);
+      sc[j][t] = p;
+      l += p;
+    }
+    red[j][tid] = l;
+  }
+  __syncthreads();
+  if (tid < R) {
+    float l = 0.f;
+    for (int k = 0; k < kThreads; ++k) l += red[tid][k];
+    stat[1][tid] = l;
+  }
+  __syncthreads();
+
+  // p . vhat: each thread owns (head, channel) pairs
+  for (int idx = tid; idx < R * kD; idx += kThreads) {
+    const int j = idx / kD, i = idx % kD;
+    const int w = i * BITS / 16;            // 16-bit word holding channel i
+    const int sh = (i * BITS) % 16;
+    float o = 0.f;
+    for (int t = start; t < end; ++t) {
+      const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + t / c.page];
+      const int off = t % c.page;
+      const int64_t u = page * c.hkv + h;
+      const int64_t tile = off >> 4;
+      const uint16_t* words =
+          reinterpret_cast<const uint16_t*>(c.vc + u * c.page * c.row_bytes + tile * 16 * c.row_bytes);
+      const uint32_t code = (static_cast<uint32_t>(words[w * 16 + (off & 15)]) >> sh) & kMask;
+      const uint32_t m = c.vm[((u * (c.page >> 4) + tile) * c.ngroups + i / G) * 16 + (off & 15)];
+      const float vhat = __builtin_fmaf(static_cast<float>(code), f16_bits_to_float(m & 0xFFFFu),
+                                        f16_bits_to_float(m >> 16));
+      o = __builtin_fmaf(sc[j][t - start], vhat, o);
+    }
+    float* part = a.partials + ((static_cast<int64_t>(b) * a.num_q_heads + h * R + j) * a.num_splits + split) * (kD + 2);
+    part[i] = o;
+    if (i == 0) {
+      part[kD] = stat[0][j];
+      part[kD + 1] = stat[1][j];
+    }
+  }
+}
+
+// Log-sum-exp merge of the partitions of one (sequence, query head).
+__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ partials,
+                                                      const int32_t* __restrict__ seq_lens, int num_q_heads,
+                                                      int num_splits, int split_len, float* __restrict__ out) {
+  constexpr int kD = 128;
+  const int bj = blockIdx.x;
+  const int b = bj / num_q_heads;
+  const int i = threadIdx.x;
+  const int T = seq_lens[b];
+  if (T <= 0) {
+    out[static_cast<int64_t>(bj) * kD + i] = 0.f;
+    return;
+  }
+  const int ns = min(num_splits, (T + split_len - 1) / split_len);
+  const float* base = partials + static_cast<int64_t>(bj) * num_splits * (kD + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * (kD + 2) + kD]);
+  float L = 0.f, o = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float* p = base + s * (kD + 2);
+    const float w = exp2f(p[kD] - M);
+    L = __builtin_fmaf(p[kD + 1], w, L);
+    o = __builtin_fmaf(p[i], w, o);
+  }
+  out[static_cast<int64_t>(bj) * kD + i] = o / L;
+}
+
+}  // namespace
+
+hipError_t launch_decode_split_reference(const DecodeArgs& a, const Geometry& g, hipStream_t stream) {
+  if (a.split_len > kMaxSplit) return hipErrorInvalidValue;
+  const int64_t units = static_cast<int64_t>(a.batch) * g.hkv * a.num_splits;
+  if (units > 0x7FFFFFFF) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(units)), block(kThreads);
+#define KVQ_DR(B, GS)                                                                                  \
+  if (g.bits == B && g.group == GS) {                                                                  \
+    hipLaunchKernelGGL((decode_split_reference_kernel<B, GS>), grid, block, 0, stream, a);            \
+    return hipGetLastError();                                                                          \
+  }
+  KVQ_DR(4, 32) KVQ_DR(4, 64) KVQ_DR(4, 128) KVQ_DR(2, 32) KVQ_DR(2, 64) KVQ_DR(2, 128)
+#undef KVQ_DR
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t stream) {
+  (void)g;
+  dim3 grid(static_cast<unsigned>(a.batch * a.num_q_heads)), block(128);
+  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, a.partials, a.seq_lens, a.num_q_heads, a.num_splits,
+                     a.split_len, a.out);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,178 @@
+// The kvq C ABI: host-side validation, split sizing and kernel dispatch.
+// Declarations, argument meaning, layout and error behaviour: include/kvq.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+Splits splits_for(const Geometry& g, int32_t batch, int32_t num_q_heads, int32_t max_seq_len, int32_t requested) {
+  return choose_splits(g, batch, num_q_heads, max_seq_len, requested, device_cus());
+}
+
+kvq_status decode_impl(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                       const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                       int32_t max_seq_len, float softmax_scale, int32_t num_splits, void* workspace,
+                       size_t workspace_bytes_given, float* out, void* stream, void* ev_begin, void* ev_end,
+                       bool reference) {
+  Geometry g;
+  kvq_status st = check_decode(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                               max_seq_len, num_splits, workspace, out, &g);
+  if (st != KVQ_OK || batch == 0) return st;
+  const Splits sp = splits_for(g, batch, num_q_heads, max_seq_len, num_splits);
+  if (workspace_bytes_given < workspace_bytes(g, batch, num_q_heads, sp)) return KVQ_ERR_WORKSPACE;
+  if (reference && sp.split_len > 2048) return KVQ_ERR_UNSUPPORTED;
+
+  DecodeArgs a;
+  a.c = dev_cache(cache, g);
+  a.q = static_cast<const uint16_t*>(q);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.partials = static_cast<float*>(workspace);
+  a.out = out;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.ratio = num_q_heads / g.hkv;
+  a.max_pages = max_pages_per_seq;
+  a.split_len = sp.split_len;
+  a.num_splits = sp.num_splits;
+  a.hblock = g.hblock;
+  a.rot_c = g.hblock > 0 ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(g.hblock))) : 1.0f;
+  const double scale = softmax_scale > 0.f ? softmax_scale : 1.0 / std::sqrt(static_cast<double>(g.d));
+  a.qscale = static_cast<float>(scale * 1.4426950408889634);  // log2(e)
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return KVQ_ERR_HIP;
+  hipError_t e = reference ? launch_decode_split_reference(a, g, s) : launch_decode_split(a, g, s);
+  if (e != hipSuccess) return KVQ_ERR_HIP;
+  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return KVQ_ERR_HIP;
+  e = launch_combine(a, g, s);
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+int64_t kvq_cache_plane_bytes(const kvq_cache* cache, int32_t plane) {
+  Geometry g;
+  const kvq_status st = check_cache(cache, false, &g);
+  if (st == KVQ_ERR_INVALID || !cache) return -1;
+  if (st == KVQ_ERR_UNSUPPORTED && cache->bits != 2 && cache->bits != 4) return -1;
+  g.d = cache->head_dim;
+  g.hkv = cache->num_kv_heads;
+  g.bits = cache->bits;
+  g.group = cache->group_size;
+  g.ngroups = cache->head_dim / cache->group_size;
+  g.page = cache->page_size;
+  g.row_bytes = cache->head_dim * cache->bits / 8;
+  g.num_pages = cache->num_pages;
+  return plane_bytes(g, plane);
+}
+
+kvq_status kvq_quantize_append(const kvq_cache* cache, const void* k_new, const void* v_new, const int64_t* slots,
+                               int64_t n_new, void* stream) {
+  Geometry g;
+  kvq_status st = check_append(cache, k_new, v_new, slots, n_new, &g);
+  if (st != KVQ_OK || n_new == 0) return st;
+  const hipError_t e =
+      launch_quantize_append(dev_cache(cache, g), g, k_new, v_new, slots, n_new, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
+                                  int32_t num_splits) {
+  Geometry g;
+  if (check_cache(cache, false, &g) != KVQ_OK) return 0;
+  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0) return 0;
+  return workspace_bytes(g, batch, num_q_heads, splits_for(g, batch, num_q_heads, max_seq_len, num_splits));
+}
+
+int32_t kvq_decode_num_splits(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
+                              int32_t num_splits) {
+  Geometry g;
+  if (check_cache(cache, false, &g) != KVQ_OK) return 0;
+  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0) return 0;
+  return splits_for(g, batch, num_q_heads, max_seq_len, num_splits).num_splits;
+}
+
+kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                                const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                int32_t max_seq_len, float softmax_scale, int32_t num_splits, void* workspace,
+                                size_t workspace_bytes, float* out, void* stream) {
+  return decode_impl(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
+                     softmax_scale, num_splits, workspace, workspace_bytes, out, stream, nullptr, nullptr, false);
+}
+
+kvq_status kvq_decode_attention_timed(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                                      const int32_t* block_table, int32_t max_pages_per_seq,
+                                      const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                                      int32_t num_splits, void* workspace, size_t workspace_bytes, float* out,
+                                      void* stream, void* split_begin, void* split_end) {
+  return decode_impl(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
+                     softmax_scale, num_splits, workspace, workspace_bytes, out, stream, split_begin, split_end,
+                     false);
+}
+
+kvq_status kvq_decode_attention_reference(const kvq_cache* cache, const void* q, int32_t batch,
+                                          int32_t num_q_heads, const int32_t* block_table,
+                                          int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                          int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                                          void* workspace, size_t workspace_bytes, float* out, void* stream) {
+  return decode_impl(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
+                     softmax_scale, num_splits, workspace, workspace_bytes, out, stream, nullptr, nullptr, true);
+}
+
+kvq_status kvq_dequantize(const kvq_cache* cache, int32_t which, const int64_t* slots, int64_t n, float* out,
+                          void* stream) {
+  Geometry g;
+  kvq_status st = check_dequantize(cache, which, slots, n, out, &g);
+  if (st != KVQ_OK || n == 0) return st;
+  const hipError_t e = launch_dequantize(dev_cache(cache, g), g, which, slots, n, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+const char* kvq_status_string(kvq_status status) {
+  switch (status) {
+    case KVQ_OK:
+      return "ok";
+    case KVQ_ERR_INVALID:
+      return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED:
+      return "unsupported configuration";
+    case KVQ_ERR_WORKSPACE:
+      return "workspace too small";
+    case KVQ_ERR_HIP:
+      return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* kvq_version(void) { return "kvq 0.1.0 (gfx950)"; }
+
+}  // extern "C"

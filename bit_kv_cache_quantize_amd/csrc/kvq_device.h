@@ -1,0 +1,82 @@
+// Device-side helpers and the launch interface shared by the kvq kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "kvq_validate.h"
+
+namespace kvq {
+
+// The cache as the kernels see it (plane pointers plus the few sizes they index with).
+struct DevCache {
+  uint8_t* kc;   // K codes  [u][P][RB]
+  uint32_t* km;  // K meta   [u][P][NG]        {scale | zero << 16}
+  uint8_t* vc;   // V codes  [u][P/16][RB/2][16] x u16
+  uint32_t* vm;  // V meta   [u][P/16][NG][16] {scale | zero << 16}
+  int hkv;
+  int page;
+  int row_bytes;
+  int ngroups;
+};
+
+inline DevCache dev_cache(const kvq_cache* c, const Geometry& g) {
+  DevCache d;
+  d.kc = static_cast<uint8_t*>(c->k_codes);
+  d.km = static_cast<uint32_t*>(c->k_meta);
+  d.vc = static_cast<uint8_t*>(c->v_codes);
+  d.vm = static_cast<uint32_t*>(c->v_meta);
+  d.hkv = g.hkv;
+  d.page = g.page;
+  d.row_bytes = g.row_bytes;
+  d.ngroups = g.ngroups;
+  return d;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float f16_bits_to_float(uint32_t h16) {
+  _Float16 h;
+  const uint16_t b = static_cast<uint16_t>(h16);
+  __builtin_memcpy(&h, &b, 2);
+  return static_cast<float>(h);
+}
+
+__device__ __forceinline__ uint32_t float_to_f16_bits(float x) {
+  const _Float16 h = static_cast<_Float16>(x);  // v_cvt_f16_f32, round to nearest even
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+
+// ---- host launchers (defined in the .hip files) ----
+hipError_t launch_quantize_append(const DevCache& c, const Geometry& g, const void* k_new,
+                                  const void* v_new, const int64_t* slots, int64_t n_new,
+                                  hipStream_t stream);
+hipError_t launch_dequantize(const DevCache& c, const Geometry& g, int which, const int64_t* slots,
+                             int64_t n, float* out, hipStream_t stream);
+
+struct DecodeArgs {
+  DevCache c;
+  const uint16_t* q;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* partials;
+  float* out;
+  int batch;
+  int num_q_heads;
+  int ratio;
+  int max_pages;
+  int split_len;
+  int num_splits;
+  int hblock;
+  float rot_c;    // float nearest 1/sqrt(hblock)
+  float qscale;   // softmax scale * log2(e): logits are kept in the exp2 domain
+};
+
+hipError_t launch_decode_split(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
+hipError_t launch_decode_split_reference(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
+hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,142 @@
+// Host-side argument checking for the kvq C ABI (no HIP dependency).
+#include "kvq_validate.h"
+
+namespace kvq {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+static bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+kvq_status check_cache(const kvq_cache* c, bool planes, Geometry* g) {
+  if (!c) return KVQ_ERR_INVALID;
+  if (c->head_dim <= 0 || c->num_kv_heads <= 0 || c->num_pages <= 0) return KVQ_ERR_INVALID;
+  if (c->bits != 2 && c->bits != 4) {
+    // other widths are well formed integers but not a packing this library defines
+    return (c->bits > 0 && c->bits <= 8) ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
+  }
+  if (c->group_size <= 0 || c->head_dim % c->group_size != 0) return KVQ_ERR_INVALID;
+  if (c->hadamard_block < 0) return KVQ_ERR_INVALID;
+  if (c->hadamard_block > 0 && (!pow2(c->hadamard_block) || c->head_dim % c->hadamard_block != 0))
+    return KVQ_ERR_INVALID;
+  if (c->page_size <= 0 || c->page_size % kTile != 0) return KVQ_ERR_INVALID;
+  if ((static_cast<int64_t>(c->head_dim) * c->bits) % 16 != 0) return KVQ_ERR_INVALID;
+  if (planes) {
+    const void* p[4] = {c->k_codes, c->k_meta, c->v_codes, c->v_meta};
+    for (const void* x : p)
+      if (!x || !aligned(x, 16)) return KVQ_ERR_INVALID;
+  }
+  Geometry t;
+  t.d = c->head_dim;
+  t.hkv = c->num_kv_heads;
+  t.bits = c->bits;
+  t.group = c->group_size;
+  t.ngroups = c->head_dim / c->group_size;
+  t.hblock = c->hadamard_block;
+  t.page = c->page_size;
+  t.row_bytes = c->head_dim * c->bits / 8;
+  t.num_pages = c->num_pages;
+  if (g) *g = t;
+  return cache_supported(t) ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
+}
+
+bool cache_supported(const Geometry& g) {
+  if (g.d != 128) return false;
+  if (g.group != 32 && g.group != 64 && g.group != 128) return false;
+  if (g.hblock != 0 && (g.hblock < 2 || g.hblock > 128)) return false;
+  return true;
+}
+
+int64_t plane_bytes(const Geometry& g, int plane) {
+  const int64_t tokens = g.num_pages * g.hkv * static_cast<int64_t>(g.page);
+  switch (plane) {
+    case 0:
+    case 2:
+      return tokens * g.row_bytes;
+    case 1:
+    case 3:
+      return tokens * g.ngroups * 4;
+    default:
+      return -1;
+  }
+}
+
+Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
+                     int32_t requested, int cus) {
+  (void)num_q_heads;
+  Splits s{1, kBlock};
+  const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
+  const int64_t blocks = (len + kBlock - 1) / kBlock;
+  int64_t n;
+  if (requested > 0) {
+    n = requested;
+  } else {
+    // Enough independent work units to keep every CU busy several times over
+    // (16 per CU), without partitions shorter than 8 blocks (256 tokens), whose
+    // partial results would cost more than they balance.
+    const int64_t units = static_cast<int64_t>(batch) * g.hkv;
+    const int64_t target = 16LL * (cus > 0 ? cus : 256);
+    n = (target + units - 1) / (units > 0 ? units : 1);
+    const int64_t min_blocks = 8;
+    int64_t cap = blocks / min_blocks;
+    if (cap < 1) cap = 1;
+    if (n > cap) n = cap;
+    // and no partition longer than 64 blocks (2048 tokens)
+    const int64_t floor_n = (blocks + 63) / 64;
+    if (n < floor_n) n = floor_n;
+  }
+  if (n < 1) n = 1;
+  if (n > blocks) n = blocks;
+  const int64_t per = (blocks + n - 1) / n;  // blocks per partition
+  s.split_len = static_cast<int32_t>(per * kBlock);
+  s.num_splits = static_cast<int32_t>((blocks + per - 1) / per);
+  return s;
+}
+
+size_t workspace_bytes(const Geometry& g, int32_t batch, int32_t num_q_heads, const Splits& s) {
+  return static_cast<size_t>(batch) * num_q_heads * s.num_splits * (g.d + 2) * sizeof(float);
+}
+
+kvq_status check_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t num_q_heads,
+                        const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                        int32_t max_seq_len, int32_t num_splits, const void* workspace, const float* out,
+                        Geometry* g) {
+  kvq_status st = check_cache(c, true, g);
+  if (st != KVQ_OK) return st;
+  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0) return KVQ_ERR_INVALID;
+  if (num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID;
+  const int ratio = num_q_heads / c->num_kv_heads;
+  if (ratio != 1 && ratio != 2 && ratio != 4) return KVQ_ERR_UNSUPPORTED;
+  if (batch == 0) return KVQ_OK;
+  if (max_pages_per_seq <= 0) return KVQ_ERR_INVALID;
+  if (static_cast<int64_t>(max_pages_per_seq) * c->page_size < max_seq_len) return KVQ_ERR_INVALID;
+  if (!q || !aligned(q, 16)) return KVQ_ERR_INVALID;
+  if (!block_table || !aligned(block_table, 4)) return KVQ_ERR_INVALID;
+  if (!seq_lens || !aligned(seq_lens, 4)) return KVQ_ERR_INVALID;
+  if (!out || !aligned(out, 16)) return KVQ_ERR_INVALID;
+  if (!workspace || !aligned(workspace, 16)) return KVQ_ERR_INVALID;
+  return KVQ_OK;
+}
+
+kvq_status check_append(const kvq_cache* c, const void* k_new, const void* v_new, const int64_t* slots,
+                        int64_t n_new, Geometry* g) {
+  kvq_status st = check_cache(c, true, g);
+  if (st != KVQ_OK) return st;
+  if (n_new < 0) return KVQ_ERR_INVALID;
+  if (n_new == 0) return KVQ_OK;
+  if (!k_new || !v_new || !slots) return KVQ_ERR_INVALID;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slots, 8)) return KVQ_ERR_INVALID;
+  return KVQ_OK;
+}
+
+kvq_status check_dequantize(const kvq_cache* c, int32_t which, const int64_t* slots, int64_t n,
+                            const float* out, Geometry* g) {
+  kvq_status st = check_cache(c, true, g);
+  if (st != KVQ_OK) return st;
+  if (which != 0 && which != 1) return KVQ_ERR_INVALID;
+  if (n < 0) return KVQ_ERR_INVALID;
+  if (n == 0) return KVQ_OK;
+  if (!slots || !aligned(slots, 8) || !out || !aligned(out, 16)) return KVQ_ERR_INVALID;
+  return KVQ_OK;
+}
+
+}  // namespace kvq

@@ -1,0 +1,55 @@
+// Host-side argument checking for the kvq C ABI. No HIP dependency: this
+// translation unit also builds with a plain host compiler for CPU-only tests.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+// Kernel granularity: the decode kernels walk the cache in 32-token blocks made of
+// two 16-token tiles; split-K partitions are whole blocks.
+constexpr int kTile = 16;
+constexpr int kBlock = 32;
+
+struct Geometry {
+  int d, hkv, bits, group, ngroups, hblock, page, row_bytes;
+  int64_t num_pages;
+};
+
+// Structural checks of a cache description. `planes` also checks the four device
+// pointers (non-null, 16-byte aligned).
+kvq_status check_cache(const kvq_cache* c, bool planes, Geometry* g);
+
+// Description is well formed but outside what the kernels are built for.
+bool cache_supported(const Geometry& g);
+
+bool aligned(const void* p, size_t a);
+
+int64_t plane_bytes(const Geometry& g, int plane);
+
+// Split-K sizing. `cus` is the device's compute-unit count (256 on MI355X).
+struct Splits {
+  int32_t num_splits;  // partitions of a max_seq_len sequence
+  int32_t split_len;   // tokens per partition, a multiple of kBlock
+};
+Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
+                     int32_t requested, int cus);
+
+size_t workspace_bytes(const Geometry& g, int32_t batch, int32_t num_q_heads, const Splits& s);
+
+// Full check of decode arguments (everything but the workspace size).
+kvq_status check_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t num_q_heads,
+                        const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                        int32_t max_seq_len, int32_t num_splits, const void* workspace, const float* out,
+                        Geometry* g);
+
+kvq_status check_append(const kvq_cache* c, const void* k_new, const void* v_new, const int64_t* slots,
+                        int64_t n_new, Geometry* g);
+
+kvq_status check_dequantize(const kvq_cache* c, int32_t which, const int64_t* slots, int64_t n,
+                            const float* out, Geometry* g);
+
+}  // namespace kvq

@@ -1,0 +1,219 @@
+// Fused rotation + low-bit group quantization on cache append, and dequantization.
+//
+// SAW-INT4: System-Aware 4-Bit KV-Cache Quantization for Real-World LLM Serving,
+// Abstract: token-wise INT4 with a block-diagonal Hadamard rotation, done by one fused
+// rotation-quantization kernel that writes straight into the paged KV layout.
+// InnerQ (Abstract): asymmetric groups with a scale and a zero point.
+//
+// Mapping: one 128-channel token row per 16 lanes, 8 consecutive channels per lane,
+// loaded with one 16-byte load. The Walsh-Hadamard butterfly (Sylvester order) runs
+// in registers: strides 1, 2, 4 inside a lane, 8..64 across lanes of the row. Group
+// min/max are reduced across the 4/8/16 lanes of a 32/64/128-channel group. Every fp32
+// step is a separate IEEE round-to-nearest-even operation in the order the library
+// documents, so the codes and fp16 scale/zero are bit-exact functions of the input.
+#include <cmath>
+
+#include "kvq_device.h"
+
+// Every fp32 operation of the quantizer is its own rounding: never fuse.
+#pragma clang fp contract(off)
+
+namespace kvq {
+namespace {
+
+constexpr int kRowsPerBlock = 16;  // 256 threads, 16 lanes per row
+
+template <int BITS, int G>
+__global__ __launch_bounds__(256) void quantize_append_kernel(DevCache c, const uint16_t* __restrict__ k_new,
+                                                              const uint16_t* __restrict__ v_new,
+                                                              const int64_t* __restrict__ slots, int64_t n_rows,
+                                                              int hblock, float rot_c) {
+  constexpr int kQmax = (1 << BITS) - 1;
+  constexpr int kLanesPerGroup = G / 8;
+  const int lane = threadIdx.x & 15;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 4);
+  if (row >= n_rows) return;  // whole 16-lane rows retire together
+  const int which = static_cast<int>(row & 1);  // 0 = K, 1 = V
+  const int64_t rh = row >> 1;                  // token * Hkv + head
+  const int h = static_cast<int>(rh % c.hkv);
+  const int64_t r = rh / c.hkv;
+
+  const uint16_t* src = (which ? v_new : k_new) + rh * 128 + lane * 8;
+  const uint4 raw = *reinterpret_cast<const uint4*>(src);
+  float x[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
+                bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+
+  if (which == 0 && hblock > 0) {
+    // in-lane strides 1, 2, 4
+#pragma unroll
+    for (int s = 1; s < 8; s <<= 1) {
+      if (s < hblock) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (!(e & s)) {
+            const float a = x[e], b = x[e + s];
+            x[e] = a + b;
+            x[e + s] = a - b;
+          }
+        }
+      }
+    }
+    // cross-lane strides 8..64: partner lane = lane ^ (stride / 8)
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      if (8 * m < hblock) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float y = __shfl_xor(x[e], m, 16);
+          x[e] = upper ? (y - x[e]) : (x[e] + y);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = x[e] * rot_c;
+  }
+
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) {
+    mn = fminf(mn, x[e]);
+    mx = fmaxf(mx, x[e]);
+  }
+#pragma unroll
+  for (int m = 1; m < kLanesPerGroup; m <<= 1) {
+    mn = fminf(mn, __shfl_xor(mn, m, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, m, 16));
+  }
+  const float range = (mx - mn) + 0.0f;  // +0.0f: a -0 range (mixed-sign zeros) becomes +0
+  const float s32 = range / static_cast<float>(kQmax);
+  const uint32_t s16 = float_to_f16_bits(s32);
+  const uint32_t z16 = float_to_f16_bits(mn + 0.0f);  // -0 minimum stored as +0
+  const float s = f16_bits_to_float(s16);
+  const float z = f16_bits_to_float(z16);
+
+  uint32_t packed = 0;
+  if (s != 0.0f) {
+    const float inv = 1.0f / s;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float diff = x[e] - z;
+      const float u = diff * inv;
+      const float rr = fminf(fmaxf(__builtin_rintf(u), 0.0f), static_cast<float>(kQmax));
+      packed |= static_cast<uint32_t>(rr) << (BITS * e);
+    }
+  }
+
+  const int64_t slot = slots[r];
+  const int64_t page = slot / c.page;
+  const int off = static_cast<int>(slot - page * c.page);
+  const int64_t u = page * c.hkv + h;
+  const int g = lane / kLanesPerGroup;
+  const uint32_t meta = s16 | (z16 << 16);
+  const bool group_leader = (lane % kLanesPerGroup) == 0;
+
+  if (which == 0) {
+    uint8_t* dst = c.kc + (u * c.page + off) * c.row_bytes;
+    if (BITS == 4)
+      reinterpret_cast<uint32_t*>(dst)[lane] = packed;
+    else
+      reinterpret_cast<uint16_t*>(dst)[lane] = static_cast<uint16_t>(packed);
+    if (group_leader) c.km[(u * c.page + off) * c.ngroups + g] = meta;
+  } else {
+    const int64_t tile = off >> 4;
+    const int o = off & 15;
+    uint16_t* words = reinterpret_cast<uint16_t*>(c.vc + u * c.page * c.row_bytes + tile * 16 * c.row_bytes);
+    if (BITS == 4) {
+      words[(2 * lane) * 16 + o] = static_cast<uint16_t>(packed);
+      words[(2 * lane + 1) * 16 + o] = static_cast<uint16_t>(packed >> 16);
+    } else {
+      words[lane * 16 + o] = static_cast<uint16_t>(packed);
+    }
+    if (group_leader) c.vm[((u * (c.page >> 4) + tile) * c.ngroups + g) * 16 + o] = meta;
+  }
+}
+
+template <int BITS, int G>
+__global__ __launch_bounds__(256) void dequantize_kernel(DevCache c, int which, const int64_t* __restrict__ slots,
+                                                         int64_t n_rows, float* __restrict__ out) {
+  constexpr int kLanesPerGroup = G / 8;
+  const int lane = threadIdx.x & 15;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 4);
+  if (row >= n_rows) return;
+  const int h = static_cast<int>(row % c.hkv);
+  const int64_t r = row / c.hkv;
+  const int64_t slot = slots[r];
+  const int64_t page = slot / c.page;
+  const int off = static_cast<int>(slot - page * c.page);
+  const int64_t u = page * c.hkv + h;
+  const int g = lane / kLanesPerGroup;
+
+  uint32_t packed, meta;
+  if (which == 0) {
+    const uint8_t* src = c.kc + (u * c.page + off) * c.row_bytes;
+    packed = BITS == 4 ? reinterpret_cast<const uint32_t*>(src)[lane] : reinterpret_cast<const uint16_t*>(src)[lane];
+    meta = c.km[(u * c.page + off) * c.ngroups + g];
+  } else {
+    const int64_t tile = off >> 4;
+    const int o = off & 15;
+    const uint16_t* words =
+        reinterpret_cast<const uint16_t*>(c.vc + u * c.page * c.row_bytes + tile * 16 * c.row_bytes);
+    if (BITS == 4)
+      packed = static_cast<uint32_t>(words[(2 * lane) * 16 + o]) |
+               (static_cast<uint32_t>(words[(2 * lane + 1) * 16 + o]) << 16);
+    else
+      packed = words[lane * 16 + o];
+    meta = c.vm[((u * (c.page >> 4) + tile) * c.ngroups + g) * 16 + o];
+  }
+  const float s = f16_bits_to_float(meta & 0xFFFFu);
+  const float z = f16_bits_to_float(meta >> 16);
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t code = (packed >> (BITS * e)) & ((1u << BITS) - 1u);
+    y[e] = __builtin_fmaf(static_cast<float>(code), s, z);
+  }
+  float4* dst = reinterpret_cast<float4*>(out + row * 128 + lane * 8);
+  dst[0] = make_float4(y[0], y[1], y[2], y[3]);
+  dst[1] = make_float4(y[4], y[5], y[6], y[7]);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_append(const DevCache& c, const Geometry& g, const void* k_new, const void* v_new,
+                                  const int64_t* slots, int64_t n_new, hipStream_t stream) {
+  const int64_t n_rows = n_new * g.hkv * 2;
+  const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const float rot_c = g.hblock > 0 ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(g.hblock))) : 1.0f;
+  const auto* k = static_cast<const uint16_t*>(k_new);
+  const auto* v = static_cast<const uint16_t*>(v_new);
+  dim3 grid(static_cast<unsigned>(blocks)), block(256);
+#define KVQ_QA(B, GS)                                                                                      \
+  if (g.bits == B && g.group == GS) {                                                                      \
+    hipLaunchKernelGGL((quantize_append_kernel<B, GS>), grid, block, 0, stream, c, k, v, slots, n_rows,   \
+                       g.hblock, rot_c);                                                                    \
+    return hipGetLastError();                                                                              \
+  }
+  KVQ_QA(4, 32) KVQ_QA(4, 64) KVQ_QA(4, 128) KVQ_QA(2, 32) KVQ_QA(2, 64) KVQ_QA(2, 128)
+#undef KVQ_QA
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_dequantize(const DevCache& c, const Geometry& g, int which, const int64_t* slots, int64_t n,
+                             float* out, hipStream_t stream) {
+  const int64_t n_rows = n * g.hkv;
+  const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(blocks)), block(256);
+#define KVQ_DQ(B, GS)                                                                                      \
+  if (g.bits == B && g.group == GS) {                                                                      \
+    hipLaunchKernelGGL((dequantize_kernel<B, GS>), grid, block, 0, stream, c, which, slots, n_rows, out); \
+    return hipGetLastError();                                                                              \
+  }
+  KVQ_DQ(4, 32) KVQ_DQ(4, 64) KVQ_DQ(4, 128) KVQ_DQ(2, 32) KVQ_DQ(2, 64) KVQ_DQ(2, 128)
+#undef KVQ_DQ
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -1,0 +1,188 @@
+/*
+ * kvq: rotated low-bit (INT4 / INT2) KV-cache quantize-append and split-K decode
+ * attention for AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The method:
+ *  - SAW-INT4: System-Aware 4-Bit KV-Cache Quantization for Real-World LLM Serving,
+ *    Abstract: keys and values are quantized token-wise to 4 bits after a
+ *    block-diagonal Hadamard rotation, by a fused rotation-quantization kernel that
+ *    writes straight into a paged KV layout; attention then runs over that cache.
+ *  - Dual-QK: Sharp Queries and Flat Keys for Prunable 2-bit KV Caches, Abstract:
+ *    the transform applied to keys is applied to queries as well, which leaves every
+ *    query-key dot product unchanged; 2-bit caches are in scope.
+ *  - InnerQ: Hardware-Aware Tuning-Free Quantization of KV Cache for Large Language
+ *    Models, Abstract: group-wise asymmetric quantization whose dequantization is
+ *    folded into the decode-time vector-matrix products.
+ *
+ * Conventions for every entry point:
+ *  - All data pointers are DEVICE pointers the caller owns (e.g. torch tensors'
+ *    data_ptr()); the library never allocates, frees or retains them. `stream` is a
+ *    hipStream_t (NULL = the null stream). Calls are asynchronous on that stream and
+ *    return before the work finishes; buffers must stay alive until it does.
+ *  - The library holds no state between calls and is safe to call from several host
+ *    threads (kernels on one stream run in order; concurrent calls that write the
+ *    same cache memory race, as any two kernels would).
+ *  - Every argument check is done on the host before any launch. On any status other
+ *    than KVQ_OK nothing was launched, except KVQ_ERR_HIP, which reports a failed
+ *    launch. Device-side contents are not checked: a slot outside the page pool,
+ *    duplicate slots in one append, seq_len beyond the pages of its block-table row,
+ *    or non-finite inputs give undefined results.
+ *  - Supported today: head_dim 128; bits 4 or 2; group_size 32, 64 or 128;
+ *    hadamard_block 0 (off) or a power of two from 2 to 128; GQA ratio
+ *    num_q_heads / num_kv_heads of 1, 2 or 4; page_size a multiple of 16.
+ *    Other well-formed descriptions return KVQ_ERR_UNSUPPORTED.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID = 1,     /* null/misaligned pointer, inconsistent sizes */
+  KVQ_ERR_UNSUPPORTED = 2, /* well-formed but not built (see the list above) */
+  KVQ_ERR_WORKSPACE = 3,   /* workspace smaller than kvq_decode_workspace_bytes() */
+  KVQ_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} kvq_status;
+
+/*
+ * A quantized KV cache: four device planes the caller allocates (sizes from
+ * kvq_cache_plane_bytes) and zero-fills once. Rows are addressed by slot =
+ * page * page_size + offset. With u = page * num_kv_heads + kv_head, RB =
+ * head_dim * bits / 8 bytes of codes per token and NG = head_dim / group_size:
+ *
+ *   k_codes  uint8 [u][page_size][RB]          token-major packed key codes
+ *   k_meta   half2 [u][page_size][NG]          {scale (low 16 bits), zero (high)}
+ *   v_codes  uint8 [u][page_size/16][RB/2][16][2]   each 16-token tile stores the
+ *            packed rows cut into 16-bit words, word-major (word w of token o at
+ *            byte (w*16 + o)*2 of the tile)
+ *   v_meta   half2 [u][page_size/16][NG][16]   {scale, zero}, group-major per tile
+ *
+ * Packed rows are little-endian: INT4 channel 2k in the low nibble of byte k and
+ * 2k+1 in the high nibble; INT2 channel 4k+e in bits 2e..2e+1 of byte k.
+ * A contiguous cache is the special case of one page of capacity tokens per
+ * sequence. Keys are stored in the rotated basis; values are not rotated.
+ * All four planes must be 16-byte aligned.
+ */
+typedef struct kvq_cache {
+  int32_t head_dim;       /* d */
+  int32_t num_kv_heads;   /* Hkv */
+  int32_t bits;           /* 4 or 2 */
+  int32_t group_size;     /* G: channels sharing one scale/zero, divides d */
+  int32_t hadamard_block; /* 0 = no rotation; else power of two dividing d */
+  int32_t page_size;      /* P tokens per page, multiple of 16 */
+  int64_t num_pages;      /* pages in the pool */
+  void* k_codes;
+  void* k_meta;
+  void* v_codes;
+  void* v_meta;
+} kvq_cache;
+
+/* Bytes of one plane: 0 = k_codes, 1 = k_meta, 2 = v_codes, 3 = v_meta.
+   Host-only; returns -1 for an invalid description or plane index. */
+int64_t kvq_cache_plane_bytes(const kvq_cache* cache, int32_t plane);
+
+/*
+ * Quantize and append n_new tokens (SAW-INT4, Abstract: fused rotation +
+ * quantization into the paged layout).
+ *   k_new, v_new : bf16 [n_new][Hkv][d], 16-byte aligned, contiguous.
+ *   slots        : int64 [n_new] device array, slot of each token (page*P + offset).
+ * For every (token, kv head): K is rotated by the block-diagonal Walsh-Hadamard
+ * matrix (Sylvester order, fp32 butterfly with strides 1,2,..,n/2 then a multiply
+ * by the float nearest 1/sqrt(n)); then K and V are quantized per group of G
+ * channels: scale = fp16((max-min)/(2^bits-1)), zero = fp16(min) (a -0 zero is
+ * stored as +0), code = clamp(rint((x-zero)*(1/scale)), 0, 2^bits-1) (all codes 0
+ * when scale is 0), all in fp32 with round-to-nearest-even. Results are bit-exact
+ * functions of the inputs. n_new == 0 is a no-op returning KVQ_OK.
+ */
+kvq_status kvq_quantize_append(const kvq_cache* cache, const void* k_new, const void* v_new,
+                               const int64_t* slots, int64_t n_new, void* stream);
+
+/*
+ * Workspace bytes kvq_decode_attention needs for these sizes: fp32 split partials
+ * [batch][num_q_heads][splits][d + 2]. num_splits 0 = the library's choice (the
+ * same choice kvq_decode_attention makes for the same arguments on the same
+ * device). Returns 0 for an invalid description.
+ */
+size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
+                                  int32_t max_seq_len, int32_t num_splits);
+
+/* The number of split-K partitions (per sequence of max_seq_len tokens) that a
+   decode call with these arguments uses; 0 for an invalid description. */
+int32_t kvq_decode_num_splits(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
+                              int32_t max_seq_len, int32_t num_splits);
+
+/*
+ * Decode-phase GQA attention over the quantized cache (one query token per
+ * sequence). Query head j reads kv head j / (num_q_heads / Hkv).
+ *   q           : bf16 [batch][num_q_heads][d] in the ORIGINAL basis (post-RoPE); the
+ *                 kernel applies the keys' rotation to it (Dual-QK, Abstract).
+ *   block_table : int32 [batch][max_pages_per_seq], physical page of each logical page.
+ *   seq_lens    : int32 [batch] on the device: tokens to attend (0 gives a zero row).
+ *   max_seq_len : host upper bound of seq_lens, used to size the split-K grid.
+ *   softmax_scale: 0 means 1/sqrt(d).
+ *   num_splits  : 0 = automatic; otherwise the number of token partitions of a
+ *                 max_seq_len sequence (rounded to the kernel's 32-token granularity).
+ *   workspace   : device scratch of at least kvq_decode_workspace_bytes() bytes,
+ *                 16-byte aligned; overwritten.
+ *   out         : fp32 [batch][num_q_heads][d]:
+ *                 softmax(scale * (R q) . khat_t) weighted sum of vhat_t, where khat/vhat
+ *                 are the dequantized rows fma(code, scale, zero).
+ * Two kernels run: split-K partial attention (online softmax, exp2 domain), then a
+ * log-sum-exp combine of the partials.
+ */
+kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                                const int32_t* block_table, int32_t max_pages_per_seq,
+                                const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                                int32_t num_splits, void* workspace, size_t workspace_bytes, float* out,
+                                void* stream);
+
+/*
+ * Same as kvq_decode_attention, and additionally records the hipEvent_t
+ * `split_begin` right before and `split_end` right after the split-K kernel on
+ * `stream` (either may be NULL), so a caller can time that kernel alone with
+ * hipEventElapsedTime. For benchmarking.
+ */
+kvq_status kvq_decode_attention_timed(const kvq_cache* cache, const void* q, int32_t batch,
+                                      int32_t num_q_heads, const int32_t* block_table,
+                                      int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                      int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                                      void* workspace, size_t workspace_bytes, float* out, void* stream,
+                                      void* split_begin, void* split_end);
+
+/*
+ * The same computation through a second, plain-VALU split-K kernel (fp32
+ * dequantization and dot products, scores staged in LDS) instead of the MFMA
+ * kernel. For cross-checking the fast path; partitions longer than 2048 tokens
+ * return KVQ_ERR_UNSUPPORTED.
+ */
+kvq_status kvq_decode_attention_reference(const kvq_cache* cache, const void* q, int32_t batch,
+                                          int32_t num_q_heads, const int32_t* block_table,
+                                          int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                          int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                                          void* workspace, size_t workspace_bytes, float* out, void* stream);
+
+/*
+ * Dequantize n stored rows: out fp32 [n][Hkv][d] = fma(code, scale, zero) per
+ * element, read from the rows at `slots` (int64 device array). which = 0 reads K
+ * (in the rotated basis), 1 reads V. Bit-exact. For checks and export.
+ */
+kvq_status kvq_dequantize(const kvq_cache* cache, int32_t which, const int64_t* slots, int64_t n,
+                          float* out, void* stream);
+
+/* Static description of a status code. */
+const char* kvq_status_string(kvq_status status);
+
+/* Library version string. */
+const char* kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,163 @@
+"""The C ABI on the CPU: the library loads, exports what include/kvq.h declares, and
+rejects every malformed argument with its documented status before launching
+anything. Every call here returns before any kernel launch (invalid arguments, or
+empty work), so these tests are safe on machines with or without a GPU; the fake
+device pointers below are never dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_kv_cache_quantize_amd as kvq
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced
+
+
+def _desc(**kw):
+    base = dict(head_dim=128, num_kv_heads=8, bits=4, group_size=32, hadamard_block=128, page_size=16,
+                num_pages=64)
+    base.update(kw)
+    d = kvq._Desc(base["head_dim"], base["num_kv_heads"], base["bits"], base["group_size"],
+                  base["hadamard_block"], base["page_size"], base["num_pages"])
+    for f in ("k_codes", "k_meta", "v_codes", "v_meta"):
+        setattr(d, f, kw.get(f, FAKE))
+    return d
+
+
+def test_library_exports_every_declared_symbol():
+    names = set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", open(HEADER).read()))
+    assert len(names) >= 9
+    lib = kvq.lib()
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+    assert set(kvq.SIGNATURES) == names
+
+
+def test_status_strings():
+    for s, text in ((0, "ok"), (1, "invalid argument"), (2, "unsupported configuration"),
+                    (3, "workspace too small"), (4, "HIP runtime error")):
+        assert kvq.status_string(s) == text
+    assert "gfx950" in kvq.version()
+
+
+def test_plane_bytes_match_oracle_layout():
+    for bits, G, P, pages in ((4, 32, 16, 10), (2, 128, 32, 3), (4, 64, 1024, 2)):
+        d = _desc(bits=bits, group_size=G, page_size=P, num_pages=pages)
+        got = [kvq.lib().kvq_cache_plane_bytes(ctypes.byref(d), i) for i in range(4)]
+        ref = oracle.Cache(128, 8, bits, G, 128, P, pages)
+        assert got == [p.size for p in ref.planes()]
+    assert kvq.lib().kvq_cache_plane_bytes(ctypes.byref(_desc()), 4) == -1
+    assert kvq.lib().kvq_cache_plane_bytes(ctypes.byref(_desc(page_size=24)), 0) == -1
+
+
+INVALID_CACHES = [
+    (dict(head_dim=0), kvq.ERR_INVALID),
+    (dict(num_kv_heads=0), kvq.ERR_INVALID),
+    (dict(num_pages=0), kvq.ERR_INVALID),
+    (dict(bits=3), kvq.ERR_UNSUPPORTED),
+    (dict(bits=0), kvq.ERR_INVALID),
+    (dict(group_size=48), kvq.ERR_INVALID),          # does not divide head_dim
+    (dict(group_size=16), kvq.ERR_UNSUPPORTED),      # divides, but no kernel for it
+    (dict(hadamard_block=96), kvq.ERR_INVALID),      # not a power of two
+    (dict(hadamard_block=-1), kvq.ERR_INVALID),
+    (dict(hadamard_block=256), kvq.ERR_INVALID),     # does not divide head_dim
+    (dict(page_size=0), kvq.ERR_INVALID),
+    (dict(page_size=24), kvq.ERR_INVALID),           # not a multiple of 16
+    (dict(head_dim=64, group_size=32, hadamard_block=64), kvq.ERR_UNSUPPORTED),
+    (dict(k_codes=0), kvq.ERR_INVALID),
+    (dict(v_meta=FAKE + 4), kvq.ERR_INVALID),        # misaligned plane
+]
+
+
+@pytest.mark.parametrize("kw,status", INVALID_CACHES)
+def test_append_rejects_bad_cache(kw, status):
+    d = _desc(**kw)
+    st = kvq.lib().kvq_quantize_append(ctypes.byref(d), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+                                       ctypes.c_void_p(FAKE), 4, None)
+    assert st == status
+
+
+def test_append_argument_checks():
+    d = _desc()
+    L = kvq.lib()
+    v = ctypes.c_void_p
+    assert L.kvq_quantize_append(None, v(FAKE), v(FAKE), v(FAKE), 1, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(d), v(FAKE), v(FAKE), v(FAKE), -1, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(d), None, v(FAKE), v(FAKE), 1, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(d), v(FAKE + 2), v(FAKE), v(FAKE), 1, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(d), v(FAKE), v(FAKE), v(FAKE + 4), 1, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(d), None, None, None, 0, None) == kvq.OK  # empty: no launch
+
+
+def _decode(d, **kw):
+    a = dict(q=FAKE, batch=2, hq=32, bt=FAKE, maxp=64, lens=FAKE, maxlen=1000, scale=0.0, splits=0, ws=FAKE,
+             wsb=1 << 40, out=FAKE)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return kvq.lib().kvq_decode_attention(ctypes.byref(d) if d is not None else None, v(a["q"]), a["batch"],
+                                          a["hq"], v(a["bt"]), a["maxp"], v(a["lens"]), a["maxlen"], a["scale"],
+                                          a["splits"], v(a["ws"]), a["wsb"], v(a["out"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hq=12), kvq.ERR_INVALID),          # not a multiple of Hkv
+    (dict(hq=64), kvq.ERR_UNSUPPORTED),      # GQA ratio 8
+    (dict(batch=-1), kvq.ERR_INVALID),
+    (dict(maxlen=-5), kvq.ERR_INVALID),
+    (dict(splits=-1), kvq.ERR_INVALID),
+    (dict(maxp=0), kvq.ERR_INVALID),
+    (dict(maxp=10), kvq.ERR_INVALID),        # 10 pages * 16 < 1000 tokens
+    (dict(q=0), kvq.ERR_INVALID),
+    (dict(q=FAKE + 8), kvq.ERR_INVALID),
+    (dict(bt=0), kvq.ERR_INVALID),
+    (dict(lens=FAKE + 2), kvq.ERR_INVALID),
+    (dict(out=FAKE + 4), kvq.ERR_INVALID),
+    (dict(ws=0), kvq.ERR_INVALID),
+    (dict(wsb=100), kvq.ERR_WORKSPACE),      # too small: rejected before launch
+])
+def test_decode_argument_checks(kw, status):
+    assert _decode(_desc(), **kw) == status
+
+
+def test_decode_bad_cache_and_empty_batch():
+    assert _decode(None) == kvq.ERR_INVALID
+    assert _decode(_desc(bits=3)) == kvq.ERR_UNSUPPORTED
+    assert _decode(_desc(), batch=0) == kvq.OK  # empty: no launch
+
+
+def test_dequantize_argument_checks():
+    d = _desc()
+    L = kvq.lib()
+    v = ctypes.c_void_p
+    assert L.kvq_dequantize(ctypes.byref(d), 2, v(FAKE), 4, v(FAKE), None) == kvq.ERR_INVALID
+    assert L.kvq_dequantize(ctypes.byref(d), 0, v(FAKE), -1, v(FAKE), None) == kvq.ERR_INVALID
+    assert L.kvq_dequantize(ctypes.byref(d), 0, v(FAKE + 4), 4, v(FAKE), None) == kvq.ERR_INVALID
+    assert L.kvq_dequantize(ctypes.byref(d), 1, v(FAKE), 4, v(FAKE + 8), None) == kvq.ERR_INVALID
+    assert L.kvq_dequantize(ctypes.byref(d), 1, None, 0, None, None) == kvq.OK
+
+
+def test_split_sizing_and_workspace():
+    """Automatic split-K sizing: whole 32-token blocks, 256..2048 tokens per partition,
+    and the workspace formula [B][Hq][S][d+2] fp32. (Off a GPU the library assumes
+    256 compute units, the MI355X count.)"""
+    L = kvq.lib()
+    d = _desc(page_size=32768, num_pages=64)
+    cases = {  # (B, Hkv, T) -> splits
+        (64, 32768): 16,    # 512 units x 16 = 8192 work units, 2048 tokens each
+        (16, 8192): 32,     # 128 units x 32, 256-token partitions
+        (1, 1024): 4,
+    }
+    for (B, T), want in cases.items():
+        assert L.kvq_decode_num_splits(ctypes.byref(d), B, 32, T, 0) == want
+        assert L.kvq_decode_workspace_bytes(ctypes.byref(d), B, 32, T, 0) == B * 32 * want * 130 * 4
+    d3 = _desc(group_size=64, page_size=131072, num_pages=1)
+    assert L.kvq_decode_num_splits(ctypes.byref(d3), 1, 32, 131072, 0) >= 256
+    # explicit requests are honoured up to one partition per 32-token block
+    assert L.kvq_decode_num_splits(ctypes.byref(d), 1, 32, 1000, 7) == 7
+    assert L.kvq_decode_num_splits(ctypes.byref(d), 1, 32, 100, 50) == 4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(_desc(bits=3)), 1, 32, 100, 0) == 0

@@ -1,0 +1,221 @@
+"""GPU path (through the C ABI) against the oracle on the same seeded inputs.
+
+Bar: quantized codes and fp16 scale/zero bit-exact (every byte of all four cache
+planes); dequantized rows bit-exact; attention output within 2e-3 max-abs of the
+fp64 oracle. Shapes are scaled-down versions of the workloads (same head counts,
+group sizes, outlier structure, paging) that span several 16/32-token tiles and end
+on ragged tails; full-size shapes are sampled in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_kv_cache_quantize_amd as kvq
+import oracle
+import workloads as wl
+from kvq_harness import TOL, append_step, decode_both, make_pair, max_err, planes_equal
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _small(name, **kw):
+    return wl.get(name).with_(**kw)
+
+
+APPEND_CASES = {
+    "c1": _small("c1"),
+    "c2_small": _small("c2", batch=3, context=700),
+    "c3_g64_sink": _small("c3", context=1000),
+    "c4_int2_g128": _small("c4", batch=2, context=333),
+    "c5_paged": _small("c5", batch=5, ragged=(1, 300)),
+    "int4_g128": _small("c2", batch=2, context=257, group_size=128),
+    "int2_g32": _small("c2", batch=2, context=129, bits=2, group_size=32),
+    "int2_g64_hb32": _small("c2", batch=2, context=95, bits=2, group_size=64, hadamard_block=32),
+    "int4_g32_no_rotation": _small("c2", batch=2, context=200, hadamard_block=0),
+    "int4_g32_hb64": _small("c2", batch=2, context=64, hadamard_block=64),
+    "int4_g64_hb16": _small("c2", batch=1, context=48, group_size=64, hadamard_block=16),
+    "int4_g32_hb2": _small("c2", batch=1, context=40, hadamard_block=2),
+}
+
+
+@pytest.mark.parametrize("name", list(APPEND_CASES))
+def test_append_bit_exact(name):
+    w = APPEND_CASES[name]
+    print(f"[append] {name}: {w}", flush=True)
+    p = make_pair(w, DEV, extra_tokens=2)
+    append_step(p, 0, DEV)
+    torch.cuda.synchronize()
+    assert planes_equal(p) == []
+
+
+def _bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+
+
+def test_append_edge_values_bit_exact():
+    """Rows that stress the formula: constant groups, mixed-sign zeros, huge offsets with
+    tiny ranges, fp16-subnormal scales, values near the fp16 range, one-hot outliers."""
+    print("[append] edge values", flush=True)
+    rng = np.random.default_rng(21)
+    rows = []
+    rows.append(np.full(128, 1.25))
+    rows.append(np.zeros(128))
+    z = np.zeros(128)
+    z[::3] = -0.0
+    rows.append(z)
+    rows.append(-np.zeros(128))
+    rows.append(1000.1 + rng.random(128) * 0.9)
+    rows.append(-3.3e4 + rng.random(128) * 0.5)
+    rows.append(rng.standard_normal(128) * 1e-6)       # scale in the fp16 subnormal range
+    rows.append(rng.standard_normal(128) * 1e-9)       # scale rounds to 0
+    rows.append(rng.standard_normal(128) * 3000.0)     # large but finite scales
+    oh = np.zeros(128)
+    oh[37] = 50.0
+    rows.append(oh)
+    rows.append(np.tile([0.5, 1.5, 2.5, 3.5], 32))     # rounding ties
+    rows.append(np.arange(128) % 16)
+    while len(rows) % 4:
+        rows.append(rng.standard_normal(128))
+    x = np.stack(rows).reshape(-1, 2, 128)             # [n][Hkv=2][d]
+    n = x.shape[0]
+    for bits, G, hb in ((4, 32, 128), (2, 128, 128), (4, 64, 0), (2, 32, 64)):
+        w = wl.Workload("edge", 1, 2, 2, 128, 32, bits, G, hb)
+        geo = wl.geometry(w)
+        gpu = kvq.KVCache.allocate(128, 2, bits, G, hb, geo.page_size, geo.num_pages, device=DEV)
+        ref = oracle.Cache(128, 2, bits, G, hb, geo.page_size, geo.num_pages)
+        k = _bf16(x)
+        v = _bf16(x[::-1].copy())
+        slots = torch.arange(n, dtype=torch.int64)
+        kvq.quantize_append(gpu, k.to(DEV), v.to(DEV), slots.to(DEV))
+        ref.append(wl.bf16_bits(k), wl.bf16_bits(v), slots.numpy())
+        torch.cuda.synchronize()
+        for g, r in zip(gpu.planes(), ref.planes()):
+            assert np.array_equal(g.cpu().numpy(), r), (bits, G, hb)
+
+
+@pytest.mark.parametrize("name", ["c1", "c4_int2_g128", "c5_paged", "int2_g64_hb32"])
+def test_dequantize_bit_exact(name):
+    w = APPEND_CASES[name]
+    print(f"[dequantize] {name}", flush=True)
+    p = make_pair(w, DEV)
+    slots = torch.cat([p.geo.slots(b, 0, int(p.lens[b])) for b in range(w.batch)])
+    for which in (0, 1):
+        got = kvq.dequantize(p.gpu, which, slots.to(DEV)).cpu().numpy()
+        want = p.ref.dequantize(which, slots.numpy())
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), which
+
+
+DECODE_CASES = {
+    "c1": _small("c1"),
+    "c2_small": _small("c2", batch=3, context=700),
+    "c3_sink_many_splits": _small("c3", context=4100),
+    "c4_int2": _small("c4", batch=3, context=1000),
+    "c5_paged_ragged": _small("c5", batch=6, ragged=(1, 600)),
+    "gqa1": _small("c2", batch=2, num_q_heads=8, context=333),
+    "gqa2": _small("c2", batch=2, num_q_heads=16, context=333),
+    "int4_g128_hb0": _small("c2", batch=2, context=257, group_size=128, hadamard_block=0),
+    "int2_g32_hb32": _small("c2", batch=2, context=190, bits=2, group_size=32, hadamard_block=32),
+}
+
+
+@pytest.mark.parametrize("reference", [False, True], ids=["mfma", "reference"])
+@pytest.mark.parametrize("name", list(DECODE_CASES))
+def test_decode_matches_oracle(name, reference):
+    w = DECODE_CASES[name]
+    print(f"[decode] {name} reference={reference}", flush=True)
+    p = make_pair(w, DEV, extra_tokens=1)
+    append_step(p, 0, DEV)
+    got, want = decode_both(p, DEV, reference=reference)
+    assert np.all(np.isfinite(got))
+    err = max_err(got, want)
+    print(f"  max-abs err {err:.3e}", flush=True)
+    assert err <= TOL
+
+
+def test_decode_zero_and_one_token_sequences():
+    w = _small("c5", batch=4, ragged=(1, 100))
+    print("[decode] zero/one-token sequences", flush=True)
+    lens = torch.tensor([0, 1, 37, 0], dtype=torch.int32)
+    p = make_pair(w, DEV, lens=lens)
+    got, want = decode_both(p, DEV)
+    assert np.all(got[0] == 0) and np.all(got[3] == 0)
+    assert max_err(got, want) <= TOL
+    # one token: the output is that token's dequantized value row for every query head
+    slot = p.geo.slots(1, 0, 1)
+    v0 = kvq.dequantize(p.gpu, 1, slot.to(DEV)).cpu().numpy()[0]  # [Hkv][d]
+    for j in range(w.num_q_heads):
+        assert np.max(np.abs(got[1, j] - v0[j // w.gqa])) <= 1e-6
+
+
+def test_decode_split_count_independence():
+    w = _small("c2", batch=2, context=1500)
+    print("[decode] split independence", flush=True)
+    p = make_pair(w, DEV)
+    q = wl.queries(w)
+    outs = []
+    for ns in (1, 2, 7, 47, 0):
+        got, want = decode_both(p, DEV, q=q, num_splits=ns)
+        assert max_err(got, want) <= TOL, ns
+        outs.append(got)
+    for o in outs[1:]:
+        assert np.max(np.abs(o - outs[0])) <= 1e-5
+
+
+def test_decode_page_permutation_invariance():
+    """Same logical content under two different physical page placements."""
+    print("[decode] page permutation", flush=True)
+    w0 = _small("c5", batch=3, ragged=(100, 300))
+    outs = []
+    for page_seed in (0, 5):
+        # same values and lengths, only the physical page permutation differs
+        w = w0.with_(page_seed=page_seed)
+        lens = wl.seq_lens(w0)
+        geo = wl.geometry(w, lens=lens)
+        gpu = kvq.KVCache.allocate(128, 8, 4, 32, 128, 16, geo.num_pages, device=DEV)
+        for b in range(w.batch):
+            T = int(lens[b])
+            slots = geo.slots(b, 0, T)
+            kvq.quantize_append(gpu, wl.keys(w0, b, 0, T).to(DEV), wl.values(w0, b, 0, T).to(DEV), slots.to(DEV))
+        out = kvq.decode_attention(gpu, wl.queries(w0).to(DEV), geo.block_table.to(DEV), lens.to(DEV),
+                                   int(lens.max()))
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_decode_deterministic():
+    w = _small("c2", batch=2, context=900)
+    print("[decode] determinism", flush=True)
+    p = make_pair(w, DEV, with_oracle=False)
+    q = wl.queries(w).to(DEV)
+    a = kvq.decode_attention(p.gpu, q, p.geo.block_table.to(DEV), p.lens.to(DEV), 900).cpu()
+    b = kvq.decode_attention(p.gpu, q, p.geo.block_table.to(DEV), p.lens.to(DEV), 900).cpu()
+    assert torch.equal(a, b)
+
+
+def test_decode_custom_softmax_scale():
+    w = _small("c2", batch=1, context=300)
+    print("[decode] softmax scale", flush=True)
+    p = make_pair(w, DEV)
+    got, want = decode_both(p, DEV, softmax_scale=0.02)
+    assert max_err(got, want) <= TOL
+
+
+def test_output_guard_bytes_untouched():
+    """Canaries around the output and workspace catch out-of-bounds writes."""
+    w = _small("c5", batch=3, ragged=(1, 200))
+    print("[decode] guard canaries", flush=True)
+    p = make_pair(w, DEV, with_oracle=False)
+    B, Hq, d = w.batch, w.num_q_heads, w.head_dim
+    guard = 4096
+    outbuf = torch.full((B * Hq * d + 2 * guard,), 12345.0, device=DEV)
+    out = outbuf[guard:guard + B * Hq * d].view(B, Hq, d)
+    ws_need = kvq.decode_workspace_bytes(p.gpu, B, Hq, int(p.lens.max()))
+    wsbuf = torch.full((ws_need + 2 * guard,), 0xAB, dtype=torch.uint8, device=DEV)
+    ws = wsbuf[guard:guard + ws_need]
+    kvq.decode_attention(p.gpu, wl.queries(w).to(DEV), p.geo.block_table.to(DEV), p.lens.to(DEV),
+                         int(p.lens.max()), workspace=ws, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(outbuf[:guard] == 12345.0) and torch.all(outbuf[-guard:] == 12345.0)
+    assert torch.all(wsbuf[:guard] == 0xAB) and torch.all(wsbuf[-guard:] == 0xAB)
