@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark on one MI355X: quantize-append + split-K decode attention.
+
+A step is one pass of the whole hot path on one batch: each sequence appends one new
+token (fused Hadamard rotation + INT4 group quantization into the cache), then every
+sequence runs GQA decode attention over its full quantized context (split-K kernel +
+combine). Inputs are seeded synthetic tensors resident in HBM before timing starts.
+
+Prints one JSON line. `value` is effective KV GB/s of the whole step (algorithmic
+bytes / step time); `roofline` covers the dominant kernel (the split-K decode), timed
+with HIP events recorded on its own stream around every launch.
+
+  python bench.py [--steps K] [--warmup W] [--workload h1] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/step + effective KV GB/s (% HBM peak) at INT4, 32K ctx"
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them; torch.cuda.Event only times
+    events torch itself recorded)."""
+
+    def __init__(self, n: int):
+        import ctypes
+
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e)
+
+    def pair(self, i: int):
+        return self.ev[2 * i].value, self.ev[2 * i + 1].value
+
+    def elapsed_ms(self, i: int) -> float:
+        f = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(f), self.ev[2 * i], self.ev[2 * i + 1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("decode_mfma.hip", "kvq_device.h"):
+        with open(os.path.join(ROOT, "bit_kv_cache_quantize_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per split-kernel launch from committed rocprofv3 counter runs, or None
+    when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"decode_split_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="h1")
+    ap.add_argument("--reference", action="store_true", help="time the plain-VALU decode kernel instead")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=3, help="sequences in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--parity-seqs", type=int, default=2, help="sequences checked against the oracle")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this benchmark runs on exactly one GPU; --gpus must be 1 (the split-K decode would "
+              "shard by batch, kv head or sequence range across GPUs, which is not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_kv_cache_quantize_amd as kvq
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.get(args.workload)
+    if w.ragged is not None:
+        lens = wl.seq_lens(w)
+    else:
+        lens = torch.full((w.batch,), w.context, dtype=torch.int32)
+    B, Hq, Hkv, d = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim
+    # the step appends token T-1 of every sequence (its slot is rewritten each step, so
+    # every step does the work of a real decode step at context T)
+    geo = wl.geometry(w, extra_tokens=0, lens=lens)
+    maxlen = int(lens.max())
+    t0 = time.time()
+    cache = kvq.KVCache.allocate(d, Hkv, w.bits, w.group_size, w.hadamard_block, geo.page_size, geo.num_pages,
+                                 device=dev)
+    log(f"[bench] {w.name}: cache {cache.nbytes / 1e9:.2f} GB, B={B} Hq={Hq} Hkv={Hkv} T<= {maxlen}")
+    for b in range(B):
+        T = int(lens[b])
+        k, v = wl.keys(w, b, 0, T, device=dev), wl.values(w, b, 0, T, device=dev)
+        kvq.quantize_append(cache, k, v, geo.slots(b, 0, T).to(dev))
+        del k, v
+    torch.cuda.synchronize()
+    log(f"[bench] cache built in {time.time() - t0:.1f}s")
+
+    # KV bytes of one layer exceed the 256 MB Infinity Cache by far for the 32K workloads;
+    # smaller ones cycle through enough distinct copies to defeat it.
+    ring = max(1, math.ceil(1.0e9 / cache.nbytes)) if cache.nbytes < 1.0e9 else 1
+    caches = [cache]
+    for _ in range(ring - 1):
+        c2 = kvq.KVCache(cache.head_dim, cache.num_kv_heads, cache.bits, cache.group_size, cache.hadamard_block,
+                         cache.page_size, cache.num_pages, *[p.clone() for p in cache.planes()])
+        caches.append(c2)
+
+    n_inputs = 4
+    qs = [wl.queries(w, step=s, device=dev) for s in range(n_inputs)]
+    news = [wl.new_tokens(w, step=s, device=dev) for s in range(n_inputs)]
+    last_slots = torch.stack([geo.slots(b, int(lens[b]) - 1, 1)[0] for b in range(B)]).to(dev)
+    bt = geo.block_table.to(dev)
+    lens_d = lens.to(dev)
+    ws_bytes = kvq.decode_workspace_bytes(cache, B, Hq, maxlen, args.num_splits)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    num_splits = kvq.decode_num_splits(cache, B, Hq, maxlen, args.num_splits)
+
+    total_steps = args.warmup + args.steps
+    hip_events = HipEvents(args.steps)
+
+    def step(i: int, events=None):
+        c = caches[i % ring]
+        kn, vn = news[i % n_inputs]
+        kvq.quantize_append(c, kn, vn, last_slots)
+        kvq.decode_attention(c, qs[i % n_inputs], bt, lens_d, maxlen, num_splits=args.num_splits, workspace=ws,
+                             out=out, events=events, reference=args.reference)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i, events=None if args.reference else hip_events.pair(i))
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    split_ms = None
+    if not args.reference:
+        split_ms = float(np.mean([hip_events.elapsed_ms(i) for i in range(args.steps)]))
+    hip_events.close()
+
+    # algorithmic bytes (what the method must move; no re-reads, no partials)
+    per_tok_head = wl.kv_bytes_per_token_head(d, w.bits, w.group_size)
+    kv_bytes = int(lens.to(torch.int64).sum()) * Hkv * per_tok_head
+    q_bytes = B * Hq * d * 2
+    out_bytes = B * Hq * d * 4
+    append_bytes = B * Hkv * (2 * d * 2 + per_tok_head)
+    step_bytes = kv_bytes + q_bytes + out_bytes + append_bytes
+    split_bytes = kv_bytes + q_bytes
+    value = step_bytes / (ms * 1e-3) / 1e9
+
+    roofline = None
+    if split_ms is not None:
+        achieved = split_bytes / (split_ms * 1e-3) / 1e9
+        traffic = traffic_from_profile(args.workload)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": "decode_split", "algorithmic_bytes_per_launch": split_bytes,
+                    "avg_launch_us": round(split_ms * 1e3, 2)}
+
+    # ---- parity on sampled sequences (the oracle recomputes them from the same bytes) ----
+    parity = None
+    cpu = None
+    want_oracle = args.parity_seqs > 0 or not args.no_cpu_baseline
+    if want_oracle:
+        import oracle
+
+        # the last timed step's inputs
+        i_last = total_steps - 1
+        kn, vn = news[i_last % n_inputs]
+        q_last = qs[i_last % n_inputs]
+        kvq.quantize_append(caches[0], kn, vn, last_slots)
+        kvq.decode_attention(caches[0], q_last, bt, lens_d, maxlen, num_splits=args.num_splits, workspace=ws,
+                             out=out, reference=args.reference)
+        torch.cuda.synchronize()
+        out_h = out.cpu().numpy().astype(np.float64)
+        n_samp = max(args.parity_seqs, 0 if args.no_cpu_baseline else args.cpu_sample_seqs)
+        seqs = [int(s) for s in np.linspace(0, B - 1, num=min(n_samp, B)).round()]
+        worst = 0.0
+        t_build = 0.0
+        t_step = 0.0
+        bytes_cpu = 0
+        for s_i, b in enumerate(seqs):
+            T = int(lens[b])
+            # a one-sequence oracle cache holding sequence b (contiguous layout)
+            P = int(math.ceil(T / 16) * 16)
+            ref = oracle.Cache(d, Hkv, w.bits, w.group_size, w.hadamard_block, P, 1)
+            k = wl.keys(w, b, 0, T, device=dev)
+            v = wl.values(w, b, 0, T, device=dev)
+            tb = time.perf_counter()
+            ref.append(wl.bf16_bits(k[:T - 1]), wl.bf16_bits(v[:T - 1]), np.arange(T - 1))
+            t_build += time.perf_counter() - tb
+            del k, v
+            # timed oracle step: append the new token, decode every query head of the sequence
+            ts = time.perf_counter()
+            ref.append(wl.bf16_bits(kn[b:b + 1]), wl.bf16_bits(vn[b:b + 1]), np.array([T - 1]))
+            o = ref.decode(wl.bf16_bits(q_last[b:b + 1]), np.zeros((1, 1), np.int32), np.array([T], np.int32))
+            t_step += time.perf_counter() - ts
+            bytes_cpu += T * Hkv * per_tok_head + Hq * d * 6 + Hkv * (2 * d * 2 + per_tok_head)
+            if s_i < args.parity_seqs:
+                worst = max(worst, float(np.max(np.abs(o[0] - out_h[b]))))
+        if args.parity_seqs > 0:
+            parity = {"max_abs_err": worst, "tolerance": 2e-3, "sequences": seqs[:args.parity_seqs],
+                      "ok": worst <= 2e-3}
+        if not args.no_cpu_baseline:
+            cpu = {"value": round(bytes_cpu / t_step / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                   "sample": f"{len(seqs)} of {B} sequences ({Hkv} kv heads, {Hq} q heads, T={int(lens[seqs[0]])}): "
+                             f"oracle append of the step's token + fp64 decode of every query head; "
+                             f"{t_step:.1f}s timed, cache build {t_build:.1f}s untimed",
+                   "cpu": platform.processor() or platform.machine()}
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"int{w.bits}-kv/bf16-qkv/f32-accum",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V with key outlier channels; no weights or datasets)",
+        "config": {"workload": w.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
+                   "context": maxlen, "bits": w.bits, "group_size": w.group_size,
+                   "hadamard_block": w.hadamard_block, "page_size": geo.page_size, "num_splits": num_splits,
+                   "kernel": "reference" if args.reference else "mfma", "layer_ring": ring,
+                   "step_bytes": step_bytes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "parity": parity,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

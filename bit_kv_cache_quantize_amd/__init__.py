@@ -193,7 +193,7 @@ def decode_attention(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor,
                      events=None, reference: bool = False) -> torch.Tensor:
     """Split-K GQA decode attention; q bf16 [B][Hq][d] (original basis) -> fp32 [B][Hq][d].
 
-    `events` = (begin, end) torch.cuda.Event pair recorded around the split-K kernel.
+    `events` = (begin, end) raw hipEvent_t handles (ints) recorded around the split-K kernel.
     `reference` routes to the plain-VALU kernel (for cross-checks).
     """
     _need(q, torch.bfloat16, "q")
@@ -212,8 +212,7 @@ def decode_attention(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor,
     if reference:
         st = lib().kvq_decode_attention_reference(*args)
     elif events is not None:
-        st = lib().kvq_decode_attention_timed(*args, ctypes.c_void_p(events[0].cuda_event),
-                                              ctypes.c_void_p(events[1].cuda_event))
+        st = lib().kvq_decode_attention_timed(*args, ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
     else:
         st = lib().kvq_decode_attention(*args)
     _check(st, "kvq_decode_attention")

@@ -1,9 +1,401 @@
-// Split-K decode attention: placeholder routing to the reference kernel until the
-// MFMA kernel lands.
+// Split-K decode attention over the packed low-bit cache, on the CDNA4 matrix cores.
+//
+// SAW-INT4 (Abstract): attention runs straight over the paged INT4 cache.
+// InnerQ (Abstract): dequantization is aligned with the decode vector-matrix
+//   products, so the per-group scale multiplies a partial dot product instead of
+//   every element.
+// Dual-QK (Abstract): the query receives the keys' rotation, so q.k is preserved.
+//
+// One wavefront (one 64-thread workgroup) owns one (sequence, kv head, partition)
+// and walks it in 32-token blocks (two 16-token tiles).
+//
+// Scores, v_mfma_f32_32x32x16_f16, 8 per block: C[row][token] = sum_ch A[row][ch] B[ch][token]
+//   A rows = (query head jj, digit d, group g): the rotated, pre-scaled query of head jj
+//     split into two f16 parts (hi = f16(x), lo = f16(x - hi)), zero outside group g.
+//   B = 4-bit (or 2-bit) codes unpacked with one mask into f16 *subnormals*, so the
+//     f16 value of code c is exactly c * 2^-24 and every product is exact.
+//   logit = 2^24 * sum_g scale_g * (C[jj,hi,g] + C[jj,lo,g]) + sum_g zero_g * Qsum[jj][g].
+// Softmax: online, exp2 domain (the query carries softmax_scale * log2 e); the running
+//   max is only rescaled when a block raises it.
+// Values, v_mfma_f32_16x16x32_f16, 16 per block: O[row][ch] += sum_t W[row][t] V[t][ch]
+//   A rows = (query head jj, group g), W = p * scale_g(t) split into f16 hi and lo (two
+//     MFMAs into the same accumulator); B = value codes as f16 subnormals, read from the
+//     cache's word-major 16-token tiles with one 16-byte load per lane; the zero term
+//     sum_t p * zero_g(t) is accumulated separately in fp32.
+// Partials (unnormalised o, running max m, sum l) go to the workspace for the combine.
 #include "kvq_device.h"
 
 namespace kvq {
-hipError_t launch_decode_split(const DecodeArgs& a, const Geometry& g, hipStream_t stream) {
-  return launch_decode_split_reference(a, g, stream);
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kTwo24 = 16777216.0f;
+
+__device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(half8, v);
 }
+
+// Channel of K-slot kappa (0..7) of lane half h in score MFMA p (0..7): the order in
+// which unpack_k() below lays codes into the B operand.
+template <int BITS>
+__device__ __forceinline__ int qk_channel(int p, int h, int kappa) {
+  if (BITS == 4) return 64 * h + 8 * p + (kappa >> 1) + 4 * (kappa & 1);
+  return 64 * h + 16 * (p >> 1) + 4 * (p & 1) + (kappa >> 1) + 8 * (kappa & 1);
+}
+
+// B operand of score MFMA p from the lane's packed key codes (kc: 8 dwords at INT4 =
+// channels 64h..64h+63 of its token, 4 dwords at INT2).
+template <int BITS>
+__device__ __forceinline__ half8 unpack_k(const uint32_t* kc, int p) {
+  if (BITS == 4) {
+    const uint32_t w = kc[p];
+    return as_half8(w & 0x000F000Fu, (w >> 4) & 0x000F000Fu, (w >> 8) & 0x000F000Fu, (w >> 12) & 0x000F000Fu);
+  }
+  const uint32_t w = kc[p >> 1] >> (8 * (p & 1));
+  return as_half8(w & 0x00030003u, (w >> 2) & 0x00030003u, (w >> 4) & 0x00030003u, (w >> 6) & 0x00030003u);
+}
+
+// Channel of column n (0..15) of value N-tile nt (0..7), matching unpack_v().
+template <int BITS>
+__device__ __forceinline__ int pv_channel(int nt, int n) {
+  if (BITS == 4) return 4 * (n + 16 * (nt >> 2)) + (nt & 3);
+  return 8 * n + nt;
+}
+
+// B operand of value N-tile nt: vc holds 8 tokens x one 16-bit code word (4 dwords, two
+// tokens each) for word n (INT4: words n and n+16, i.e. vc[0..3] and vc[4..7]).
+template <int BITS>
+__device__ __forceinline__ half8 unpack_v(const uint32_t* vc, int nt) {
+  if (BITS == 4) {
+    const uint32_t* w = vc + 4 * (nt >> 2);
+    const int s = 4 * (nt & 3);
+    return as_half8((w[0] >> s) & 0x000F000Fu, (w[1] >> s) & 0x000F000Fu, (w[2] >> s) & 0x000F000Fu,
+                    (w[3] >> s) & 0x000F000Fu);
+  }
+  const int s = 2 * nt;
+  return as_half8((vc[0] >> s) & 0x00030003u, (vc[1] >> s) & 0x00030003u, (vc[2] >> s) & 0x00030003u,
+                  (vc[3] >> s) & 0x00030003u);
+}
+
+__device__ __forceinline__ float lo_f16(uint32_t m) { return f16_bits_to_float(m & 0xFFFFu); }
+__device__ __forceinline__ float hi_f16(uint32_t m) { return f16_bits_to_float(m >> 16); }
+
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return float_to_f16_bits(a) | (float_to_f16_bits(b) << 16);
+}
+
+template <int BITS, int NG>
+struct Block {
+  uint32_t kc[BITS == 4 ? 8 : 4];  // key codes of the lane's token, channels 64h..64h+63
+  uint32_t km[NG];                 // key {scale, zero} of the lane's token
+  uint32_t vc[BITS == 4 ? 8 : 4];  // value code words, 8 tokens
+  uint32_t vm[8];                  // value {scale, zero} of group g, 8 tokens
+};
+
+template <int BITS, int G, int R>
+__global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
+  constexpr int NG = 128 / G;
+  constexpr int RB = 128 * BITS / 8;
+  const DevCache& c = a.c;
+  const int lane = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int split = unit % a.num_splits;
+  const int bh = unit / a.num_splits;
+  const int hk = bh % c.hkv;
+  const int b = bh / c.hkv;
+  const int T = a.seq_lens[b];
+  const int start = split * a.split_len;
+  if (start >= T) return;
+  const int end = min(T, start + a.split_len);
+
+  __shared__ float q_s[4][128];
+  __shared__ float p_s[4][32];
+  __shared__ float qsum_s[4][4];
+
+  // ---- rotated, scaled query of the R heads of this kv head (LDS) ----
+  for (int idx = lane; idx < R * 128; idx += 64) {
+    const int j = idx >> 7, i = idx & 127;
+    const uint16_t bits = a.q[(static_cast<int64_t>(b) * a.num_q_heads + hk * R + j) * 128 + i];
+    q_s[j][i] = __uint_as_float(static_cast<uint32_t>(bits) << 16);
+  }
+  __syncthreads();
+  if (a.hblock > 0) {
+    for (int s = 1; s < a.hblock; s <<= 1) {
+      for (int idx = lane; idx < R * 64; idx += 64) {
+        const int j = idx >> 6, pi = idx & 63;
+        const int i = (pi / s) * 2 * s + (pi % s);
+        const float x0 = q_s[j][i], x1 = q_s[j][i + s];
+        q_s[j][i] = x0 + x1;
+        q_s[j][i + s] = x0 - x1;
+      }
+      __syncthreads();
+    }
+  }
+  const float qmul = (a.hblock > 0 ? a.rot_c : 1.0f) * a.qscale;
+  for (int idx = lane; idx < R * 128; idx += 64) q_s[idx >> 7][idx & 127] *= qmul;
+  __syncthreads();
+
+  // Qsum[jj][g]: group sums of the query as the MFMA sees it (hi + lo)
+  {
+    const int jj = lane >> 4, c8 = lane & 15;
+    float part = 0.f;
+    if (jj < R) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = q_s[jj][8 * c8 + e];
+        const float hi = static_cast<float>(static_cast<_Float16>(x));
+        const float lo = static_cast<float>(static_cast<_Float16>(x - hi));
+        part += hi + lo;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < G / 8; m <<= 1) part += __shfl_xor(part, m, 64);
+    if (jj < R && (c8 % (G / 8)) == 0) qsum_s[jj][(8 * c8) / G] = part;
+  }
+
+  // score A operands: lane = (half hA, row rho), rho = 8g + 4(jj>>1) + 2(jj&1) + d
+  half8 aqk[8];
+  {
+    const int hA = lane >> 5, rho = lane & 31;
+    const int gA = rho >> 3, jjA = ((rho >> 2) & 1) * 2 + ((rho >> 1) & 1), dA = rho & 1;
+    const bool row_ok = gA < NG && jjA < R;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int ch = qk_channel<BITS>(p, hA, k);
+        _Float16 v = 0;
+        if (row_ok && ch / G == gA) {
+          const float x = q_s[jjA][ch];
+          const _Float16 hi = static_cast<_Float16>(x);
+          v = dA ? static_cast<_Float16>(x - static_cast<float>(hi)) : hi;
+        }
+        aqk[p][k] = v;
+      }
+    }
+  }
+  __syncthreads();
+
+  // lane roles: scores use (hQ, nQ) = (lane / 32, lane % 32): heads 2hQ, 2hQ+1 of token nQ;
+  // values use (q4, r16) = (lane / 16, lane % 16): A row r16 = 4g + jj, tokens 8q4..8q4+7,
+  // B column r16.
+  const int hQ = lane >> 5, nQ = lane & 31;
+  const int q4 = lane >> 4, r16 = lane & 15;
+  const int jjV = r16 & 3, gV = r16 >> 2;
+  const int gVc = gV < NG ? gV : NG - 1;
+  const bool rowV = gV < NG && jjV < R;
+
+  float qsum[2][NG];
+#pragma unroll
+  for (int j2 = 0; j2 < 2; ++j2)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) qsum[j2][g] = (2 * hQ + j2 < R) ? qsum_s[2 * hQ + j2][g] : 0.f;
+
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
+  const int P = c.page;
+
+  auto load = [&](int t0) {
+    Block<BITS, NG> blk;
+    // the pages of the block's two 16-token tiles; a tile past the partition end
+    // reads the first tile again (its tokens are masked)
+    const int t1 = (t0 + 16 < end) ? t0 + 16 : t0;
+    const int64_t u0 = static_cast<int64_t>(bt[t0 / P]) * c.hkv + hk;
+    const int64_t u1 = static_cast<int64_t>(bt[t1 / P]) * c.hkv + hk;
+    const int64_t row0 = u0 * P + t0 % P;  // token row of tile 0's first token
+    const int64_t row1 = u1 * P + t1 % P;
+    {
+      const int64_t row = ((nQ < 16) ? row0 : row1) + (nQ & 15);
+      const u32x4* src = reinterpret_cast<const u32x4*>(c.kc + row * RB + (RB / 2) * hQ);
+      const u32x4 x0 = src[0];
+      blk.kc[0] = x0[0]; blk.kc[1] = x0[1]; blk.kc[2] = x0[2]; blk.kc[3] = x0[3];
+      if (BITS == 4) {
+        const u32x4 x1 = src[1];
+        blk.kc[4] = x1[0]; blk.kc[5] = x1[1]; blk.kc[6] = x1[2]; blk.kc[7] = x1[3];
+      }
+      const uint32_t* m = c.km + row * NG;
+      if (NG == 4) {
+        const u32x4 mm = *reinterpret_cast<const u32x4*>(m);
+        blk.km[0] = mm[0]; blk.km[1] = mm[1]; blk.km[2 % NG] = mm[2]; blk.km[3 % NG] = mm[3];
+      } else if (NG == 2) {
+        const uint2 mm = *reinterpret_cast<const uint2*>(m);
+        blk.km[0] = mm.x; blk.km[1 % NG] = mm.y;
+      } else {
+        blk.km[0] = m[0];
+      }
+    }
+    {
+      const int64_t trow = (q4 < 2) ? row0 : row1;  // value tile of tokens 8q4..8q4+7
+      const uint8_t* tile = c.vc + trow * RB;
+      const int o = 8 * (q4 & 1);
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(tile + (r16 * 16 + o) * 2);
+      blk.vc[0] = w0[0]; blk.vc[1] = w0[1]; blk.vc[2] = w0[2]; blk.vc[3] = w0[3];
+      if (BITS == 4) {
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(tile + ((r16 + 16) * 16 + o) * 2);
+        blk.vc[4] = w1[0]; blk.vc[5] = w1[1]; blk.vc[6] = w1[2]; blk.vc[7] = w1[3];
+      }
+      const int64_t mrow = trow / 16;  // = u * (P/16) + tile index
+      const u32x4* vm = reinterpret_cast<const u32x4*>(c.vm + (mrow * NG + gVc) * 16 + o);
+      const u32x4 m0 = vm[0], m1 = vm[1];
+      blk.vm[0] = m0[0]; blk.vm[1] = m0[1]; blk.vm[2] = m0[2]; blk.vm[3] = m0[3];
+      blk.vm[4] = m1[0]; blk.vm[5] = m1[1]; blk.vm[6] = m1[2]; blk.vm[7] = m1[3];
+    }
+    return blk;
+  };
+
+  float mrun[2] = {-INFINITY, -INFINITY};  // running max of heads 2hQ, 2hQ+1 (exp2 domain)
+  float lsum[2] = {0.f, 0.f};              // lane-partial sums of p
+  floatx4 acc[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float zacc = 0.f;  // lane-partial sum_t p * zero for row (jjV, gV)
+
+  Block<BITS, NG> cur = load(start);
+  for (int t0 = start; t0 < end; t0 += 32) {
+    Block<BITS, NG> nxt = cur;
+    if (t0 + 32 < end) nxt = load(t0 + 32);
+
+    // ---- scores ----
+    floatx16 cs = {0.f};
+#pragma unroll
+    for (int p = 0; p < 8; ++p)
+      cs = __builtin_amdgcn_mfma_f32_32x32x16_f16(aqk[p], unpack_k<BITS>(cur.kc, p), cs, 0, 0, 0);
+    const bool tok_ok = t0 + nQ < end;
+    float logit[2];
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+      float sa = 0.f, zb = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float sum = cs[4 * g + 2 * j2] + cs[4 * g + 2 * j2 + 1];
+        sa = __builtin_fmaf(lo_f16(cur.km[g]), sum, sa);
+        zb = __builtin_fmaf(hi_f16(cur.km[g]), qsum[j2][g], zb);
+      }
+      logit[j2] = tok_ok ? __builtin_fmaf(sa, kTwo24, zb) : -INFINITY;
+    }
+
+    // ---- online softmax (exp2 domain) ----
+    const bool raise = logit[0] > mrun[0] || logit[1] > mrun[1];
+    if (__any(raise)) {
+      float bm0 = logit[0], bm1 = logit[1];
+#pragma unroll
+      for (int m = 16; m >= 1; m >>= 1) {
+        bm0 = fmaxf(bm0, __shfl_xor(bm0, m, 64));
+        bm1 = fmaxf(bm1, __shfl_xor(bm1, m, 64));
+      }
+      const float n0 = fmaxf(mrun[0], bm0), n1 = fmaxf(mrun[1], bm1);
+      const float al0 = exp2f(mrun[0] - n0), al1 = exp2f(mrun[1] - n1);
+      mrun[0] = n0;
+      mrun[1] = n1;
+      lsum[0] *= al0;
+      lsum[1] *= al1;
+      // scale factors of all four heads, everywhere (heads 0,1 live in lanes 0..31)
+      const float alpha[4] = {__shfl(al0, 0, 64), __shfl(al1, 0, 64), __shfl(al0, 32, 64), __shfl(al1, 32, 64)};
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nt][r] *= alpha[r];
+      zacc *= alpha[jjV];
+    }
+    const float p0 = exp2f(logit[0] - mrun[0]);
+    const float p1 = exp2f(logit[1] - mrun[1]);
+    lsum[0] += p0;
+    lsum[1] += p1;
+    p_s[2 * hQ][nQ] = p0;
+    p_s[2 * hQ + 1][nQ] = p1;
+    __syncthreads();
+
+    // ---- values ----
+    float pv[8];
+    {
+      const floatx4* src = reinterpret_cast<const floatx4*>(&p_s[jjV][8 * q4]);
+      const floatx4 x0 = src[0], x1 = src[1];
+      pv[0] = x0[0]; pv[1] = x0[1]; pv[2] = x0[2]; pv[3] = x0[3];
+      pv[4] = x1[0]; pv[5] = x1[1]; pv[6] = x1[2]; pv[7] = x1[3];
+    }
+    uint32_t ahi[4], alo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float w[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int kk = 2 * k + e;
+        const bool ok = rowV && (t0 + 8 * q4 + kk < end);
+        const float wt = pv[kk] * lo_f16(cur.vm[kk]);
+        w[e] = ok ? wt : 0.f;
+        zacc += ok ? pv[kk] * hi_f16(cur.vm[kk]) : 0.f;
+      }
+      const uint32_t hb = pack_f16x2(w[0], w[1]);
+      ahi[k] = hb;
+      alo[k] = pack_f16x2(w[0] - lo_f16(hb), w[1] - hi_f16(hb));
+    }
+    const half8 Ahi = as_half8(ahi[0], ahi[1], ahi[2], ahi[3]);
+    const half8 Alo = as_half8(alo[0], alo[1], alo[2], alo[3]);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const half8 bv = unpack_v<BITS>(cur.vc, nt);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, bv, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, bv, acc[nt], 0, 0, 0);
+    }
+    __syncthreads();
+    cur = nxt;
+  }
+
+  // ---- partials: o[jj][ch] = 2^24 acc + Z[jj][g(ch)], m, l ----
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) {
+    lsum[0] += __shfl_xor(lsum[0], m, 64);
+    lsum[1] += __shfl_xor(lsum[1], m, 64);
+  }
+  zacc += __shfl_xor(zacc, 16, 64);
+  zacc += __shfl_xor(zacc, 32, 64);  // every lane r16 now holds Z of row (jjV, gV)
+  float* part = a.partials + (static_cast<int64_t>(b) * a.num_q_heads + hk * R) * a.num_splits * 130 +
+                static_cast<int64_t>(split) * 130;
+  const int64_t head_stride = static_cast<int64_t>(a.num_splits) * 130;
+  // lane (q4, r16) owns accumulator rows 4*q4 + r = (jj = r, g = q4) at column r16
+  float zrow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) zrow[r] = __shfl(zacc, 4 * (q4 < NG ? q4 : 0) + r, 64);
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const int ch = pv_channel<BITS>(nt, r16);
+    if (ch / G == q4) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) part[r * head_stride + ch] = __builtin_fmaf(acc[nt][r], kTwo24, zrow[r]);
+    }
+  }
+  if (nQ == 0) {
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+      const int jj = 2 * hQ + j2;
+      if (jj < R) {
+        part[jj * head_stride + 128] = mrun[j2];
+        part[jj * head_stride + 129] = lsum[j2];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_split(const DecodeArgs& a, const Geometry& g, hipStream_t stream) {
+  const int64_t units = static_cast<int64_t>(a.batch) * g.hkv * a.num_splits;
+  if (units > 0x7FFFFFFF) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(units)), block(64);
+#define KVQ_DM(B, GS, RR)                                                                              \
+  if (g.bits == B && g.group == GS && a.ratio == RR) {                                                 \
+    hipLaunchKernelGGL((decode_split_mfma_kernel<B, GS, RR>), grid, block, 0, stream, a);             \
+    return hipGetLastError();                                                                          \
+  }
+#define KVQ_DM_R(B, GS) KVQ_DM(B, GS, 1) KVQ_DM(B, GS, 2) KVQ_DM(B, GS, 4)
+  KVQ_DM_R(4, 32) KVQ_DM_R(4, 64) KVQ_DM_R(4, 128) KVQ_DM_R(2, 32) KVQ_DM_R(2, 64) KVQ_DM_R(2, 128)
+#undef KVQ_DM_R
+#undef KVQ_DM
+  return hipErrorInvalidValue;
+}
+
 }  // namespace kvq
