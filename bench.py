@@ -96,6 +96,9 @@ def main():
     ap.add_argument("--cpu-sample-seqs", type=int, default=3, help="sequences in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--parity-seqs", type=int, default=2, help="sequences checked against the oracle")
+    ap.add_argument("--calibration-copy-mb", type=int, default=0,
+                    help="run one plain elementwise copy (torch.neg, fp32) of this many MiB before timing, "
+                         "so hardware byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -152,6 +155,15 @@ def main():
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     num_splits = kvq.decode_num_splits(cache, B, Hq, maxlen, args.num_splits)
+
+    if args.calibration_copy_mb > 0:
+        n = args.calibration_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)  # reads and writes exactly n*4 bytes
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy: {args.calibration_copy_mb} MiB read + written")
 
     total_steps = args.warmup + args.steps
     hip_events = HipEvents(args.steps)

@@ -31,10 +31,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the kvq library needs ROCm's hipcc to build")
 
 
+# per-source extra flags: keep MFMA accumulators in ordinary VGPRs (the decode kernel
+# reads and rescales them with VALU code; AGPR placement would add copies)
+EXTRA = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc(), *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"  # host pass; harmless
     msgs = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)

@@ -23,6 +23,8 @@
 //     cache's word-major 16-token tiles with one 16-byte load per lane; the zero term
 //     sum_t p * zero_g(t) is accumulated separately in fp32.
 // Partials (unnormalised o, running max m, sum l) go to the workspace for the combine.
+#include <type_traits>
+
 #include "kvq_device.h"
 
 namespace kvq {
@@ -116,6 +118,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   __shared__ float q_s[4][128];
   __shared__ float p_s[4][32];
   __shared__ float qsum_s[4][4];
+  __shared__ half8 aqk_s[8][64];  // score A operands, re-read from LDS for every block
 
   // ---- rotated, scaled query of the R heads of this kv head (LDS) ----
   for (int idx = lane; idx < R * 128; idx += 64) {
@@ -159,7 +162,6 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   }
 
   // score A operands: lane = (half hA, row rho), rho = 8g + 4(jj>>1) + 2(jj&1) + d
-  half8 aqk[8];
   {
     const int hA = lane >> 5, rho = lane & 31;
     const int gA = rho >> 3, jjA = ((rho >> 2) & 1) * 2 + ((rho >> 1) & 1), dA = rho & 1;
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
           const _Float16 hi = static_cast<_Float16>(x);
           v = dA ? static_cast<_Float16>(x - static_cast<float>(hi)) : hi;
         }
-        aqk[p][k] = v;
+        aqk_s[p][lane][k] = v;
       }
     }
   }
@@ -254,28 +256,29 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   for (int nt = 0; nt < 8; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
   float zacc = 0.f;  // lane-partial sum_t p * zero for row (jjV, gV)
 
-  Block<BITS, NG> cur = load(start);
-  for (int t0 = start; t0 < end; t0 += 32) {
-    Block<BITS, NG> nxt = cur;
-    if (t0 + 32 < end) nxt = load(t0 + 32);
-
+  // one 32-token block: scores, online softmax, values. TAIL is the partition's last
+  // block when it ends inside the block: only there are tokens masked.
+  auto compute = [&](const Block<BITS, NG>& cur, int t0, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
     // ---- scores ----
-    floatx16 cs = {0.f};
+    floatx16 cs = __builtin_amdgcn_mfma_f32_32x32x16_f16(aqk_s[0][lane], unpack_k<BITS>(cur.kc, 0),
+                                                          floatx16{}, 0, 0, 0);
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
-      cs = __builtin_amdgcn_mfma_f32_32x32x16_f16(aqk[p], unpack_k<BITS>(cur.kc, p), cs, 0, 0, 0);
-    const bool tok_ok = t0 + nQ < end;
+    for (int p = 1; p < 8; ++p)
+      cs = __builtin_amdgcn_mfma_f32_32x32x16_f16(aqk_s[p][lane], unpack_k<BITS>(cur.kc, p), cs, 0, 0, 0);
     float logit[2];
 #pragma unroll
     for (int j2 = 0; j2 < 2; ++j2) {
       float sa = 0.f, zb = 0.f;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const float sum = cs[4 * g + 2 * j2] + cs[4 * g + 2 * j2 + 1];
-        sa = __builtin_fmaf(lo_f16(cur.km[g]), sum, sa);
+        // fp16 scale/zero feed the fused mixed-precision FMAs directly
+        sa = __builtin_fmaf(lo_f16(cur.km[g]), cs[4 * g + 2 * j2], sa);
+        sa = __builtin_fmaf(lo_f16(cur.km[g]), cs[4 * g + 2 * j2 + 1], sa);
         zb = __builtin_fmaf(hi_f16(cur.km[g]), qsum[j2][g], zb);
       }
-      logit[j2] = tok_ok ? __builtin_fmaf(sa, kTwo24, zb) : -INFINITY;
+      logit[j2] = __builtin_fmaf(sa, kTwo24, zb);
+      if (TAIL) logit[j2] = (t0 + nQ < end) ? logit[j2] : -INFINITY;
     }
 
     // ---- online softmax (exp2 domain) ----
@@ -305,9 +308,13 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     const float p1 = exp2f(logit[1] - mrun[1]);
     lsum[0] += p0;
     lsum[1] += p1;
+    // A single wavefront owns this LDS: its DS instructions complete in program order,
+    // so the exchange needs no barrier, only a compiler fence.
     p_s[2 * hQ][nQ] = p0;
     p_s[2 * hQ + 1][nQ] = p1;
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- values ----
     float pv[8];
@@ -317,21 +324,27 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       pv[0] = x0[0]; pv[1] = x0[1]; pv[2] = x0[2]; pv[3] = x0[3];
       pv[4] = x1[0]; pv[5] = x1[1]; pv[6] = x1[2]; pv[7] = x1[3];
     }
+    // w = p * scale (masked tokens have p = 0 exactly); split w = hi + lo with hi = w's
+    // top 11 significant bits (exact in f16) and lo = the exact remainder
     uint32_t ahi[4], alo[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      float w[2];
+      float hi[2], lo[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int kk = 2 * k + e;
-        const bool ok = rowV && (t0 + 8 * q4 + kk < end);
-        const float wt = pv[kk] * lo_f16(cur.vm[kk]);
-        w[e] = ok ? wt : 0.f;
-        zacc += ok ? pv[kk] * hi_f16(cur.vm[kk]) : 0.f;
+        float w = __builtin_fmaf(lo_f16(cur.vm[kk]), pv[kk], 0.f);
+        float zp = hi_f16(cur.vm[kk]);
+        if (TAIL && t0 + 8 * q4 + kk >= end) {
+          w = 0.f;
+          zp = 0.f;
+        }
+        zacc = __builtin_fmaf(zp, pv[kk], zacc);
+        hi[e] = __uint_as_float(__float_as_uint(w) & 0xFFFFE000u);
+        lo[e] = w - hi[e];
       }
-      const uint32_t hb = pack_f16x2(w[0], w[1]);
-      ahi[k] = hb;
-      alo[k] = pack_f16x2(w[0] - lo_f16(hb), w[1] - hi_f16(hb));
+      ahi[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi[0], hi[1]));
+      alo[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo[0], lo[1]));
     }
     const half8 Ahi = as_half8(ahi[0], ahi[1], ahi[2], ahi[3]);
     const half8 Alo = as_half8(alo[0], alo[1], alo[2], alo[3]);
@@ -341,8 +354,32 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, bv, acc[nt], 0, 0, 0);
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, bv, acc[nt], 0, 0, 0);
     }
-    __syncthreads();
-    cur = nxt;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto run = [&](const Block<BITS, NG>& cur, int t0) {
+    if (t0 + 32 <= end)
+      compute(cur, t0, std::false_type{});
+    else
+      compute(cur, t0, std::true_type{});
+  };
+
+  // Software pipeline: the next block's loads are in flight while one block is
+  // computed. Loads are issued unconditionally (a block past the end re-reads the last
+  // block, already in cache) so the number of outstanding loads is the same on every
+  // path and each block waits only for its own data. The two buffers alternate
+  // through a 2x unrolled loop, so no register copies are needed.
+  const int last = start + ((end - 1 - start) & ~31);
+  Block<BITS, NG> b0 = load(start);
+  Block<BITS, NG> b1;
+  for (int t0 = start;;) {
+    b1 = load(min(t0 + 32, last));
+    run(b0, t0);
+    if ((t0 += 32) >= end) break;
+    b0 = load(min(t0 + 32, last));
+    run(b1, t0);
+    if ((t0 += 32) >= end) break;
   }
 
   // ---- partials: o[jj][ch] = 2^24 acc + Z[jj][g(ch)], m, l ----

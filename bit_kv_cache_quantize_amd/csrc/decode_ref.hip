@@ -144,11 +144,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
   }
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, query head).
+// Log-sum-exp merge of the partitions of one (sequence, query head). Every thread reads
+// the (m, l) pairs of all partitions (independent loads, one round trip), then its
+// channel of each partition's o.
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ partials,
                                                       const int32_t* __restrict__ seq_lens, int num_q_heads,
                                                       int num_splits, int split_len, float* __restrict__ out) {
   constexpr int kD = 128;
+  constexpr int kChunk = 16;
   const int bj = blockIdx.x;
   const int b = bj / num_q_heads;
   const int i = threadIdx.x;
@@ -160,13 +163,30 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   const int ns = min(num_splits, (T + split_len - 1) / split_len);
   const float* base = partials + static_cast<int64_t>(bj) * num_splits * (kD + 2);
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, base[s * (kD + 2) + kD]);
+  for (int s0 = 0; s0 < ns; s0 += kChunk) {
+    float m[kChunk];
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) m[k] = s0 + k < ns ? base[(s0 + k) * (kD + 2) + kD] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) M = fmaxf(M, m[k]);
+  }
   float L = 0.f, o = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float* p = base + s * (kD + 2);
-    const float w = exp2f(p[kD] - M);
-    L = __builtin_fmaf(p[kD + 1], w, L);
-    o = __builtin_fmaf(p[i], w, o);
+  for (int s0 = 0; s0 < ns; s0 += kChunk) {
+    float m[kChunk], l[kChunk], v[kChunk];
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const bool ok = s0 + k < ns;
+      const float* p = base + (s0 + k) * (kD + 2);
+      m[k] = ok ? p[kD] : -INFINITY;
+      l[k] = ok ? p[kD + 1] : 0.f;
+      v[k] = ok ? p[i] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const float w = exp2f(m[k] - M);
+      L = __builtin_fmaf(l[k], w, L);
+      o = __builtin_fmaf(v[k], w, o);
+    }
   }
   out[static_cast<int64_t>(bj) * kD + i] = o / L;
 }
