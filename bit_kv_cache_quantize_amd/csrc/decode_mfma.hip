@@ -12,16 +12,22 @@
 // Scores, v_mfma_f32_32x32x16_f16, 8 per block: C[row][token] = sum_ch A[row][ch] B[ch][token]
 //   A rows = (query head jj, digit d, group g): the rotated, pre-scaled query of head jj
 //     split into two f16 parts (hi = f16(x), lo = f16(x - hi)), zero outside group g.
-//   B = 4-bit (or 2-bit) codes unpacked with one mask into f16 *subnormals*, so the
-//     f16 value of code c is exactly c * 2^-24 and every product is exact.
-//   logit = 2^24 * sum_g scale_g * (C[jj,hi,g] + C[jj,lo,g]) + sum_g zero_g * Qsum[jj][g].
+//   B = the codes as exact f16 integers: a mask spreads the 4-bit (2-bit) codes into
+//     bytes, and bytes 0..15 read as fp8-e4m3 are exactly c * 2^-9, which the scaled
+//     fp8->f16 conversion turns into c. Every product is exact. (Codes could also be
+//     fed as f16 subnormals c * 2^-24 with a mask alone, but the matrix core sums
+//     products of subnormal operands with visibly less precision.)
+//   logit = sum_g scale_g * (C[jj,hi,g] + C[jj,lo,g]) + sum_g zero_g * Qsum[jj][g].
 // Softmax: online, exp2 domain (the query carries softmax_scale * log2 e); the running
 //   max is only rescaled when a block raises it.
 // Values, v_mfma_f32_16x16x32_f16, 16 per block: O[row][ch] += sum_t W[row][t] V[t][ch]
-//   A rows = (query head jj, group g), W = p * scale_g(t) split into f16 hi and lo (two
-//     MFMAs into the same accumulator); B = value codes as f16 subnormals, read from the
-//     cache's word-major 16-token tiles with one 16-byte load per lane; the zero term
-//     sum_t p * zero_g(t) is accumulated separately in fp32.
+//   A rows = (query head jj, group g), W = 2^8 p * scale_g(t) split into f16 hi (w's top
+//     11 bits) and lo (the remainder), two MFMAs into the same accumulator; the 2^8 keeps
+//     lo out of the f16 subnormal range (and drops to 1, exactly, if any scale >= 128);
+//   B = value codes as exact f16 integers, from one 16-byte load per lane of the cache's
+//     16-token tiles, where each word's token pairs are byte-interleaved so one mask
+//     yields both tokens' codes for a channel side by side;
+//   the zero term sum_t p * zero_g(t) is accumulated separately in fp32.
 // Partials (unnormalised o, running max m, sum l) go to the workspace for the combine.
 #include <type_traits>
 
@@ -35,19 +41,25 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float kTwo24 = 16777216.0f;
 
 __device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4 v = {a, b, c, d};
   return __builtin_bit_cast(half8, v);
 }
 
+// Two fp8-e4m3 bytes (values c * 2^-9, c = 0..15) of `bytes` -> f16x2 holding the
+// integers c exactly (word 0 = bytes 0,1; word 1 = bytes 2,3).
+template <bool HI_WORD>
+__device__ __forceinline__ uint32_t codes_f16x2(uint32_t bytes) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bytes, 512.0f, HI_WORD));
+}
+
 // Channel of K-slot kappa (0..7) of lane half h in score MFMA p (0..7): the order in
 // which unpack_k() below lays codes into the B operand.
 template <int BITS>
 __device__ __forceinline__ int qk_channel(int p, int h, int kappa) {
-  if (BITS == 4) return 64 * h + 8 * p + (kappa >> 1) + 4 * (kappa & 1);
-  return 64 * h + 16 * (p >> 1) + 4 * (p & 1) + (kappa >> 1) + 8 * (kappa & 1);
+  if (BITS == 4) return 64 * h + 8 * p + 2 * (kappa & 3) + (kappa >> 2);
+  return 64 * h + 16 * (p >> 1) + 8 * (p & 1) + (kappa >> 1) + 4 * (kappa & 1);
 }
 
 // B operand of score MFMA p from the lane's packed key codes (kc: 8 dwords at INT4 =
@@ -56,40 +68,48 @@ template <int BITS>
 __device__ __forceinline__ half8 unpack_k(const uint32_t* kc, int p) {
   if (BITS == 4) {
     const uint32_t w = kc[p];
-    return as_half8(w & 0x000F000Fu, (w >> 4) & 0x000F000Fu, (w >> 8) & 0x000F000Fu, (w >> 12) & 0x000F000Fu);
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // nibbles 0,2,4,6 / 1,3,5,7
+    return as_half8(codes_f16x2<false>(lo), codes_f16x2<true>(lo), codes_f16x2<false>(hi), codes_f16x2<true>(hi));
   }
-  const uint32_t w = kc[p >> 1] >> (8 * (p & 1));
-  return as_half8(w & 0x00030003u, (w >> 2) & 0x00030003u, (w >> 4) & 0x00030003u, (w >> 6) & 0x00030003u);
+  const uint32_t w = kc[p >> 1];
+  const uint32_t b0 = w & 0x03030303u, b1 = (w >> 2) & 0x03030303u;  // crumbs j, j+4, j+8, j+12
+  const uint32_t b2 = (w >> 4) & 0x03030303u, b3 = (w >> 6) & 0x03030303u;
+  if (p & 1)
+    return as_half8(codes_f16x2<true>(b0), codes_f16x2<true>(b1), codes_f16x2<true>(b2), codes_f16x2<true>(b3));
+  return as_half8(codes_f16x2<false>(b0), codes_f16x2<false>(b1), codes_f16x2<false>(b2), codes_f16x2<false>(b3));
 }
 
 // Channel of column n (0..15) of value N-tile nt (0..7), matching unpack_v().
 template <int BITS>
 __device__ __forceinline__ int pv_channel(int nt, int n) {
-  if (BITS == 4) return 4 * (n + 16 * (nt >> 2)) + (nt & 3);
-  return 8 * n + nt;
+  if (BITS == 4) return 4 * (n + 16 * (nt >> 2)) + 2 * (nt & 1) + ((nt >> 1) & 1);
+  return 8 * n + (nt >> 1) + 4 * (nt & 1);
 }
 
-// B operand of value N-tile nt: vc holds 8 tokens x one 16-bit code word (4 dwords, two
-// tokens each) for word n (INT4: words n and n+16, i.e. vc[0..3] and vc[4..7]).
+// B operand of value N-tile nt: vc holds, for 8 tokens (4 token pairs, one dword each),
+// one 16-bit code word with the pair's bytes interleaved: [t0 byte0, t1 byte0, t0 byte1,
+// t1 byte1]. INT4: words n and n+16 in vc[0..3] and vc[4..7].
 template <int BITS>
 __device__ __forceinline__ half8 unpack_v(const uint32_t* vc, int nt) {
+  uint32_t x[4];
   if (BITS == 4) {
     const uint32_t* w = vc + 4 * (nt >> 2);
-    const int s = 4 * (nt & 3);
-    return as_half8((w[0] >> s) & 0x000F000Fu, (w[1] >> s) & 0x000F000Fu, (w[2] >> s) & 0x000F000Fu,
-                    (w[3] >> s) & 0x000F000Fu);
+    const int sh = 4 * ((nt >> 1) & 1);  // low or high nibbles
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = (w[k] >> sh) & 0x0F0F0F0Fu;
+  } else {
+    const int sh = 2 * (nt >> 1);  // crumb j of each byte
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = (vc[k] >> sh) & 0x03030303u;
   }
-  const int s = 2 * nt;
-  return as_half8((vc[0] >> s) & 0x00030003u, (vc[1] >> s) & 0x00030003u, (vc[2] >> s) & 0x00030003u,
-                  (vc[3] >> s) & 0x00030003u);
+  if (nt & 1)
+    return as_half8(codes_f16x2<true>(x[0]), codes_f16x2<true>(x[1]), codes_f16x2<true>(x[2]), codes_f16x2<true>(x[3]));
+  return as_half8(codes_f16x2<false>(x[0]), codes_f16x2<false>(x[1]), codes_f16x2<false>(x[2]),
+                  codes_f16x2<false>(x[3]));
 }
 
 __device__ __forceinline__ float lo_f16(uint32_t m) { return f16_bits_to_float(m & 0xFFFFu); }
 __device__ __forceinline__ float hi_f16(uint32_t m) { return f16_bits_to_float(m >> 16); }
-
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  return float_to_f16_bits(a) | (float_to_f16_bits(b) << 16);
-}
 
 template <int BITS, int NG>
 struct Block {
@@ -254,7 +274,8 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   floatx4 acc[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float zacc = 0.f;  // lane-partial sum_t p * zero for row (jjV, gV)
+  float zacc = 0.f;       // lane-partial sum_t p * zero for row (jjV, gV)
+  float wscale = 256.0f;  // power-of-two scale on the value weights (see the value step)
 
   // one 32-token block: scores, online softmax, values. TAIL is the partition's last
   // block when it ends inside the block: only there are tokens masked.
@@ -264,8 +285,12 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     floatx16 cs = __builtin_amdgcn_mfma_f32_32x32x16_f16(aqk_s[0][lane], unpack_k<BITS>(cur.kc, 0),
                                                           floatx16{}, 0, 0, 0);
 #pragma unroll
-    for (int p = 1; p < 8; ++p)
+    for (int p = 1; p < 8; ++p) {
+      // keep each unpack next to its MFMA (bounds the live operand registers)
+      __builtin_amdgcn_sched_barrier(0);
       cs = __builtin_amdgcn_mfma_f32_32x32x16_f16(aqk_s[p][lane], unpack_k<BITS>(cur.kc, p), cs, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float logit[2];
 #pragma unroll
     for (int j2 = 0; j2 < 2; ++j2) {
@@ -277,7 +302,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
         sa = __builtin_fmaf(lo_f16(cur.km[g]), cs[4 * g + 2 * j2 + 1], sa);
         zb = __builtin_fmaf(hi_f16(cur.km[g]), qsum[j2][g], zb);
       }
-      logit[j2] = __builtin_fmaf(sa, kTwo24, zb);
+      logit[j2] = sa + zb;
       if (TAIL) logit[j2] = (t0 + nQ < end) ? logit[j2] : -INFINITY;
     }
 
@@ -324,8 +349,23 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       pv[0] = x0[0]; pv[1] = x0[1]; pv[2] = x0[2]; pv[3] = x0[3];
       pv[4] = x1[0]; pv[5] = x1[1]; pv[6] = x1[2]; pv[7] = x1[3];
     }
-    // w = p * scale (masked tokens have p = 0 exactly); split w = hi + lo with hi = w's
-    // top 11 significant bits (exact in f16) and lo = the exact remainder
+    // w = wscale * p * scale (masked tokens have p = 0 exactly); w = hi + lo with hi =
+    // w's top 11 significant bits (exact in f16) and lo the exact remainder, rounded
+    // toward zero to f16. wscale = 2^8 keeps lo clear of the f16 subnormal range; if a
+    // value scale >= 128 ever appears (w could then pass the f16 maximum), the
+    // accumulators are rescaled by the exact power of two and wscale becomes 1.
+    if (wscale > 1.0f) {
+      bool big = false;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) big |= lo_f16(cur.vm[kk]) >= 128.0f;
+      if (__any(big)) {
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[nt][r] *= 1.0f / 256.0f;
+        wscale = 1.0f;
+      }
+    }
     uint32_t ahi[4], alo[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -333,7 +373,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int kk = 2 * k + e;
-        float w = __builtin_fmaf(lo_f16(cur.vm[kk]), pv[kk], 0.f);
+        float w = __builtin_fmaf(lo_f16(cur.vm[kk]), pv[kk] * wscale, 0.f);
         float zp = hi_f16(cur.vm[kk]);
         if (TAIL && t0 + 8 * q4 + kk >= end) {
           w = 0.f;
@@ -350,6 +390,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     const half8 Alo = as_half8(alo[0], alo[1], alo[2], alo[3]);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
+      __builtin_amdgcn_sched_barrier(0);
       const half8 bv = unpack_v<BITS>(cur.vc, nt);
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, bv, acc[nt], 0, 0, 0);
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, bv, acc[nt], 0, 0, 0);
@@ -402,7 +443,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     const int ch = pv_channel<BITS>(nt, r16);
     if (ch / G == q4) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) part[r * head_stride + ch] = __builtin_fmaf(acc[nt][r], kTwo24, zrow[r]);
+      for (int r = 0; r < R; ++r) part[r * head_stride + ch] = __builtin_fmaf(acc[nt][r], 1.0f / wscale, zrow[r]);
     }
   }
   if (nQ == 0) {

@@ -119,17 +119,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
   // p . vhat: each thread owns (head, channel) pairs
   for (int idx = tid; idx < R * kD; idx += kThreads) {
     const int j = idx / kD, i = idx % kD;
-    const int w = i * BITS / 16;            // 16-bit word holding channel i
-    const int sh = (i * BITS) % 16;
+    const int byte = i * BITS / 8;          // byte of the packed row holding channel i
+    const int sh = (i * BITS) % 8;
     float o = 0.f;
     for (int t = start; t < end; ++t) {
       const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + t / c.page];
       const int off = t % c.page;
       const int64_t u = page * c.hkv + h;
       const int64_t tile = off >> 4;
-      const uint16_t* words =
-          reinterpret_cast<const uint16_t*>(c.vc + u * c.page * c.row_bytes + tile * 16 * c.row_bytes);
-      const uint32_t code = (static_cast<uint32_t>(words[w * 16 + (off & 15)]) >> sh) & kMask;
+      const uint8_t* tb = c.vc + ((u * c.page) + (off & ~15)) * c.row_bytes;
+      const int ot = off & 15;
+      const uint32_t code =
+          (static_cast<uint32_t>(tb[(byte >> 1) * 32 + (ot >> 1) * 4 + (byte & 1) * 2 + (ot & 1)]) >> sh) & kMask;
       const uint32_t m = c.vm[((u * (c.page >> 4) + tile) * c.ngroups + i / G) * 16 + (off & 15)];
       const float vhat = __builtin_fmaf(static_cast<float>(code), f16_bits_to_float(m & 0xFFFFu),
                                         f16_bits_to_float(m >> 16));

@@ -120,14 +120,19 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(DevCache c, const 
       reinterpret_cast<uint16_t*>(dst)[lane] = static_cast<uint16_t>(packed);
     if (group_leader) c.km[(u * c.page + off) * c.ngroups + g] = meta;
   } else {
+    // V tiles: 16-token tiles, rows cut into 16-bit words, each word's token pairs
+    // byte-interleaved (byte b of word w of token o at w*32 + (o/2)*4 + b*2 + o%2), so
+    // the decode kernel's one mask turns a token pair's same-channel codes into
+    // adjacent bytes. Every token owns whole bytes: appends never share a byte.
+    uint8_t* tb = c.vc + ((u * c.page) + (off & ~15)) * c.row_bytes;
     const int64_t tile = off >> 4;
     const int o = off & 15;
-    uint16_t* words = reinterpret_cast<uint16_t*>(c.vc + u * c.page * c.row_bytes + tile * 16 * c.row_bytes);
-    if (BITS == 4) {
-      words[(2 * lane) * 16 + o] = static_cast<uint16_t>(packed);
-      words[(2 * lane + 1) * 16 + o] = static_cast<uint16_t>(packed >> 16);
-    } else {
-      words[lane * 16 + o] = static_cast<uint16_t>(packed);
+    const int pair = (o >> 1) * 4 + (o & 1);
+    constexpr int kBytes = BITS * 8 / 8;  // packed bytes held by this lane (8 channels)
+#pragma unroll
+    for (int k = 0; k < kBytes; ++k) {
+      const int byte = lane * kBytes + k;  // byte index within the token row
+      tb[(byte >> 1) * 32 + pair + (byte & 1) * 2] = static_cast<uint8_t>(packed >> (8 * k));
     }
     if (group_leader) c.vm[((u * (c.page >> 4) + tile) * c.ngroups + g) * 16 + o] = meta;
   }
@@ -156,13 +161,15 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DevCache c, int which, 
   } else {
     const int64_t tile = off >> 4;
     const int o = off & 15;
-    const uint16_t* words =
-        reinterpret_cast<const uint16_t*>(c.vc + u * c.page * c.row_bytes + tile * 16 * c.row_bytes);
-    if (BITS == 4)
-      packed = static_cast<uint32_t>(words[(2 * lane) * 16 + o]) |
-               (static_cast<uint32_t>(words[(2 * lane + 1) * 16 + o]) << 16);
-    else
-      packed = words[lane * 16 + o];
+    const uint8_t* tb = c.vc + ((u * c.page) + (off & ~15)) * c.row_bytes;
+    const int pair = (o >> 1) * 4 + (o & 1);
+    constexpr int kBytes = BITS * 8 / 8;
+    packed = 0;
+#pragma unroll
+    for (int k = 0; k < kBytes; ++k) {
+      const int byte = lane * kBytes + k;
+      packed |= static_cast<uint32_t>(tb[(byte >> 1) * 32 + pair + (byte & 1) * 2]) << (8 * k);
+    }
     meta = c.vm[((u * (c.page >> 4) + tile) * c.ngroups + g) * 16 + o];
   }
   const float s = f16_bits_to_float(meta & 0xFFFFu);

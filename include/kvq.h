@@ -58,9 +58,10 @@ typedef enum kvq_status {
  *
  *   k_codes  uint8 [u][page_size][RB]          token-major packed key codes
  *   k_meta   half2 [u][page_size][NG]          {scale (low 16 bits), zero (high)}
- *   v_codes  uint8 [u][page_size/16][RB/2][16][2]   each 16-token tile stores the
- *            packed rows cut into 16-bit words, word-major (word w of token o at
- *            byte (w*16 + o)*2 of the tile)
+ *   v_codes  uint8 [u][page_size/16][RB/2][8][2][2] each 16-token tile stores the
+ *            packed rows cut into 16-bit words, word-major; within a word the 8
+ *            token pairs keep both tokens' low bytes, then both high bytes (byte b
+ *            of word w of token o at w*32 + (o/2)*4 + b*2 + o%2 of the tile)
  *   v_meta   half2 [u][page_size/16][NG][16]   {scale, zero}, group-major per tile
  *
  * Packed rows are little-endian: INT4 channel 2k in the low nibble of byte k and

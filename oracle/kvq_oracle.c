@@ -264,10 +264,15 @@ static int64_t k_code_off(const orc_cache* c, int64_t page, int h, int off) {
 static int64_t k_meta_off(const orc_cache* c, int64_t page, int h, int off, int g) {
   return (((page * c->num_kv_heads + h) * c->page_size + off) * n_groups(c) + g) * 4;
 }
-static int64_t v_word_off(const orc_cache* c, int64_t page, int h, int off, int w) {
+/* byte k (0..RB-1) of the packed V row of token `off`: 16-token tiles; inside a tile the
+   row is cut into 16-bit words and each word holds its 16 tokens as 8 token pairs, the
+   pair's low bytes then its high bytes, byte-interleaved by token:
+   word w, token o, byte b -> w*32 + (o/2)*4 + b*2 + (o%2) */
+static int64_t v_byte_off(const orc_cache* c, int64_t page, int h, int off, int k) {
   int64_t base = (page * c->num_kv_heads + h) * c->page_size * row_bytes(c);
   int64_t tile = (off / 16) * 16 * row_bytes(c);
-  return base + tile + ((int64_t)w * 16 + off % 16) * 2;
+  int o = off % 16, w = k / 2, b = k % 2;
+  return base + tile + (int64_t)w * 32 + (o / 2) * 4 + b * 2 + (o % 2);
 }
 static int64_t v_meta_off(const orc_cache* c, int64_t page, int h, int off, int g) {
   int64_t tiles = c->page_size / 16;
@@ -292,11 +297,7 @@ static void store_row(const orc_cache* c, int which, int64_t page, int h, int of
       put_u16(m + 2, zero[g]);
     }
   } else {
-    for (int w = 0; w < rb / 2; ++w) {
-      uint8_t* p = c->v_codes + v_word_off(c, page, h, off, w);
-      p[0] = packed[2 * w];
-      p[1] = packed[2 * w + 1];
-    }
+    for (int k = 0; k < rb; ++k) c->v_codes[v_byte_off(c, page, h, off, k)] = packed[k];
     for (int g = 0; g < n_groups(c); ++g) {
       uint8_t* m = c->v_meta + v_meta_off(c, page, h, off, g);
       put_u16(m, scale[g]);
@@ -316,11 +317,7 @@ static void load_row(const orc_cache* c, int which, int64_t page, int h, int off
       zero[g] = get_u16(m + 2);
     }
   } else {
-    for (int w = 0; w < rb / 2; ++w) {
-      const uint8_t* p = c->v_codes + v_word_off(c, page, h, off, w);
-      packed[2 * w] = p[0];
-      packed[2 * w + 1] = p[1];
-    }
+    for (int k = 0; k < rb; ++k) packed[k] = c->v_codes[v_byte_off(c, page, h, off, k)];
     for (int g = 0; g < n_groups(c); ++g) {
       const uint8_t* m = c->v_meta + v_meta_off(c, page, h, off, g);
       scale[g] = get_u16(m);

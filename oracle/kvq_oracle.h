@@ -39,9 +39,11 @@
  *                                             (INT4) 2k at bits 0-3, 2k+1 at 4-7;
  *                                             (INT2) 4k+e at bits 2e.
  *   K meta        [u][P][NG] x {u16 scale, u16 zero}  (scale in the low half)
- *   V codes       [u][P/16][RB/2][16][2 bytes] the same packed row cut into 16-bit
- *                                             words; word w of token o of a 16-token
- *                                             tile sits at (w*16 + o)*2.
+ *   V codes       [u][P/16][RB/2][8][2][2]    the same packed row cut into 16-bit
+ *                                             words; per 16-token tile and word, the
+ *                                             8 token pairs each store both tokens'
+ *                                             low bytes then both high bytes: word w,
+ *                                             token o, byte b at w*32 + (o/2)*4 + b*2 + o%2.
  *   V meta        [u][P/16][NG][16] x {u16 scale, u16 zero}
  */
 #ifndef KVQ_ORACLE_H

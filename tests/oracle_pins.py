@@ -325,9 +325,10 @@ def check_cache_layout_bytes():
     kmeta = ((page * Hkv + 1) * P + off) * 4 * 4
     assert list(c.k_meta[kmeta:kmeta + 4]) == [0x00, 0x3C, 0x00, 0x00]  # scale 1.0, zero 0.0
     vbase = (page * Hkv + 1) * P * rb + (off // 16) * 16 * rb
-    for w in range(rb // 2):
-        o = vbase + (w * 16 + off % 16) * 2
-        assert list(c.v_codes[o:o + 2]) == list(packed[2 * w:2 * w + 2]), w
+    o = off % 16
+    for k in range(rb):
+        w, b = divmod(k, 2)
+        assert c.v_codes[vbase + w * 32 + (o // 2) * 4 + b * 2 + o % 2] == packed[k], k
     vmeta = (((page * Hkv + 1) * (P // 16) + off // 16) * 4 + 3) * 16 + off % 16
     assert list(c.v_meta[vmeta * 4:vmeta * 4 + 4]) == [0x00, 0x3C, 0x00, 0x00]
 

@@ -41,8 +41,8 @@ MUTANTS = [
      "int h = j % c->num_kv_heads;\n      double* o = out + ((int64_t)b * num_q_heads + j) * d;\n      if (T <= 0)"),
     ("softmax_scale", "double sigma = softmax_scale > 0.0 ? softmax_scale : 1.0 / sqrt((double)d);\n  double* qv",
      "double sigma = softmax_scale > 0.0 ? softmax_scale : 1.0 / (double)d;\n  double* qv"),
-    ("v_words_token_major", "return base + tile + ((int64_t)w * 16 + off % 16) * 2;",
-     "return base + tile + ((int64_t)(off % 16) * (row_bytes(c) / 2) + w) * 2;"),
+    ("v_tokens_not_interleaved", "return base + tile + (int64_t)w * 32 + (o / 2) * 4 + b * 2 + (o % 2);",
+     "return base + tile + (int64_t)w * 32 + o * 2 + b;"),
     ("meta_swapped", "      put_u16(m, scale[g]);\n      put_u16(m + 2, zero[g]);\n    }\n  } else {",
      "      put_u16(m, zero[g]);\n      put_u16(m + 2, scale[g]);\n    }\n  } else {"),
     ("q_not_rotated", "orc_rotate_dense_f64(qv, qr, d, c->hadamard_block);", "orc_rotate_dense_f64(qv, qr, d, 0);"),
