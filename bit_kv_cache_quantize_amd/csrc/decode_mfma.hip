@@ -7,7 +7,7 @@
 // Dual-QK (Abstract): the query receives the keys' rotation, so q.k is preserved.
 //
 // One wavefront (one 64-thread workgroup) owns one (sequence, kv head, partition)
-// and walks it in 32-token blocks (two 16-token tiles).
+// and walks it in 32-token blocks (two 16-token tiles), grouped in super-blocks of 8.
 //
 // Scores, v_mfma_f32_32x32x16_f16, 8 per block: C[row][token] = sum_ch A[row][ch] B[ch][token]
 //   A rows = (query head jj, digit d, group g): the rotated, pre-scaled query of head jj
@@ -18,17 +18,21 @@
 //     fed as f16 subnormals c * 2^-24 with a mask alone, but the matrix core sums
 //     products of subnormal operands with visibly less precision.)
 //   logit = sum_g scale_g * (C[jj,hi,g] + C[jj,lo,g]) + sum_g zero_g * Qsum[jj][g].
-// Softmax: online, exp2 domain (the query carries softmax_scale * log2 e); the running
-//   max is only rescaled when a block raises it.
+// Softmax: exp2 domain (the query carries softmax_scale * log2 e). A super-block first
+//   computes the logits of all its blocks (kept in registers), then updates the running
+//   max once and rescales the state once, then runs the values: no data-dependent
+//   branch touches the accumulators.
 // Values, v_mfma_f32_16x16x32_f16, 16 per block: O[row][ch] += sum_t W[row][t] V[t][ch]
-//   A rows = (query head jj, group g), W = 2^8 p * scale_g(t) split into f16 hi (w's top
-//     11 bits) and lo (the remainder), two MFMAs into the same accumulator; the 2^8 keeps
-//     lo out of the f16 subnormal range (and drops to 1, exactly, if any scale >= 128);
+//   A rows = (query head jj, group g), W = 2^8 p * scale_g(t) split into f16 hi (W
+//     rounded toward zero to f16: its top 11 bits) and lo (the exact remainder, rounded
+//     toward zero), two MFMAs into the same accumulator; the 2^8 keeps lo out of the f16
+//     subnormal range. A value scale >= 128 could push W past the f16 maximum: the
+//     partition is then recomputed with W = p * scale.
 //   B = value codes as exact f16 integers, from one 16-byte load per lane of the cache's
 //     16-token tiles, where each word's token pairs are byte-interleaved so one mask
 //     yields both tokens' codes for a channel side by side;
 //   the zero term sum_t p * zero_g(t) is accumulated separately in fp32.
-// Partials (unnormalised o, running max m, sum l) go to the workspace for the combine.
+// Partials (unnormalised o, reference max m, sum l) go to the workspace for the combine.
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -40,7 +44,6 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 
 __device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   u32x4 v = {a, b, c, d};
@@ -112,12 +115,23 @@ __device__ __forceinline__ float lo_f16(uint32_t m) { return f16_bits_to_float(m
 __device__ __forceinline__ float hi_f16(uint32_t m) { return f16_bits_to_float(m >> 16); }
 
 template <int BITS, int NG>
-struct Block {
+struct KBlock {
   uint32_t kc[BITS == 4 ? 8 : 4];  // key codes of the lane's token, channels 64h..64h+63
   uint32_t km[NG];                 // key {scale, zero} of the lane's token
+};
+
+template <int BITS>
+struct VBlock {
   uint32_t vc[BITS == 4 ? 8 : 4];  // value code words, 8 tokens
   uint32_t vm[8];                  // value {scale, zero} of group g, 8 tokens
 };
+
+__device__ __forceinline__ _Float16 f16_lo(uint32_t m) {
+  return __builtin_bit_cast(_Float16, static_cast<uint16_t>(m & 0xFFFFu));
+}
+
+constexpr int NBS = 8;  // blocks per super-block
+constexpr int PF = 2;   // blocks loaded ahead
 
 template <int BITS, int G, int R>
 __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
@@ -140,27 +154,174 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   __shared__ float qsum_s[4][4];
   __shared__ half8 aqk_s[8][64];  // score A operands, re-read from LDS for every block
 
-  // ---- rotated, scaled query of the R heads of this kv head (LDS) ----
-  for (int idx = lane; idx < R * 128; idx += 64) {
-    const int j = idx >> 7, i = idx & 127;
-    const uint16_t bits = a.q[(static_cast<int64_t>(b) * a.num_q_heads + hk * R + j) * 128 + i];
-    q_s[j][i] = __uint_as_float(static_cast<uint32_t>(bits) << 16);
-  }
-  __syncthreads();
-  if (a.hblock > 0) {
-    for (int s = 1; s < a.hblock; s <<= 1) {
-      for (int idx = lane; idx < R * 64; idx += 64) {
-        const int j = idx >> 6, pi = idx & 63;
-        const int i = (pi / s) * 2 * s + (pi % s);
-        const float x0 = q_s[j][i], x1 = q_s[j][i + s];
-        q_s[j][i] = x0 + x1;
-        q_s[j][i + s] = x0 - x1;
+  // lane roles: scores use (hQ, nQ) = (lane / 32, lane % 32): heads 2hQ, 2hQ+1 of token nQ;
+  // values use (q4, r16) = (lane / 16, lane % 16): A row r16 = 4g + jj, tokens 8q4..8q4+7,
+  // B column r16.
+  const int hQ = lane >> 5, nQ = lane & 31;
+  const int q4 = lane >> 4, r16 = lane & 15;
+  const int jjV = r16 & 3, gV = r16 >> 2;
+  const int gVc = gV < NG ? gV : NG - 1;
+  // -1 the compiler cannot see: keeps fma(f16 -> f32 x, -1, y) a single mixed-precision FMA
+  float neg1 = -1.0f;
+  asm("" : "+s"(neg1));
+
+  // ---- where the partition's blocks live ----
+  // nfull full 32-token blocks, then possibly one partial block
+  const int nblk = (end - start + 31) >> 5;
+  const int nfull = (end - start) >> 5;
+  const int P = c.page;
+  const int pg_first = start / P;
+  const int pg_last = (end - 1) / P;
+  // contiguous case: the whole partition in one page, token t in row row_base + t
+  const bool one_page = pg_last == pg_first;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
+  const int64_t row_base =
+      (static_cast<int64_t>(bt[pg_first]) * c.hkv + hk) * P - static_cast<int64_t>(pg_first) * P;
+  // Blocks are loaded in order, each kind through its own cursor: block index, the
+  // page and in-page offset of its first token, and (paged case) a window of 64
+  // block-table entries in a register, lane i holding logical page wbase + i. Past the
+  // last block the cursor stays (the load re-reads the last block; nothing is computed
+  // from it).
+  struct Cursor {
+    int blk, pg, off, wbase;
+    int32_t bt_w;
+  };
+  auto window = [&](int first) -> int32_t { return (first + lane <= pg_last) ? bt[first + lane] : 0; };
+  const Cursor cur0 = {0, pg_first, start - pg_first * P, pg_first, one_page ? 0 : window(pg_first)};
+  auto page_row = [&](Cursor& cu, int pg, int off) -> int64_t {  // row of token pg * P + off
+    if (pg - cu.wbase >= 64) {  // a cursor visits pages in increasing order
+      cu.wbase = pg;
+      cu.bt_w = window(pg);
+    }
+    const int32_t phys = __builtin_amdgcn_readlane(cu.bt_w, pg - cu.wbase);
+    return (static_cast<int64_t>(phys) * c.hkv + hk) * P + off;
+  };
+  auto advance = [&](Cursor& cu) {
+    if (cu.blk + 1 < nblk) {
+      ++cu.blk;
+      cu.off += 32;
+      while (cu.off >= P) {
+        cu.off -= P;
+        ++cu.pg;
       }
-      __syncthreads();
+    }
+  };
+  // rows of the cursor block's two 16-token tiles (a tile past the partition end: the
+  // first tile again)
+  auto tile_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
+    const int t0 = start + 32 * cu.blk;
+    if (one_page) {
+      row0 = row_base + t0;
+      row1 = (t0 + 16 < end) ? row0 + 16 : row0;
+      return;
+    }
+    row0 = page_row(cu, cu.pg, cu.off);
+    if (t0 + 16 >= end) {
+      row1 = row0;
+    } else if (cu.off + 16 < P) {
+      row1 = row0 + 16;
+    } else {
+      row1 = page_row(cu, cu.pg + 1, cu.off + 16 - P);
+    }
+  };
+
+  auto load_k = [&](Cursor& cu) {
+    KBlock<BITS, NG> kb;
+    int64_t row0, row1;
+    tile_rows(cu, row0, row1);
+    advance(cu);
+    const int64_t row = ((nQ < 16) ? row0 : row1) + (nQ & 15);
+    const u32x4* src = reinterpret_cast<const u32x4*>(c.kc + row * RB + (RB / 2) * hQ);
+    const u32x4 x0 = src[0];
+    kb.kc[0] = x0[0]; kb.kc[1] = x0[1]; kb.kc[2] = x0[2]; kb.kc[3] = x0[3];
+    if (BITS == 4) {
+      const u32x4 x1 = src[1];
+      kb.kc[4] = x1[0]; kb.kc[5] = x1[1]; kb.kc[6] = x1[2]; kb.kc[7] = x1[3];
+    }
+    const uint32_t* m = c.km + row * NG;
+    if (NG == 4) {
+      const u32x4 mm = *reinterpret_cast<const u32x4*>(m);
+      kb.km[0] = mm[0]; kb.km[1] = mm[1]; kb.km[2 % NG] = mm[2]; kb.km[3 % NG] = mm[3];
+    } else if (NG == 2) {
+      const uint2 mm = *reinterpret_cast<const uint2*>(m);
+      kb.km[0] = mm.x; kb.km[1 % NG] = mm.y;
+    } else {
+      kb.km[0] = m[0];
+    }
+    return kb;
+  };
+  auto load_v = [&](Cursor& cu) {
+    VBlock<BITS> vb;
+    int64_t row0, row1;
+    tile_rows(cu, row0, row1);
+    advance(cu);
+    const int64_t trow = (q4 < 2) ? row0 : row1;  // value tile of tokens 8q4..8q4+7
+    const uint8_t* tile = c.vc + trow * RB;
+    const int o = 8 * (q4 & 1);
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(tile + (r16 * 16 + o) * 2);
+    vb.vc[0] = w0[0]; vb.vc[1] = w0[1]; vb.vc[2] = w0[2]; vb.vc[3] = w0[3];
+    if (BITS == 4) {
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(tile + ((r16 + 16) * 16 + o) * 2);
+      vb.vc[4] = w1[0]; vb.vc[5] = w1[1]; vb.vc[6] = w1[2]; vb.vc[7] = w1[3];
+    }
+    const int64_t mrow = trow / 16;  // = u * (P/16) + tile index
+    const u32x4* vm = reinterpret_cast<const u32x4*>(c.vm + (mrow * NG + gVc) * 16 + o);
+    const u32x4 m0 = vm[0], m1 = vm[1];
+    vb.vm[0] = m0[0]; vb.vm[1] = m0[1]; vb.vm[2] = m0[2]; vb.vm[3] = m0[3];
+    vb.vm[4] = m1[0]; vb.vm[5] = m1[1]; vb.vm[6] = m1[2]; vb.vm[7] = m1[3];
+    return vb;
+  };
+
+  // the first key blocks are in flight while the query is prepared
+  KBlock<BITS, NG> kb[PF + 1];
+  VBlock<BITS> vb[PF + 1];
+  Cursor kcur = cur0, vcur = cur0;
+#pragma unroll
+  for (int j = 0; j < PF; ++j) kb[j] = load_k(kcur);
+
+  // ---- rotated, scaled query of the R heads of this kv head ----
+  // lane (head lane / 16, channels 8 * (lane % 16) + 0..7); the Walsh-Hadamard butterfly
+  // in registers: strides 1, 2, 4 in the lane, 8..64 across the 16 lanes of the head
+  {
+    const int jq = lane >> 4, c16 = lane & 15;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (jq < R) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(
+          a.q + (static_cast<int64_t>(b) * a.num_q_heads + hk * R + jq) * 128 + 8 * c16);
+      x[0] = bf16_lo(raw.x); x[1] = bf16_hi(raw.x); x[2] = bf16_lo(raw.y); x[3] = bf16_hi(raw.y);
+      x[4] = bf16_lo(raw.z); x[5] = bf16_hi(raw.z); x[6] = bf16_lo(raw.w); x[7] = bf16_hi(raw.w);
+    }
+    const int hb = a.hblock;
+#pragma unroll
+    for (int s = 1; s < 8; s <<= 1) {
+      if (s < hb) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (!(e & s)) {
+            const float u = x[e], v = x[e + s];
+            x[e] = u + v;
+            x[e + s] = u - v;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      if (8 * m < hb) {
+        const bool upper = (c16 & m) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float y = __shfl_xor(x[e], m, 64);
+          x[e] = upper ? (y - x[e]) : (x[e] + y);
+        }
+      }
+    }
+    const float qmul = (hb > 0 ? a.rot_c : 1.0f) * a.qscale;
+    if (jq < R) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q_s[jq][8 * c16 + e] = x[e] * qmul;
     }
   }
-  const float qmul = (a.hblock > 0 ? a.rot_c : 1.0f) * a.qscale;
-  for (int idx = lane; idx < R * 128; idx += 64) q_s[idx >> 7][idx & 127] *= qmul;
   __syncthreads();
 
   // Qsum[jj][g]: group sums of the query as the MFMA sees it (hi + lo)
@@ -203,134 +364,92 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // lane roles: scores use (hQ, nQ) = (lane / 32, lane % 32): heads 2hQ, 2hQ+1 of token nQ;
-  // values use (q4, r16) = (lane / 16, lane % 16): A row r16 = 4g + jj, tokens 8q4..8q4+7,
-  // B column r16.
-  const int hQ = lane >> 5, nQ = lane & 31;
-  const int q4 = lane >> 4, r16 = lane & 15;
-  const int jjV = r16 & 3, gV = r16 >> 2;
-  const int gVc = gV < NG ? gV : NG - 1;
-  const bool rowV = gV < NG && jjV < R;
-
   float qsum[2][NG];
 #pragma unroll
   for (int j2 = 0; j2 < 2; ++j2)
 #pragma unroll
     for (int g = 0; g < NG; ++g) qsum[j2][g] = (2 * hQ + j2 < R) ? qsum_s[2 * hQ + j2][g] : 0.f;
 
-  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
-  const int P = c.page;
-
-  auto load = [&](int t0) {
-    Block<BITS, NG> blk;
-    // the pages of the block's two 16-token tiles; a tile past the partition end
-    // reads the first tile again (its tokens are masked)
-    const int t1 = (t0 + 16 < end) ? t0 + 16 : t0;
-    const int64_t u0 = static_cast<int64_t>(bt[t0 / P]) * c.hkv + hk;
-    const int64_t u1 = static_cast<int64_t>(bt[t1 / P]) * c.hkv + hk;
-    const int64_t row0 = u0 * P + t0 % P;  // token row of tile 0's first token
-    const int64_t row1 = u1 * P + t1 % P;
-    {
-      const int64_t row = ((nQ < 16) ? row0 : row1) + (nQ & 15);
-      const u32x4* src = reinterpret_cast<const u32x4*>(c.kc + row * RB + (RB / 2) * hQ);
-      const u32x4 x0 = src[0];
-      blk.kc[0] = x0[0]; blk.kc[1] = x0[1]; blk.kc[2] = x0[2]; blk.kc[3] = x0[3];
-      if (BITS == 4) {
-        const u32x4 x1 = src[1];
-        blk.kc[4] = x1[0]; blk.kc[5] = x1[1]; blk.kc[6] = x1[2]; blk.kc[7] = x1[3];
-      }
-      const uint32_t* m = c.km + row * NG;
-      if (NG == 4) {
-        const u32x4 mm = *reinterpret_cast<const u32x4*>(m);
-        blk.km[0] = mm[0]; blk.km[1] = mm[1]; blk.km[2 % NG] = mm[2]; blk.km[3 % NG] = mm[3];
-      } else if (NG == 2) {
-        const uint2 mm = *reinterpret_cast<const uint2*>(m);
-        blk.km[0] = mm.x; blk.km[1 % NG] = mm.y;
-      } else {
-        blk.km[0] = m[0];
-      }
-    }
-    {
-      const int64_t trow = (q4 < 2) ? row0 : row1;  // value tile of tokens 8q4..8q4+7
-      const uint8_t* tile = c.vc + trow * RB;
-      const int o = 8 * (q4 & 1);
-      const u32x4 w0 = *reinterpret_cast<const u32x4*>(tile + (r16 * 16 + o) * 2);
-      blk.vc[0] = w0[0]; blk.vc[1] = w0[1]; blk.vc[2] = w0[2]; blk.vc[3] = w0[3];
-      if (BITS == 4) {
-        const u32x4 w1 = *reinterpret_cast<const u32x4*>(tile + ((r16 + 16) * 16 + o) * 2);
-        blk.vc[4] = w1[0]; blk.vc[5] = w1[1]; blk.vc[6] = w1[2]; blk.vc[7] = w1[3];
-      }
-      const int64_t mrow = trow / 16;  // = u * (P/16) + tile index
-      const u32x4* vm = reinterpret_cast<const u32x4*>(c.vm + (mrow * NG + gVc) * 16 + o);
-      const u32x4 m0 = vm[0], m1 = vm[1];
-      blk.vm[0] = m0[0]; blk.vm[1] = m0[1]; blk.vm[2] = m0[2]; blk.vm[3] = m0[3];
-      blk.vm[4] = m1[0]; blk.vm[5] = m1[1]; blk.vm[6] = m1[2]; blk.vm[7] = m1[3];
-    }
-    return blk;
-  };
-
-  float mrun[2] = {-INFINITY, -INFINITY};  // running max of heads 2hQ, 2hQ+1 (exp2 domain)
-  float lsum[2] = {0.f, 0.f};              // lane-partial sums of p
+  // ---- state (exp2 domain) ----
+  // p = 2^(logit - mref) with mref = mrun - shift, mrun the running max: the value
+  // weights carry 2^shift (shift = 8), which keeps the f16 split of p * scale clear of the
+  // f16 subnormal range; written partials hold mref, so the factor cancels in the
+  // combine. A value scale >= 128 could push the weights past the f16 maximum: the
+  // partition is then recomputed with shift = 0.
+  float mrun[2], mref[2], lsum[2], zacc;
   floatx4 acc[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float zacc = 0.f;       // lane-partial sum_t p * zero for row (jjV, gV)
-  float wscale = 256.0f;  // power-of-two scale on the value weights (see the value step)
 
-  // one 32-token block: scores, online softmax, values. TAIL is the partition's last
-  // block when it ends inside the block: only there are tokens masked.
-  auto compute = [&](const Block<BITS, NG>& cur, int t0, auto tail) {
+  // scores of one block: logits of heads 2hQ, 2hQ+1 for token nQ
+  auto qk = [&](const KBlock<BITS, NG>& kb, int t0, auto tail, float (&logit)[2]) {
     constexpr bool TAIL = decltype(tail)::value;
-    // ---- scores ----
-    floatx16 cs = __builtin_amdgcn_mfma_f32_32x32x16_f16(aqk_s[0][lane], unpack_k<BITS>(cur.kc, 0),
-                                                          floatx16{}, 0, 0, 0);
+    half8 a_next[2] = {aqk_s[0][lane], aqk_s[1][lane]};
+    floatx16 cs;
 #pragma unroll
-    for (int p = 1; p < 8; ++p) {
-      // keep each unpack next to its MFMA (bounds the live operand registers)
+    for (int p = 0; p < 8; ++p) {
+      // keep each unpack next to its MFMA (bounds the live operand registers); the A
+      // operand is read from LDS two MFMAs ahead
       __builtin_amdgcn_sched_barrier(0);
-      cs = __builtin_amdgcn_mfma_f32_32x32x16_f16(aqk_s[p][lane], unpack_k<BITS>(cur.kc, p), cs, 0, 0, 0);
+      const half8 ap = a_next[p & 1];
+      if (p + 2 < 8) a_next[p & 1] = aqk_s[p + 2][lane];
+      cs = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap, unpack_k<BITS>(kb.kc, p), p == 0 ? floatx16{} : cs, 0, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    float logit[2];
 #pragma unroll
     for (int j2 = 0; j2 < 2; ++j2) {
       float sa = 0.f, zb = 0.f;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         // fp16 scale/zero feed the fused mixed-precision FMAs directly
-        sa = __builtin_fmaf(lo_f16(cur.km[g]), cs[4 * g + 2 * j2], sa);
-        sa = __builtin_fmaf(lo_f16(cur.km[g]), cs[4 * g + 2 * j2 + 1], sa);
-        zb = __builtin_fmaf(hi_f16(cur.km[g]), qsum[j2][g], zb);
+        sa = __builtin_fmaf(lo_f16(kb.km[g]), cs[4 * g + 2 * j2], sa);
+        sa = __builtin_fmaf(lo_f16(kb.km[g]), cs[4 * g + 2 * j2 + 1], sa);
+        zb = __builtin_fmaf(hi_f16(kb.km[g]), qsum[j2][g], zb);
       }
       logit[j2] = sa + zb;
       if (TAIL) logit[j2] = (t0 + nQ < end) ? logit[j2] : -INFINITY;
     }
+    // materialise the logits here: left to the compiler, the fold sinks to the logits'
+    // later use and every block's 16 score registers stay live until then
+    asm volatile("" : "+v"(logit[0]), "+v"(logit[1]));
+  };
 
-    // ---- online softmax (exp2 domain) ----
-    const bool raise = logit[0] > mrun[0] || logit[1] > mrun[1];
-    if (__any(raise)) {
-      float bm0 = logit[0], bm1 = logit[1];
+  // new running max from the lane-local maxima bm of a group of blocks; rescales the
+  // state to the new reference (unconditionally: alpha = 1 when the max is unchanged)
+  auto advance_max = [&](float bm0, float bm1, float shift) {
 #pragma unroll
-      for (int m = 16; m >= 1; m >>= 1) {
-        bm0 = fmaxf(bm0, __shfl_xor(bm0, m, 64));
-        bm1 = fmaxf(bm1, __shfl_xor(bm1, m, 64));
-      }
-      const float n0 = fmaxf(mrun[0], bm0), n1 = fmaxf(mrun[1], bm1);
-      const float al0 = exp2f(mrun[0] - n0), al1 = exp2f(mrun[1] - n1);
-      mrun[0] = n0;
-      mrun[1] = n1;
-      lsum[0] *= al0;
-      lsum[1] *= al1;
-      // scale factors of all four heads, everywhere (heads 0,1 live in lanes 0..31)
-      const float alpha[4] = {__shfl(al0, 0, 64), __shfl(al1, 0, 64), __shfl(al0, 32, 64), __shfl(al1, 32, 64)};
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[nt][r] *= alpha[r];
-      zacc *= alpha[jjV];
+    for (int m = 16; m >= 1; m >>= 1) {
+      bm0 = fmaxf(bm0, __shfl_xor(bm0, m, 64));
+      bm1 = fmaxf(bm1, __shfl_xor(bm1, m, 64));
     }
-    const float p0 = exp2f(logit[0] - mrun[0]);
-    const float p1 = exp2f(logit[1] - mrun[1]);
+    const float n0 = fmaxf(mrun[0], bm0), n1 = fmaxf(mrun[1], bm1);
+    const float r0 = n0 - shift, r1 = n1 - shift;
+    const float al0 = __builtin_amdgcn_exp2f(mref[0] - r0), al1 = __builtin_amdgcn_exp2f(mref[1] - r1);
+    mrun[0] = n0;
+    mrun[1] = n1;
+    mref[0] = r0;
+    mref[1] = r1;
+    lsum[0] *= al0;
+    lsum[1] *= al1;
+    // scale factors of all four heads, everywhere (heads 0,1 live in lanes 0..31)
+    const float alpha[4] = {__shfl(al0, 0, 64), __shfl(al1, 0, 64), __shfl(al0, 32, 64), __shfl(al1, 32, 64)};
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[nt][r] *= alpha[r];
+    zacc *= alpha[jjV];
+  };
+
+  // values of one block from its logits; false if a value scale is too large for the
+  // f16 weights at this shift (nothing is accumulated then)
+  auto pv = [&](const VBlock<BITS>& vb, const float (&logit)[2], int t0, auto tail, bool check_big) -> bool {
+    constexpr bool TAIL = decltype(tail)::value;
+    if (check_big) {
+      _Float16 smax = 0;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) smax = __builtin_fmaxf16(smax, f16_lo(vb.vm[kk]));
+      if (__any(smax >= static_cast<_Float16>(128.0f))) return false;
+    }
+    const float p0 = __builtin_amdgcn_exp2f(logit[0] - mref[0]);
+    const float p1 = __builtin_amdgcn_exp2f(logit[1] - mref[1]);
     lsum[0] += p0;
     lsum[1] += p1;
     // A single wavefront owns this LDS: its DS instructions complete in program order,
@@ -340,8 +459,6 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- values ----
     float pv[8];
     {
       const floatx4* src = reinterpret_cast<const floatx4*>(&p_s[jjV][8 * q4]);
@@ -349,81 +466,110 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       pv[0] = x0[0]; pv[1] = x0[1]; pv[2] = x0[2]; pv[3] = x0[3];
       pv[4] = x1[0]; pv[5] = x1[1]; pv[6] = x1[2]; pv[7] = x1[3];
     }
-    // w = wscale * p * scale (masked tokens have p = 0 exactly); w = hi + lo with hi =
-    // w's top 11 significant bits (exact in f16) and lo the exact remainder, rounded
-    // toward zero to f16. wscale = 2^8 keeps lo clear of the f16 subnormal range; if a
-    // value scale >= 128 ever appears (w could then pass the f16 maximum), the
-    // accumulators are rescaled by the exact power of two and wscale becomes 1.
-    if (wscale > 1.0f) {
-      bool big = false;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) big |= lo_f16(cur.vm[kk]) >= 128.0f;
-      if (__any(big)) {
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[nt][r] *= 1.0f / 256.0f;
-        wscale = 1.0f;
-      }
-    }
+    // w = p * scale (masked tokens have p = 0 exactly); w = hi + lo with hi = w's top 11
+    // significant bits (exact in f16) and lo the exact remainder, rounded toward zero to f16
     uint32_t ahi[4], alo[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      float hi[2], lo[2];
+      float w[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int kk = 2 * k + e;
-        float w = __builtin_fmaf(lo_f16(cur.vm[kk]), pv[kk] * wscale, 0.f);
-        float zp = hi_f16(cur.vm[kk]);
-        if (TAIL && t0 + 8 * q4 + kk >= end) {
-          w = 0.f;
+        w[e] = __builtin_fmaf(lo_f16(vb.vm[kk]), pv[kk], 0.f);
+        float zp = hi_f16(vb.vm[kk]);
+        if (TAIL && t0 + 8 * q4 + kk >= end) {  // slots past the end may hold anything
+          w[e] = 0.f;
           zp = 0.f;
         }
         zacc = __builtin_fmaf(zp, pv[kk], zacc);
-        hi[e] = __uint_as_float(__float_as_uint(w) & 0xFFFFE000u);
-        lo[e] = w - hi[e];
       }
-      ahi[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi[0], hi[1]));
-      alo[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo[0], lo[1]));
+      // hi = w rounded toward zero to f16 (w's top 11 significant bits), lo = the exact
+      // remainder w - hi, rounded toward zero to f16
+      ahi[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w[0], w[1]));
+      const float lo0 = __builtin_fmaf(lo_f16(ahi[k]), neg1, w[0]);
+      const float lo1 = __builtin_fmaf(hi_f16(ahi[k]), neg1, w[1]);
+      alo[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo0, lo1));
     }
     const half8 Ahi = as_half8(ahi[0], ahi[1], ahi[2], ahi[3]);
     const half8 Alo = as_half8(alo[0], alo[1], alo[2], alo[3]);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
+    for (int nt = 0; nt < 8; nt += 2) {
+      // two N-tiles at a time: the hi and lo products of one tile are not back to back
       __builtin_amdgcn_sched_barrier(0);
-      const half8 bv = unpack_v<BITS>(cur.vc, nt);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, bv, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, bv, acc[nt], 0, 0, 0);
+      const half8 bv0 = unpack_v<BITS>(vb.vc, nt);
+      const half8 bv1 = unpack_v<BITS>(vb.vc, nt + 1);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, bv0, acc[nt], 0, 0, 0);
+      acc[nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, bv1, acc[nt + 1], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, bv0, acc[nt], 0, 0, 0);
+      acc[nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, bv1, acc[nt + 1], 0, 0, 0);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
-  auto run = [&](const Block<BITS, NG>& cur, int t0) {
-    if (t0 + 32 <= end)
-      compute(cur, t0, std::false_type{});
-    else
-      compute(cur, t0, std::true_type{});
+    return true;
   };
 
-  // Software pipeline: the next block's loads are in flight while one block is
-  // computed. Loads are issued unconditionally (a block past the end re-reads the last
-  // block, already in cache) so the number of outstanding loads is the same on every
-  // path and each block waits only for its own data. The two buffers alternate
-  // through a 2x unrolled loop, so no register copies are needed.
-  const int last = start + ((end - 1 - start) & ~31);
-  Block<BITS, NG> b0 = load(start);
-  Block<BITS, NG> b1;
-  for (int t0 = start;;) {
-    b1 = load(min(t0 + 32, last));
-    run(b0, t0);
-    if ((t0 += 32) >= end) break;
-    b0 = load(min(t0 + 32, last));
-    run(b1, t0);
-    if ((t0 += 32) >= end) break;
+  // The partition in super-blocks of NBS blocks, each in two passes: the scores of all
+  // its blocks (logits stay in registers), one max update, then the values. Loads run
+  // two blocks ahead through the sequence K(0..NBS-1), V(0..NBS-1), K of the next
+  // super-block, ... into three rotating buffers per kind (static slots: the super-block
+  // body is fully unrolled). Super-blocks of NBS full blocks run without guards or
+  // masks; the rest of the partition (fewer than NBS full blocks and a partial block)
+  // forms one last, guarded and masked super-block.
+  auto super_block = [&](int base, int n, auto guard, bool check_big) -> bool {
+    constexpr bool GUARD = decltype(guard)::value;
+    float lg[NBS][2];
+    float bm0 = -INFINITY, bm1 = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NBS; ++j) {
+      if (j + PF < NBS)
+        kb[(j + PF) % (PF + 1)] = load_k(kcur);
+      else
+        vb[(j + PF - NBS) % (PF + 1)] = load_v(vcur);
+      if (!GUARD || j < n) {
+        qk(kb[j % (PF + 1)], start + 32 * (base + j), guard, lg[j]);
+        bm0 = fmaxf(bm0, lg[j][0]);
+        bm1 = fmaxf(bm1, lg[j][1]);
+      }
+    }
+    advance_max(bm0, bm1, check_big ? 8.0f : 0.0f);
+#pragma unroll
+    for (int j = 0; j < NBS; ++j) {
+      if (j + PF < NBS)
+        vb[(j + PF) % (PF + 1)] = load_v(vcur);
+      else
+        kb[(j + PF - NBS) % (PF + 1)] = load_k(kcur);
+      if (!GUARD || j < n) {
+        if (!pv(vb[j % (PF + 1)], lg[j], start + 32 * (base + j), guard, check_big)) return false;
+      }
+    }
+    return true;
+  };
+  // p carries 2^8 (check_big) unless a value scale >= 128 shows up: the partition is
+  // then recomputed with p unscaled
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    const bool check_big = attempt == 0;
+    mrun[0] = mrun[1] = -INFINITY;
+    mref[0] = mref[1] = -INFINITY;
+    lsum[0] = lsum[1] = 0.f;
+    zacc = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (attempt > 0) {
+      kcur = cur0;
+      vcur = cur0;
+#pragma unroll
+      for (int j = 0; j < PF; ++j) kb[j] = load_k(kcur);
+    }
+    const int nsbf = nfull / NBS;
+    bool ok = true;
+    for (int sb = 0; sb < nsbf && ok; ++sb) ok = super_block(sb * NBS, NBS, std::false_type{}, check_big);
+    const int rem = nblk - nsbf * NBS;
+    if (ok && rem > 0) ok = super_block(nsbf * NBS, rem, std::true_type{}, check_big);
+    if (ok) break;
   }
 
-  // ---- partials: o[jj][ch] = 2^24 acc + Z[jj][g(ch)], m, l ----
+  // ---- partials: o[jj][ch] = acc + Z[jj][g(ch)], m = mref, l ----
 #pragma unroll
   for (int m = 16; m >= 1; m >>= 1) {
     lsum[0] += __shfl_xor(lsum[0], m, 64);
@@ -443,7 +589,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     const int ch = pv_channel<BITS>(nt, r16);
     if (ch / G == q4) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) part[r * head_stride + ch] = __builtin_fmaf(acc[nt][r], 1.0f / wscale, zrow[r]);
+      for (int r = 0; r < R; ++r) part[r * head_stride + ch] = acc[nt][r] + zrow[r];
     }
   }
   if (nQ == 0) {
@@ -451,7 +597,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     for (int j2 = 0; j2 < 2; ++j2) {
       const int jj = 2 * hQ + j2;
       if (jj < R) {
-        part[jj * head_stride + 128] = mrun[j2];
+        part[jj * head_stride + 128] = mref[j2];
         part[jj * head_stride + 129] = lsum[j2];
       }
     }

@@ -117,6 +117,8 @@ DECODE_CASES = {
     "gqa2": _small("c2", batch=2, num_q_heads=16, context=333),
     "int4_g128_hb0": _small("c2", batch=2, context=257, group_size=128, hadamard_block=0),
     "int2_g32_hb32": _small("c2", batch=2, context=190, bits=2, group_size=32, hadamard_block=32),
+    # 48-token pages: a 32-token block's second tile often starts on the next page
+    "paged48": _small("c5", batch=4, ragged=(40, 900), page_size=48),
 }
 
 
@@ -228,3 +230,49 @@ def test_output_guard_bytes_untouched():
     torch.cuda.synchronize()
     assert torch.all(outbuf[:guard] == 12345.0) and torch.all(outbuf[-guard:] == 12345.0)
     assert torch.all(wsbuf[:guard] == 0xAB) and torch.all(wsbuf[-guard:] == 0xAB)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 0])
+def test_decode_long_paged_partitions(num_splits):
+    """16-token pages, partitions of up to ~160 pages: the kernel walks its block table
+    through a 64-entry window that must move forward several times per partition."""
+    w = _small("c5", batch=2, ragged=(1500, 2600))
+    print(f"[decode] long paged partitions, num_splits={num_splits}", flush=True)
+    p = make_pair(w, DEV, extra_tokens=1)
+    append_step(p, 0, DEV)
+    got, want = decode_both(p, DEV, num_splits=num_splits)
+    err = max_err(got, want)
+    record(f"long_paged/splits={num_splits}", err)
+    assert err <= TOL
+
+
+def test_decode_large_value_scales():
+    """A few tokens with values in the thousands (value scales >= 128): the kernel's
+    scaled f16 value weights would overflow, so it must fall back to unscaled weights
+    for the partition and still match the oracle."""
+    w = _small("c2", batch=2, context=700)
+    print("[decode] large value scales", flush=True)
+    lens = wl.seq_lens(w)
+    geo = wl.geometry(w, lens=lens)
+    gpu = kvq.KVCache.allocate(128, 8, 4, 32, 128, geo.page_size, geo.num_pages, device=DEV)
+    ref = oracle.Cache(128, 8, 4, 32, 128, geo.page_size, geo.num_pages)
+    for b in range(w.batch):
+        T = int(lens[b])
+        k = wl.keys(w, b, 0, T)
+        v = wl.values(w, b, 0, T).float()
+        v[400 + 37 * b] *= 4000.0          # one token per sequence, mid-partition
+        v[650, :2] *= 300.0                # and a few large channels near the end
+        v = v.to(torch.bfloat16)
+        slots = geo.slots(b, 0, T)
+        kvq.quantize_append(gpu, k.to(DEV), v.to(DEV), slots.to(DEV))
+        ref.append(wl.bf16_bits(k), wl.bf16_bits(v), slots.numpy())
+    q = wl.queries(w)
+    for ns in (1, 0):
+        out = kvq.decode_attention(gpu, q.to(DEV), geo.block_table.to(DEV), lens.to(DEV), int(lens.max()),
+                                   num_splits=ns)
+        got = out.cpu().numpy().astype(np.float64)
+        want = ref.decode(wl.bf16_bits(q), geo.block_table.numpy(), lens.numpy())
+        err = max_err(got, want)
+        record(f"large_value_scales/splits={ns}", err)
+        print(f"  splits={ns}: max |o| {np.max(np.abs(want)):.1f}, max-abs err {err:.3e}", flush=True)
+        assert np.all(np.isfinite(got)) and err <= TOL
