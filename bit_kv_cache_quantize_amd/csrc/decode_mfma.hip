@@ -57,12 +57,13 @@ __device__ __forceinline__ uint32_t codes_f16x2(uint32_t bytes) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bytes, 512.0f, HI_WORD));
 }
 
-// Channel of K-slot kappa (0..7) of lane half h in score MFMA p (0..7): the order in
-// which unpack_k() below lays codes into the B operand.
+// Score MFMA p, lane half h covers the 8 channels 64h + 8p .. 64h + 8p + 7; its K-slot
+// kappa (0..7) holds the channel at this position within them, the order in which
+// unpack_k() below lays codes into the B operand.
 template <int BITS>
-__device__ __forceinline__ int qk_channel(int p, int h, int kappa) {
-  if (BITS == 4) return 64 * h + 8 * p + 2 * (kappa & 3) + (kappa >> 2);
-  return 64 * h + 16 * (p >> 1) + 8 * (p & 1) + (kappa >> 1) + 4 * (kappa & 1);
+__device__ __forceinline__ int qk_slot_channel(int kappa) {
+  if (BITS == 4) return 2 * (kappa & 3) + (kappa >> 2);
+  return (kappa >> 1) + 4 * (kappa & 1);
 }
 
 // B operand of score MFMA p from the lane's packed key codes (kc: 8 dwords at INT4 =
@@ -149,7 +150,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   if (start >= T) return;
   const int end = min(T, start + a.split_len);
 
-  __shared__ float q_s[4][128];
+  __shared__ float o_s[4][128];  // partial outputs, staged for the workspace stores
   __shared__ float p_s[4][32];
   __shared__ float qsum_s[4][4];
   __shared__ half8 aqk_s[8][64];  // score A operands, re-read from LDS for every block
@@ -225,48 +226,70 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     }
   };
 
+  // per-lane byte offsets of a full block of a contiguous partition (rows r0 .. r0 + 31)
+  const uint32_t koff = static_cast<uint32_t>(nQ * RB + (RB / 2) * hQ);
+  const uint32_t kmoff = static_cast<uint32_t>(nQ * NG * 4);
+  const uint32_t voff = static_cast<uint32_t>((q4 < 2 ? 0 : 16 * RB) + (r16 * 16 + 8 * (q4 & 1)) * 2);
+  const uint32_t vmoff = static_cast<uint32_t>(((q4 < 2 ? 0 : NG) + gVc) * 64 + 8 * (q4 & 1) * 4);
+
   auto load_k = [&](Cursor& cu) {
     KBlock<BITS, NG> kb;
-    int64_t row0, row1;
-    tile_rows(cu, row0, row1);
+    const uint8_t* src;
+    const uint8_t* msrc;
+    if (one_page && start + 32 * cu.blk + 32 <= end) {
+      const int64_t r0 = row_base + start + 32 * cu.blk;
+      src = c.kc + r0 * RB + koff;
+      msrc = reinterpret_cast<const uint8_t*>(c.km) + r0 * (NG * 4) + kmoff;
+    } else {
+      int64_t row0, row1;
+      tile_rows(cu, row0, row1);
+      const int64_t row = ((nQ < 16) ? row0 : row1) + (nQ & 15);
+      src = c.kc + row * RB + (RB / 2) * hQ;
+      msrc = reinterpret_cast<const uint8_t*>(c.km + row * NG);
+    }
     advance(cu);
-    const int64_t row = ((nQ < 16) ? row0 : row1) + (nQ & 15);
-    const u32x4* src = reinterpret_cast<const u32x4*>(c.kc + row * RB + (RB / 2) * hQ);
-    const u32x4 x0 = src[0];
+    const u32x4 x0 = *reinterpret_cast<const u32x4*>(src);
     kb.kc[0] = x0[0]; kb.kc[1] = x0[1]; kb.kc[2] = x0[2]; kb.kc[3] = x0[3];
     if (BITS == 4) {
-      const u32x4 x1 = src[1];
+      const u32x4 x1 = *reinterpret_cast<const u32x4*>(src + 16);
       kb.kc[4] = x1[0]; kb.kc[5] = x1[1]; kb.kc[6] = x1[2]; kb.kc[7] = x1[3];
     }
-    const uint32_t* m = c.km + row * NG;
     if (NG == 4) {
-      const u32x4 mm = *reinterpret_cast<const u32x4*>(m);
+      const u32x4 mm = *reinterpret_cast<const u32x4*>(msrc);
       kb.km[0] = mm[0]; kb.km[1] = mm[1]; kb.km[2 % NG] = mm[2]; kb.km[3 % NG] = mm[3];
     } else if (NG == 2) {
-      const uint2 mm = *reinterpret_cast<const uint2*>(m);
+      const uint2 mm = *reinterpret_cast<const uint2*>(msrc);
       kb.km[0] = mm.x; kb.km[1 % NG] = mm.y;
     } else {
-      kb.km[0] = m[0];
+      kb.km[0] = *reinterpret_cast<const uint32_t*>(msrc);
     }
     return kb;
   };
   auto load_v = [&](Cursor& cu) {
     VBlock<BITS> vb;
-    int64_t row0, row1;
-    tile_rows(cu, row0, row1);
+    const uint8_t* src;   // this lane's first code word of its 8 tokens
+    const uint8_t* msrc;  // this lane's value {scale, zero} of group gVc, its 8 tokens
+    if (one_page && start + 32 * cu.blk + 32 <= end) {
+      const int64_t r0 = row_base + start + 32 * cu.blk;  // a multiple of 16
+      src = c.vc + r0 * RB + voff;
+      msrc = reinterpret_cast<const uint8_t*>(c.vm) + (r0 / 16) * (NG * 64) + vmoff;
+    } else {
+      int64_t row0, row1;
+      tile_rows(cu, row0, row1);
+      const int64_t trow = (q4 < 2) ? row0 : row1;  // value tile of tokens 8q4..8q4+7
+      const int o = 8 * (q4 & 1);
+      src = c.vc + trow * RB + (r16 * 16 + o) * 2;
+      msrc = reinterpret_cast<const uint8_t*>(c.vm + ((trow / 16) * NG + gVc) * 16 + o);
+    }
     advance(cu);
-    const int64_t trow = (q4 < 2) ? row0 : row1;  // value tile of tokens 8q4..8q4+7
-    const uint8_t* tile = c.vc + trow * RB;
-    const int o = 8 * (q4 & 1);
-    const u32x4 w0 = *reinterpret_cast<const u32x4*>(tile + (r16 * 16 + o) * 2);
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(src);
     vb.vc[0] = w0[0]; vb.vc[1] = w0[1]; vb.vc[2] = w0[2]; vb.vc[3] = w0[3];
     if (BITS == 4) {
-      const u32x4 w1 = *reinterpret_cast<const u32x4*>(tile + ((r16 + 16) * 16 + o) * 2);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 16 * 16 * 2);
       vb.vc[4] = w1[0]; vb.vc[5] = w1[1]; vb.vc[6] = w1[2]; vb.vc[7] = w1[3];
     }
-    const int64_t mrow = trow / 16;  // = u * (P/16) + tile index
-    const u32x4* vm = reinterpret_cast<const u32x4*>(c.vm + (mrow * NG + gVc) * 16 + o);
-    const u32x4 m0 = vm[0], m1 = vm[1];
+    const u32x4 m0 = *reinterpret_cast<const u32x4*>(msrc);
+    const u32x4 m1 = *reinterpret_cast<const u32x4*>(msrc + 16);
     vb.vm[0] = m0[0]; vb.vm[1] = m0[1]; vb.vm[2] = m0[2]; vb.vm[3] = m0[3];
     vb.vm[4] = m1[0]; vb.vm[5] = m1[1]; vb.vm[6] = m1[2]; vb.vm[7] = m1[3];
     return vb;
@@ -279,9 +302,12 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < PF; ++j) kb[j] = load_k(kcur);
 
-  // ---- rotated, scaled query of the R heads of this kv head ----
-  // lane (head lane / 16, channels 8 * (lane % 16) + 0..7); the Walsh-Hadamard butterfly
-  // in registers: strides 1, 2, 4 in the lane, 8..64 across the 16 lanes of the head
+  // ---- rotated, scaled query of the R heads: score A operands and group sums ----
+  // Lane (head jq = lane / 16, chunk c16 = lane % 16) holds channels 8 c16 .. 8 c16 + 7.
+  // The Walsh-Hadamard butterfly runs in registers: strides 1, 2, 4 in the lane, 8..64
+  // across the 16 lanes of the head. A chunk is exactly the channel set of score MFMA
+  // p = c16 % 8 in lane half c16 / 8, so each lane writes its own two A rows (hi and lo
+  // digit of head jq, group of the chunk); every other row of an A operand is zero.
   {
     const int jq = lane >> 4, c16 = lane & 15;
     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -317,50 +343,33 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       }
     }
     const float qmul = (hb > 0 ? a.rot_c : 1.0f) * a.qscale;
-    if (jq < R) {
+    _Float16 hi[8], lo[8];
+    float part = 0.f;  // group sum of the query as the MFMA sees it (hi + lo)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) q_s[jq][8 * c16 + e] = x[e] * qmul;
+    for (int e = 0; e < 8; ++e) {
+      const float v = x[e] * qmul;
+      hi[e] = static_cast<_Float16>(v);
+      lo[e] = static_cast<_Float16>(v - static_cast<float>(hi[e]));
+      part += static_cast<float>(hi[e]) + static_cast<float>(lo[e]);
     }
-  }
-  __syncthreads();
-
-  // Qsum[jj][g]: group sums of the query as the MFMA sees it (hi + lo)
-  {
-    const int jj = lane >> 4, c8 = lane & 15;
-    float part = 0.f;
-    if (jj < R) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = q_s[jj][8 * c8 + e];
-        const float hi = static_cast<float>(static_cast<_Float16>(x));
-        const float lo = static_cast<float>(static_cast<_Float16>(x - hi));
-        part += hi + lo;
+    for (int p = 0; p < 8; ++p) aqk_s[p][lane] = half8{};
+    __syncthreads();
+    if (jq < R) {
+      const int p = c16 & 7, hA = c16 >> 3, g = (8 * c16) / G;
+      const int rho = 8 * g + 4 * (jq >> 1) + 2 * (jq & 1);
+      half8 vh, vl;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        vh[k] = hi[qk_slot_channel<BITS>(k)];
+        vl[k] = lo[qk_slot_channel<BITS>(k)];
       }
+      aqk_s[p][32 * hA + rho] = vh;
+      aqk_s[p][32 * hA + rho + 1] = vl;
     }
 #pragma unroll
     for (int m = 1; m < G / 8; m <<= 1) part += __shfl_xor(part, m, 64);
-    if (jj < R && (c8 % (G / 8)) == 0) qsum_s[jj][(8 * c8) / G] = part;
-  }
-
-  // score A operands: lane = (half hA, row rho), rho = 8g + 4(jj>>1) + 2(jj&1) + d
-  {
-    const int hA = lane >> 5, rho = lane & 31;
-    const int gA = rho >> 3, jjA = ((rho >> 2) & 1) * 2 + ((rho >> 1) & 1), dA = rho & 1;
-    const bool row_ok = gA < NG && jjA < R;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int ch = qk_channel<BITS>(p, hA, k);
-        _Float16 v = 0;
-        if (row_ok && ch / G == gA) {
-          const float x = q_s[jjA][ch];
-          const _Float16 hi = static_cast<_Float16>(x);
-          v = dA ? static_cast<_Float16>(x - static_cast<float>(hi)) : hi;
-        }
-        aqk_s[p][lane][k] = v;
-      }
-    }
+    if (jq < R && (c16 % (G / 8)) == 0) qsum_s[jq][(8 * c16) / G] = part;
   }
   __syncthreads();
 
@@ -580,7 +589,9 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   float* part = a.partials + (static_cast<int64_t>(b) * a.num_q_heads + hk * R) * a.num_splits * 130 +
                 static_cast<int64_t>(split) * 130;
   const int64_t head_stride = static_cast<int64_t>(a.num_splits) * 130;
-  // lane (q4, r16) owns accumulator rows 4*q4 + r = (jj = r, g = q4) at column r16
+  // lane (q4, r16) owns accumulator rows 4*q4 + r = (jj = r, g = q4) at column r16; the
+  // rows of group q4 hold head jj's output for the channels of that group. Staged in LDS
+  // so the workspace is written with 8-byte stores.
   float zrow[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) zrow[r] = __shfl(zacc, 4 * (q4 < NG ? q4 : 0) + r, 64);
@@ -589,7 +600,16 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     const int ch = pv_channel<BITS>(nt, r16);
     if (ch / G == q4) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) part[r * head_stride + ch] = acc[nt][r] + zrow[r];
+      for (int r = 0; r < R; ++r) o_s[r][ch] = acc[nt][r] + zrow[r];
+    }
+  }
+  __syncthreads();
+  {
+    const int jo = lane >> 4, c8 = 8 * (lane & 15);
+    if (jo < R) {
+      float2* dst = reinterpret_cast<float2*>(part + jo * head_stride + c8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = make_float2(o_s[jo][c8 + 2 * e], o_s[jo][c8 + 2 * e + 1]);
     }
   }
   if (nQ == 0) {
