@@ -120,8 +120,9 @@ def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
 class KVCache:
     """A quantized KV cache: four caller-owned device planes plus the description.
 
-    Layout (see include/kvq.h): K codes token-major, K meta token-major, V codes in
-    16-token word-major tiles, V meta group-major per tile; fp16 {scale, zero} pairs.
+    Layout (see include/kvq.h): 16-token tiles; K codes chunk-major per tile, K meta
+    token-major, V codes word-major per tile with token pairs byte-interleaved, V meta
+    in two 4-token parts per group and half-tile; fp16 {scale, zero} pairs.
     """
 
     head_dim: int

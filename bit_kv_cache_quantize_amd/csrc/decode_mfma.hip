@@ -132,7 +132,7 @@ __device__ __forceinline__ _Float16 f16_lo(uint32_t m) {
 }
 
 constexpr int NBS = 8;  // blocks per super-block
-constexpr int PF = 2;   // blocks loaded ahead
+constexpr int PF = 3;   // blocks loaded ahead
 
 template <int BITS, int G, int R>
 __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   const int end = min(T, start + a.split_len);
 
   __shared__ float o_s[4][128];  // partial outputs, staged for the workspace stores
-  __shared__ float p_s[4][32];
+  __shared__ float p_s[NBS][4][32];  // p of a super-block's blocks, per head and token
   __shared__ float qsum_s[4][4];
   __shared__ half8 aqk_s[8][64];  // score A operands, re-read from LDS for every block
 
@@ -226,49 +226,62 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  // per-lane byte offsets of a full block of a contiguous partition (rows r0 .. r0 + 31)
-  const uint32_t koff = static_cast<uint32_t>(nQ * RB + (RB / 2) * hQ);
+  // This lane's pieces of a block, relative to the first token row (tile_row) of its
+  // tile: key codes, the 16-byte chunk(s) of channels 64 hQ .. 64 hQ + 63 of token nQ
+  // (tiles are chunk-major, so one load instruction reads whole cache lines); value code
+  // words r16 and r16 + 16 of tokens 8 (q4 % 2) ..; value {scale, zero} of group gVc,
+  // tokens 8 (q4 % 2) + 0..3 (part 0) and + 4..7 (part 1).
+  constexpr int KCH = BITS == 4 ? 2 : 1;  // key code chunks per lane
+  const uint32_t kc_lane = static_cast<uint32_t>((KCH * hQ * 16 + (nQ & 15)) * 16);
+  const uint32_t vc_lane = static_cast<uint32_t>((r16 * 16 + 8 * (q4 & 1)) * 2);
+  const uint32_t vm_lane = static_cast<uint32_t>((gVc * 2 + (q4 & 1)) * 4 * 4);
+  // the same for a full block of a contiguous partition, relative to the block's first row
+  const uint32_t koff = static_cast<uint32_t>((nQ >> 4) * 16 * RB) + kc_lane;
   const uint32_t kmoff = static_cast<uint32_t>(nQ * NG * 4);
-  const uint32_t voff = static_cast<uint32_t>((q4 < 2 ? 0 : 16 * RB) + (r16 * 16 + 8 * (q4 & 1)) * 2);
-  const uint32_t vmoff = static_cast<uint32_t>(((q4 < 2 ? 0 : NG) + gVc) * 64 + 8 * (q4 & 1) * 4);
+  const uint32_t voff = static_cast<uint32_t>(q4 < 2 ? 0 : 16 * RB) + vc_lane;
+  const uint32_t vmoff = static_cast<uint32_t>(q4 < 2 ? 0 : NG * 64) + vm_lane;
+  // Key and value streams are read once: non-temporal loads. V meta loads cover whole
+  // cache lines only with 4 groups; with fewer they read half lines and stay cached.
+  auto ld16 = [](const uint8_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); };
 
   auto load_k = [&](Cursor& cu) {
     KBlock<BITS, NG> kb;
     const uint8_t* src;
     const uint8_t* msrc;
     if (one_page && start + 32 * cu.blk + 32 <= end) {
-      const int64_t r0 = row_base + start + 32 * cu.blk;
+      const int64_t r0 = row_base + start + 32 * cu.blk;  // a multiple of 16
       src = c.kc + r0 * RB + koff;
       msrc = reinterpret_cast<const uint8_t*>(c.km) + r0 * (NG * 4) + kmoff;
     } else {
       int64_t row0, row1;
       tile_rows(cu, row0, row1);
-      const int64_t row = ((nQ < 16) ? row0 : row1) + (nQ & 15);
-      src = c.kc + row * RB + (RB / 2) * hQ;
-      msrc = reinterpret_cast<const uint8_t*>(c.km + row * NG);
+      const int64_t trow = (nQ < 16) ? row0 : row1;
+      src = c.kc + trow * RB + kc_lane;
+      msrc = reinterpret_cast<const uint8_t*>(c.km + (trow + (nQ & 15)) * NG);
     }
     advance(cu);
-    const u32x4 x0 = *reinterpret_cast<const u32x4*>(src);
+    const u32x4 x0 = ld16(src);
     kb.kc[0] = x0[0]; kb.kc[1] = x0[1]; kb.kc[2] = x0[2]; kb.kc[3] = x0[3];
     if (BITS == 4) {
-      const u32x4 x1 = *reinterpret_cast<const u32x4*>(src + 16);
+      const u32x4 x1 = ld16(src + 16 * 16);  // the next chunk of the same token
       kb.kc[4] = x1[0]; kb.kc[5] = x1[1]; kb.kc[6] = x1[2]; kb.kc[7] = x1[3];
     }
     if (NG == 4) {
-      const u32x4 mm = *reinterpret_cast<const u32x4*>(msrc);
+      const u32x4 mm = ld16(msrc);
       kb.km[0] = mm[0]; kb.km[1] = mm[1]; kb.km[2 % NG] = mm[2]; kb.km[3 % NG] = mm[3];
     } else if (NG == 2) {
-      const uint2 mm = *reinterpret_cast<const uint2*>(msrc);
-      kb.km[0] = mm.x; kb.km[1 % NG] = mm.y;
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 mm = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(msrc));
+      kb.km[0] = mm[0]; kb.km[1 % NG] = mm[1];
     } else {
-      kb.km[0] = *reinterpret_cast<const uint32_t*>(msrc);
+      kb.km[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(msrc));
     }
     return kb;
   };
   auto load_v = [&](Cursor& cu) {
     VBlock<BITS> vb;
     const uint8_t* src;   // this lane's first code word of its 8 tokens
-    const uint8_t* msrc;  // this lane's value {scale, zero} of group gVc, its 8 tokens
+    const uint8_t* msrc;  // this lane's value {scale, zero}, part 0
     if (one_page && start + 32 * cu.blk + 32 <= end) {
       const int64_t r0 = row_base + start + 32 * cu.blk;  // a multiple of 16
       src = c.vc + r0 * RB + voff;
@@ -277,19 +290,19 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       int64_t row0, row1;
       tile_rows(cu, row0, row1);
       const int64_t trow = (q4 < 2) ? row0 : row1;  // value tile of tokens 8q4..8q4+7
-      const int o = 8 * (q4 & 1);
-      src = c.vc + trow * RB + (r16 * 16 + o) * 2;
-      msrc = reinterpret_cast<const uint8_t*>(c.vm + ((trow / 16) * NG + gVc) * 16 + o);
+      src = c.vc + trow * RB + vc_lane;
+      msrc = reinterpret_cast<const uint8_t*>(c.vm) + (trow / 16) * (NG * 64) + vm_lane;
     }
     advance(cu);
-    const u32x4 w0 = *reinterpret_cast<const u32x4*>(src);
+    const u32x4 w0 = ld16(src);
     vb.vc[0] = w0[0]; vb.vc[1] = w0[1]; vb.vc[2] = w0[2]; vb.vc[3] = w0[3];
     if (BITS == 4) {
-      const u32x4 w1 = *reinterpret_cast<const u32x4*>(src + 16 * 16 * 2);
+      const u32x4 w1 = ld16(src + 16 * 16 * 2);
       vb.vc[4] = w1[0]; vb.vc[5] = w1[1]; vb.vc[6] = w1[2]; vb.vc[7] = w1[3];
     }
-    const u32x4 m0 = *reinterpret_cast<const u32x4*>(msrc);
-    const u32x4 m1 = *reinterpret_cast<const u32x4*>(msrc + 16);
+    const uint8_t* msrc1 = msrc + NG * 8 * 4;  // part 1
+    const u32x4 m0 = NG == 4 ? ld16(msrc) : *reinterpret_cast<const u32x4*>(msrc);
+    const u32x4 m1 = NG == 4 ? ld16(msrc1) : *reinterpret_cast<const u32x4*>(msrc1);
     vb.vm[0] = m0[0]; vb.vm[1] = m0[1]; vb.vm[2] = m0[2]; vb.vm[3] = m0[3];
     vb.vm[4] = m1[0]; vb.vm[5] = m1[1]; vb.vm[6] = m1[2]; vb.vm[7] = m1[3];
     return vb;
@@ -447,9 +460,35 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     zacc *= alpha[jjV];
   };
 
-  // values of one block from its logits; false if a value scale is too large for the
+  // p = 2^(logit - mref) of the super-block's first n blocks: summed into l and published
+  // in LDS for the value steps (lane (hQ, nQ) holds heads 2hQ, 2hQ + 1 of token nQ; a
+  // value lane needs 8 tokens of one head)
+  auto publish_p = [&](const float (&lg)[NBS][2], int n, auto guard) {
+    constexpr bool GUARD = decltype(guard)::value;
+    // A single wavefront owns this LDS: its DS instructions complete in program order,
+    // so reads of the previous super-block's p are done before these writes land, and
+    // the exchange needs no barrier, only compiler fences.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < NBS; ++j) {
+      if (!GUARD || j < n) {
+        const float p0 = __builtin_amdgcn_exp2f(lg[j][0] - mref[0]);
+        const float p1 = __builtin_amdgcn_exp2f(lg[j][1] - mref[1]);
+        lsum[0] += p0;
+        lsum[1] += p1;
+        p_s[j][2 * hQ][nQ] = p0;
+        p_s[j][2 * hQ + 1][nQ] = p1;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // values of block j of the super-block; false if a value scale is too large for the
   // f16 weights at this shift (nothing is accumulated then)
-  auto pv = [&](const VBlock<BITS>& vb, const float (&logit)[2], int t0, auto tail, bool check_big) -> bool {
+  auto pv = [&](const VBlock<BITS>& vb, int j, int t0, auto tail, bool check_big) -> bool {
     constexpr bool TAIL = decltype(tail)::value;
     if (check_big) {
       _Float16 smax = 0;
@@ -457,20 +496,9 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       for (int kk = 0; kk < 8; ++kk) smax = __builtin_fmaxf16(smax, f16_lo(vb.vm[kk]));
       if (__any(smax >= static_cast<_Float16>(128.0f))) return false;
     }
-    const float p0 = __builtin_amdgcn_exp2f(logit[0] - mref[0]);
-    const float p1 = __builtin_amdgcn_exp2f(logit[1] - mref[1]);
-    lsum[0] += p0;
-    lsum[1] += p1;
-    // A single wavefront owns this LDS: its DS instructions complete in program order,
-    // so the exchange needs no barrier, only a compiler fence.
-    p_s[2 * hQ][nQ] = p0;
-    p_s[2 * hQ + 1][nQ] = p1;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float pv[8];
     {
-      const floatx4* src = reinterpret_cast<const floatx4*>(&p_s[jjV][8 * q4]);
+      const floatx4* src = reinterpret_cast<const floatx4*>(&p_s[j][jjV][8 * q4]);
       const floatx4 x0 = src[0], x1 = src[1];
       pv[0] = x0[0]; pv[1] = x0[1]; pv[2] = x0[2]; pv[3] = x0[3];
       pv[4] = x1[0]; pv[5] = x1[1]; pv[6] = x1[2]; pv[7] = x1[3];
@@ -512,9 +540,6 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, bv0, acc[nt], 0, 0, 0);
       acc[nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, bv1, acc[nt + 1], 0, 0, 0);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     return true;
   };
 
@@ -542,6 +567,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       }
     }
     advance_max(bm0, bm1, check_big ? 8.0f : 0.0f);
+    publish_p(lg, n, guard);
 #pragma unroll
     for (int j = 0; j < NBS; ++j) {
       if (j + PF < NBS)
@@ -549,7 +575,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       else
         kb[(j + PF - NBS) % (PF + 1)] = load_k(kcur);
       if (!GUARD || j < n) {
-        if (!pv(vb[j % (PF + 1)], lg[j], start + 32 * (base + j), guard, check_big)) return false;
+        if (!pv(vb[j % (PF + 1)], j, start + 32 * (base + j), guard, check_big)) return false;
       }
     }
     return true;

@@ -71,11 +71,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
     const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + t / c.page];
     const int off = t % c.page;
     const int64_t u = page * c.hkv + h;
-    const uint8_t* codes = c.kc + (u * c.page + off) * c.row_bytes;
+    const int64_t tile_row = u * c.page + (off & ~15);
     const uint32_t* meta = c.km + (u * c.page + off) * c.ngroups;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < kD; ++i) {
-      const uint32_t byte = codes[i * BITS / 8];
+      const uint32_t byte = c.kc[k_code_byte(tile_row, c.row_bytes, off & 15, i * BITS / 8)];
       const uint32_t code = (byte >> ((i * BITS) % 8)) & kMask;
       const uint32_t m = meta[i / G];
       const float khat = __builtin_fmaf(static_cast<float>(code), f16_bits_to_float(m & 0xFFFFu),
@@ -126,12 +126,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
       const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + t / c.page];
       const int off = t % c.page;
       const int64_t u = page * c.hkv + h;
-      const int64_t tile = off >> 4;
-      const uint8_t* tb = c.vc + ((u * c.page) + (off & ~15)) * c.row_bytes;
-      const int ot = off & 15;
-      const uint32_t code =
-          (static_cast<uint32_t>(tb[(byte >> 1) * 32 + (ot >> 1) * 4 + (byte & 1) * 2 + (ot & 1)]) >> sh) & kMask;
-      const uint32_t m = c.vm[((u * (c.page >> 4) + tile) * c.ngroups + i / G) * 16 + (off & 15)];
+      const int64_t tile_row = u * c.page + (off & ~15);
+      const uint32_t code = (static_cast<uint32_t>(c.vc[v_code_byte(tile_row, c.row_bytes, off & 15, byte)]) >> sh) & kMask;
+      const uint32_t m = c.vm[v_meta_entry(tile_row >> 4, c.ngroups, i / G, off & 15)];
       const float vhat = __builtin_fmaf(static_cast<float>(code), f16_bits_to_float(m & 0xFFFFu),
                                         f16_bits_to_float(m >> 16));
       o = __builtin_fmaf(sc[j][t - start], vhat, o);
@@ -145,9 +142,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
   }
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, query head). Every thread reads
-// the (m, l) pairs of all partitions (independent loads, one round trip), then its
-// channel of each partition's o.
+// Log-sum-exp merge of the partitions of one (sequence, query head): thread i owns
+// channel i and reads each partition's (m, l) and o[i], 16 partitions per round trip.
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ partials,
                                                       const int32_t* __restrict__ seq_lens, int num_q_heads,
                                                       int num_splits, int split_len, float* __restrict__ out) {
@@ -163,15 +159,10 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
   }
   const int ns = min(num_splits, (T + split_len - 1) / split_len);
   const float* base = partials + static_cast<int64_t>(bj) * num_splits * (kD + 2);
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < ns; s0 += kChunk) {
-    float m[kChunk];
-#pragma unroll
-    for (int k = 0; k < kChunk; ++k) m[k] = s0 + k < ns ? base[(s0 + k) * (kD + 2) + kD] : -INFINITY;
-#pragma unroll
-    for (int k = 0; k < kChunk; ++k) M = fmaxf(M, m[k]);
-  }
-  float L = 0.f, o = 0.f;
+  // one pass, kChunk partitions at a time, every load of a chunk issued together: the
+  // running reference M moves up chunk by chunk and rescales (L, o) exactly like the
+  // online softmax inside a partition
+  float M = -INFINITY, L = 0.f, o = 0.f;
   for (int s0 = 0; s0 < ns; s0 += kChunk) {
     float m[kChunk], l[kChunk], v[kChunk];
 #pragma unroll
@@ -182,12 +173,19 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
       l[k] = ok ? p[kD + 1] : 0.f;
       v[k] = ok ? p[i] : 0.f;
     }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) Mn = fmaxf(Mn, m[k]);
+    const float r = exp2f(M - Mn);  // 0 on the first chunk (M = -inf), 1 when M holds
+    L *= r;
+    o *= r;
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) {
-      const float w = exp2f(m[k] - M);
+      const float w = exp2f(m[k] - Mn);  // 0 for padding (m = -inf)
       L = __builtin_fmaf(l[k], w, L);
       o = __builtin_fmaf(v[k], w, o);
     }
+    M = Mn;
   }
   out[static_cast<int64_t>(bj) * kD + i] = o / L;
 }

@@ -9,11 +9,12 @@
 namespace kvq {
 
 // The cache as the kernels see it (plane pointers plus the few sizes they index with).
+// u = page * Hkv + kv head; tokens live in 16-token tiles (see the byte helpers below).
 struct DevCache {
-  uint8_t* kc;   // K codes  [u][P][RB]
-  uint32_t* km;  // K meta   [u][P][NG]        {scale | zero << 16}
-  uint8_t* vc;   // V codes  [u][P/16][RB/2][16] x u16
-  uint32_t* vm;  // V meta   [u][P/16][NG][16] {scale | zero << 16}
+  uint8_t* kc;   // K codes  [u][P/16][RB/16][16][16 B]  tile rows in 16-byte chunks, chunk-major
+  uint32_t* km;  // K meta   [u][P][NG]                  {scale | zero << 16}
+  uint8_t* vc;   // V codes  [u][P/16][RB/2][8][2][2]    16-bit words, token pairs byte-interleaved
+  uint32_t* vm;  // V meta   [u][P/16][2][NG][2][4]      {scale | zero << 16}
   int hkv;
   int page;
   int row_bytes;
@@ -31,6 +32,21 @@ inline DevCache dev_cache(const kvq_cache* c, const Geometry& g) {
   d.row_bytes = g.row_bytes;
   d.ngroups = g.ngroups;
   return d;
+}
+
+// Byte of the K code plane holding byte `k` of the packed row of token o (0..15) of the
+// tile whose first token is row `tile_row` (= u * P + 16 * tile).
+__host__ __device__ __forceinline__ int64_t k_code_byte(int64_t tile_row, int row_bytes, int o, int k) {
+  return tile_row * row_bytes + ((k >> 4) * 16 + o) * 16 + (k & 15);
+}
+// Byte of the V code plane holding byte `k` of the packed row of token o of that tile.
+__host__ __device__ __forceinline__ int64_t v_code_byte(int64_t tile_row, int row_bytes, int o, int k) {
+  return tile_row * row_bytes + (k >> 1) * 32 + (o >> 1) * 4 + (k & 1) * 2 + (o & 1);
+}
+// Entry of the V meta plane for group g of token o of tile `tile` (= u * P / 16 + tile
+// index): token o = 8 half + 4 part + i at ((part * NG + g) * 2 + half) * 4 + i.
+__host__ __device__ __forceinline__ int64_t v_meta_entry(int64_t tile, int ngroups, int g, int o) {
+  return tile * ngroups * 16 + ((((o >> 2) & 1) * ngroups + g) * 2 + (o >> 3)) * 4 + (o & 3);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

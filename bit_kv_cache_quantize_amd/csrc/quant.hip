@@ -112,29 +112,27 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(DevCache c, const 
   const uint32_t meta = s16 | (z16 << 16);
   const bool group_leader = (lane % kLanesPerGroup) == 0;
 
+  const int64_t tile_row = u * c.page + (off & ~15);  // first token row of the 16-token tile
+  const int o = off & 15;
+  constexpr int kBytes = BITS * 8 / 8;  // packed bytes held by this lane (8 channels)
   if (which == 0) {
-    uint8_t* dst = c.kc + (u * c.page + off) * c.row_bytes;
+    // K tiles: rows cut into 16-byte chunks, chunk-major, so the decode kernel's loads of
+    // one channel range of a tile's tokens are whole cache lines. The lane's bytes sit
+    // in one chunk.
+    uint8_t* dst = c.kc + k_code_byte(tile_row, c.row_bytes, o, lane * kBytes);
     if (BITS == 4)
-      reinterpret_cast<uint32_t*>(dst)[lane] = packed;
+      *reinterpret_cast<uint32_t*>(dst) = packed;
     else
-      reinterpret_cast<uint16_t*>(dst)[lane] = static_cast<uint16_t>(packed);
+      *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
     if (group_leader) c.km[(u * c.page + off) * c.ngroups + g] = meta;
   } else {
-    // V tiles: 16-token tiles, rows cut into 16-bit words, each word's token pairs
-    // byte-interleaved (byte b of word w of token o at w*32 + (o/2)*4 + b*2 + o%2), so
-    // the decode kernel's one mask turns a token pair's same-channel codes into
-    // adjacent bytes. Every token owns whole bytes: appends never share a byte.
-    uint8_t* tb = c.vc + ((u * c.page) + (off & ~15)) * c.row_bytes;
-    const int64_t tile = off >> 4;
-    const int o = off & 15;
-    const int pair = (o >> 1) * 4 + (o & 1);
-    constexpr int kBytes = BITS * 8 / 8;  // packed bytes held by this lane (8 channels)
+    // V tiles: rows cut into 16-bit words, each word's token pairs byte-interleaved, so
+    // the decode kernel's one mask turns a token pair's same-channel codes into adjacent
+    // bytes. Every token owns whole bytes: appends never share a byte.
 #pragma unroll
-    for (int k = 0; k < kBytes; ++k) {
-      const int byte = lane * kBytes + k;  // byte index within the token row
-      tb[(byte >> 1) * 32 + pair + (byte & 1) * 2] = static_cast<uint8_t>(packed >> (8 * k));
-    }
-    if (group_leader) c.vm[((u * (c.page >> 4) + tile) * c.ngroups + g) * 16 + o] = meta;
+    for (int k = 0; k < kBytes; ++k)
+      c.vc[v_code_byte(tile_row, c.row_bytes, o, lane * kBytes + k)] = static_cast<uint8_t>(packed >> (8 * k));
+    if (group_leader) c.vm[v_meta_entry(tile_row >> 4, c.ngroups, g, o)] = meta;
   }
 }
 
@@ -153,24 +151,19 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DevCache c, int which, 
   const int64_t u = page * c.hkv + h;
   const int g = lane / kLanesPerGroup;
 
-  uint32_t packed, meta;
+  const int64_t tile_row = u * c.page + (off & ~15);
+  const int o = off & 15;
+  constexpr int kBytes = BITS * 8 / 8;
+  uint32_t packed = 0, meta;
   if (which == 0) {
-    const uint8_t* src = c.kc + (u * c.page + off) * c.row_bytes;
-    packed = BITS == 4 ? reinterpret_cast<const uint32_t*>(src)[lane] : reinterpret_cast<const uint16_t*>(src)[lane];
+    const uint8_t* src = c.kc + k_code_byte(tile_row, c.row_bytes, o, lane * kBytes);
+    packed = BITS == 4 ? *reinterpret_cast<const uint32_t*>(src) : *reinterpret_cast<const uint16_t*>(src);
     meta = c.km[(u * c.page + off) * c.ngroups + g];
   } else {
-    const int64_t tile = off >> 4;
-    const int o = off & 15;
-    const uint8_t* tb = c.vc + ((u * c.page) + (off & ~15)) * c.row_bytes;
-    const int pair = (o >> 1) * 4 + (o & 1);
-    constexpr int kBytes = BITS * 8 / 8;
-    packed = 0;
 #pragma unroll
-    for (int k = 0; k < kBytes; ++k) {
-      const int byte = lane * kBytes + k;
-      packed |= static_cast<uint32_t>(tb[(byte >> 1) * 32 + pair + (byte & 1) * 2]) << (8 * k);
-    }
-    meta = c.vm[((u * (c.page >> 4) + tile) * c.ngroups + g) * 16 + o];
+    for (int k = 0; k < kBytes; ++k)
+      packed |= static_cast<uint32_t>(c.vc[v_code_byte(tile_row, c.row_bytes, o, lane * kBytes + k)]) << (8 * k);
+    meta = c.vm[v_meta_entry(tile_row >> 4, c.ngroups, g, o)];
   }
   const float s = f16_bits_to_float(meta & 0xFFFFu);
   const float z = f16_bits_to_float(meta >> 16);

@@ -56,13 +56,19 @@ typedef enum kvq_status {
  * page * page_size + offset. With u = page * num_kv_heads + kv_head, RB =
  * head_dim * bits / 8 bytes of codes per token and NG = head_dim / group_size:
  *
- *   k_codes  uint8 [u][page_size][RB]          token-major packed key codes
+ * Tokens are grouped in 16-token tiles (page_size is a multiple of 16):
+ *   k_codes  uint8 [u][page_size/16][RB/16][16][16] each tile's packed rows cut into
+ *            16-byte chunks, chunk-major (byte b of chunk j of token o at
+ *            (j*16 + o)*16 + b of the tile), so a load of one channel range of a
+ *            tile's tokens reads whole cache lines
  *   k_meta   half2 [u][page_size][NG]          {scale (low 16 bits), zero (high)}
- *   v_codes  uint8 [u][page_size/16][RB/2][8][2][2] each 16-token tile stores the
- *            packed rows cut into 16-bit words, word-major; within a word the 8
- *            token pairs keep both tokens' low bytes, then both high bytes (byte b
- *            of word w of token o at w*32 + (o/2)*4 + b*2 + o%2 of the tile)
- *   v_meta   half2 [u][page_size/16][NG][16]   {scale, zero}, group-major per tile
+ *   v_codes  uint8 [u][page_size/16][RB/2][8][2][2] each tile's packed rows cut into
+ *            16-bit words, word-major; within a word the 8 token pairs keep both
+ *            tokens' low bytes, then both high bytes (byte b of word w of token o at
+ *            w*32 + (o/2)*4 + b*2 + o%2 of the tile)
+ *   v_meta   half2 [u][page_size/16][2][NG][2][4] {scale, zero}; token
+ *            o = 8*half + 4*part + i of group g at entry ((part*NG + g)*2 + half)*4 + i
+ *            of the tile
  *
  * Packed rows are little-endian: INT4 channel 2k in the low nibble of byte k and
  * 2k+1 in the high nibble; INT2 channel 4k+e in bits 2e..2e+1 of byte k.

@@ -254,12 +254,18 @@ int orc_check_cache(const orc_cache* c) {
     if (c->head_dim % c->hadamard_block) return 4;
   }
   if (c->page_size <= 0 || c->page_size % 16) return 5;
-  if ((c->head_dim * c->bits) % 16) return 6;
+  if ((c->head_dim * c->bits) % 128) return 6; /* whole 16-byte chunks per row */
   return 0;
 }
 
-static int64_t k_code_off(const orc_cache* c, int64_t page, int h, int off) {
-  return ((page * c->num_kv_heads + h) * c->page_size + off) * row_bytes(c);
+/* byte k (0..RB-1) of the packed K row of token `off`: 16-token tiles; inside a tile the
+   rows are cut into 16-byte chunks stored chunk-major: chunk j of tokens 0..15, then chunk
+   j+1: chunk k/16, token o, byte k%16 -> ((k/16)*16 + o)*16 + k%16 */
+static int64_t k_byte_off(const orc_cache* c, int64_t page, int h, int off, int k) {
+  int64_t base = (page * c->num_kv_heads + h) * c->page_size * row_bytes(c);
+  int64_t tile = (off / 16) * 16 * row_bytes(c);
+  int o = off % 16;
+  return base + tile + ((int64_t)(k / 16) * 16 + o) * 16 + k % 16;
 }
 static int64_t k_meta_off(const orc_cache* c, int64_t page, int h, int off, int g) {
   return (((page * c->num_kv_heads + h) * c->page_size + off) * n_groups(c) + g) * 4;
@@ -274,10 +280,13 @@ static int64_t v_byte_off(const orc_cache* c, int64_t page, int h, int off, int 
   int o = off % 16, w = k / 2, b = k % 2;
   return base + tile + (int64_t)w * 32 + (o / 2) * 4 + b * 2 + (o % 2);
 }
+/* V {scale, zero} of token `off`, group g: 16-token tiles of NG*16 entries; token
+   o = 8*half + 4*part + i sits at entry ((part*NG + g)*2 + half)*4 + i */
 static int64_t v_meta_off(const orc_cache* c, int64_t page, int h, int off, int g) {
   int64_t tiles = c->page_size / 16;
   int64_t t = (page * c->num_kv_heads + h) * tiles + off / 16;
-  return ((t * n_groups(c) + g) * 16 + off % 16) * 4;
+  int o = off % 16, half = o / 8, part = (o % 8) / 4, i = o % 4;
+  return (t * n_groups(c) * 16 + (((int64_t)part * n_groups(c) + g) * 2 + half) * 4 + i) * 4;
 }
 
 static void put_u16(uint8_t* p, uint16_t v) {
@@ -290,7 +299,7 @@ static void store_row(const orc_cache* c, int which, int64_t page, int h, int of
                       const uint16_t* scale, const uint16_t* zero) {
   int64_t rb = row_bytes(c);
   if (which == 0) {
-    memcpy(c->k_codes + k_code_off(c, page, h, off), packed, (size_t)rb);
+    for (int k = 0; k < rb; ++k) c->k_codes[k_byte_off(c, page, h, off, k)] = packed[k];
     for (int g = 0; g < n_groups(c); ++g) {
       uint8_t* m = c->k_meta + k_meta_off(c, page, h, off, g);
       put_u16(m, scale[g]);
@@ -310,7 +319,7 @@ static void load_row(const orc_cache* c, int which, int64_t page, int h, int off
                      uint16_t* scale, uint16_t* zero) {
   int64_t rb = row_bytes(c);
   if (which == 0) {
-    memcpy(packed, c->k_codes + k_code_off(c, page, h, off), (size_t)rb);
+    for (int k = 0; k < rb; ++k) packed[k] = c->k_codes[k_byte_off(c, page, h, off, k)];
     for (int g = 0; g < n_groups(c); ++g) {
       const uint8_t* m = c->k_meta + k_meta_off(c, page, h, off, g);
       scale[g] = get_u16(m);

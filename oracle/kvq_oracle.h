@@ -32,19 +32,24 @@
  *   attention (fp64): qr = dense (H/sqrt(n)) q per block; logit_t = sigma * qr . khat_t;
  *             o = sum_t exp(logit_t - max) vhat_t / sum_t exp(logit_t - max).
  *
- * Cache layout (all byte offsets; RB = head_dim*bits/8 bytes per token row,
- * NG = head_dim/group_size groups, P = page_size, a multiple of 16):
+ * Cache layout (all byte offsets; RB = head_dim*bits/8 bytes per token row, a multiple
+ * of 16, NG = head_dim/group_size groups, P = page_size, a multiple of 16; tokens are
+ * stored in 16-token tiles):
  *   row base      u = page*Hkv + h
- *   K codes       [u][P][RB]                  token-major; byte k holds channels
- *                                             (INT4) 2k at bits 0-3, 2k+1 at 4-7;
- *                                             (INT2) 4k+e at bits 2e.
+ *   packed row    byte k holds channels (INT4) 2k at bits 0-3, 2k+1 at 4-7;
+ *                 (INT2) 4k+e at bits 2e.
+ *   K codes       [u][P/16][RB/16][16][16]    each tile's rows cut into 16-byte chunks,
+ *                                             chunk-major: chunk j, token o, byte b at
+ *                                             (j*16 + o)*16 + b.
  *   K meta        [u][P][NG] x {u16 scale, u16 zero}  (scale in the low half)
- *   V codes       [u][P/16][RB/2][8][2][2]    the same packed row cut into 16-bit
- *                                             words; per 16-token tile and word, the
- *                                             8 token pairs each store both tokens'
- *                                             low bytes then both high bytes: word w,
- *                                             token o, byte b at w*32 + (o/2)*4 + b*2 + o%2.
- *   V meta        [u][P/16][NG][16] x {u16 scale, u16 zero}
+ *   V codes       [u][P/16][RB/2][8][2][2]    the row cut into 16-bit words; per tile and
+ *                                             word, the 8 token pairs each store both
+ *                                             tokens' low bytes then both high bytes:
+ *                                             word w, token o, byte b at
+ *                                             w*32 + (o/2)*4 + b*2 + o%2.
+ *   V meta        [u][P/16][2][NG][2][4] x {u16 scale, u16 zero}: token
+ *                                             o = 8*half + 4*part + i of group g at
+ *                                             entry ((part*NG + g)*2 + half)*4 + i.
  */
 #ifndef KVQ_ORACLE_H
 #define KVQ_ORACLE_H

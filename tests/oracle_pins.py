@@ -320,17 +320,28 @@ def check_cache_layout_bytes():
     c.append(_bf16(k), _bf16(v), np.array([page * P + off]))
     packed = oracle.pack_row(x.astype(np.uint8), 4)
     rb = d * 4 // 8
-    kbase = ((page * Hkv + 1) * P + off) * rb
-    assert np.array_equal(c.k_codes[kbase:kbase + rb], packed)
+    o = off % 16
+    # K codes: 16-token tiles, rows cut into 16-byte chunks stored chunk-major
+    ktile = ((page * Hkv + 1) * P + (off // 16) * 16) * rb
+    for k in range(rb):
+        assert c.k_codes[ktile + ((k // 16) * 16 + o) * 16 + k % 16] == packed[k], k
     kmeta = ((page * Hkv + 1) * P + off) * 4 * 4
     assert list(c.k_meta[kmeta:kmeta + 4]) == [0x00, 0x3C, 0x00, 0x00]  # scale 1.0, zero 0.0
     vbase = (page * Hkv + 1) * P * rb + (off // 16) * 16 * rb
-    o = off % 16
     for k in range(rb):
         w, b = divmod(k, 2)
         assert c.v_codes[vbase + w * 32 + (o // 2) * 4 + b * 2 + o % 2] == packed[k], k
-    vmeta = (((page * Hkv + 1) * (P // 16) + off // 16) * 4 + 3) * 16 + off % 16
-    assert list(c.v_meta[vmeta * 4:vmeta * 4 + 4]) == [0x00, 0x3C, 0x00, 0x00]
+    # V meta: per tile NG*16 entries; token o = 8*half + 4*part + i of group g at
+    # entry ((part*NG + g)*2 + half)*4 + i
+    half, part, i = o // 8, (o % 8) // 4, o % 4
+    vtile = ((page * Hkv + 1) * (P // 16) + off // 16) * 4 * 16
+    for g in range(4):
+        e = vtile + ((part * 4 + g) * 2 + half) * 4 + i
+        assert list(c.v_meta[e * 4:e * 4 + 4]) == [0x00, 0x3C, 0x00, 0x00], g
+    # nothing else was written
+    assert np.count_nonzero(c.k_codes) == np.count_nonzero(packed)
+    assert np.count_nonzero(c.v_codes) == np.count_nonzero(packed)
+    assert np.count_nonzero(c.k_meta) == 4 and np.count_nonzero(c.v_meta) == 4
 
 
 def check_v_not_rotated_and_k_rotated():

@@ -43,6 +43,10 @@ MUTANTS = [
      "double sigma = softmax_scale > 0.0 ? softmax_scale : 1.0 / (double)d;\n  double* qv"),
     ("v_tokens_not_interleaved", "return base + tile + (int64_t)w * 32 + (o / 2) * 4 + b * 2 + (o % 2);",
      "return base + tile + (int64_t)w * 32 + o * 2 + b;"),
+    ("k_tile_token_major", "return base + tile + ((int64_t)(k / 16) * 16 + o) * 16 + k % 16;",
+     "return base + tile + (int64_t)o * row_bytes(c) + k;"),
+    ("v_meta_parts_swapped", "(((int64_t)part * n_groups(c) + g) * 2 + half) * 4 + i) * 4;",
+     "(((int64_t)half * n_groups(c) + g) * 2 + part) * 4 + i) * 4;"),
     ("meta_swapped", "      put_u16(m, scale[g]);\n      put_u16(m + 2, zero[g]);\n    }\n  } else {",
      "      put_u16(m, zero[g]);\n      put_u16(m + 2, scale[g]);\n    }\n  } else {"),
     ("q_not_rotated", "orc_rotate_dense_f64(qv, qr, d, c->hadamard_block);", "orc_rotate_dense_f64(qv, qr, d, 0);"),
