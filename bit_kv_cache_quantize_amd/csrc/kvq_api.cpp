@@ -28,8 +28,18 @@ int device_cus() {
   return cus;
 }
 
-Splits splits_for(const Geometry& g, int32_t batch, int32_t num_q_heads, int32_t max_seq_len, int32_t requested) {
-  return choose_splits(g, batch, num_q_heads, max_seq_len, requested, device_cus());
+Splits splits_for(const Geometry& g, int32_t batch, int32_t num_q_heads, int32_t max_seq_len, int32_t requested,
+                  SplitKernel kernel = SplitKernel::kMatrix) {
+  return choose_splits(g, batch, num_q_heads, max_seq_len, requested, device_cus(), kernel);
+}
+
+// Workspace for either decode kernel with these arguments.
+size_t workspace_for(const Geometry& g, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
+                     int32_t requested) {
+  const size_t a = workspace_bytes(g, batch, num_q_heads, splits_for(g, batch, num_q_heads, max_seq_len, requested));
+  const size_t b = workspace_bytes(
+      g, batch, num_q_heads, splits_for(g, batch, num_q_heads, max_seq_len, requested, SplitKernel::kReference));
+  return a > b ? a : b;
 }
 
 kvq_status decode_impl(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
@@ -41,7 +51,8 @@ kvq_status decode_impl(const kvq_cache* cache, const void* q, int32_t batch, int
   kvq_status st = check_decode(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                                max_seq_len, num_splits, workspace, out, &g);
   if (st != KVQ_OK || batch == 0) return st;
-  const Splits sp = splits_for(g, batch, num_q_heads, max_seq_len, num_splits);
+  const Splits sp = splits_for(g, batch, num_q_heads, max_seq_len, num_splits,
+                               reference ? SplitKernel::kReference : SplitKernel::kMatrix);
   if (workspace_bytes_given < workspace_bytes(g, batch, num_q_heads, sp)) return KVQ_ERR_WORKSPACE;
   if (reference && sp.split_len > 2048) return KVQ_ERR_UNSUPPORTED;
 
@@ -110,7 +121,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t
   Geometry g;
   if (check_cache(cache, false, &g) != KVQ_OK) return 0;
   if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0) return 0;
-  return workspace_bytes(g, batch, num_q_heads, splits_for(g, batch, num_q_heads, max_seq_len, num_splits));
+  return workspace_for(g, batch, num_q_heads, max_seq_len, num_splits);
 }
 
 int32_t kvq_decode_num_splits(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,

@@ -61,32 +61,35 @@ int64_t plane_bytes(const Geometry& g, int plane) {
 }
 
 Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
-                     int32_t requested, int cus) {
+                     int32_t requested, int cus, SplitKernel kernel) {
   (void)num_q_heads;
   Splits s{1, kBlock};
   const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
   const int64_t blocks = (len + kBlock - 1) / kBlock;
+  const bool matrix = kernel == SplitKernel::kMatrix;
   int64_t n;
+  int64_t per;  // blocks per partition
   if (requested > 0) {
-    n = requested;
+    n = requested < blocks ? requested : blocks;
+    per = (blocks + n - 1) / n;
   } else {
     // Enough independent work units to keep every CU busy several times over
     // (16 per CU), without partitions shorter than 8 blocks (256 tokens), whose
-    // partial results would cost more than they balance.
+    // partial results would cost more than they balance, nor longer than the kernel's
+    // limit (128 blocks for the matrix kernel, 64 for the reference kernel).
     const int64_t units = static_cast<int64_t>(batch) * g.hkv;
     const int64_t target = 16LL * (cus > 0 ? cus : 256);
     n = (target + units - 1) / (units > 0 ? units : 1);
-    const int64_t min_blocks = 8;
-    int64_t cap = blocks / min_blocks;
+    int64_t cap = blocks / 8;
     if (cap < 1) cap = 1;
     if (n > cap) n = cap;
-    // and no partition longer than 64 blocks (2048 tokens)
-    const int64_t floor_n = (blocks + 63) / 64;
+    const int64_t max_per = matrix ? 128 : 64;
+    const int64_t floor_n = (blocks + max_per - 1) / max_per;
     if (n < floor_n) n = floor_n;
+    per = (blocks + n - 1) / n;
+    // the matrix kernel walks whole 8-block super-blocks: the nearest multiple of 8
+    if (matrix && per > 8) per = (per + 4) / 8 * 8;
   }
-  if (n < 1) n = 1;
-  if (n > blocks) n = blocks;
-  const int64_t per = (blocks + n - 1) / n;  // blocks per partition
   s.split_len = static_cast<int32_t>(per * kBlock);
   s.num_splits = static_cast<int32_t>((blocks + per - 1) / per);
   return s;

@@ -35,8 +35,12 @@ struct Splits {
   int32_t num_splits;  // partitions of a max_seq_len sequence
   int32_t split_len;   // tokens per partition, a multiple of kBlock
 };
+// Automatic choices differ per decode kernel: the matrix-core kernel takes partitions of
+// up to 128 blocks in whole 8-block super-blocks; the plain reference kernel keeps a
+// partition's scores in LDS and takes at most 64 blocks.
+enum class SplitKernel { kMatrix, kReference };
 Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
-                     int32_t requested, int cus);
+                     int32_t requested, int cus, SplitKernel kernel);
 
 size_t workspace_bytes(const Geometry& g, int32_t batch, int32_t num_q_heads, const Splits& s);
 

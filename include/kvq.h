@@ -111,16 +111,17 @@ kvq_status kvq_quantize_append(const kvq_cache* cache, const void* k_new, const 
                                const int64_t* slots, int64_t n_new, void* stream);
 
 /*
- * Workspace bytes kvq_decode_attention needs for these sizes: fp32 split partials
- * [batch][num_q_heads][splits][d + 2]. num_splits 0 = the library's choice (the
- * same choice kvq_decode_attention makes for the same arguments on the same
- * device). Returns 0 for an invalid description.
+ * Workspace bytes kvq_decode_attention (and kvq_decode_attention_reference) need for
+ * these sizes: fp32 split partials [batch][num_q_heads][splits][d + 2]. num_splits 0 =
+ * the library's choice, made the same way for the same arguments on the same device
+ * (up to 4096 tokens per partition for kvq_decode_attention, up to 2048 for the
+ * reference kernel; the size covers both). Returns 0 for an invalid description.
  */
 size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
                                   int32_t max_seq_len, int32_t num_splits);
 
-/* The number of split-K partitions (per sequence of max_seq_len tokens) that a
-   decode call with these arguments uses; 0 for an invalid description. */
+/* The number of split-K partitions (per sequence of max_seq_len tokens) that
+   kvq_decode_attention uses with these arguments; 0 for an invalid description. */
 int32_t kvq_decode_num_splits(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
                               int32_t max_seq_len, int32_t num_splits);
 

@@ -142,19 +142,21 @@ def test_dequantize_argument_checks():
 
 
 def test_split_sizing_and_workspace():
-    """Automatic split-K sizing: whole 32-token blocks, 256..2048 tokens per partition,
-    and the workspace formula [B][Hq][S][d+2] fp32. (Off a GPU the library assumes
-    256 compute units, the MI355X count.)"""
+    """Automatic split-K sizing: whole 32-token blocks, 256..4096 tokens per partition in
+    whole 8-block super-blocks for the matrix kernel (the reference kernel: at most 2048),
+    and the workspace formula [B][Hq][S][d+2] fp32 for the larger of the two choices.
+    (Off a GPU the library assumes 256 compute units, the MI355X count.)"""
     L = kvq.lib()
     d = _desc(page_size=32768, num_pages=64)
-    cases = {  # (B, Hkv, T) -> splits
-        (64, 32768): 16,    # 512 units x 16 = 8192 work units, 2048 tokens each
-        (16, 8192): 32,     # 128 units x 32, 256-token partitions
-        (1, 1024): 4,
+    cases = {  # (B, T) -> (matrix splits, reference splits)
+        (64, 32768): (8, 16),   # 512 units: 4096-token partitions (2048 for the reference)
+        (16, 8192): (32, 32),   # 128 units x 32, 256-token partitions
+        (1, 1024): (4, 4),
+        (3, 5000): (20, 18),    # 157 blocks: 8 per partition (9 for the reference)
     }
-    for (B, T), want in cases.items():
+    for (B, T), (want, want_ref) in cases.items():
         assert L.kvq_decode_num_splits(ctypes.byref(d), B, 32, T, 0) == want
-        assert L.kvq_decode_workspace_bytes(ctypes.byref(d), B, 32, T, 0) == B * 32 * want * 130 * 4
+        assert L.kvq_decode_workspace_bytes(ctypes.byref(d), B, 32, T, 0) == B * 32 * max(want, want_ref) * 130 * 4
     d3 = _desc(group_size=64, page_size=131072, num_pages=1)
     assert L.kvq_decode_num_splits(ctypes.byref(d3), 1, 32, 131072, 0) >= 256
     # explicit requests are honoured up to one partition per 32-token block
