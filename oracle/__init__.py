@@ -104,6 +104,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "orc_dequantize": (None, [ctypes.POINTER(_Cache), ctypes.c_int, vp, i64, vp]),
         "orc_decode_attention": (None, [ctypes.POINTER(_Cache), vp, i32, i32, vp, i32, vp, f64, vp]),
         "orc_attention_bf16": (None, [vp, vp, vp, i32, i32, i32, i32, i32, f64, vp]),
+        "orc_window_slot": (ctypes.c_int, [ctypes.POINTER(_Window), ctypes.c_int]),
+        "orc_window_append": (None, [ctypes.POINTER(_Cache), ctypes.POINTER(_Window), vp, vp, vp, vp, vp, i64]),
+        "orc_decode_attention_window": (None, [ctypes.POINTER(_Cache), ctypes.POINTER(_Window), vp, i32, i32, vp,
+                                               i32, vp, f64, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -259,6 +263,66 @@ class Cache:
         out = np.empty((B, Hq, d), np.float64)
         load().orc_decode_attention(ctypes.byref(self.desc), _p(q), B, Hq, _p(bt), bt.shape[1], _p(sl),
                                     float(softmax_scale), _p(out))
+        return out
+
+
+# ----------------------------------------------------------------------------- windows
+
+class _Window(ctypes.Structure):
+    _fields_ = [
+        ("head_dim", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("sink", ctypes.c_int32),
+        ("recent", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+    ]
+
+
+@dataclass
+class Window:
+    """bf16 high-precision windows (first `sink`, last `recent` tokens per sequence)."""
+
+    head_dim: int
+    num_kv_heads: int
+    sink: int
+    recent: int
+    batch: int
+
+    def __post_init__(self):
+        shape = (self.batch, self.sink + self.recent, self.num_kv_heads, self.head_dim)
+        self.k = np.zeros(shape, np.uint16)
+        self.v = np.zeros(shape, np.uint16)
+
+    @property
+    def desc(self) -> _Window:
+        return _Window(self.head_dim, self.num_kv_heads, self.sink, self.recent, self.batch, self.k.ctypes.data,
+                       self.v.ctypes.data)
+
+    def slot(self, t: int) -> int:
+        return load().orc_window_slot(ctypes.byref(self.desc), t)
+
+    def append(self, cache: Cache, k_bf16, v_bf16, seqs, positions, evict_slots) -> None:
+        """One token per row: bf16 bits [n][Hkv][d]; int32 seqs, positions; int64 evict_slots."""
+        k = np.ascontiguousarray(k_bf16, dtype=np.uint16)
+        v = np.ascontiguousarray(v_bf16, dtype=np.uint16)
+        sq = np.ascontiguousarray(seqs, dtype=np.int32)
+        pos = np.ascontiguousarray(positions, dtype=np.int32)
+        ev = np.ascontiguousarray(evict_slots, dtype=np.int64)
+        n = sq.size
+        assert k.shape == v.shape == (n, self.num_kv_heads, self.head_dim) and pos.size == n and ev.size == n
+        load().orc_window_append(ctypes.byref(cache.desc), ctypes.byref(self.desc), _p(k), _p(v), _p(sq), _p(pos),
+                                 _p(ev), n)
+
+    def decode(self, cache: Cache, q_bf16, block_table, seq_lens, softmax_scale: float = 0.0) -> np.ndarray:
+        q = np.ascontiguousarray(q_bf16, dtype=np.uint16)
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        B, Hq, d = q.shape
+        out = np.empty((B, Hq, d), np.float64)
+        load().orc_decode_attention_window(ctypes.byref(cache.desc), ctypes.byref(self.desc), _p(q), B, Hq, _p(bt),
+                                           bt.shape[1], _p(sl), float(softmax_scale), _p(out))
         return out
 
 

@@ -351,33 +351,38 @@ static void dequant_row(const orc_cache* c, int which, int64_t page, int h, int 
   }
 }
 
-void orc_quantize_append(const orc_cache* c, const uint16_t* k_new, const uint16_t* v_new,
-                         const int64_t* slots, int64_t n) {
+/* Quantize the bf16 K and V rows of kv head h and store them at `slot` (K rotated). */
+static void quantize_store_pair(const orc_cache* c, const uint16_t* krow, const uint16_t* vrow, int64_t slot, int h) {
   int d = c->head_dim;
   float* x = (float*)malloc(sizeof(float) * (size_t)d);
   uint8_t* codes = (uint8_t*)malloc((size_t)d);
   uint8_t* packed = (uint8_t*)malloc((size_t)d);
   uint16_t* sc = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)d);
   uint16_t* ze = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)d);
-  for (int64_t r = 0; r < n; ++r) {
-    int64_t page = slots[r] / c->page_size;
-    int off = (int)(slots[r] % c->page_size);
-    for (int h = 0; h < c->num_kv_heads; ++h) {
-      for (int which = 0; which < 2; ++which) {
-        const uint16_t* src = (which == 0 ? k_new : v_new) + (r * c->num_kv_heads + h) * d;
-        for (int i = 0; i < d; ++i) x[i] = orc_bf16_to_f32(src[i]);
-        if (which == 0) orc_rotate(x, d, c->hadamard_block); /* keys only */
-        orc_quantize_row(x, d, c->bits, c->group_size, codes, sc, ze);
-        orc_pack_row(codes, d, c->bits, packed);
-        store_row(c, which, page, h, off, packed, sc, ze);
-      }
-    }
+  int64_t page = slot / c->page_size;
+  int off = (int)(slot % c->page_size);
+  for (int which = 0; which < 2; ++which) {
+    const uint16_t* src = which == 0 ? krow : vrow;
+    for (int i = 0; i < d; ++i) x[i] = orc_bf16_to_f32(src[i]);
+    if (which == 0) orc_rotate(x, d, c->hadamard_block); /* keys only */
+    orc_quantize_row(x, d, c->bits, c->group_size, codes, sc, ze);
+    orc_pack_row(codes, d, c->bits, packed);
+    store_row(c, which, page, h, off, packed, sc, ze);
   }
   free(x);
   free(codes);
   free(packed);
   free(sc);
   free(ze);
+}
+
+void orc_quantize_append(const orc_cache* c, const uint16_t* k_new, const uint16_t* v_new,
+                         const int64_t* slots, int64_t n) {
+  int d = c->head_dim;
+  for (int64_t r = 0; r < n; ++r)
+    for (int h = 0; h < c->num_kv_heads; ++h)
+      quantize_store_pair(c, k_new + (r * c->num_kv_heads + h) * d, v_new + (r * c->num_kv_heads + h) * d, slots[r],
+                          h);
 }
 
 void orc_dequantize(const orc_cache* c, int which, const int64_t* slots, int64_t n, float* out) {
@@ -435,6 +440,92 @@ void orc_decode_attention(const orc_cache* c, const uint16_t* q, int32_t batch, 
         int64_t page = block_table[(int64_t)b * max_pages + t / P];
         dequant_row(c, 1, page, h, t % P, row);
         for (int i = 0; i < d; ++i) acc[i] += w * (double)row[i];
+      }
+      for (int i = 0; i < d; ++i) o[i] = acc[i] / den;
+    }
+    free(logit);
+  }
+  free(qv);
+  free(qr);
+  free(row);
+  free(acc);
+}
+
+/* ------------------------------------------------------------------------- */
+/* High-precision windows (InnerQ, Abstract: windows of recent tokens and of attention
+   sink tokens stay in high precision). Reading: the first `sink` tokens and the last
+   `recent` tokens of every sequence stay in bf16, keys in the original (unrotated)
+   basis; a token leaving the recent window is quantized into the cache at its own slot;
+   the tokens between are the quantized cache. */
+
+int orc_window_slot(const orc_window* w, int t) { return t < w->sink ? t : w->sink + (t - w->sink) % w->recent; }
+
+void orc_window_append(const orc_cache* c, const orc_window* w, const uint16_t* k_new, const uint16_t* v_new,
+                       const int32_t* seqs, const int32_t* positions, const int64_t* evict_slots, int64_t n) {
+  int d = w->head_dim, H = w->num_kv_heads, S = w->sink, R = w->recent;
+  for (int64_t r = 0; r < n; ++r) {
+    int b = seqs[r], t = positions[r];
+    int ws = orc_window_slot(w, t);
+    for (int h = 0; h < H; ++h) {
+      uint16_t* kw = w->k + (((int64_t)b * (S + R) + ws) * H + h) * d;
+      uint16_t* vw = w->v + (((int64_t)b * (S + R) + ws) * H + h) * d;
+      /* the recent ring is full: its slot holds token t - R, which now leaves the window */
+      if (t >= S && t - R >= S) quantize_store_pair(c, kw, vw, evict_slots[r], h);
+      memcpy(kw, k_new + (r * H + h) * d, sizeof(uint16_t) * (size_t)d);
+      memcpy(vw, v_new + (r * H + h) * d, sizeof(uint16_t) * (size_t)d);
+    }
+  }
+}
+
+void orc_decode_attention_window(const orc_cache* c, const orc_window* w, const uint16_t* q, int32_t batch,
+                                 int32_t num_q_heads, const int32_t* block_table, int32_t max_pages,
+                                 const int32_t* seq_lens, double softmax_scale, double* out) {
+  int d = c->head_dim, P = c->page_size, H = w->num_kv_heads, S = w->sink, R = w->recent;
+  int ratio = num_q_heads / c->num_kv_heads;
+  double sigma = softmax_scale > 0.0 ? softmax_scale : 1.0 / sqrt((double)d);
+  double* qv = (double*)malloc(sizeof(double) * (size_t)d);
+  double* qr = (double*)malloc(sizeof(double) * (size_t)d);
+  float* row = (float*)malloc(sizeof(float) * (size_t)d);
+  double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int b = 0; b < batch; ++b) {
+    int T = seq_lens[b];
+    double* logit = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    for (int j = 0; j < num_q_heads; ++j) {
+      int h = j / ratio;
+      double* o = out + ((int64_t)b * num_q_heads + j) * d;
+      if (T <= 0) {
+        for (int i = 0; i < d; ++i) o[i] = 0.0;
+        continue;
+      }
+      for (int i = 0; i < d; ++i) qv[i] = (double)orc_bf16_to_f32(q[((int64_t)b * num_q_heads + j) * d + i]);
+      orc_rotate_dense_f64(qv, qr, d, c->hadamard_block);
+      double m = -INFINITY;
+      for (int t = 0; t < T; ++t) {
+        double dot = 0.0;
+        if (t < S || t >= T - R) { /* window token: original bf16 key, original query */
+          const uint16_t* kw = w->k + (((int64_t)b * (S + R) + orc_window_slot(w, t)) * H + h) * d;
+          for (int i = 0; i < d; ++i) dot += qv[i] * (double)orc_bf16_to_f32(kw[i]);
+        } else {
+          int64_t page = block_table[(int64_t)b * max_pages + t / P];
+          dequant_row(c, 0, page, h, t % P, row);
+          for (int i = 0; i < d; ++i) dot += qr[i] * (double)row[i];
+        }
+        logit[t] = sigma * dot;
+        if (logit[t] > m) m = logit[t];
+      }
+      double den = 0.0;
+      for (int i = 0; i < d; ++i) acc[i] = 0.0;
+      for (int t = 0; t < T; ++t) {
+        double wt = exp(logit[t] - m);
+        den += wt;
+        if (t < S || t >= T - R) {
+          const uint16_t* vw = w->v + (((int64_t)b * (S + R) + orc_window_slot(w, t)) * H + h) * d;
+          for (int i = 0; i < d; ++i) acc[i] += wt * (double)orc_bf16_to_f32(vw[i]);
+        } else {
+          int64_t page = block_table[(int64_t)b * max_pages + t / P];
+          dequant_row(c, 1, page, h, t % P, row);
+          for (int i = 0; i < d; ++i) acc[i] += wt * (double)row[i];
+        }
       }
       for (int i = 0; i < d; ++i) o[i] = acc[i] / den;
     }

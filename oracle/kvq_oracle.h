@@ -111,6 +111,32 @@ void orc_dequantize(const orc_cache* c, int which, const int64_t* slots, int64_t
 void orc_decode_attention(const orc_cache* c, const uint16_t* q, int32_t batch, int32_t num_q_heads,
                           const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
                           double softmax_scale, double* out);
+/* ---- high-precision windows (InnerQ, Abstract) ----
+   The first `sink` and the last `recent` tokens of every sequence stay in bf16 (keys in
+   the original basis); token t sits in window slot t (t < sink) or
+   sink + (t - sink) % recent. Tokens sink <= t < T - recent are in the quantized cache,
+   at their own slots. */
+typedef struct {
+  int32_t head_dim;
+  int32_t num_kv_heads;
+  int32_t sink;
+  int32_t recent; /* >= 1 */
+  int32_t batch;
+  uint16_t* k; /* bf16 [batch][sink + recent][Hkv][d] */
+  uint16_t* v;
+} orc_window;
+
+int orc_window_slot(const orc_window* w, int t);
+/* One new token per row r: sequence seqs[r], position positions[r] (= tokens before it).
+   A full recent window first moves its oldest token (position t - recent) into the cache
+   at evict_slots[r]. */
+void orc_window_append(const orc_cache* c, const orc_window* w, const uint16_t* k_new, const uint16_t* v_new,
+                       const int32_t* seqs, const int32_t* positions, const int64_t* evict_slots, int64_t n);
+/* Attention over window tokens (bf16, original query) and cache tokens (as
+   orc_decode_attention) together; seq_lens counts all tokens. */
+void orc_decode_attention_window(const orc_cache* c, const orc_window* w, const uint16_t* q, int32_t batch,
+                                 int32_t num_q_heads, const int32_t* block_table, int32_t max_pages,
+                                 const int32_t* seq_lens, double softmax_scale, double* out);
 /* fp64 attention over unquantized bf16 K/V ([B][T][Hkv][d] contiguous), no rotation:
    the loss-free reference the quantized cache approximates (information only). */
 void orc_attention_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, int32_t batch,

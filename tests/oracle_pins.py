@@ -445,6 +445,83 @@ def check_attention_page_permutation():
     assert np.array_equal(outs[0], outs[1])
 
 
+# ----------------------------------------------------------------------------- windows
+
+def _window_stream(rng, T, S, R, B=2, Hkv=2, d=128, P=16, bits=4, G=32, hb=128):
+    """Append T tokens one at a time through the windows; returns the oracle objects and
+    the raw bf16 tokens [B][T][Hkv][d]. Contiguous pages: slot of position t = b*cap + t."""
+    cap = (T + P - 1) // P * P
+    c = oracle.Cache(d, Hkv, bits, G, hb, cap, B)
+    w = oracle.Window(d, Hkv, S, R, B)
+    k = _bf16(rng.standard_normal((B, T, Hkv, d)) * np.exp(rng.standard_normal((1, 1, Hkv, d))))
+    v = _bf16(rng.standard_normal((B, T, Hkv, d)))
+    for t in range(T):
+        ev = np.array([b * cap + (t - R) for b in range(B)], np.int64)
+        w.append(c, k[:, t], v[:, t], np.arange(B), np.full(B, t), ev)
+    bt = np.arange(B, dtype=np.int32).reshape(B, 1)
+    return c, w, bt, k, v, cap
+
+
+def check_window_all_tokens_in_windows():
+    """Every token still in a window: plain fp64 attention over the raw bf16 rows."""
+    rng = np.random.default_rng(31)
+    for T, S, R in ((40, 32, 16), (20, 32, 4), (33, 32, 1)):
+        c, w, bt, k, v, cap = _window_stream(rng, T, S, R)
+        q = _bf16(rng.standard_normal((2, 8, 128)))
+        out = w.decode(c, q, bt, np.array([T, T], np.int32))
+        ref = oracle.attention_bf16(q, k, v, 2)
+        assert np.max(np.abs(out - ref)) < 1e-12, (T, S, R)
+        assert not c.k_codes.any() and not c.v_codes.any()  # nothing was quantized
+
+
+def check_window_evictions_match_direct_quantization():
+    """Tokens that left the recent window are in the cache exactly as a direct append of
+    them would put them; the windows hold the sink tokens and the last R tokens."""
+    rng = np.random.default_rng(32)
+    T, S, R = 100, 32, 8
+    c, w, bt, k, v, cap = _window_stream(rng, T, S, R)
+    ref = oracle.Cache(128, 2, 4, 32, 128, cap, 2)
+    for b in range(2):
+        t = np.arange(S, T - R)
+        ref.append(k[b, S:T - R], v[b, S:T - R], b * cap + t)
+    for g, r in zip(c.planes(), ref.planes()):
+        assert np.array_equal(g, r)
+    for b in range(2):
+        for t in list(range(S)) + list(range(T - R, T)):
+            slot = S + (t - S) % R if t >= S else t
+            assert np.array_equal(w.k[b, slot], k[b, t]) and np.array_equal(w.v[b, slot], v[b, t]), (b, t)
+
+
+def check_window_decode_mixed():
+    """Window tokens with the original query and raw rows, cache tokens with the rotated
+    query (scipy Hadamard) and the oracle's dequantized rows, one softmax: against a
+    direct fp64 softmax written out in numpy over the assembled rows."""
+    rng = np.random.default_rng(33)
+    T, S, R, P = 100, 32, 8, 16
+    c, w, bt, k, v, cap = _window_stream(rng, T, S, R)
+    q = _bf16(rng.standard_normal((2, 8, 128)))
+    lens = np.array([T, T], np.int32)  # the windows hold the state after T appends
+    out = w.decode(c, q, bt, lens)
+    Rm = scipy.linalg.hadamard(128) / np.sqrt(128)
+    for b in range(2):
+        qf = oracle.bf16_to_f32(q[b]).astype(np.float64)  # [Hq][d]
+        logits = np.empty((8, T))
+        vals = np.empty((T, 2, 128))
+        for t in range(T):
+            if t < S or t >= T - R:  # window token: raw rows, original query
+                kt = oracle.bf16_to_f32(k[b, t]).astype(np.float64)
+                vals[t] = oracle.bf16_to_f32(v[b, t]).astype(np.float64)
+                logits[:, t] = np.einsum("jd,jd->j", qf, np.repeat(kt, 4, axis=0))
+            else:  # cache token: dequantized rows, rotated query
+                kt = c.dequantize(0, np.array([b * cap + t]))[0].astype(np.float64)
+                vals[t] = c.dequantize(1, np.array([b * cap + t]))[0].astype(np.float64)
+                logits[:, t] = np.einsum("jd,jd->j", qf @ Rm.T, np.repeat(kt, 4, axis=0))
+        logits /= np.sqrt(128)
+        p = np.exp(logits - logits.max(1, keepdims=True))
+        ref = np.einsum("jt,jtd->jd", p, np.repeat(vals, 4, axis=1).transpose(1, 0, 2)) / p.sum(1, keepdims=True)
+        assert np.max(np.abs(out[b] - ref)) < 1e-12, b
+
+
 ALL_CHECKS = [
     check_hadamard_is_sylvester,
     check_hadamard_orthogonal,
@@ -467,4 +544,7 @@ ALL_CHECKS = [
     check_attention_matches_sdpa,
     check_attention_special_cases,
     check_attention_page_permutation,
+    check_window_all_tokens_in_windows,
+    check_window_evictions_match_direct_quantization,
+    check_window_decode_mixed,
 ]

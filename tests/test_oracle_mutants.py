@@ -47,6 +47,14 @@ MUTANTS = [
      "return base + tile + (int64_t)o * row_bytes(c) + k;"),
     ("v_meta_parts_swapped", "(((int64_t)part * n_groups(c) + g) * 2 + half) * 4 + i) * 4;",
      "(((int64_t)half * n_groups(c) + g) * 2 + part) * 4 + i) * 4;"),
+    ("window_evict_late", "if (t >= S && t - R >= S) quantize_store_pair(c, kw, vw, evict_slots[r], h);",
+     "if (t >= S && t - R > S) quantize_store_pair(c, kw, vw, evict_slots[r], h);"),
+    ("window_ring_index", "return t < w->sink ? t : w->sink + (t - w->sink) % w->recent;",
+     "return t < w->sink ? t : w->sink + (t - w->sink + 1) % w->recent;"),
+    ("window_recent_edge", "if (t < S || t >= T - R) { /* window token: original bf16 key, original query */",
+     "if (t < S || t > T - R) { /* window token: original bf16 key, original query */"),
+    ("window_query_rotated", "for (int i = 0; i < d; ++i) dot += qv[i] * (double)orc_bf16_to_f32(kw[i]);",
+     "for (int i = 0; i < d; ++i) dot += qr[i] * (double)orc_bf16_to_f32(kw[i]);"),
     ("meta_swapped", "      put_u16(m, scale[g]);\n      put_u16(m + 2, zero[g]);\n    }\n  } else {",
      "      put_u16(m, zero[g]);\n      put_u16(m + 2, scale[g]);\n    }\n  } else {"),
     ("q_not_rotated", "orc_rotate_dense_f64(qv, qr, d, c->hadamard_block);", "orc_rotate_dense_f64(qv, qr, d, 0);"),
@@ -69,7 +77,8 @@ print("SURVIVED"); sys.exit(0)
 
 def _run(name, old, new, tmp):
     src = open(SRC).read()
-    assert src.count(old) == 1, f"mutant {name}: pattern not found exactly once"
+    # a pattern shared by the plain and the windowed decode is mutated in both
+    assert src.count(old) >= 1, f"mutant {name}: pattern not found"
     path = os.path.join(tmp, f"mut_{name}.c")
     with open(path, "w") as f:
         f.write(src.replace(old, new))
