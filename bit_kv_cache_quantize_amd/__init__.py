@@ -43,11 +43,22 @@ class _Desc(ctypes.Structure):
     ]
 
 
+class _Window(ctypes.Structure):
+    _fields_ = [
+        ("sink", ctypes.c_int32),
+        ("recent", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 # name -> (restype, argtypes); every symbol include/kvq.h declares
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
 _DP = ctypes.POINTER(_Desc)
+_WP = ctypes.POINTER(_Window)
 SIGNATURES = {
     "kvq_cache_plane_bytes": (_i64, [_DP, _i32]),
     "kvq_quantize_append": (ctypes.c_int, [_DP, _vp, _vp, _vp, _i64, _vp]),
@@ -59,6 +70,11 @@ SIGNATURES = {
                                                   _sz, _vp, _vp, _vp, _vp]),
     "kvq_decode_attention_reference": (ctypes.c_int, [_DP, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32,
                                                       _vp, _sz, _vp, _vp]),
+    "kvq_window_plane_bytes": (_i64, [_DP, _WP]),
+    "kvq_window_append": (ctypes.c_int, [_DP, _WP, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
+    "kvq_decode_window_workspace_bytes": (_sz, [_DP, _WP, _i32, _i32, _i32, _i32]),
+    "kvq_decode_attention_window": (ctypes.c_int, [_DP, _WP, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32,
+                                                   _vp, _sz, _vp, _vp]),
     "kvq_dequantize": (ctypes.c_int, [_DP, _i32, _vp, _i64, _vp, _vp]),
     "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvq_version": (ctypes.c_char_p, []),
@@ -231,4 +247,86 @@ def dequantize(cache: KVCache, which: int, slots: torch.Tensor, out: torch.Tenso
     _need(out, torch.float32, "out")
     st = lib().kvq_dequantize(ctypes.byref(cache.desc), which, _ptr(slots), n, _ptr(out), _stream(stream))
     _check(st, "kvq_dequantize")
+    return out
+
+
+@dataclass
+class KVWindow:
+    """High-precision windows: the first `sink` and last `recent` tokens of every sequence
+    in bf16 [batch][sink + recent][Hkv][d] (keys unrotated); token t in row t (t < sink) or
+    sink + (t - sink) % recent. Caller-owned device planes (see include/kvq.h)."""
+
+    sink: int
+    recent: int
+    batch: int
+    k: torch.Tensor
+    v: torch.Tensor
+
+    @classmethod
+    def allocate(cls, cache: KVCache, sink: int, recent: int, batch: int, device="cuda") -> "KVWindow":
+        w = _Window(sink, recent, batch)
+        n = lib().kvq_window_plane_bytes(ctypes.byref(cache.desc), ctypes.byref(w))
+        if n < 0:
+            raise KVQError(ERR_INVALID, "window description")
+        shape = (batch, sink + recent, cache.num_kv_heads, cache.head_dim)
+        k = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        v = torch.zeros(shape, dtype=torch.bfloat16, device=device)
+        assert k.numel() * 2 == n
+        return cls(sink, recent, batch, k, v)
+
+    @property
+    def desc(self) -> _Window:
+        return _Window(self.sink, self.recent, self.batch, self.k.data_ptr(), self.v.data_ptr())
+
+    def row(self, t: int) -> int:
+        return t if t < self.sink else self.sink + (t - self.sink) % self.recent
+
+
+def window_append(cache: KVCache, window: KVWindow, k_new: torch.Tensor, v_new: torch.Tensor, seqs: torch.Tensor,
+                  positions: torch.Tensor, evict_slots: torch.Tensor, stream=None) -> None:
+    """One new token per listed sequence through the windows; a token leaving the recent
+    window is rotated and quantized into the cache at its evict slot (int64)."""
+    _need(k_new, torch.bfloat16, "k_new")
+    _need(v_new, torch.bfloat16, "v_new")
+    _need(seqs, torch.int32, "seqs")
+    _need(positions, torch.int32, "positions")
+    _need(evict_slots, torch.int64, "evict_slots")
+    n = seqs.numel()
+    if positions.numel() != n or evict_slots.numel() != n:
+        raise ValueError("seqs, positions and evict_slots must have one entry per new token")
+    if k_new.shape != (n, cache.num_kv_heads, cache.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [{n}][{cache.num_kv_heads}][{cache.head_dim}]")
+    st = lib().kvq_window_append(ctypes.byref(cache.desc), ctypes.byref(window.desc), _ptr(k_new), _ptr(v_new),
+                                 _ptr(seqs), _ptr(positions), _ptr(evict_slots), n, _stream(stream))
+    _check(st, "kvq_window_append")
+
+
+def decode_window_workspace_bytes(cache: KVCache, window: KVWindow, batch: int, num_q_heads: int,
+                                  max_seq_len: int, num_splits: int = 0) -> int:
+    return lib().kvq_decode_window_workspace_bytes(ctypes.byref(cache.desc), ctypes.byref(window.desc), batch,
+                                                   num_q_heads, max_seq_len, num_splits)
+
+
+def decode_attention_window(cache: KVCache, window: KVWindow, q: torch.Tensor, block_table: torch.Tensor,
+                            seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float = 0.0,
+                            num_splits: int = 0, workspace: torch.Tensor | None = None,
+                            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode attention over windows (bf16, original query) and cache (rotated query) in one
+    softmax; q bf16 [B][Hq][d] -> fp32 [B][Hq][d]; seq_lens count all tokens."""
+    _need(q, torch.bfloat16, "q")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    need = decode_window_workspace_bytes(cache, window, B, Hq, max_seq_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, torch.uint8, "workspace")
+    st = lib().kvq_decode_attention_window(ctypes.byref(cache.desc), ctypes.byref(window.desc), _ptr(q), B, Hq,
+                                           _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_seq_len,
+                                           softmax_scale, num_splits, _ptr(workspace), workspace.numel(),
+                                           _ptr(out), _stream(stream))
+    _check(st, "kvq_decode_attention_window")
     return out

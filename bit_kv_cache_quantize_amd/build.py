@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "kvq")
 
-SOURCES = ["kvq_validate.cpp", "kvq_api.cpp", "quant.hip", "decode_ref.hip", "decode_mfma.hip"]
+SOURCES = ["kvq_validate.cpp", "kvq_api.cpp", "quant.hip", "decode_ref.hip", "decode_mfma.hip", "decode_window.hip"]
 
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 # -packed-fp32-ops: never emit packed fp32 VALU forms (v_pk_fma_f32 and friends).

@@ -146,9 +146,10 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   const int hk = bh % c.hkv;
   const int b = bh / c.hkv;
   const int T = a.seq_lens[b];
-  const int start = split * a.split_len;
-  if (start >= T) return;
-  const int end = min(T, start + a.split_len);
+  const int qend = max(a.tok_begin, T - a.tok_tail);  // the span this kernel covers ends here
+  const int start = a.tok_begin + split * a.split_len;
+  if (start >= qend) return;
+  const int end = min(qend, start + a.split_len);
 
   __shared__ float o_s[4][128];  // partial outputs, staged for the workspace stores
   __shared__ float p_s[NBS][4][32];  // p of a super-block's blocks, per head and token
@@ -612,9 +613,9 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   }
   zacc += __shfl_xor(zacc, 16, 64);
   zacc += __shfl_xor(zacc, 32, 64);  // every lane r16 now holds Z of row (jjV, gV)
-  float* part = a.partials + (static_cast<int64_t>(b) * a.num_q_heads + hk * R) * a.num_splits * 130 +
+  float* part = a.partials + (static_cast<int64_t>(b) * a.num_q_heads + hk * R) * a.part_stride * 130 +
                 static_cast<int64_t>(split) * 130;
-  const int64_t head_stride = static_cast<int64_t>(a.num_splits) * 130;
+  const int64_t head_stride = static_cast<int64_t>(a.part_stride) * 130;
   // lane (q4, r16) owns accumulator rows 4*q4 + r = (jj = r, g = q4) at column r16; the
   // rows of group q4 hold head jj's output for the channels of that group. Staged in LDS
   // so the workspace is written with 8-byte stores.

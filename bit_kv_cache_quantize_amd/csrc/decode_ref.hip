@@ -30,9 +30,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
   const int h = bh % c.hkv;
   const int b = bh / c.hkv;
   const int T = a.seq_lens[b];
-  const int start = split * a.split_len;
-  if (start >= T) return;
-  const int end = min(T, start + a.split_len);
+  const int qend = max(a.tok_begin, T - a.tok_tail);  // the span this kernel covers ends here
+  const int start = a.tok_begin + split * a.split_len;
+  if (start >= qend) return;
+  const int end = min(qend, start + a.split_len);
   const int n = end - start;
   const int R = a.ratio;
   const int tid = threadIdx.x;
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
                                         f16_bits_to_float(m >> 16));
       o = __builtin_fmaf(sc[j][t - start], vhat, o);
     }
-    float* part = a.partials + ((static_cast<int64_t>(b) * a.num_q_heads + h * R + j) * a.num_splits + split) * (kD + 2);
+    float* part = a.partials + ((static_cast<int64_t>(b) * a.num_q_heads + h * R + j) * a.part_stride + split) * (kD + 2);
     part[i] = o;
     if (i == 0) {
       part[kD] = stat[0][j];
@@ -142,11 +143,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
   }
 }
 
-// Log-sum-exp merge of the partitions of one (sequence, query head): thread i owns
-// channel i and reads each partition's (m, l) and o[i], 16 partitions per round trip.
+// Log-sum-exp merge of the partials of one (sequence, query head): thread i owns
+// channel i and reads each partial's (m, l) and o[i], 16 partials per round trip. The
+// partials present are the split kernel's partitions that hold tokens of the covered
+// span, then (with windows) the window partial in slot num_splits.
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ partials,
                                                       const int32_t* __restrict__ seq_lens, int num_q_heads,
-                                                      int num_splits, int split_len, float* __restrict__ out) {
+                                                      int num_splits, int split_len, int tok_begin, int tok_tail,
+                                                      int part_stride, int window, float* __restrict__ out) {
   constexpr int kD = 128;
   constexpr int kChunk = 16;
   const int bj = blockIdx.x;
@@ -157,9 +161,11 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
     out[static_cast<int64_t>(bj) * kD + i] = 0.f;
     return;
   }
-  const int ns = min(num_splits, (T + split_len - 1) / split_len);
-  const float* base = partials + static_cast<int64_t>(bj) * num_splits * (kD + 2);
-  // one pass, kChunk partitions at a time, every load of a chunk issued together: the
+  const int span = max(tok_begin, T - tok_tail) - tok_begin;
+  const int nq = min(num_splits, (span + split_len - 1) / split_len);
+  const int ns = nq + window;  // >= 1: a sequence with T > 0 has a split or window token
+  const float* base = partials + static_cast<int64_t>(bj) * part_stride * (kD + 2);
+  // one pass, kChunk partials at a time, every load of a chunk issued together: the
   // running reference M moves up chunk by chunk and rescales (L, o) exactly like the
   // online softmax inside a partition
   float M = -INFINITY, L = 0.f, o = 0.f;
@@ -167,8 +173,9 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
     float m[kChunk], l[kChunk], v[kChunk];
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) {
-      const bool ok = s0 + k < ns;
-      const float* p = base + (s0 + k) * (kD + 2);
+      const int idx = s0 + k;
+      const bool ok = idx < ns;
+      const float* p = base + (idx < nq ? idx : num_splits) * (kD + 2);
       m[k] = ok ? p[kD] : -INFINITY;
       l[k] = ok ? p[kD + 1] : 0.f;
       v[k] = ok ? p[i] : 0.f;
@@ -211,7 +218,7 @@ hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t st
   (void)g;
   dim3 grid(static_cast<unsigned>(a.batch * a.num_q_heads)), block(128);
   hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, a.partials, a.seq_lens, a.num_q_heads, a.num_splits,
-                     a.split_len, a.out);
+                     a.split_len, a.tok_begin, a.tok_tail, a.part_stride, a.window, a.out);
   return hipGetLastError();
 }
 

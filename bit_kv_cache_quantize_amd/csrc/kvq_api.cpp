@@ -42,20 +42,9 @@ size_t workspace_for(const Geometry& g, int32_t batch, int32_t num_q_heads, int3
   return a > b ? a : b;
 }
 
-kvq_status decode_impl(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+DecodeArgs decode_args(const kvq_cache* cache, const Geometry& g, const void* q, int32_t batch, int32_t num_q_heads,
                        const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
-                       int32_t max_seq_len, float softmax_scale, int32_t num_splits, void* workspace,
-                       size_t workspace_bytes_given, float* out, void* stream, void* ev_begin, void* ev_end,
-                       bool reference) {
-  Geometry g;
-  kvq_status st = check_decode(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
-                               max_seq_len, num_splits, workspace, out, &g);
-  if (st != KVQ_OK || batch == 0) return st;
-  const Splits sp = splits_for(g, batch, num_q_heads, max_seq_len, num_splits,
-                               reference ? SplitKernel::kReference : SplitKernel::kMatrix);
-  if (workspace_bytes_given < workspace_bytes(g, batch, num_q_heads, sp)) return KVQ_ERR_WORKSPACE;
-  if (reference && sp.split_len > 2048) return KVQ_ERR_UNSUPPORTED;
-
+                       float softmax_scale, const Splits& sp, void* workspace, float* out) {
   DecodeArgs a;
   a.c = dev_cache(cache, g);
   a.q = static_cast<const uint16_t*>(q);
@@ -69,10 +58,32 @@ kvq_status decode_impl(const kvq_cache* cache, const void* q, int32_t batch, int
   a.max_pages = max_pages_per_seq;
   a.split_len = sp.split_len;
   a.num_splits = sp.num_splits;
+  a.tok_begin = 0;
+  a.tok_tail = 0;
+  a.part_stride = sp.num_splits;
+  a.window = 0;
   a.hblock = g.hblock;
   a.rot_c = g.hblock > 0 ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(g.hblock))) : 1.0f;
   const double scale = softmax_scale > 0.f ? softmax_scale : 1.0 / std::sqrt(static_cast<double>(g.d));
   a.qscale = static_cast<float>(scale * 1.4426950408889634);  // log2(e)
+  return a;
+}
+
+kvq_status decode_impl(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                       const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                       int32_t max_seq_len, float softmax_scale, int32_t num_splits, void* workspace,
+                       size_t workspace_bytes_given, float* out, void* stream, void* ev_begin, void* ev_end,
+                       bool reference) {
+  Geometry g;
+  kvq_status st = check_decode(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                               max_seq_len, num_splits, workspace, out, &g);
+  if (st != KVQ_OK || batch == 0) return st;
+  const Splits sp = splits_for(g, batch, num_q_heads, max_seq_len, num_splits,
+                               reference ? SplitKernel::kReference : SplitKernel::kMatrix);
+  if (workspace_bytes_given < workspace_bytes(g, batch, num_q_heads, sp)) return KVQ_ERR_WORKSPACE;
+  if (reference && sp.split_len > 2048) return KVQ_ERR_UNSUPPORTED;
+  const DecodeArgs a = decode_args(cache, g, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                                   softmax_scale, sp, workspace, out);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return KVQ_ERR_HIP;
@@ -81,6 +92,15 @@ kvq_status decode_impl(const kvq_cache* cache, const void* q, int32_t batch, int
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return KVQ_ERR_HIP;
   e = launch_combine(a, g, s);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+DevWindow dev_window(const kvq_window* w) {
+  DevWindow d;
+  d.k = static_cast<uint16_t*>(w->k);
+  d.v = static_cast<uint16_t*>(w->v);
+  d.sink = w->sink;
+  d.recent = w->recent;
+  return d;
 }
 
 }  // namespace
@@ -157,6 +177,59 @@ kvq_status kvq_decode_attention_reference(const kvq_cache* cache, const void* q,
                                           void* workspace, size_t workspace_bytes, float* out, void* stream) {
   return decode_impl(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
                      softmax_scale, num_splits, workspace, workspace_bytes, out, stream, nullptr, nullptr, true);
+}
+
+int64_t kvq_window_plane_bytes(const kvq_cache* cache, const kvq_window* window) {
+  Geometry g;
+  if (check_cache(cache, false, &g) != KVQ_OK || check_window(cache, window, false) != KVQ_OK) return -1;
+  return window_plane_bytes(g, window);
+}
+
+kvq_status kvq_window_append(const kvq_cache* cache, const kvq_window* window, const void* k_new, const void* v_new,
+                             const int32_t* seqs, const int32_t* positions, const int64_t* evict_slots,
+                             int64_t n_new, void* stream) {
+  Geometry g;
+  kvq_status st = check_window_append(cache, window, k_new, v_new, seqs, positions, evict_slots, n_new, &g);
+  if (st != KVQ_OK || n_new == 0) return st;
+  const hipError_t e = launch_window_append(dev_cache(cache, g), dev_window(window), g, k_new, v_new, seqs,
+                                            positions, evict_slots, n_new, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+size_t kvq_decode_window_workspace_bytes(const kvq_cache* cache, const kvq_window* window, int32_t batch,
+                                         int32_t num_q_heads, int32_t max_seq_len, int32_t num_splits) {
+  Geometry g;
+  if (check_cache(cache, false, &g) != KVQ_OK || check_window(cache, window, false) != KVQ_OK) return 0;
+  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0) return 0;
+  const Splits sp = splits_for(g, batch, num_q_heads, window_span(window, max_seq_len), num_splits);
+  return window_workspace_bytes(g, batch, num_q_heads, sp);
+}
+
+kvq_status kvq_decode_attention_window(const kvq_cache* cache, const kvq_window* window, const void* q,
+                                       int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                       int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                       float softmax_scale, int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes_given, float* out, void* stream) {
+  Geometry g;
+  kvq_status st = check_decode(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                               max_seq_len, num_splits, workspace, out, &g);
+  if (st != KVQ_OK) return st;
+  st = check_window(cache, window, true);
+  if (st != KVQ_OK) return st;
+  if (batch > window->batch) return KVQ_ERR_INVALID;
+  if (batch == 0) return KVQ_OK;
+  const Splits sp = splits_for(g, batch, num_q_heads, window_span(window, max_seq_len), num_splits);
+  if (workspace_bytes_given < window_workspace_bytes(g, batch, num_q_heads, sp)) return KVQ_ERR_WORKSPACE;
+  DecodeArgs a = decode_args(cache, g, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                             softmax_scale, sp, workspace, out);
+  a.tok_begin = window->sink;
+  a.tok_tail = window->recent;
+  a.part_stride = sp.num_splits + 1;
+  a.window = 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_decode_split(a, g, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (launch_decode_window(a, dev_window(window), g, s) != hipSuccess) return KVQ_ERR_HIP;
+  return launch_combine(a, g, s) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
 kvq_status kvq_dequantize(const kvq_cache* cache, int32_t which, const int64_t* slots, int64_t n, float* out,

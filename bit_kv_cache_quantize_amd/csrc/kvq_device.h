@@ -66,10 +66,21 @@ __device__ __forceinline__ uint32_t float_to_f16_bits(float x) {
   return b;
 }
 
+// bf16 windows: row w of sequence b, kv head h at ((b * (sink + recent) + w) * Hkv + h) * 128.
+struct DevWindow {
+  uint16_t* k;
+  uint16_t* v;
+  int sink;
+  int recent;
+};
+
 // ---- host launchers (defined in the .hip files) ----
 hipError_t launch_quantize_append(const DevCache& c, const Geometry& g, const void* k_new,
                                   const void* v_new, const int64_t* slots, int64_t n_new,
                                   hipStream_t stream);
+hipError_t launch_window_append(const DevCache& c, const DevWindow& w, const Geometry& g, const void* k_new,
+                                const void* v_new, const int32_t* seqs, const int32_t* positions,
+                                const int64_t* evict_slots, int64_t n_new, hipStream_t stream);
 hipError_t launch_dequantize(const DevCache& c, const Geometry& g, int which, const int64_t* slots,
                              int64_t n, float* out, hipStream_t stream);
 
@@ -86,6 +97,14 @@ struct DecodeArgs {
   int max_pages;
   int split_len;
   int num_splits;
+  // The split kernels cover tokens [tok_begin, max(tok_begin, T - tok_tail)) of each
+  // sequence (0, 0 without windows); partition p starts at tok_begin + p * split_len.
+  int tok_begin;
+  int tok_tail;
+  // partial slots per (sequence, query head): num_splits, plus one for the window
+  // partial (slot num_splits) when `window` is set
+  int part_stride;
+  int window;
   int hblock;
   float rot_c;    // float nearest 1/sqrt(hblock)
   float qscale;   // softmax scale * log2(e): logits are kept in the exp2 domain
@@ -94,5 +113,6 @@ struct DecodeArgs {
 hipError_t launch_decode_split(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_split_reference(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
+hipError_t launch_decode_window(const DecodeArgs& a, const DevWindow& w, const Geometry& g, hipStream_t stream);
 
 }  // namespace kvq

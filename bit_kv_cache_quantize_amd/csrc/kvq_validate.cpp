@@ -131,6 +131,46 @@ kvq_status check_append(const kvq_cache* c, const void* k_new, const void* v_new
   return KVQ_OK;
 }
 
+kvq_status check_window(const kvq_cache* c, const kvq_window* w, bool planes) {
+  if (!c || !w) return KVQ_ERR_INVALID;
+  if (w->sink < 0 || w->recent < 1 || w->batch < 0) return KVQ_ERR_INVALID;
+  if (static_cast<int64_t>(w->sink) + w->recent > kMaxWindow) return KVQ_ERR_UNSUPPORTED;
+  // the quantized span starts at `sink`, which the decode kernels need on a tile boundary
+  if (w->sink % kTile != 0) return KVQ_ERR_UNSUPPORTED;
+  if (planes && (!w->k || !w->v || !aligned(w->k, 16) || !aligned(w->v, 16))) return KVQ_ERR_INVALID;
+  return KVQ_OK;
+}
+
+int64_t window_plane_bytes(const Geometry& g, const kvq_window* w) {
+  return static_cast<int64_t>(w->batch) * (w->sink + w->recent) * g.hkv * g.d * 2;
+}
+
+kvq_status check_window_append(const kvq_cache* c, const kvq_window* w, const void* k_new, const void* v_new,
+                               const int32_t* seqs, const int32_t* positions, const int64_t* evict_slots,
+                               int64_t n_new, Geometry* g) {
+  kvq_status st = check_cache(c, true, g);
+  if (st != KVQ_OK) return st;
+  st = check_window(c, w, true);
+  if (st != KVQ_OK) return st;
+  if (n_new < 0) return KVQ_ERR_INVALID;
+  if (n_new == 0) return KVQ_OK;
+  if (n_new > w->batch) return KVQ_ERR_INVALID;  // at most one token per sequence
+  if (!k_new || !v_new || !seqs || !positions || !evict_slots) return KVQ_ERR_INVALID;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(seqs, 4) || !aligned(positions, 4) ||
+      !aligned(evict_slots, 8))
+    return KVQ_ERR_INVALID;
+  return KVQ_OK;
+}
+
+int32_t window_span(const kvq_window* w, int32_t max_seq_len) {
+  const int64_t n = static_cast<int64_t>(max_seq_len) - w->sink - w->recent;
+  return n > 0 ? static_cast<int32_t>(n) : 0;
+}
+
+size_t window_workspace_bytes(const Geometry& g, int32_t batch, int32_t num_q_heads, const Splits& s) {
+  return static_cast<size_t>(batch) * num_q_heads * (s.num_splits + 1) * (g.d + 2) * sizeof(float);
+}
+
 kvq_status check_dequantize(const kvq_cache* c, int32_t which, const int64_t* slots, int64_t n,
                             const float* out, Geometry* g) {
   kvq_status st = check_cache(c, true, g);

@@ -53,6 +53,19 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t batch, int32_
 kvq_status check_append(const kvq_cache* c, const void* k_new, const void* v_new, const int64_t* slots,
                         int64_t n_new, Geometry* g);
 
+// Window description against the cache (sizes only; `planes` also checks k and v).
+constexpr int kMaxWindow = 1024;  // sink + recent
+kvq_status check_window(const kvq_cache* c, const kvq_window* w, bool planes);
+int64_t window_plane_bytes(const Geometry& g, const kvq_window* w);
+
+kvq_status check_window_append(const kvq_cache* c, const kvq_window* w, const void* k_new, const void* v_new,
+                               const int32_t* seqs, const int32_t* positions, const int64_t* evict_slots,
+                               int64_t n_new, Geometry* g);
+
+// Splits of the quantized span of a max_seq_len sequence (max_seq_len - sink - recent).
+int32_t window_span(const kvq_window* w, int32_t max_seq_len);
+size_t window_workspace_bytes(const Geometry& g, int32_t batch, int32_t num_q_heads, const Splits& s);
+
 kvq_status check_dequantize(const kvq_cache* c, int32_t which, const int64_t* slots, int64_t n,
                             const float* out, Geometry* g);
 

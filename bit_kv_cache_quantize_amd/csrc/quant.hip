@@ -23,26 +23,13 @@ namespace {
 
 constexpr int kRowsPerBlock = 16;  // 256 threads, 16 lanes per row
 
+// One 128-channel K (which = 0, rotated first) or V row of kv head h, 8 channels per lane
+// in x, 16 lanes per row: group parameters, codes, packing, and the stores at `slot`.
 template <int BITS, int G>
-__global__ __launch_bounds__(256) void quantize_append_kernel(DevCache c, const uint16_t* __restrict__ k_new,
-                                                              const uint16_t* __restrict__ v_new,
-                                                              const int64_t* __restrict__ slots, int64_t n_rows,
-                                                              int hblock, float rot_c) {
+__device__ __forceinline__ void quantize_store_row(const DevCache& c, int which, int h, int64_t slot, float (&x)[8],
+                                                   int lane, int hblock, float rot_c) {
   constexpr int kQmax = (1 << BITS) - 1;
   constexpr int kLanesPerGroup = G / 8;
-  const int lane = threadIdx.x & 15;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 4);
-  if (row >= n_rows) return;  // whole 16-lane rows retire together
-  const int which = static_cast<int>(row & 1);  // 0 = K, 1 = V
-  const int64_t rh = row >> 1;                  // token * Hkv + head
-  const int h = static_cast<int>(rh % c.hkv);
-  const int64_t r = rh / c.hkv;
-
-  const uint16_t* src = (which ? v_new : k_new) + rh * 128 + lane * 8;
-  const uint4 raw = *reinterpret_cast<const uint4*>(src);
-  float x[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
-                bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
-
   if (which == 0 && hblock > 0) {
     // in-lane strides 1, 2, 4
 #pragma unroll
@@ -104,7 +91,6 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(DevCache c, const 
     }
   }
 
-  const int64_t slot = slots[r];
   const int64_t page = slot / c.page;
   const int off = static_cast<int>(slot - page * c.page);
   const int64_t u = page * c.hkv + h;
@@ -134,6 +120,57 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(DevCache c, const 
       c.vc[v_code_byte(tile_row, c.row_bytes, o, lane * kBytes + k)] = static_cast<uint8_t>(packed >> (8 * k));
     if (group_leader) c.vm[v_meta_entry(tile_row >> 4, c.ngroups, g, o)] = meta;
   }
+}
+
+
+template <int BITS, int G>
+__global__ __launch_bounds__(256) void quantize_append_kernel(DevCache c, const uint16_t* __restrict__ k_new,
+                                                              const uint16_t* __restrict__ v_new,
+                                                              const int64_t* __restrict__ slots, int64_t n_rows,
+                                                              int hblock, float rot_c) {
+  const int lane = threadIdx.x & 15;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 4);
+  if (row >= n_rows) return;  // whole 16-lane rows retire together
+  const int which = static_cast<int>(row & 1);  // 0 = K, 1 = V
+  const int64_t rh = row >> 1;                  // token * Hkv + head
+  const int h = static_cast<int>(rh % c.hkv);
+  const int64_t r = rh / c.hkv;
+  const uint4 raw = *reinterpret_cast<const uint4*>((which ? v_new : k_new) + rh * 128 + lane * 8);
+  float x[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
+                bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+  quantize_store_row<BITS, G>(c, which, h, slots[r], x, lane, hblock, rot_c);
+}
+
+// High-precision windows (InnerQ, Abstract): one new token per row of (seqs, positions).
+// The token at position t goes to window slot t (t < sink) or to the recent ring slot
+// sink + (t - sink) % recent. A full ring first hands the token it holds there, position
+// t - recent, to the quantizer, which stores it at evict_slots[r]. Each lane reads its
+// 16 bytes of the evicted row before it writes the same 16 bytes of the new row.
+template <int BITS, int G>
+__global__ __launch_bounds__(256) void window_append_kernel(DevCache c, DevWindow w, const uint16_t* __restrict__ k_new,
+                                                            const uint16_t* __restrict__ v_new,
+                                                            const int32_t* __restrict__ seqs,
+                                                            const int32_t* __restrict__ positions,
+                                                            const int64_t* __restrict__ evict_slots, int64_t n_rows,
+                                                            int hblock, float rot_c) {
+  const int lane = threadIdx.x & 15;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + (threadIdx.x >> 4);
+  if (row >= n_rows) return;
+  const int which = static_cast<int>(row & 1);
+  const int64_t rh = row >> 1;
+  const int h = static_cast<int>(rh % c.hkv);
+  const int64_t r = rh / c.hkv;
+  const int b = seqs[r], t = positions[r];
+  const int ws = t < w.sink ? t : w.sink + (t - w.sink) % w.recent;
+  uint16_t* wrow = (which ? w.v : w.k) + ((static_cast<int64_t>(b) * (w.sink + w.recent) + ws) * c.hkv + h) * 128;
+  uint4* mine = reinterpret_cast<uint4*>(wrow + lane * 8);
+  if (t >= w.sink && t - w.recent >= w.sink) {  // uniform over the row's 16 lanes
+    const uint4 old = *mine;
+    float x[8] = {bf16_lo(old.x), bf16_hi(old.x), bf16_lo(old.y), bf16_hi(old.y),
+                  bf16_lo(old.z), bf16_hi(old.z), bf16_lo(old.w), bf16_hi(old.w)};
+    quantize_store_row<BITS, G>(c, which, h, evict_slots[r], x, lane, hblock, rot_c);
+  }
+  *mine = *reinterpret_cast<const uint4*>((which ? v_new : k_new) + rh * 128 + lane * 8);
 }
 
 template <int BITS, int G>
@@ -197,6 +234,27 @@ hipError_t launch_quantize_append(const DevCache& c, const Geometry& g, const vo
   }
   KVQ_QA(4, 32) KVQ_QA(4, 64) KVQ_QA(4, 128) KVQ_QA(2, 32) KVQ_QA(2, 64) KVQ_QA(2, 128)
 #undef KVQ_QA
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_window_append(const DevCache& c, const DevWindow& w, const Geometry& g, const void* k_new,
+                                const void* v_new, const int32_t* seqs, const int32_t* positions,
+                                const int64_t* evict_slots, int64_t n_new, hipStream_t stream) {
+  const int64_t n_rows = n_new * g.hkv * 2;
+  const int64_t blocks = (n_rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const float rot_c = g.hblock > 0 ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(g.hblock))) : 1.0f;
+  const auto* k = static_cast<const uint16_t*>(k_new);
+  const auto* v = static_cast<const uint16_t*>(v_new);
+  dim3 grid(static_cast<unsigned>(blocks)), block(256);
+#define KVQ_WA(B, GS)                                                                                      \
+  if (g.bits == B && g.group == GS) {                                                                      \
+    hipLaunchKernelGGL((window_append_kernel<B, GS>), grid, block, 0, stream, c, w, k, v, seqs, positions, \
+                       evict_slots, n_rows, g.hblock, rot_c);                                              \
+    return hipGetLastError();                                                                              \
+  }
+  KVQ_WA(4, 32) KVQ_WA(4, 64) KVQ_WA(4, 128) KVQ_WA(2, 32) KVQ_WA(2, 64) KVQ_WA(2, 128)
+#undef KVQ_WA
   return hipErrorInvalidValue;
 }
 

@@ -183,6 +183,68 @@ kvq_status kvq_decode_attention_reference(const kvq_cache* cache, const void* q,
 kvq_status kvq_dequantize(const kvq_cache* cache, int32_t which, const int64_t* slots, int64_t n,
                           float* out, void* stream);
 
+/*
+ * High-precision windows (InnerQ, Abstract: the tokens of a recent window and the
+ * attention-sink tokens are kept in high precision). The first `sink` tokens and the
+ * last `recent` tokens of every sequence stay in bf16, keys in the ORIGINAL basis
+ * (not rotated); tokens sink <= t < T - recent live quantized in the cache at their own
+ * slots. Token t of sequence b sits in window row
+ *   w = t                               (t < sink)
+ *   w = sink + (t - sink) % recent      (t >= sink, a ring of `recent` rows)
+ * of the planes k, v: bf16 [batch][sink + recent][Hkv][d], 16-byte aligned, owned and
+ * zero-filled (or written directly) by the caller, sizes from kvq_window_plane_bytes.
+ * Supported: sink a multiple of 16 (the cache's tile), recent >= 1,
+ * sink + recent <= 1024.
+ */
+typedef struct kvq_window {
+  int32_t sink;   /* S */
+  int32_t recent; /* R */
+  int32_t batch;  /* sequences the planes hold */
+  void* k;
+  void* v;
+} kvq_window;
+
+/* Bytes of one window plane (k or v) for this cache's d and Hkv; -1 if invalid. */
+int64_t kvq_window_plane_bytes(const kvq_cache* cache, const kvq_window* window);
+
+/*
+ * Append one new token to each of n_new sequences through the windows.
+ *   k_new, v_new : bf16 [n_new][Hkv][d] in the original basis, 16-byte aligned.
+ *   seqs         : int32 [n_new] device array, sequence (row of the window planes);
+ *                  at most one row per sequence in one call.
+ *   positions    : int32 [n_new] device array, position t of the token (= tokens the
+ *                  sequence held before it).
+ *   evict_slots  : int64 [n_new] device array, cache slot of token t - recent.
+ * The token is written to its window row. When t >= sink + recent the ring row already
+ * holds token t - recent, which leaves the window: before being overwritten it is
+ * rotated and quantized (exactly as kvq_quantize_append does) into evict_slots[r];
+ * otherwise evict_slots[r] is not read. n_new == 0 is a no-op returning KVQ_OK.
+ */
+kvq_status kvq_window_append(const kvq_cache* cache, const kvq_window* window, const void* k_new,
+                             const void* v_new, const int32_t* seqs, const int32_t* positions,
+                             const int64_t* evict_slots, int64_t n_new, void* stream);
+
+/* Workspace bytes of kvq_decode_attention_window: fp32 partials
+   [batch][num_q_heads][splits + 1][d + 2]; 0 for an invalid description. */
+size_t kvq_decode_window_workspace_bytes(const kvq_cache* cache, const kvq_window* window, int32_t batch,
+                                         int32_t num_q_heads, int32_t max_seq_len, int32_t num_splits);
+
+/*
+ * Decode attention over the windows and the cache together: one softmax over all
+ * seq_lens[b] tokens, window tokens scored with the original query against their bf16
+ * keys, cache tokens with the rotated query against the dequantized keys (Dual-QK,
+ * Abstract), values likewise. Arguments as kvq_decode_attention, plus the window
+ * (batch <= window->batch; sequence b uses window row b). num_splits partitions the
+ * quantized span of a max_seq_len sequence (max_seq_len - sink - recent tokens).
+ * Three kernels: the split-K kernel over the quantized span, one partial over the
+ * window tokens, the combine.
+ */
+kvq_status kvq_decode_attention_window(const kvq_cache* cache, const kvq_window* window, const void* q,
+                                       int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                       int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                       float softmax_scale, int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes, float* out, void* stream);
+
 /* Static description of a status code. */
 const char* kvq_status_string(kvq_status status);
 

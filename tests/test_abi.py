@@ -163,3 +163,81 @@ def test_split_sizing_and_workspace():
     assert L.kvq_decode_num_splits(ctypes.byref(d), 1, 32, 1000, 7) == 7
     assert L.kvq_decode_num_splits(ctypes.byref(d), 1, 32, 100, 50) == 4
     assert L.kvq_decode_workspace_bytes(ctypes.byref(_desc(bits=3)), 1, 32, 100, 0) == 0
+
+
+def _win(**kw):
+    base = dict(sink=32, recent=128, batch=4, k=FAKE, v=FAKE)
+    base.update(kw)
+    return kvq._Window(base["sink"], base["recent"], base["batch"], base["k"], base["v"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(recent=0), kvq.ERR_INVALID),
+    (dict(sink=-16), kvq.ERR_INVALID),
+    (dict(batch=-1), kvq.ERR_INVALID),
+    (dict(sink=8), kvq.ERR_UNSUPPORTED),          # not on a 16-token tile boundary
+    (dict(sink=512, recent=513), kvq.ERR_UNSUPPORTED),  # more than 1024 window rows
+    (dict(k=0), kvq.ERR_INVALID),
+    (dict(v=FAKE + 2), kvq.ERR_INVALID),
+])
+def test_window_append_rejects_bad_window(kw, status):
+    v = ctypes.c_void_p
+    st = kvq.lib().kvq_window_append(ctypes.byref(_desc()), ctypes.byref(_win(**kw)), v(FAKE), v(FAKE), v(FAKE),
+                                     v(FAKE), v(FAKE), 2, None)
+    assert st == status
+
+
+def test_window_append_argument_checks():
+    L, v = kvq.lib(), ctypes.c_void_p
+    d, w = ctypes.byref(_desc()), ctypes.byref(_win())
+    args = [v(FAKE)] * 5
+    assert L.kvq_window_append(None, w, *args, 1, None) == kvq.ERR_INVALID
+    assert L.kvq_window_append(d, None, *args, 1, None) == kvq.ERR_INVALID
+    assert L.kvq_window_append(d, w, *args, -1, None) == kvq.ERR_INVALID
+    assert L.kvq_window_append(d, w, *args, 5, None) == kvq.ERR_INVALID   # more rows than sequences
+    for i, bad in ((0, FAKE + 2), (2, FAKE + 2), (3, 0), (4, FAKE + 4)):
+        a = list(args)
+        a[i] = v(bad)
+        assert L.kvq_window_append(d, w, *a, 1, None) == kvq.ERR_INVALID, i
+    assert L.kvq_window_append(ctypes.byref(_desc(bits=3)), w, *args, 1, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_window_append(d, w, None, None, None, None, None, 0, None) == kvq.OK  # empty: no launch
+
+
+def test_window_sizes():
+    L = kvq.lib()
+    d = _desc(page_size=32768, num_pages=64)
+    w = _win(sink=64, recent=64, batch=3)
+    assert L.kvq_window_plane_bytes(ctypes.byref(d), ctypes.byref(w)) == 3 * 128 * 8 * 128 * 2
+    assert L.kvq_window_plane_bytes(ctypes.byref(d), ctypes.byref(_win(recent=0))) == -1
+    # the split count follows the quantized span (max_seq_len - sink - recent), plus one
+    # partial for the windows
+    for B, T in ((64, 32768), (3, 5000), (2, 100)):
+        span = max(T - 128, 0)
+        s = L.kvq_decode_num_splits(ctypes.byref(d), B, 32, span, 0)
+        assert L.kvq_decode_window_workspace_bytes(ctypes.byref(d), ctypes.byref(w), B, 32, T, 0) == \
+            B * 32 * (s + 1) * 130 * 4
+    assert L.kvq_decode_window_workspace_bytes(ctypes.byref(d), ctypes.byref(_win(sink=8)), 1, 32, 100, 0) == 0
+
+
+def _decode_window(d, w, **kw):
+    a = dict(q=FAKE, batch=2, hq=32, bt=FAKE, maxp=64, lens=FAKE, maxlen=1000, scale=0.0, splits=0, ws=FAKE,
+             wsb=1 << 40, out=FAKE)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return kvq.lib().kvq_decode_attention_window(
+        ctypes.byref(d) if d is not None else None, ctypes.byref(w) if w is not None else None, v(a["q"]),
+        a["batch"], a["hq"], v(a["bt"]), a["maxp"], v(a["lens"]), a["maxlen"], a["scale"], a["splits"], v(a["ws"]),
+        a["wsb"], v(a["out"]), None)
+
+
+def test_decode_window_argument_checks():
+    d, w = _desc(), _win()
+    assert _decode_window(None, w) == kvq.ERR_INVALID
+    assert _decode_window(d, None) == kvq.ERR_INVALID
+    assert _decode_window(d, _win(recent=0)) == kvq.ERR_INVALID
+    assert _decode_window(d, _win(sink=24)) == kvq.ERR_UNSUPPORTED
+    assert _decode_window(d, w, batch=5) == kvq.ERR_INVALID      # more sequences than window rows
+    assert _decode_window(d, w, hq=64) == kvq.ERR_UNSUPPORTED
+    assert _decode_window(d, w, q=FAKE + 8) == kvq.ERR_INVALID
+    assert _decode_window(d, w, wsb=100) == kvq.ERR_WORKSPACE
+    assert _decode_window(d, w, batch=0) == kvq.OK  # empty: no launch
