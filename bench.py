@@ -10,7 +10,11 @@ Prints one JSON line. `value` is effective KV GB/s of the whole step (algorithmi
 bytes / step time); `roofline` covers the dominant kernel (the split-K decode), timed
 with HIP events recorded on its own stream around every launch.
 
-  python bench.py [--steps K] [--warmup W] [--workload h1] [--gpus 1]
+  python bench.py [--steps K] [--warmup W] [--workload h1] [--gpus 1] [--window S,R]
+
+With --window S,R the first S and last R tokens of every sequence stay in bf16
+windows (InnerQ, Abstract): a step appends through the windows (the token leaving the
+recent window is quantized into the cache) and decodes over windows and cache together.
 """
 from __future__ import annotations
 
@@ -96,6 +100,7 @@ def main():
     ap.add_argument("--cpu-sample-seqs", type=int, default=3, help="sequences in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--parity-seqs", type=int, default=2, help="sequences checked against the oracle")
+    ap.add_argument("--window", default="", help="S,R: bf16 sink and recent windows of S and R tokens")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg, fp32) of this many MiB before timing, "
                          "so hardware byte counters can be scaled against a kernel of known traffic")
@@ -123,15 +128,29 @@ def main():
     # the step appends token T-1 of every sequence (its slot is rewritten each step, so
     # every step does the work of a real decode step at context T)
     geo = wl.geometry(w, extra_tokens=0, lens=lens)
+    win_S, win_R = (int(x) for x in args.window.split(",")) if args.window else (0, 0)
+    windowed = bool(args.window)
     maxlen = int(lens.max())
     t0 = time.time()
     cache = kvq.KVCache.allocate(d, Hkv, w.bits, w.group_size, w.hadamard_block, geo.page_size, geo.num_pages,
                                  device=dev)
     log(f"[bench] {w.name}: cache {cache.nbytes / 1e9:.2f} GB, B={B} Hq={Hq} Hkv={Hkv} T<= {maxlen}")
+    window = kvq.KVWindow.allocate(cache, win_S, win_R, B, device=dev) if windowed else None
     for b in range(B):
         T = int(lens[b])
         k, v = wl.keys(w, b, 0, T, device=dev), wl.values(w, b, 0, T, device=dev)
-        kvq.quantize_append(cache, k, v, geo.slots(b, 0, T).to(dev))
+        if not windowed:
+            kvq.quantize_append(cache, k, v, geo.slots(b, 0, T).to(dev))
+        else:
+            # state before the step's token T-1: sink rows, the ring holding T-1-R..T-2,
+            # and the tokens between quantized
+            lo, hi = win_S, T - 1 - win_R
+            if hi > lo:
+                kvq.quantize_append(cache, k[lo:hi].contiguous(), v[lo:hi].contiguous(),
+                                    geo.slots(b, lo, hi - lo).to(dev))
+            for t in list(range(min(win_S, T - 1))) + list(range(max(win_S, T - 1 - win_R), T - 1)):
+                window.k[b, window.row(t)] = k[t]
+                window.v[b, window.row(t)] = v[t]
         del k, v
     torch.cuda.synchronize()
     log(f"[bench] cache built in {time.time() - t0:.1f}s")
@@ -140,10 +159,12 @@ def main():
     # smaller ones cycle through enough distinct copies to defeat it.
     ring = max(1, math.ceil(1.0e9 / cache.nbytes)) if cache.nbytes < 1.0e9 else 1
     caches = [cache]
+    windows = [window]
     for _ in range(ring - 1):
         c2 = kvq.KVCache(cache.head_dim, cache.num_kv_heads, cache.bits, cache.group_size, cache.hadamard_block,
                          cache.page_size, cache.num_pages, *[p.clone() for p in cache.planes()])
         caches.append(c2)
+        windows.append(kvq.KVWindow(win_S, win_R, B, window.k.clone(), window.v.clone()) if windowed else None)
 
     n_inputs = 4
     qs = [wl.queries(w, step=s, device=dev) for s in range(n_inputs)]
@@ -151,10 +172,17 @@ def main():
     last_slots = torch.stack([geo.slots(b, int(lens[b]) - 1, 1)[0] for b in range(B)]).to(dev)
     bt = geo.block_table.to(dev)
     lens_d = lens.to(dev)
-    ws_bytes = kvq.decode_workspace_bytes(cache, B, Hq, maxlen, args.num_splits)
+    if windowed:
+        ws_bytes = kvq.decode_window_workspace_bytes(cache, window, B, Hq, maxlen, args.num_splits)
+        num_splits = kvq.decode_num_splits(cache, B, Hq, max(maxlen - win_S - win_R, 0), args.num_splits)
+        seqs_d = torch.arange(B, dtype=torch.int32, device=dev)
+        pos_d = (lens - 1).to(dev)
+        evict_d = torch.stack([geo.slots(b, max(int(lens[b]) - 1 - win_R, 0), 1)[0] for b in range(B)]).to(dev)
+    else:
+        ws_bytes = kvq.decode_workspace_bytes(cache, B, Hq, maxlen, args.num_splits)
+        num_splits = kvq.decode_num_splits(cache, B, Hq, maxlen, args.num_splits)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-    num_splits = kvq.decode_num_splits(cache, B, Hq, maxlen, args.num_splits)
 
     if args.calibration_copy_mb > 0:
         n = args.calibration_copy_mb * (1 << 20) // 4
@@ -168,9 +196,18 @@ def main():
     total_steps = args.warmup + args.steps
     hip_events = HipEvents(args.steps)
 
+    applied0 = []  # input indices of the steps applied to caches[0], in order
+
     def step(i: int, events=None):
         c = caches[i % ring]
         kn, vn = news[i % n_inputs]
+        if i % ring == 0:
+            applied0.append(i % n_inputs)
+        if windowed:
+            kvq.window_append(c, windows[i % ring], kn, vn, seqs_d, pos_d, evict_d)
+            kvq.decode_attention_window(c, windows[i % ring], qs[i % n_inputs], bt, lens_d, maxlen,
+                                        num_splits=args.num_splits, workspace=ws, out=out)
+            return
         kvq.quantize_append(c, kn, vn, last_slots)
         kvq.decode_attention(c, qs[i % n_inputs], bt, lens_d, maxlen, num_splits=args.num_splits, workspace=ws,
                              out=out, events=events, reference=args.reference)
@@ -181,12 +218,12 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(args.steps):
-        step(args.warmup + i, events=None if args.reference else hip_events.pair(i))
+        step(args.warmup + i, events=None if (args.reference or windowed) else hip_events.pair(i))
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     split_ms = None
-    if not args.reference:
+    if not (args.reference or windowed):
         split_ms = float(np.mean([hip_events.elapsed_ms(i) for i in range(args.steps)]))
     hip_events.close()
 
@@ -196,6 +233,12 @@ def main():
     q_bytes = B * Hq * d * 2
     out_bytes = B * Hq * d * 4
     append_bytes = B * Hkv * (2 * d * 2 + per_tok_head)
+    if windowed:
+        # window tokens are read as bf16 K and V rows; the append reads the new token,
+        # writes it to the ring, reads the evicted row and writes its quantized form
+        n_win = sum(min(win_S, int(T)) + min(win_R, max(int(T) - win_S, 0)) for T in lens)
+        kv_bytes = (int(lens.to(torch.int64).sum()) - n_win) * Hkv * per_tok_head + n_win * Hkv * 2 * d * 2
+        append_bytes = B * Hkv * (3 * 2 * d * 2 + per_tok_head)
     step_bytes = kv_bytes + q_bytes + out_bytes + append_bytes
     split_bytes = kv_bytes + q_bytes
     value = step_bytes / (ms * 1e-3) / 1e9
@@ -212,6 +255,8 @@ def main():
     # ---- parity on sampled sequences (the oracle recomputes them from the same bytes) ----
     parity = None
     cpu = None
+    if windowed:
+        args.no_cpu_baseline = True  # the CPU baseline is the default (window-free) workload's
     want_oracle = args.parity_seqs > 0 or not args.no_cpu_baseline
     if want_oracle:
         import oracle
@@ -220,9 +265,15 @@ def main():
         i_last = total_steps - 1
         kn, vn = news[i_last % n_inputs]
         q_last = qs[i_last % n_inputs]
-        kvq.quantize_append(caches[0], kn, vn, last_slots)
-        kvq.decode_attention(caches[0], q_last, bt, lens_d, maxlen, num_splits=args.num_splits, workspace=ws,
-                             out=out, reference=args.reference)
+        applied0.append(i_last % n_inputs)
+        if windowed:
+            kvq.window_append(caches[0], windows[0], kn, vn, seqs_d, pos_d, evict_d)
+            kvq.decode_attention_window(caches[0], windows[0], q_last, bt, lens_d, maxlen,
+                                        num_splits=args.num_splits, workspace=ws, out=out)
+        else:
+            kvq.quantize_append(caches[0], kn, vn, last_slots)
+            kvq.decode_attention(caches[0], q_last, bt, lens_d, maxlen, num_splits=args.num_splits, workspace=ws,
+                                 out=out, reference=args.reference)
         torch.cuda.synchronize()
         out_h = out.cpu().numpy().astype(np.float64)
         n_samp = max(args.parity_seqs, 0 if args.no_cpu_baseline else args.cpu_sample_seqs)
@@ -238,6 +289,25 @@ def main():
             ref = oracle.Cache(d, Hkv, w.bits, w.group_size, w.hadamard_block, P, 1)
             k = wl.keys(w, b, 0, T, device=dev)
             v = wl.values(w, b, 0, T, device=dev)
+            if windowed:
+                # prefill state, then the last two steps applied to this cache: each step
+                # rewrites the same ring row and evicted slot, so they fix the final state
+                rw = oracle.Window(d, Hkv, win_S, win_R, 1)
+                lo, hi = win_S, T - 1 - win_R
+                if hi > lo:
+                    ref.append(wl.bf16_bits(k[lo:hi]), wl.bf16_bits(v[lo:hi]), np.arange(lo, hi))
+                for t in list(range(min(win_S, T - 1))) + list(range(max(win_S, T - 1 - win_R), T - 1)):
+                    rw.k[0, window.row(t)] = wl.bf16_bits(k[t])
+                    rw.v[0, window.row(t)] = wl.bf16_bits(v[t])
+                for j in applied0[-2:]:
+                    kj, vj = news[j]
+                    rw.append(ref, wl.bf16_bits(kj[b:b + 1]), wl.bf16_bits(vj[b:b + 1]), np.zeros(1, np.int32),
+                              np.array([T - 1], np.int32), np.array([max(T - 1 - win_R, 0)], np.int64))
+                o = rw.decode(ref, wl.bf16_bits(q_last[b:b + 1]), np.zeros((1, 1), np.int32),
+                              np.array([T], np.int32))
+                worst = max(worst, float(np.max(np.abs(o[0] - out_h[b]))))
+                del k, v
+                continue
             tb = time.perf_counter()
             ref.append(wl.bf16_bits(k[:T - 1]), wl.bf16_bits(v[:T - 1]), np.arange(T - 1))
             t_build += time.perf_counter() - tb
@@ -279,7 +349,8 @@ def main():
                    "context": maxlen, "bits": w.bits, "group_size": w.group_size,
                    "hadamard_block": w.hadamard_block, "page_size": geo.page_size, "num_splits": num_splits,
                    "kernel": "reference" if args.reference else "mfma", "layer_ring": ring,
-                   "step_bytes": step_bytes},
+                   "step_bytes": step_bytes,
+                   **({"window_sink": win_S, "window_recent": win_R} if windowed else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,

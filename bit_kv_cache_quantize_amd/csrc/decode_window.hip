@@ -5,10 +5,13 @@
 // rotation; its scale is the split kernels' (softmax scale * log2 e, exp2 domain), and
 // the partial (o, m, l) is merged with the quantized partitions' by the combine kernel.
 //
-// One workgroup of 256 threads per (sequence, kv head). Rows are read by 16-lane
-// groups, 8 channels (16 bytes) per lane: scores reduce across the group, the value
-// sums across the 16 groups through LDS. Each wave turns one head's scores into
-// probabilities on its own (max, exp2, sum).
+// One workgroup of 256 threads per (sequence, kv head), 16 groups of 16 lanes, 8
+// channels (16 bytes of a row) per lane. Group g takes window tokens g, g + 16, ...,
+// kNB at a time: the K and V rows of all kNB tokens are loaded together, then the
+// scores (reduced across the group's lanes) update the group's online softmax. The 16
+// groups' (m, l, o) are merged through LDS at the end.
+#include <type_traits>
+
 #include "kvq_device.h"
 
 namespace kvq {
@@ -16,6 +19,27 @@ namespace {
 
 constexpr int kWThreads = 256;
 constexpr int kGroups = kWThreads / 16;
+constexpr int kNB = 8;  // tokens per group per round
+
+// Sum over the 16 lanes of a row, in every lane: DPP quad swaps (lane ^ 1, lane ^ 2), then
+// the half-row mirror (lane i <-> 7 - i) and the row mirror (i <-> 15 - i); each step adds
+// a partner holding a disjoint partial sum.
+__device__ __forceinline__ float dpp_sum16(float x) {
+  auto step = [](float v, auto ctrl) {
+    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, true);
+    return v + __int_as_float(y);
+  };
+  x = step(x, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+  x = step(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+  x = step(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  x = step(x, std::integral_constant<int, 0x140>{});  // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ void bf16x8(const uint4 raw, float (&x)[8]) {
+  x[0] = bf16_lo(raw.x); x[1] = bf16_hi(raw.x); x[2] = bf16_lo(raw.y); x[3] = bf16_hi(raw.y);
+  x[4] = bf16_lo(raw.z); x[5] = bf16_hi(raw.z); x[6] = bf16_lo(raw.w); x[7] = bf16_hi(raw.w);
+}
 
 template <int R>
 __global__ __launch_bounds__(kWThreads) void decode_window_kernel(DecodeArgs a, DevWindow w) {
@@ -31,14 +55,13 @@ __global__ __launch_bounds__(kWThreads) void decode_window_kernel(DecodeArgs a, 
   const int rbeg = max(S, T - RW);
   const int n = ns + max(0, T - rbeg);  // 1 .. S + RW
 
-  __shared__ float sc[R][kMaxWindow];
-  __shared__ float red[kGroups][R][kD];
-  __shared__ float stat[2][R];
+  __shared__ float red_o[kGroups][R][kD];
+  __shared__ float red_ml[kGroups][R][2];
 
   const int tid = threadIdx.x;
   const int lane16 = tid & 15, grp = tid >> 4;
   const int64_t rows = static_cast<int64_t>(b) * (S + RW);
-  auto row_of = [&](int i) -> int64_t {  // window row of the i-th window token
+  auto row_of = [&](int i) -> int64_t {  // element offset of this lane's 8 channels
     const int wr = i < ns ? i : S + (rbeg + (i - ns) - S) % RW;
     return ((rows + wr) * hkv + hk) * kD + 8 * lane16;
   };
@@ -49,87 +72,97 @@ __global__ __launch_bounds__(kWThreads) void decode_window_kernel(DecodeArgs a, 
   for (int j = 0; j < R; ++j) {
     const uint4 raw =
         *reinterpret_cast<const uint4*>(a.q + (static_cast<int64_t>(b) * a.num_q_heads + hk * R + j) * kD + 8 * lane16);
-    const float x[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
-                        bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+    bf16x8(raw, q[j]);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[j][e] = x[e] * a.qscale;
+    for (int e = 0; e < 8; ++e) q[j][e] *= a.qscale;
   }
 
-  // scores
-  for (int i = grp; i < n; i += kGroups) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(w.k + row_of(i));
-    const float k[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
-                        bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+  float m[R], l[R], acc[R][8];
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s = __builtin_fmaf(q[j][e], k[e], s);
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
-      if (lane16 == 0) sc[j][i] = s;
-    }
-  }
-  __syncthreads();
-
-  // wave j: probabilities of head j, p = exp2(s - max), and their sum
-  {
-    const int j = tid >> 6, l64 = tid & 63;
-    if (j < R) {
-      float m = -INFINITY;
-      for (int i = l64; i < n; i += 64) m = fmaxf(m, sc[j][i]);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      float l = 0.f;
-      for (int i = l64; i < n; i += 64) {
-        const float p = exp2f(sc[j][i] - m);
-        sc[j][i] = p;
-        l += p;
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
-      if (l64 == 0) {
-        stat[0][j] = m;
-        stat[1][j] = l;
-      }
-    }
-  }
-  __syncthreads();
-
-  // p . v: group grp sums its tokens, then the groups are added through LDS
-  float acc[R][8];
-#pragma unroll
-  for (int j = 0; j < R; ++j)
+  for (int j = 0; j < R; ++j) {
+    m[j] = -INFINITY;
+    l[j] = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
-  for (int i = grp; i < n; i += kGroups) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(w.v + row_of(i));
-    const float v[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
-                        bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+  }
+
+  for (int i0 = grp; i0 < n; i0 += kGroups * kNB) {
+    uint4 kr[kNB], vr[kNB];
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) {  // every load of the round in flight together
+      const int i = i0 + kGroups * u;
+      const int64_t off = row_of(i < n ? i : i0);
+      kr[u] = *reinterpret_cast<const uint4*>(w.k + off);
+      vr[u] = *reinterpret_cast<const uint4*>(w.v + off);
+    }
+    float s[R][kNB];
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) {
+      float k[8];
+      bf16x8(kr[u], k);
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d = __builtin_fmaf(q[j][e], k[e], d);
+        d = dpp_sum16(d);
+        s[j][u] = (i0 + kGroups * u < n) ? d : -INFINITY;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      const float p = sc[j][i];
+      float mn = m[j];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j][e] = __builtin_fmaf(p, v[e], acc[j][e]);
+      for (int u = 0; u < kNB; ++u) mn = fmaxf(mn, s[j][u]);  // finite: token i0 is valid
+      const float alpha = exp2f(m[j] - mn);                   // 0 on the first round
+      l[j] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] *= alpha;
+      m[j] = mn;
+    }
+#pragma unroll
+    for (int u = 0; u < kNB; ++u) {
+      float v[8];
+      bf16x8(vr[u], v);
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const float p = exp2f(s[j][u] - m[j]);  // 0 for tokens past the end
+        l[j] += p;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[j][e] = __builtin_fmaf(p, v[e], acc[j][e]);
+      }
     }
   }
-#pragma unroll
-  for (int j = 0; j < R; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red[grp][j][8 * lane16 + e] = acc[j][e];
-  __syncthreads();
 
+  // merge the groups (a group without tokens has m = -inf, l = 0, o = 0)
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red_o[grp][j][8 * lane16 + e] = acc[j][e];
+    if (lane16 == 0) {
+      red_ml[grp][j][0] = m[j];
+      red_ml[grp][j][1] = l[j];
+    }
+  }
+  __syncthreads();
   for (int idx = tid; idx < R * kD; idx += kWThreads) {
     const int j = idx / kD, ch = idx % kD;
-    float o = 0.f;
+    float M = -INFINITY;
 #pragma unroll
-    for (int g = 0; g < kGroups; ++g) o += red[g][j][ch];
+    for (int g = 0; g < kGroups; ++g) M = fmaxf(M, red_ml[g][j][0]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      const float f = exp2f(red_ml[g][j][0] - M);  // M is finite: group 0 holds token 0
+      o = __builtin_fmaf(red_o[g][j][ch], f, o);
+      L = __builtin_fmaf(red_ml[g][j][1], f, L);
+    }
     float* part = a.partials +
                   ((static_cast<int64_t>(b) * a.num_q_heads + hk * R + j) * a.part_stride + a.num_splits) * (kD + 2);
     part[ch] = o;
     if (ch == 0) {
-      part[kD] = stat[0][j];
-      part[kD + 1] = stat[1][j];
+      part[kD] = M;
+      part[kD + 1] = L;
     }
   }
 }
