@@ -48,6 +48,7 @@ class _Cache(ctypes.Structure):
         ("k_meta", ctypes.c_void_p),
         ("v_codes", ctypes.c_void_p),
         ("v_meta", ctypes.c_void_p),
+        ("quant_mode", ctypes.c_int32),
     ]
 
 
@@ -96,6 +97,7 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "orc_rotate": (None, [vp, ctypes.c_int, ctypes.c_int]),
         "orc_rotate_dense_f64": (None, [vp, vp, ctypes.c_int, ctypes.c_int]),
         "orc_quantize_row": (None, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]),
+        "orc_quantize_row_hybrid": (None, [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]),
         "orc_pack_row": (None, [vp, ctypes.c_int, ctypes.c_int, vp]),
         "orc_unpack_row": (None, [vp, ctypes.c_int, ctypes.c_int, vp]),
         "orc_plane_bytes": (i64, [ctypes.POINTER(_Cache), ctypes.c_int]),
@@ -174,14 +176,16 @@ def rotate_dense_f64(x: np.ndarray, block: int) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- quantizer
 
-def quantize_row(x: np.ndarray, bits: int, group: int):
-    """One token row (already rotated if needed) -> (codes u8[d], scale f16 bits, zero f16 bits)."""
+def quantize_row(x: np.ndarray, bits: int, group: int, hybrid: bool = False):
+    """One token row (already rotated if needed) -> (codes u8[d], scale f16 bits, zero f16 bits).
+    hybrid: per group the symmetric or asymmetric pair with the smaller largest error."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     d = x.size
     codes = np.empty(d, np.uint8)
     sc = np.empty(d // group, np.uint16)
     ze = np.empty(d // group, np.uint16)
-    load().orc_quantize_row(_p(x), d, bits, group, _p(codes), _p(sc), _p(ze))
+    fn = load().orc_quantize_row_hybrid if hybrid else load().orc_quantize_row
+    fn(_p(x), d, bits, group, _p(codes), _p(sc), _p(ze))
     return codes, sc, ze
 
 
@@ -212,6 +216,7 @@ class Cache:
     hadamard_block: int
     page_size: int
     num_pages: int
+    quant_mode: int = 0  # 0 = asymmetric min/max, 1 = hybrid symmetric/asymmetric
 
     def __post_init__(self):
         desc = self._desc(None)
@@ -228,6 +233,7 @@ class Cache:
     def _desc(self, planes) -> _Cache:
         d = _Cache(self.head_dim, self.num_kv_heads, self.bits, self.group_size, self.hadamard_block,
                    self.page_size, self.num_pages)
+        d.quant_mode = self.quant_mode
         if planes is not None:
             d.k_codes, d.k_meta, d.v_codes, d.v_meta = [p.ctypes.data for p in planes]
         return d

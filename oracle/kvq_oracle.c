@@ -185,9 +185,40 @@ void orc_rotate_dense_f64(const double* x, double* y, int d, int block) {
    asymmetric groups; SAW-INT4, Abstract: token-wise groups; the fp32 formula itself is
    this library's reading, spelled out in kvq_oracle.h). */
 
-void orc_quantize_row(const float* x, int d, int bits, int group, uint8_t* codes, uint16_t* scale,
-                      uint16_t* zero) {
+/* codes of one group for the stored pair (s16, z16) */
+static void group_codes(const float* xg, int group, int qmax, uint16_t s16, uint16_t z16, uint8_t* codes) {
+  float s = orc_f16_to_f32(s16), z = orc_f16_to_f32(z16);
+  if (s == 0.0f) {
+    for (int i = 0; i < group; ++i) codes[i] = 0;
+    return;
+  }
+  float inv = 1.0f / s;
+  for (int i = 0; i < group; ++i) {
+    float diff = xg[i] - z;
+    float u = diff * inv;
+    float r = rintf(u);
+    int c = (int)r;
+    if (r < 0.0f) c = 0;
+    if (r > (float)qmax) c = qmax;
+    codes[i] = (uint8_t)c;
+  }
+}
+
+/* largest |x - fmaf(code, s, z)| of one group, in fp32 */
+static float group_max_error(const float* xg, int group, const uint8_t* codes, uint16_t s16, uint16_t z16) {
+  float s = orc_f16_to_f32(s16), z = orc_f16_to_f32(z16);
+  float e = 0.0f;
+  for (int i = 0; i < group; ++i) {
+    float d = fabsf(xg[i] - fmaf((float)codes[i], s, z));
+    if (d > e) e = d;
+  }
+  return e;
+}
+
+static void quantize_row_mode(const float* x, int d, int bits, int group, int hybrid, uint8_t* codes,
+                              uint16_t* scale, uint16_t* zero) {
   const int qmax = (1 << bits) - 1;
+  uint8_t* alt = (uint8_t*)malloc((size_t)group);
   for (int g = 0; g < d / group; ++g) {
     const float* xg = x + g * group;
     float mn = xg[0], mx = xg[0];
@@ -199,24 +230,40 @@ void orc_quantize_row(const float* x, int d, int bits, int group, uint8_t* codes
     float s32 = range / (float)qmax;
     uint16_t s16 = orc_f32_to_f16(s32);
     uint16_t z16 = orc_f32_to_f16(mn + 0.0f); /* +0.0f turns -0 into +0 */
+    group_codes(xg, group, qmax, s16, z16, codes + g * group);
+    if (hybrid) {
+      /* InnerQ, Abstract: each group takes the symmetric or the asymmetric quantizer
+         from its own statistics. Reading: symmetric = scale max|x| / (2^(b-1) - 1) with
+         codes centred on 2^(b-1), stored as the pair {scale, zero = -2^(b-1) scale}
+         (exact in fp16); the group keeps the candidate with the smaller largest
+         reconstruction error, the asymmetric one on a tie. */
+      const int mid = 1 << (bits - 1);
+      float a = fabsf(mn) > fabsf(mx) ? fabsf(mn) : fabsf(mx);
+      uint16_t ss16 = orc_f32_to_f16(a / (float)(mid - 1));
+      uint16_t sz16 = orc_f32_to_f16(-((float)mid * orc_f16_to_f32(ss16)) + 0.0f);
+      group_codes(xg, group, qmax, ss16, sz16, alt);
+      float err_a = group_max_error(xg, group, codes + g * group, s16, z16);
+      float err_s = group_max_error(xg, group, alt, ss16, sz16);
+      if (err_s < err_a) {
+        s16 = ss16;
+        z16 = sz16;
+        for (int i = 0; i < group; ++i) codes[g * group + i] = alt[i];
+      }
+    }
     scale[g] = s16;
     zero[g] = z16;
-    float s = orc_f16_to_f32(s16), z = orc_f16_to_f32(z16);
-    if (s == 0.0f) {
-      for (int i = 0; i < group; ++i) codes[g * group + i] = 0;
-      continue;
-    }
-    float inv = 1.0f / s;
-    for (int i = 0; i < group; ++i) {
-      float diff = xg[i] - z;
-      float u = diff * inv;
-      float r = rintf(u);
-      int c = (int)r;
-      if (r < 0.0f) c = 0;
-      if (r > (float)qmax) c = qmax;
-      codes[g * group + i] = (uint8_t)c;
-    }
   }
+  free(alt);
+}
+
+void orc_quantize_row(const float* x, int d, int bits, int group, uint8_t* codes, uint16_t* scale,
+                      uint16_t* zero) {
+  quantize_row_mode(x, d, bits, group, 0, codes, scale, zero);
+}
+
+void orc_quantize_row_hybrid(const float* x, int d, int bits, int group, uint8_t* codes, uint16_t* scale,
+                             uint16_t* zero) {
+  quantize_row_mode(x, d, bits, group, 1, codes, scale, zero);
 }
 
 void orc_pack_row(const uint8_t* codes, int d, int bits, uint8_t* packed) {
@@ -255,6 +302,7 @@ int orc_check_cache(const orc_cache* c) {
   }
   if (c->page_size <= 0 || c->page_size % 16) return 5;
   if ((c->head_dim * c->bits) % 128) return 6; /* whole 16-byte chunks per row */
+  if (c->quant_mode != 0 && c->quant_mode != 1) return 7;
   return 0;
 }
 
@@ -365,7 +413,7 @@ static void quantize_store_pair(const orc_cache* c, const uint16_t* krow, const 
     const uint16_t* src = which == 0 ? krow : vrow;
     for (int i = 0; i < d; ++i) x[i] = orc_bf16_to_f32(src[i]);
     if (which == 0) orc_rotate(x, d, c->hadamard_block); /* keys only */
-    orc_quantize_row(x, d, c->bits, c->group_size, codes, sc, ze);
+    quantize_row_mode(x, d, c->bits, c->group_size, c->quant_mode == 1, codes, sc, ze);
     orc_pack_row(codes, d, c->bits, packed);
     store_row(c, which, page, h, off, packed, sc, ze);
   }

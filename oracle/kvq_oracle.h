@@ -28,6 +28,9 @@
  *             scale = fp16(s32); zero = fp16(mn + 0.0f).
  *   codes   : s = float(scale), z = float(zero); s == 0 -> all 0; else
  *             inv = 1/s; u = (x - z) * inv (two roundings); code = clamp(rint(u), 0, 2^bits-1).
+ *   hybrid  : (quant_mode 1) per group also the symmetric pair scale = fp16(max|x| /
+ *             (2^(bits-1) - 1)), zero = -2^(bits-1) * scale, codes by the same formula;
+ *             the pair with the smaller largest |x - xhat| is stored (asymmetric on a tie).
  *   dequant : xhat = fmaf(code, s, z).
  *   attention (fp64): qr = dense (H/sqrt(n)) q per block; logit_t = sigma * qr . khat_t;
  *             o = sum_t exp(logit_t - max) vhat_t / sum_t exp(logit_t - max).
@@ -78,6 +81,12 @@ void orc_rotate_dense_f64(const double* x, double* y, int d, int block);
 /* ---- quantizer (one token row of d channels, already rotated when needed) ---- */
 void orc_quantize_row(const float* x, int d, int bits, int group,
                       uint8_t* codes, uint16_t* scale, uint16_t* zero);
+/* hybrid (InnerQ, Abstract): per group the asymmetric pair above or the symmetric pair
+   scale = fp16(max|x| / (2^(bits-1) - 1)), zero = -2^(bits-1) * scale, whichever has the
+   smaller largest |x - fmaf(code, scale, zero)| (asymmetric on a tie); codes by the same
+   formula from the chosen pair */
+void orc_quantize_row_hybrid(const float* x, int d, int bits, int group,
+                             uint8_t* codes, uint16_t* scale, uint16_t* zero);
 void orc_pack_row(const uint8_t* codes, int d, int bits, uint8_t* packed);
 void orc_unpack_row(const uint8_t* packed, int d, int bits, uint8_t* codes);
 
@@ -94,6 +103,7 @@ typedef struct {
   uint8_t* k_meta;
   uint8_t* v_codes;
   uint8_t* v_meta;
+  int32_t quant_mode; /* 0 = asymmetric min/max, 1 = hybrid symmetric/asymmetric */
 } orc_cache;
 
 /* bytes of each plane: 0 = K codes, 1 = K meta, 2 = V codes, 3 = V meta */

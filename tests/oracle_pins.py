@@ -15,6 +15,9 @@ IEEE definitions, library routines and hand derivations):
   fmaf               exact rational arithmetic rounded to nearest-even binary32.
   quantizer          hand-derived worked examples (tests/golden); code range; round-trip
                      bound |x - xhat| <= scale/2 (+ zero rounding + ulps).
+  hybrid quantizer   hand-derived worked examples (tests/golden/hybrid_worked_examples.json);
+                     per group the asymmetric pair or an independently computed symmetric
+                     candidate, never a larger largest error; a hybrid cache stores them.
   packing            documented nibble/crumb order; the documented cache byte layout.
   storage            bits per element = b + 32/G (2.25 at INT2 g128, as the QuaRot page's
                      "BPE ~2.25" for INT2 group 128).
@@ -366,10 +369,10 @@ def check_v_not_rotated_and_k_rotated():
 
 # ----------------------------------------------------------------------------- attention
 
-def _rand_cache(rng, d=128, Hkv=2, T=40, bits=4, G=32, hb=128, P=16, paged_perm=None, B=2):
+def _rand_cache(rng, d=128, Hkv=2, T=40, bits=4, G=32, hb=128, P=16, paged_perm=None, B=2, mode=0):
     pages_per = (T + P - 1) // P
     num_pages = B * pages_per
-    c = oracle.Cache(d, Hkv, bits, G, hb, P, num_pages)
+    c = oracle.Cache(d, Hkv, bits, G, hb, P, num_pages, quant_mode=mode)
     perm = np.arange(num_pages) if paged_perm is None else paged_perm
     bt = perm.reshape(B, pages_per).astype(np.int32)
     k = _bf16(rng.standard_normal((B, T, Hkv, d)))
@@ -383,9 +386,9 @@ def _rand_cache(rng, d=128, Hkv=2, T=40, bits=4, G=32, hb=128, P=16, paged_perm=
 
 def check_attention_matches_sdpa():
     rng = np.random.default_rng(11)
-    for hb, bits, G in ((128, 4, 32), (0, 4, 64), (128, 2, 128), (64, 4, 32)):
+    for hb, bits, G, mode in ((128, 4, 32, 0), (0, 4, 64, 0), (128, 2, 128, 0), (64, 4, 32, 0), (128, 2, 32, 1)):
         B, Hq, Hkv, d, T, P = 2, 8, 2, 128, 45, 16
-        c, bt, k, v = _rand_cache(rng, d, Hkv, T, bits, G, hb, P, B=B)
+        c, bt, k, v = _rand_cache(rng, d, Hkv, T, bits, G, hb, P, B=B, mode=mode)
         q = _bf16(rng.standard_normal((B, Hq, d)))
         lens = np.array([T, 17], np.int32)
         out = c.decode(q, bt, lens, 0.0)
@@ -522,6 +525,96 @@ def check_window_decode_mixed():
         assert np.max(np.abs(out[b] - ref)) < 1e-12, b
 
 
+# ----------------------------------------------------------------------------- hybrid quantizer
+
+HYBRID_GOLDEN = os.path.join(HERE, "golden", "hybrid_worked_examples.json")
+
+
+def check_hybrid_worked_examples():
+    with open(HYBRID_GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        x = np.array(c["x"], np.float32)
+        codes, sc, ze = oracle.quantize_row(x, c["bits"], c["group"], hybrid=True)
+        assert sc[0] == int(c["scale_bits"], 16), (c["name"], hex(sc[0]))
+        assert ze[0] == int(c["zero_bits"], 16), (c["name"], hex(ze[0]))
+        assert np.array_equal(codes, np.array(c["codes"], np.uint8)), (c["name"], codes)
+
+
+def _max_err(x, codes, sc, ze, group):
+    """Largest |x - fma(code, s, z)| per group, fma evaluated exactly in fp64 then rounded."""
+    s = np.repeat(sc.view(np.float16).astype(np.float64), group)
+    z = np.repeat(ze.view(np.float16).astype(np.float64), group)
+    xh = (codes.astype(np.float64) * s + z).astype(np.float32)  # one rounding: the product is exact
+    return np.abs(x - xh).reshape(-1, group).max(axis=1)
+
+
+def check_hybrid_never_worse_and_one_of_two():
+    """Per group the hybrid pair is the asymmetric one or the symmetric candidate
+    (computed here in numpy: scale = f16(max|x| / (2^(b-1)-1)), zero = -2^(b-1) scale,
+    codes by the shared formula), and its largest error never exceeds the asymmetric one."""
+    rng = np.random.default_rng(41)
+    n_sym = 0
+    for bits in (2, 4):
+        mid = 1 << (bits - 1)
+        for group in (32, 64, 128):
+            for trial in range(60):
+                kind = trial % 3
+                x = rng.standard_normal(128) if kind == 0 else (
+                    rng.uniform(-1, 1, 128) if kind == 1 else rng.laplace(size=128))
+                x = (x * np.exp(rng.standard_normal())).astype(np.float32)
+                ca, sa, za = oracle.quantize_row(x, bits, group)
+                ch, sh, zh = oracle.quantize_row(x, bits, group, hybrid=True)
+                ea, eh = _max_err(x, ca, sa, za, group), _max_err(x, ch, sh, zh, group)
+                assert np.all(eh <= ea), (bits, group, trial)
+                for g in range(128 // group):
+                    sl = slice(g * group, (g + 1) * group)
+                    if sh[g] == sa[g] and zh[g] == za[g]:
+                        assert np.array_equal(ch[sl], ca[sl])
+                        continue
+                    n_sym += 1
+                    xg = x[sl]
+                    a = np.float32(np.max(np.abs(xg)))
+                    s16 = np.float16(a / np.float32(mid - 1))
+                    z16 = np.float16(-np.float32(mid) * np.float32(s16))
+                    assert sh[g] == s16.view(np.uint16) and zh[g] == z16.view(np.uint16), (bits, group, trial, g)
+                    s, z = np.float32(s16), np.float32(z16)
+                    u = ((xg - z) * (np.float32(1.0) / s)).astype(np.float32)
+                    want = np.clip(np.rint(u), 0, (1 << bits) - 1).astype(np.uint8)
+                    assert np.array_equal(ch[sl], want)
+                    assert eh[g] < ea[g]
+    assert n_sym > 0  # the symmetric branch was exercised
+
+
+def check_hybrid_cache_append_stores_the_hybrid_rows():
+    """A hybrid cache dequantizes every appended row to the hybrid quantizer's values
+    (keys after the rotation), and an asymmetric cache to the asymmetric ones."""
+    rng = np.random.default_rng(42)
+    for mode in (0, 1):
+        c = oracle.Cache(128, 2, 2, 32, 128, 16, 2, quant_mode=mode)
+        k = _bf16(rng.uniform(-1, 1, (20, 2, 128)))
+        # ternary values (power-of-two scaled) make the symmetric INT2 pair exact
+        v = _bf16(rng.integers(-1, 2, (20, 2, 128)) * 2.0 ** rng.integers(-3, 4, (20, 2, 1)))
+        slots = np.arange(20, dtype=np.int64) + 5
+        c.append(k, v, slots)
+        if mode == 1:  # the mode matters: some stored V groups are symmetric (zero = -2 scale)
+            ve = oracle.Cache(128, 2, 2, 32, 128, 16, 2)
+            ve.append(k, v, slots)
+            assert not np.array_equal(c.dequantize(1, slots), ve.dequantize(1, slots))
+        for which, src in ((0, k), (1, v)):
+            got = c.dequantize(which, slots)
+            for r in range(20):
+                for h in range(2):
+                    x = oracle.bf16_to_f32(src[r, h])
+                    if which == 0:
+                        x = oracle.rotate(x, 128)
+                    codes, sc, ze = oracle.quantize_row(x, 2, 32, hybrid=bool(mode))
+                    s = np.repeat(sc.view(np.float16).astype(np.float64), 32)
+                    z = np.repeat(ze.view(np.float16).astype(np.float64), 32)
+                    want = (codes * s + z).astype(np.float32)
+                    assert np.array_equal(got[r, h], want), (mode, which, r, h)
+
+
 ALL_CHECKS = [
     check_hadamard_is_sylvester,
     check_hadamard_orthogonal,
@@ -547,4 +640,7 @@ ALL_CHECKS = [
     check_window_all_tokens_in_windows,
     check_window_evictions_match_direct_quantization,
     check_window_decode_mixed,
+    check_hybrid_worked_examples,
+    check_hybrid_never_worse_and_one_of_two,
+    check_hybrid_cache_append_stores_the_hybrid_rows,
 ]

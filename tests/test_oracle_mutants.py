@@ -59,6 +59,11 @@ MUTANTS = [
      "      put_u16(m, zero[g]);\n      put_u16(m + 2, scale[g]);\n    }\n  } else {"),
     ("q_not_rotated", "orc_rotate_dense_f64(qv, qr, d, c->hadamard_block);", "orc_rotate_dense_f64(qv, qr, d, 0);"),
     ("softmax_no_norm", "for (int i = 0; i < d; ++i) o[i] = acc[i] / den;", "for (int i = 0; i < d; ++i) o[i] = acc[i];"),
+    ("hybrid_tie_to_symmetric", "if (err_s < err_a) {", "if (err_s <= err_a) {"),
+    ("hybrid_choice_inverted", "if (err_s < err_a) {", "if (err_s > err_a) {"),
+    ("hybrid_sym_divisor", "a / (float)(mid - 1)", "a / (float)mid"),
+    ("hybrid_sym_zero_sign", "-((float)mid * orc_f16_to_f32(ss16)) + 0.0f", "((float)mid * orc_f16_to_f32(ss16)) + 0.0f"),
+    ("hybrid_ignored_in_cache", "c->quant_mode == 1, codes, sc, ze", "0, codes, sc, ze"),
 ]
 
 RUNNER = r"""
