@@ -101,6 +101,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--parity-seqs", type=int, default=2, help="sequences checked against the oracle")
     ap.add_argument("--window", default="", help="S,R: bf16 sink and recent windows of S and R tokens")
+    ap.add_argument("--hybrid", action="store_true", help="hybrid symmetric/asymmetric groups (quant_mode 1)")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg, fp32) of this many MiB before timing, "
                          "so hardware byte counters can be scaled against a kernel of known traffic")
@@ -133,7 +134,7 @@ def main():
     maxlen = int(lens.max())
     t0 = time.time()
     cache = kvq.KVCache.allocate(d, Hkv, w.bits, w.group_size, w.hadamard_block, geo.page_size, geo.num_pages,
-                                 device=dev)
+                                 device=dev, quant_mode=1 if args.hybrid else 0)
     log(f"[bench] {w.name}: cache {cache.nbytes / 1e9:.2f} GB, B={B} Hq={Hq} Hkv={Hkv} T<= {maxlen}")
     window = kvq.KVWindow.allocate(cache, win_S, win_R, B, device=dev) if windowed else None
     for b in range(B):
@@ -161,9 +162,7 @@ def main():
     caches = [cache]
     windows = [window]
     for _ in range(ring - 1):
-        c2 = kvq.KVCache(cache.head_dim, cache.num_kv_heads, cache.bits, cache.group_size, cache.hadamard_block,
-                         cache.page_size, cache.num_pages, *[p.clone() for p in cache.planes()])
-        caches.append(c2)
+        caches.append(cache.clone())
         windows.append(kvq.KVWindow(win_S, win_R, B, window.k.clone(), window.v.clone()) if windowed else None)
 
     n_inputs = 4
@@ -286,7 +285,7 @@ def main():
             T = int(lens[b])
             # a one-sequence oracle cache holding sequence b (contiguous layout)
             P = int(math.ceil(T / 16) * 16)
-            ref = oracle.Cache(d, Hkv, w.bits, w.group_size, w.hadamard_block, P, 1)
+            ref = oracle.Cache(d, Hkv, w.bits, w.group_size, w.hadamard_block, P, 1, quant_mode=cache.quant_mode)
             k = wl.keys(w, b, 0, T, device=dev)
             v = wl.values(w, b, 0, T, device=dev)
             if windowed:
@@ -349,7 +348,7 @@ def main():
                    "context": maxlen, "bits": w.bits, "group_size": w.group_size,
                    "hadamard_block": w.hadamard_block, "page_size": geo.page_size, "num_splits": num_splits,
                    "kernel": "reference" if args.reference else "mfma", "layer_ring": ring,
-                   "step_bytes": step_bytes,
+                   "step_bytes": step_bytes, "quant_mode": cache.quant_mode,
                    **({"window_sink": win_S, "window_recent": win_R} if windowed else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -40,6 +40,7 @@ class _Desc(ctypes.Structure):
         ("k_meta", ctypes.c_void_p),
         ("v_codes", ctypes.c_void_p),
         ("v_meta", ctypes.c_void_p),
+        ("quant_mode", ctypes.c_int32),
     ]
 
 
@@ -152,6 +153,7 @@ class KVCache:
     k_meta: torch.Tensor
     v_codes: torch.Tensor
     v_meta: torch.Tensor
+    quant_mode: int = 0  # 0 = asymmetric min/max groups, 1 = hybrid symmetric/asymmetric
 
     @staticmethod
     def plane_bytes(head_dim, num_kv_heads, bits, group_size, hadamard_block, page_size, num_pages) -> list[int]:
@@ -163,16 +165,22 @@ class KVCache:
 
     @classmethod
     def allocate(cls, head_dim: int, num_kv_heads: int, bits: int, group_size: int, hadamard_block: int,
-                 page_size: int, num_pages: int, device="cuda") -> "KVCache":
+                 page_size: int, num_pages: int, device="cuda", quant_mode: int = 0) -> "KVCache":
         sizes = cls.plane_bytes(head_dim, num_kv_heads, bits, group_size, hadamard_block, page_size, num_pages)
         planes = [torch.zeros(n, dtype=torch.uint8, device=device) for n in sizes]
-        return cls(head_dim, num_kv_heads, bits, group_size, hadamard_block, page_size, num_pages, *planes)
+        return cls(head_dim, num_kv_heads, bits, group_size, hadamard_block, page_size, num_pages, *planes,
+                   quant_mode=quant_mode)
+
+    def clone(self) -> "KVCache":
+        return KVCache(self.head_dim, self.num_kv_heads, self.bits, self.group_size, self.hadamard_block,
+                       self.page_size, self.num_pages, *[p.clone() for p in self.planes()],
+                       quant_mode=self.quant_mode)
 
     @property
     def desc(self) -> _Desc:
         return _Desc(self.head_dim, self.num_kv_heads, self.bits, self.group_size, self.hadamard_block,
                      self.page_size, self.num_pages, self.k_codes.data_ptr(), self.k_meta.data_ptr(),
-                     self.v_codes.data_ptr(), self.v_meta.data_ptr())
+                     self.v_codes.data_ptr(), self.v_meta.data_ptr(), self.quant_mode)
 
     def planes(self):
         return self.k_codes, self.k_meta, self.v_codes, self.v_meta

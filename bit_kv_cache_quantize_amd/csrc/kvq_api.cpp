@@ -123,6 +123,7 @@ int64_t kvq_cache_plane_bytes(const kvq_cache* cache, int32_t plane) {
   g.page = cache->page_size;
   g.row_bytes = cache->head_dim * cache->bits / 8;
   g.num_pages = cache->num_pages;
+  g.quant_mode = 0;
   return plane_bytes(g, plane);
 }
 

@@ -19,6 +19,7 @@ struct DevCache {
   int page;
   int row_bytes;
   int ngroups;
+  int quant_mode;  // 0 = asymmetric min/max, 1 = hybrid symmetric/asymmetric per group
 };
 
 inline DevCache dev_cache(const kvq_cache* c, const Geometry& g) {
@@ -31,6 +32,7 @@ inline DevCache dev_cache(const kvq_cache* c, const Geometry& g) {
   d.page = g.page;
   d.row_bytes = g.row_bytes;
   d.ngroups = g.ngroups;
+  d.quant_mode = g.quant_mode;
   return d;
 }
 

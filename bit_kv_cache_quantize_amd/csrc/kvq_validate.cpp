@@ -20,6 +20,7 @@ kvq_status check_cache(const kvq_cache* c, bool planes, Geometry* g) {
     return KVQ_ERR_INVALID;
   if (c->page_size <= 0 || c->page_size % kTile != 0) return KVQ_ERR_INVALID;
   if ((static_cast<int64_t>(c->head_dim) * c->bits) % 16 != 0) return KVQ_ERR_INVALID;
+  if (c->quant_mode != 0 && c->quant_mode != 1) return KVQ_ERR_INVALID;
   if (planes) {
     const void* p[4] = {c->k_codes, c->k_meta, c->v_codes, c->v_meta};
     for (const void* x : p)
@@ -35,6 +36,7 @@ kvq_status check_cache(const kvq_cache* c, bool planes, Geometry* g) {
   t.page = c->page_size;
   t.row_bytes = c->head_dim * c->bits / 8;
   t.num_pages = c->num_pages;
+  t.quant_mode = c->quant_mode;
   if (g) *g = t;
   return cache_supported(t) ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
 }

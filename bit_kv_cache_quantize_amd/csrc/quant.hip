@@ -28,6 +28,7 @@ constexpr int kRowsPerBlock = 16;  // 256 threads, 16 lanes per row
 template <int BITS, int G>
 __device__ __forceinline__ void quantize_store_row(const DevCache& c, int which, int h, int64_t slot, float (&x)[8],
                                                    int lane, int hblock, float rot_c) {
+  const bool hybrid = c.quant_mode == 1;
   constexpr int kQmax = (1 << BITS) - 1;
   constexpr int kLanesPerGroup = G / 8;
   if (which == 0 && hblock > 0) {
@@ -74,22 +75,59 @@ __device__ __forceinline__ void quantize_store_row(const DevCache& c, int which,
   }
   const float range = (mx - mn) + 0.0f;  // +0.0f: a -0 range (mixed-sign zeros) becomes +0
   const float s32 = range / static_cast<float>(kQmax);
-  const uint32_t s16 = float_to_f16_bits(s32);
-  const uint32_t z16 = float_to_f16_bits(mn + 0.0f);  // -0 minimum stored as +0
-  const float s = f16_bits_to_float(s16);
-  const float z = f16_bits_to_float(z16);
+  uint32_t s16 = float_to_f16_bits(s32);
+  uint32_t z16 = float_to_f16_bits(mn + 0.0f);  // -0 minimum stored as +0
 
-  uint32_t packed = 0;
-  if (s != 0.0f) {
+  // codes of the lane's 8 channels for the stored pair (s16, z16)
+  auto group_codes = [&](uint32_t sb, uint32_t zb, uint32_t (&cd)[8]) {
+    const float s = f16_bits_to_float(sb), z = f16_bits_to_float(zb);
+    if (s == 0.0f) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cd[e] = 0;
+      return;
+    }
     const float inv = 1.0f / s;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float diff = x[e] - z;
       const float u = diff * inv;
-      const float rr = fminf(fmaxf(__builtin_rintf(u), 0.0f), static_cast<float>(kQmax));
-      packed |= static_cast<uint32_t>(rr) << (BITS * e);
+      cd[e] = static_cast<uint32_t>(fminf(fmaxf(__builtin_rintf(u), 0.0f), static_cast<float>(kQmax)));
+    }
+  };
+  uint32_t cd[8];
+  group_codes(s16, z16, cd);
+
+  if (hybrid) {
+    // InnerQ (Abstract): per group, symmetric or asymmetric. The symmetric pair is
+    // scale = fp16(max|x| / (2^(b-1) - 1)), zero = -2^(b-1) * scale (exact in fp16); the
+    // group keeps the pair with the smaller largest |x - fma(code, scale, zero)| (max is
+    // exact and order-free, so every lane of the group decides alike), asymmetric on a tie.
+    constexpr int kMid = 1 << (BITS - 1);
+    auto group_err = [&](uint32_t sb, uint32_t zb, const uint32_t (&c8)[8]) {
+      const float s = f16_bits_to_float(sb), z = f16_bits_to_float(zb);
+      float err = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) err = fmaxf(err, fabsf(x[e] - __builtin_fmaf(static_cast<float>(c8[e]), s, z)));
+#pragma unroll
+      for (int m = 1; m < kLanesPerGroup; m <<= 1) err = fmaxf(err, __shfl_xor(err, m, 16));
+      return err;
+    };
+    const float amax = fmaxf(fabsf(mn), fabsf(mx));
+    const uint32_t ss16 = float_to_f16_bits(amax / static_cast<float>(kMid - 1));
+    const uint32_t sz16 = float_to_f16_bits(-(static_cast<float>(kMid) * f16_bits_to_float(ss16)) + 0.0f);
+    uint32_t cs[8];
+    group_codes(ss16, sz16, cs);
+    if (group_err(ss16, sz16, cs) < group_err(s16, z16, cd)) {
+      s16 = ss16;
+      z16 = sz16;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cd[e] = cs[e];
     }
   }
+
+  uint32_t packed = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) packed |= cd[e] << (BITS * e);
 
   const int64_t page = slot / c.page;
   const int off = static_cast<int>(slot - page * c.page);

@@ -88,6 +88,7 @@ typedef struct kvq_cache {
   void* k_meta;
   void* v_codes;
   void* v_meta;
+  int32_t quant_mode;     /* 0 = asymmetric min/max groups; 1 = hybrid (below) */
 } kvq_cache;
 
 /* Bytes of one plane: 0 = k_codes, 1 = k_meta, 2 = v_codes, 3 = v_meta.
@@ -109,6 +110,15 @@ int64_t kvq_cache_plane_bytes(const kvq_cache* cache, int32_t plane);
  */
 kvq_status kvq_quantize_append(const kvq_cache* cache, const void* k_new, const void* v_new,
                                const int64_t* slots, int64_t n_new, void* stream);
+/*
+ * quant_mode 1, hybrid groups (InnerQ, Abstract: each group chooses symmetric or
+ * asymmetric quantization from its own statistics): besides the pair above, a symmetric
+ * pair scale = fp16(fl32(max|x| / (2^(bits-1) - 1))), zero = -2^(bits-1) * scale (exact)
+ * with codes by the same formula; the group stores the pair whose largest
+ * |x - fmaf(code, scale, zero)| (fp32) is smaller, the asymmetric one on a tie. Both
+ * are stored as {scale, zero}, so decode and dequantize read either alike. Applies to
+ * every append into the cache (kvq_quantize_append and the window append).
+ */
 
 /*
  * Workspace bytes kvq_decode_attention (and kvq_decode_attention_reference) need for

@@ -26,6 +26,7 @@ def _desc(**kw):
                   base["hadamard_block"], base["page_size"], base["num_pages"])
     for f in ("k_codes", "k_meta", "v_codes", "v_meta"):
         setattr(d, f, kw.get(f, FAKE))
+    d.quant_mode = kw.get("quant_mode", 0)
     return d
 
 
@@ -71,6 +72,8 @@ INVALID_CACHES = [
     (dict(head_dim=64, group_size=32, hadamard_block=64), kvq.ERR_UNSUPPORTED),
     (dict(k_codes=0), kvq.ERR_INVALID),
     (dict(v_meta=FAKE + 4), kvq.ERR_INVALID),        # misaligned plane
+    (dict(quant_mode=2), kvq.ERR_INVALID),            # neither asymmetric nor hybrid
+    (dict(quant_mode=-1), kvq.ERR_INVALID),
 ]
 
 

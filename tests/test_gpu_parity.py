@@ -80,11 +80,12 @@ def test_append_edge_values_bit_exact():
         rows.append(rng.standard_normal(128))
     x = np.stack(rows).reshape(-1, 2, 128)             # [n][Hkv=2][d]
     n = x.shape[0]
-    for bits, G, hb in ((4, 32, 128), (2, 128, 128), (4, 64, 0), (2, 32, 64)):
+    for bits, G, hb, mode in ((4, 32, 128, 0), (2, 128, 128, 0), (4, 64, 0, 0), (2, 32, 64, 0),
+                              (4, 32, 128, 1), (2, 32, 0, 1), (4, 128, 0, 1)):
         w = wl.Workload("edge", 1, 2, 2, 128, 32, bits, G, hb)
         geo = wl.geometry(w)
-        gpu = kvq.KVCache.allocate(128, 2, bits, G, hb, geo.page_size, geo.num_pages, device=DEV)
-        ref = oracle.Cache(128, 2, bits, G, hb, geo.page_size, geo.num_pages)
+        gpu = kvq.KVCache.allocate(128, 2, bits, G, hb, geo.page_size, geo.num_pages, device=DEV, quant_mode=mode)
+        ref = oracle.Cache(128, 2, bits, G, hb, geo.page_size, geo.num_pages, quant_mode=mode)
         k = _bf16(x)
         v = _bf16(x[::-1].copy())
         slots = torch.arange(n, dtype=torch.int64)
@@ -92,7 +93,7 @@ def test_append_edge_values_bit_exact():
         ref.append(wl.bf16_bits(k), wl.bf16_bits(v), slots.numpy())
         torch.cuda.synchronize()
         for g, r in zip(gpu.planes(), ref.planes()):
-            assert np.array_equal(g.cpu().numpy(), r), (bits, G, hb)
+            assert np.array_equal(g.cpu().numpy(), r), (bits, G, hb, mode)
 
 
 @pytest.mark.parametrize("name", ["c1", "c4_int2_g128", "c5_paged", "int2_g64_hb32"])
@@ -276,3 +277,54 @@ def test_decode_large_value_scales():
         record(f"large_value_scales/splits={ns}", err)
         print(f"  splits={ns}: max |o| {np.max(np.abs(want)):.1f}, max-abs err {err:.3e}", flush=True)
         assert np.all(np.isfinite(got)) and err <= TOL
+
+
+def _structured_rows(rng, n, Hkv, hb):
+    """Rows on which the symmetric groups win: integers in [-7, 7] and power-of-two-scaled
+    ternary values for V; for K the same, mapped through the rotation's inverse (the
+    rotation is its own inverse) so the rotated keys land near those grids."""
+    ints = rng.integers(-7, 8, (n, Hkv, 128)).astype(np.float64)
+    tern = rng.integers(-1, 2, (n, Hkv, 128)) * 2.0 ** rng.integers(-3, 4, (n, Hkv, 1))
+    mix = rng.standard_normal((n, Hkv, 128))
+    pick = rng.integers(0, 3, (n, Hkv, 1))
+    v = np.where(pick == 0, ints, np.where(pick == 1, tern, mix))
+    k = v.copy()
+    if hb:
+        Rm = np.kron(np.eye(128 // hb), __import__("scipy.linalg").linalg.hadamard(hb) / np.sqrt(hb))
+        k = k @ Rm.T
+    return _bf16(k), _bf16(v[:, ::-1].copy())
+
+
+@pytest.mark.parametrize("bits,G,hb", [(4, 32, 128), (2, 32, 128), (2, 128, 128), (4, 64, 0), (2, 64, 32)])
+def test_hybrid_append_and_decode(bits, G, hb):
+    """quant_mode 1: every cache byte equal to the oracle's hybrid quantizer (which picks
+    symmetric groups on these rows), decode within the tolerance."""
+    print(f"[hybrid] bits={bits} G={G} hb={hb}", flush=True)
+    rng = np.random.default_rng(61 + bits * G + hb)
+    B, Hkv, Hq, T = 2, 2, 8, 300
+    w = wl.Workload("hybrid", B, Hq, Hkv, 128, T, bits, G, hb, page_size=16)
+    lens = torch.tensor([T, 137], dtype=torch.int32)
+    geo = wl.geometry(w, lens=lens)
+    gpu = kvq.KVCache.allocate(128, Hkv, bits, G, hb, geo.page_size, geo.num_pages, device=DEV, quant_mode=1)
+    ref = oracle.Cache(128, Hkv, bits, G, hb, geo.page_size, geo.num_pages, quant_mode=1)
+    asym = oracle.Cache(128, Hkv, bits, G, hb, geo.page_size, geo.num_pages)
+    for b in range(B):
+        n = int(lens[b])
+        k, v = _structured_rows(rng, n, Hkv, hb)
+        slots = geo.slots(b, 0, n)
+        kvq.quantize_append(gpu, k.to(DEV), v.to(DEV), slots.to(DEV))
+        ref.append(wl.bf16_bits(k), wl.bf16_bits(v), slots.numpy())
+        asym.append(wl.bf16_bits(k), wl.bf16_bits(v), slots.numpy())
+    torch.cuda.synchronize()
+    for name, g, r in zip(("k_codes", "k_meta", "v_codes", "v_meta"), gpu.planes(), ref.planes()):
+        gn = g.cpu().numpy()
+        assert np.array_equal(gn, r), f"{name}: {int(np.sum(gn != r))} bytes differ"
+    # the hybrid choice made a difference on these rows
+    assert not np.array_equal(ref.v_meta, asym.v_meta)
+    q = _bf16(rng.standard_normal((B, Hq, 128)))
+    out = kvq.decode_attention(gpu, q.to(DEV), geo.block_table.to(DEV), lens.to(DEV), T)
+    torch.cuda.synchronize()
+    want = ref.decode(wl.bf16_bits(q), geo.block_table.numpy(), lens.numpy())
+    err = max_err(out.cpu().numpy().astype(np.float64), want)
+    record(f"hybrid_b{bits}_g{G}_hb{hb}", err)
+    assert err <= TOL, err
