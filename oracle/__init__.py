@@ -105,6 +105,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
         "orc_quantize_append": (None, [ctypes.POINTER(_Cache), vp, vp, vp, i64]),
         "orc_dequantize": (None, [ctypes.POINTER(_Cache), ctypes.c_int, vp, i64, vp]),
         "orc_decode_attention": (None, [ctypes.POINTER(_Cache), vp, i32, i32, vp, i32, vp, f64, vp]),
+        "orc_decode_attention_pruned": (None, [ctypes.POINTER(_Cache), vp, i32, i32, vp, i32, vp, f64, vp, vp]),
+        "orc_prune_energy": (None, [ctypes.POINTER(_Cache), vp, i32, i32, vp]),
         "orc_attention_bf16": (None, [vp, vp, vp, i32, i32, i32, i32, i32, f64, vp]),
         "orc_window_slot": (ctypes.c_int, [ctypes.POINTER(_Window), ctypes.c_int]),
         "orc_window_append": (None, [ctypes.POINTER(_Cache), ctypes.POINTER(_Window), vp, vp, vp, vp, vp, i64]),
@@ -269,6 +271,29 @@ class Cache:
         out = np.empty((B, Hq, d), np.float64)
         load().orc_decode_attention(ctypes.byref(self.desc), _p(q), B, Hq, _p(bt), bt.shape[1], _p(sl),
                                     float(softmax_scale), _p(out))
+        return out
+
+    def decode_pruned(self, q_bf16: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray,
+                      keep_mask: np.ndarray, softmax_scale: float = 0.0) -> np.ndarray:
+        """Decode with the rotated query restricted to the kept key chunks: keep_mask int32
+        [B][Hkv], bit j = channels j*W..j*W+W-1, W = 128 / bits."""
+        q = np.ascontiguousarray(q_bf16, dtype=np.uint16)
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        km = np.ascontiguousarray(keep_mask, dtype=np.int32)
+        B, Hq, d = q.shape
+        assert km.shape == (B, self.num_kv_heads)
+        out = np.empty((B, Hq, d), np.float64)
+        load().orc_decode_attention_pruned(ctypes.byref(self.desc), _p(q), B, Hq, _p(bt), bt.shape[1], _p(sl),
+                                           float(softmax_scale), _p(km), _p(out))
+        return out
+
+    def prune_energy(self, q_bf16: np.ndarray) -> np.ndarray:
+        """fp64 [B][Hkv][n_chunks]: per key chunk, the kv head's summed squared rotated query."""
+        q = np.ascontiguousarray(q_bf16, dtype=np.uint16)
+        B, Hq, d = q.shape
+        out = np.empty((B, self.num_kv_heads, d * self.bits // 128), np.float64)
+        load().orc_prune_energy(ctypes.byref(self.desc), _p(q), B, Hq, _p(out))
         return out
 
 

@@ -448,9 +448,10 @@ void orc_dequantize(const orc_cache* c, int which, const int64_t* slots, int64_t
    over the INT4 paged cache; Dual-QK, Abstract: queries get the keys' rotation so q.k is
    preserved). Query head j reads KV head j / (Hq / Hkv). */
 
-void orc_decode_attention(const orc_cache* c, const uint16_t* q, int32_t batch, int32_t num_q_heads,
-                          const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
-                          double softmax_scale, double* out) {
+static void decode_attention_masked(const orc_cache* c, const uint16_t* q, int32_t batch, int32_t num_q_heads,
+                                    const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                                    double softmax_scale, const int32_t* keep_mask, double* out) {
+  int width = 128 / c->bits; /* channels of one 16-byte chunk of a packed key row */
   int d = c->head_dim;
   int P = c->page_size;
   int ratio = num_q_heads / c->num_kv_heads;
@@ -471,6 +472,11 @@ void orc_decode_attention(const orc_cache* c, const uint16_t* q, int32_t batch, 
       }
       for (int i = 0; i < d; ++i) qv[i] = (double)orc_bf16_to_f32(q[((int64_t)b * num_q_heads + j) * d + i]);
       orc_rotate_dense_f64(qv, qr, d, c->hadamard_block);
+      if (keep_mask) { /* pruned query channels take no part in the scores */
+        int32_t mask = keep_mask[(int64_t)b * c->num_kv_heads + h];
+        for (int i = 0; i < d; ++i)
+          if (!((mask >> (i / width)) & 1)) qr[i] = 0.0;
+      }
       double m = -INFINITY;
       for (int t = 0; t < T; ++t) {
         int64_t page = block_table[(int64_t)b * max_pages + t / P];
@@ -497,6 +503,43 @@ void orc_decode_attention(const orc_cache* c, const uint16_t* q, int32_t batch, 
   free(qr);
   free(row);
   free(acc);
+}
+
+void orc_decode_attention(const orc_cache* c, const uint16_t* q, int32_t batch, int32_t num_q_heads,
+                          const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                          double softmax_scale, double* out) {
+  decode_attention_masked(c, q, batch, num_q_heads, block_table, max_pages, seq_lens, softmax_scale, NULL, out);
+}
+
+/* Query-channel pruning of key reads (Dual-QK, Abstract: dynamic query-channel pruning
+   further reduces key-cache reads). Reading: per (sequence, kv head) the rotated query
+   keeps whole 16-byte chunks of the packed key row (128 / bits channels each, the unit in
+   which key codes are read); bit j of keep_mask[b * Hkv + h] keeps chunk j, the other
+   channels count as zero in every score. Values are not pruned. */
+void orc_decode_attention_pruned(const orc_cache* c, const uint16_t* q, int32_t batch, int32_t num_q_heads,
+                                 const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                                 double softmax_scale, const int32_t* keep_mask, double* out) {
+  decode_attention_masked(c, q, batch, num_q_heads, block_table, max_pages, seq_lens, softmax_scale, keep_mask,
+                          out);
+}
+
+/* Energy of each chunk of the rotated query, summed over the query heads of each kv head:
+   energy[(b * Hkv + h) * n_chunks + j] = sum over heads of h, channels of chunk j, of qr^2
+   (fp64), n_chunks = head_dim * bits / 128. The pruning keeps the largest. */
+void orc_prune_energy(const orc_cache* c, const uint16_t* q, int32_t batch, int32_t num_q_heads, double* energy) {
+  int d = c->head_dim, H = c->num_kv_heads, width = 128 / c->bits, nch = d / width;
+  int ratio = num_q_heads / H;
+  double* qv = (double*)malloc(sizeof(double) * (size_t)d);
+  double* qr = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int64_t i = 0; i < (int64_t)batch * H * nch; ++i) energy[i] = 0.0;
+  for (int b = 0; b < batch; ++b)
+    for (int j = 0; j < num_q_heads; ++j) {
+      for (int i = 0; i < d; ++i) qv[i] = (double)orc_bf16_to_f32(q[((int64_t)b * num_q_heads + j) * d + i]);
+      orc_rotate_dense_f64(qv, qr, d, c->hadamard_block);
+      for (int i = 0; i < d; ++i) energy[((int64_t)b * H + j / ratio) * nch + i / width] += qr[i] * qr[i];
+    }
+  free(qv);
+  free(qr);
 }
 
 /* ------------------------------------------------------------------------- */

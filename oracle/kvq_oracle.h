@@ -121,6 +121,14 @@ void orc_dequantize(const orc_cache* c, int which, const int64_t* slots, int64_t
 void orc_decode_attention(const orc_cache* c, const uint16_t* q, int32_t batch, int32_t num_q_heads,
                           const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
                           double softmax_scale, double* out);
+/* Query-channel pruning (Dual-QK, Abstract): as orc_decode_attention, with bit j of
+   keep_mask[b * Hkv + h] keeping channels j*W .. j*W + W - 1 of the rotated query,
+   W = 128 / bits (one 16-byte chunk of a packed key row); other channels are zero. */
+void orc_decode_attention_pruned(const orc_cache* c, const uint16_t* q, int32_t batch, int32_t num_q_heads,
+                                 const int32_t* block_table, int32_t max_pages, const int32_t* seq_lens,
+                                 double softmax_scale, const int32_t* keep_mask, double* out);
+/* energy [B][Hkv][d*bits/128]: per chunk, sum over the kv head's query heads of qr^2 */
+void orc_prune_energy(const orc_cache* c, const uint16_t* q, int32_t batch, int32_t num_q_heads, double* energy);
 /* ---- high-precision windows (InnerQ, Abstract) ----
    The first `sink` and the last `recent` tokens of every sequence stay in bf16 (keys in
    the original basis); token t sits in window slot t (t < sink) or

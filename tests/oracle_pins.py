@@ -615,6 +615,59 @@ def check_hybrid_cache_append_stores_the_hybrid_rows():
                     assert np.array_equal(got[r, h], want), (mode, which, r, h)
 
 
+# ----------------------------------------------------------------------------- query-channel pruning
+
+def check_pruned_all_kept_equals_plain():
+    rng = np.random.default_rng(51)
+    for bits, G in ((4, 32), (2, 128)):
+        c, bt, k, v = _rand_cache(rng, 128, 2, 40, bits, G, 128, 16)
+        q = _bf16(rng.standard_normal((2, 8, 128)))
+        lens = np.array([40, 23], np.int32)
+        full = np.full((2, 2), (1 << bits) - 1, np.int32)  # d * bits / 128 = bits chunks per key row
+        assert np.array_equal(c.decode_pruned(q, bt, lens, full), c.decode(q, bt, lens))
+
+
+def check_pruned_matches_restricted_sdpa():
+    """Pruned decode = fp64 SDPA with the scipy-rotated query zeroed outside the kept
+    chunks (W = 128 / bits channels each), on the oracle's dequantized K/V."""
+    rng = np.random.default_rng(52)
+    for bits, G, hb in ((4, 32, 128), (4, 64, 64), (2, 128, 128), (2, 32, 0)):
+        B, Hq, Hkv, d, T, P = 2, 8, 2, 128, 45, 16
+        W, nch = 128 // bits, bits
+        c, bt, k, v = _rand_cache(rng, d, Hkv, T, bits, G, hb, P, B=B)
+        q = _bf16(rng.standard_normal((B, Hq, d)))
+        lens = np.array([T, 29], np.int32)
+        mask = rng.integers(1, 1 << nch, (B, Hkv)).astype(np.int32)
+        out = c.decode_pruned(q, bt, lens, mask)
+        Rm = np.kron(np.eye(d // hb), scipy.linalg.hadamard(hb) / np.sqrt(hb)) if hb else np.eye(d)
+        for b in range(B):
+            t = np.arange(lens[b])
+            slots = bt[b][t // P].astype(np.int64) * P + t % P
+            kh = torch.from_numpy(c.dequantize(0, slots).astype(np.float64))
+            vh = torch.from_numpy(c.dequantize(1, slots).astype(np.float64))
+            qf = oracle.bf16_to_f32(q[b]).astype(np.float64) @ Rm.T
+            for h in range(Hkv):
+                keep = np.repeat([(mask[b, h] >> j) & 1 for j in range(nch)], W).astype(np.float64)
+                qf[h * (Hq // Hkv):(h + 1) * (Hq // Hkv)] *= keep
+            qt = torch.from_numpy(qf).reshape(Hkv, Hq // Hkv, 1, d)
+            kt = kh.permute(1, 0, 2).reshape(Hkv, 1, -1, d).contiguous()
+            vt = vh.permute(1, 0, 2).reshape(Hkv, 1, -1, d).contiguous()
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).reshape(Hq, d).numpy()
+            assert np.max(np.abs(out[b] - ref)) < 1e-12, (bits, G, hb, b)
+
+
+def check_prune_energy():
+    rng = np.random.default_rng(53)
+    for bits, hb in ((4, 128), (2, 32)):
+        c = oracle.Cache(128, 2, bits, 32, hb, 16, 1)
+        q = _bf16(rng.standard_normal((3, 8, 128)))
+        e = c.prune_energy(q)
+        Rm = np.kron(np.eye(128 // hb), scipy.linalg.hadamard(hb) / np.sqrt(hb))
+        qf = oracle.bf16_to_f32(q).astype(np.float64) @ Rm.T          # [B][Hq][d]
+        want = (qf ** 2).reshape(3, 2, 4, bits, 128 // bits).sum(axis=(2, 4))
+        assert np.allclose(e, want, rtol=1e-12, atol=0), bits
+
+
 ALL_CHECKS = [
     check_hadamard_is_sylvester,
     check_hadamard_orthogonal,
@@ -643,4 +696,7 @@ ALL_CHECKS = [
     check_hybrid_worked_examples,
     check_hybrid_never_worse_and_one_of_two,
     check_hybrid_cache_append_stores_the_hybrid_rows,
+    check_pruned_all_kept_equals_plain,
+    check_pruned_matches_restricted_sdpa,
+    check_prune_energy,
 ]

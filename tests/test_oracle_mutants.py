@@ -64,6 +64,11 @@ MUTANTS = [
     ("hybrid_sym_divisor", "a / (float)(mid - 1)", "a / (float)mid"),
     ("hybrid_sym_zero_sign", "-((float)mid * orc_f16_to_f32(ss16)) + 0.0f", "((float)mid * orc_f16_to_f32(ss16)) + 0.0f"),
     ("hybrid_ignored_in_cache", "c->quant_mode == 1, codes, sc, ze", "0, codes, sc, ze"),
+    ("prune_chunk_width", "int width = 128 / c->bits; /* channels of one 16-byte chunk",
+     "int width = 64 / c->bits; /* channels of one 16-byte chunk"),
+    ("prune_bit_order", "if (!((mask >> (i / width)) & 1)) qr[i] = 0.0;", "if (!((mask >> (d / width - 1 - i / width)) & 1)) qr[i] = 0.0;"),
+    ("prune_mask_ignored", "if (!((mask >> (i / width)) & 1)) qr[i] = 0.0;", "(void)mask;"),
+    ("prune_energy_abs", "+= qr[i] * qr[i];", "+= fabs(qr[i]);"),
 ]
 
 RUNNER = r"""
