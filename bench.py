@@ -70,7 +70,7 @@ class HipEvents:
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("decode_mfma.hip", "kvq_device.h"):
+    for f in ("decode_mfma.h", "decode_mfma.hip", "kvq_device.h"):
         with open(os.path.join(ROOT, "bit_kv_cache_quantize_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--parity-seqs", type=int, default=2, help="sequences checked against the oracle")
     ap.add_argument("--window", default="", help="S,R: bf16 sink and recent windows of S and R tokens")
     ap.add_argument("--hybrid", action="store_true", help="hybrid symmetric/asymmetric groups (quant_mode 1)")
+    ap.add_argument("--prune", type=int, default=0,
+                    help="query-channel pruning: key chunks kept per (sequence, kv head), of bits * head_dim / 128")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg, fp32) of this many MiB before timing, "
                          "so hardware byte counters can be scaled against a kernel of known traffic")
@@ -182,6 +184,9 @@ def main():
         num_splits = kvq.decode_num_splits(cache, B, Hq, maxlen, args.num_splits)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    if args.prune and (windowed or args.reference):
+        sys.exit("bench.py: --prune runs the matrix kernel without windows")
+    chunk_mask = torch.zeros((B, Hkv), dtype=torch.int32, device=dev)
 
     if args.calibration_copy_mb > 0:
         n = args.calibration_copy_mb * (1 << 20) // 4
@@ -208,6 +213,11 @@ def main():
                                         num_splits=args.num_splits, workspace=ws, out=out)
             return
         kvq.quantize_append(c, kn, vn, last_slots)
+        if args.prune:
+            kvq.decode_attention_pruned(c, qs[i % n_inputs], bt, lens_d, maxlen, args.prune,
+                                        num_splits=args.num_splits, chunk_mask=chunk_mask, workspace=ws, out=out,
+                                        events=events)
+            return
         kvq.decode_attention(c, qs[i % n_inputs], bt, lens_d, maxlen, num_splits=args.num_splits, workspace=ws,
                              out=out, events=events, reference=args.reference)
 
@@ -232,6 +242,11 @@ def main():
     q_bytes = B * Hq * d * 2
     out_bytes = B * Hq * d * 4
     append_bytes = B * Hkv * (2 * d * 2 + per_tok_head)
+    n_chunks = d * w.bits // 128
+    if args.prune:
+        # pruned key chunks are not read: per token and kv head the K codes shrink to
+        # keep / n_chunks of a row
+        kv_bytes -= int(lens.to(torch.int64).sum()) * Hkv * (d * w.bits // 8) * (n_chunks - args.prune) // n_chunks
     if windowed:
         # window tokens are read as bf16 K and V rows; the append reads the new token,
         # writes it to the ring, reads the evicted row and writes its quantized form
@@ -269,11 +284,16 @@ def main():
             kvq.window_append(caches[0], windows[0], kn, vn, seqs_d, pos_d, evict_d)
             kvq.decode_attention_window(caches[0], windows[0], q_last, bt, lens_d, maxlen,
                                         num_splits=args.num_splits, workspace=ws, out=out)
+        elif args.prune:
+            kvq.quantize_append(caches[0], kn, vn, last_slots)
+            kvq.decode_attention_pruned(caches[0], q_last, bt, lens_d, maxlen, args.prune,
+                                        num_splits=args.num_splits, chunk_mask=chunk_mask, workspace=ws, out=out)
         else:
             kvq.quantize_append(caches[0], kn, vn, last_slots)
             kvq.decode_attention(caches[0], q_last, bt, lens_d, maxlen, num_splits=args.num_splits, workspace=ws,
                                  out=out, reference=args.reference)
         torch.cuda.synchronize()
+        mask_h = chunk_mask.cpu().numpy()
         out_h = out.cpu().numpy().astype(np.float64)
         n_samp = max(args.parity_seqs, 0 if args.no_cpu_baseline else args.cpu_sample_seqs)
         seqs = [int(s) for s in np.linspace(0, B - 1, num=min(n_samp, B)).round()]
@@ -314,7 +334,11 @@ def main():
             # timed oracle step: append the new token, decode every query head of the sequence
             ts = time.perf_counter()
             ref.append(wl.bf16_bits(kn[b:b + 1]), wl.bf16_bits(vn[b:b + 1]), np.array([T - 1]))
-            o = ref.decode(wl.bf16_bits(q_last[b:b + 1]), np.zeros((1, 1), np.int32), np.array([T], np.int32))
+            if args.prune:  # the oracle takes the kernel's choice of kept chunks
+                o = ref.decode_pruned(wl.bf16_bits(q_last[b:b + 1]), np.zeros((1, 1), np.int32),
+                                      np.array([T], np.int32), mask_h[b:b + 1])
+            else:
+                o = ref.decode(wl.bf16_bits(q_last[b:b + 1]), np.zeros((1, 1), np.int32), np.array([T], np.int32))
             t_step += time.perf_counter() - ts
             bytes_cpu += T * Hkv * per_tok_head + Hq * d * 6 + Hkv * (2 * d * 2 + per_tok_head)
             if s_i < args.parity_seqs:
@@ -349,6 +373,10 @@ def main():
                    "hadamard_block": w.hadamard_block, "page_size": geo.page_size, "num_splits": num_splits,
                    "kernel": "reference" if args.reference else "mfma", "layer_ring": ring,
                    "step_bytes": step_bytes, "quant_mode": cache.quant_mode,
+                   **({"keep_chunks": args.prune, "chunks": n_chunks,
+                       "kv_bits_capacity": round(per_tok_head * 8 / (2 * d), 4),
+                       "kv_bits_bandwidth": round(kv_bytes * 8 / (2 * d * Hkv * int(lens.to(torch.int64).sum())), 4)}
+                      if args.prune else {}),
                    **({"window_sink": win_S, "window_recent": win_R} if windowed else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -76,6 +76,8 @@ SIGNATURES = {
     "kvq_decode_window_workspace_bytes": (_sz, [_DP, _WP, _i32, _i32, _i32, _i32]),
     "kvq_decode_attention_window": (ctypes.c_int, [_DP, _WP, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32,
                                                    _vp, _sz, _vp, _vp]),
+    "kvq_decode_attention_pruned": (ctypes.c_int, [_DP, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32, _i32,
+                                                   _vp, _vp, _sz, _vp, _vp, _vp, _vp]),
     "kvq_dequantize": (ctypes.c_int, [_DP, _i32, _vp, _i64, _vp, _vp]),
     "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvq_version": (ctypes.c_char_p, []),
@@ -242,6 +244,38 @@ def decode_attention(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor,
     else:
         st = lib().kvq_decode_attention(*args)
     _check(st, "kvq_decode_attention")
+    return out
+
+
+def decode_attention_pruned(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                            max_seq_len: int, keep_chunks: int, softmax_scale: float = 0.0, num_splits: int = 0,
+                            chunk_mask: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                            out: torch.Tensor | None = None, stream=None, events=None) -> torch.Tensor:
+    """Decode with query-channel pruning: per (sequence, kv head) only the keep_chunks
+    16-byte key chunks (128/bits channels each) with the largest rotated-query energy are
+    read and scored. chunk_mask (int32 [B][Hkv], optional) receives the kept chunks."""
+    _need(q, torch.bfloat16, "q")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    B, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    if chunk_mask is not None:
+        _need(chunk_mask, torch.int32, "chunk_mask")
+        if chunk_mask.shape != (B, cache.num_kv_heads):
+            raise ValueError(f"chunk_mask must be [{B}][{cache.num_kv_heads}]")
+    need = decode_workspace_bytes(cache, B, Hq, max_seq_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, torch.uint8, "workspace")
+    ev = events if events is not None else (None, None)
+    st = lib().kvq_decode_attention_pruned(ctypes.byref(cache.desc), _ptr(q), B, Hq, _ptr(block_table),
+                                           block_table.shape[1], _ptr(seq_lens), max_seq_len, softmax_scale,
+                                           num_splits, keep_chunks, _ptr(chunk_mask), _ptr(workspace),
+                                           workspace.numel(), _ptr(out), _stream(stream), ctypes.c_void_p(ev[0]),
+                                           ctypes.c_void_p(ev[1]))
+    _check(st, "kvq_decode_attention_pruned")
     return out
 
 

@@ -1,0 +1,699 @@
+// Split-K decode attention over the packed low-bit cache, on the CDNA4 matrix cores.
+//
+// SAW-INT4 (Abstract): attention runs straight over the paged INT4 cache.
+// InnerQ (Abstract): dequantization is aligned with the decode vector-matrix
+//   products, so the per-group scale multiplies a partial dot product instead of
+//   every element.
+// Dual-QK (Abstract): the query receives the keys' rotation, so q.k is preserved.
+//
+// One wavefront (one 64-thread workgroup) owns one (sequence, kv head, partition)
+// and walks it in 32-token blocks (two 16-token tiles), grouped in super-blocks of 8.
+//
+// Scores, v_mfma_f32_32x32x16_f16, 8 per block: C[row][token] = sum_ch A[row][ch] B[ch][token]
+//   A rows = (query head jj, digit d, group g): the rotated, pre-scaled query of head jj
+//     split into two f16 parts (hi = f16(x), lo = f16(x - hi)), zero outside group g.
+//   B = the codes as exact f16 integers: a mask spreads the 4-bit (2-bit) codes into
+//     bytes, and bytes 0..15 read as fp8-e4m3 are exactly c * 2^-9, which the scaled
+//     fp8->f16 conversion turns into c. Every product is exact. (Codes could also be
+//     fed as f16 subnormals c * 2^-24 with a mask alone, but the matrix core sums
+//     products of subnormal operands with visibly less precision.)
+//   logit = sum_g scale_g * (C[jj,hi,g] + C[jj,lo,g]) + sum_g zero_g * Qsum[jj][g].
+// Softmax: exp2 domain (the query carries softmax_scale * log2 e). A super-block first
+//   computes the logits of all its blocks (kept in registers), then updates the running
+//   max once and rescales the state once, then runs the values: no data-dependent
+//   branch touches the accumulators.
+// Values, v_mfma_f32_16x16x32_f16, 16 per block: O[row][ch] += sum_t W[row][t] V[t][ch]
+//   A rows = (query head jj, group g), W = 2^8 p * scale_g(t) split into f16 hi (W
+//     rounded toward zero to f16: its top 11 bits) and lo (the exact remainder, rounded
+//     toward zero), two MFMAs into the same accumulator; the 2^8 keeps lo out of the f16
+//     subnormal range. A value scale >= 128 could push W past the f16 maximum: the
+//     partition is then recomputed with W = p * scale.
+//   B = value codes as exact f16 integers, from one 16-byte load per lane of the cache's
+//     16-token tiles, where each word's token pairs are byte-interleaved so one mask
+//     yields both tokens' codes for a channel side by side;
+//   the zero term sum_t p * zero_g(t) is accumulated separately in fp32.
+// Partials (unnormalised o, reference max m, sum l) go to the workspace for the combine.
+#pragma once
+
+#include <type_traits>
+
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ half8 as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(half8, v);
+}
+
+// Two fp8-e4m3 bytes (values c * 2^-9, c = 0..15) of `bytes` -> f16x2 holding the
+// integers c exactly (word 0 = bytes 0,1; word 1 = bytes 2,3).
+template <bool HI_WORD>
+__device__ __forceinline__ uint32_t codes_f16x2(uint32_t bytes) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bytes, 512.0f, HI_WORD));
+}
+
+// Score MFMA p, lane half h covers the 8 channels 64h + 8p .. 64h + 8p + 7; its K-slot
+// kappa (0..7) holds the channel at this position within them, the order in which
+// unpack_k() below lays codes into the B operand.
+template <int BITS>
+__device__ __forceinline__ int qk_slot_channel(int kappa) {
+  if (BITS == 4) return 2 * (kappa & 3) + (kappa >> 2);
+  return (kappa >> 1) + 4 * (kappa & 1);
+}
+
+// B operand of score MFMA p from the lane's packed key codes (kc: 8 dwords at INT4 =
+// channels 64h..64h+63 of its token, 4 dwords at INT2).
+template <int BITS>
+__device__ __forceinline__ half8 unpack_k(const uint32_t* kc, int p) {
+  if (BITS == 4) {
+    const uint32_t w = kc[p];
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // nibbles 0,2,4,6 / 1,3,5,7
+    return as_half8(codes_f16x2<false>(lo), codes_f16x2<true>(lo), codes_f16x2<false>(hi), codes_f16x2<true>(hi));
+  }
+  const uint32_t w = kc[p >> 1];
+  const uint32_t b0 = w & 0x03030303u, b1 = (w >> 2) & 0x03030303u;  // crumbs j, j+4, j+8, j+12
+  const uint32_t b2 = (w >> 4) & 0x03030303u, b3 = (w >> 6) & 0x03030303u;
+  if (p & 1)
+    return as_half8(codes_f16x2<true>(b0), codes_f16x2<true>(b1), codes_f16x2<true>(b2), codes_f16x2<true>(b3));
+  return as_half8(codes_f16x2<false>(b0), codes_f16x2<false>(b1), codes_f16x2<false>(b2), codes_f16x2<false>(b3));
+}
+
+// Channel of column n (0..15) of value N-tile nt (0..7), matching unpack_v().
+template <int BITS>
+__device__ __forceinline__ int pv_channel(int nt, int n) {
+  if (BITS == 4) return 4 * (n + 16 * (nt >> 2)) + 2 * (nt & 1) + ((nt >> 1) & 1);
+  return 8 * n + (nt >> 1) + 4 * (nt & 1);
+}
+
+// B operand of value N-tile nt: vc holds, for 8 tokens (4 token pairs, one dword each),
+// one 16-bit code word with the pair's bytes interleaved: [t0 byte0, t1 byte0, t0 byte1,
+// t1 byte1]. INT4: words n and n+16 in vc[0..3] and vc[4..7].
+template <int BITS>
+__device__ __forceinline__ half8 unpack_v(const uint32_t* vc, int nt) {
+  uint32_t x[4];
+  if (BITS == 4) {
+    const uint32_t* w = vc + 4 * (nt >> 2);
+    const int sh = 4 * ((nt >> 1) & 1);  // low or high nibbles
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = (w[k] >> sh) & 0x0F0F0F0Fu;
+  } else {
+    const int sh = 2 * (nt >> 1);  // crumb j of each byte
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x[k] = (vc[k] >> sh) & 0x03030303u;
+  }
+  if (nt & 1)
+    return as_half8(codes_f16x2<true>(x[0]), codes_f16x2<true>(x[1]), codes_f16x2<true>(x[2]), codes_f16x2<true>(x[3]));
+  return as_half8(codes_f16x2<false>(x[0]), codes_f16x2<false>(x[1]), codes_f16x2<false>(x[2]),
+                  codes_f16x2<false>(x[3]));
+}
+
+__device__ __forceinline__ float lo_f16(uint32_t m) { return f16_bits_to_float(m & 0xFFFFu); }
+__device__ __forceinline__ float hi_f16(uint32_t m) { return f16_bits_to_float(m >> 16); }
+
+template <int BITS, int NG>
+struct KBlock {
+  uint32_t kc[BITS == 4 ? 8 : 4];  // key codes of the lane's token, channels 64h..64h+63
+  uint32_t km[NG];                 // key {scale, zero} of the lane's token
+};
+
+template <int BITS>
+struct VBlock {
+  uint32_t vc[BITS == 4 ? 8 : 4];  // value code words, 8 tokens
+  uint32_t vm[8];                  // value {scale, zero} of group g, 8 tokens
+};
+
+__device__ __forceinline__ _Float16 f16_lo(uint32_t m) {
+  return __builtin_bit_cast(_Float16, static_cast<uint16_t>(m & 0xFFFFu));
+}
+
+constexpr int NBS = 8;  // blocks per super-block
+constexpr int PF = 3;   // blocks loaded ahead
+
+// PRUNE: query-channel pruning of key reads (Dual-QK, Abstract: dynamic query-channel
+// pruning further cuts key-cache reads). Per (sequence, kv head) the rotated query keeps
+// the a.keep_chunks 16-byte chunks of the packed key row (128 / BITS channels each) with
+// the largest summed squared query over the kv head's query heads (ties: lower chunk);
+// the other channels are zeroed in the query and their key chunks are never loaded
+// (the first PF blocks, loaded before the query is known, read every chunk).
+template <int BITS, int G, int R, bool PRUNE>
+__global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
+  constexpr int NG = 128 / G;
+  constexpr int RB = 128 * BITS / 8;
+  const DevCache& c = a.c;
+  const int lane = threadIdx.x;
+  const int unit = blockIdx.x;
+  const int split = unit % a.num_splits;
+  const int bh = unit / a.num_splits;
+  const int hk = bh % c.hkv;
+  const int b = bh / c.hkv;
+  const int T = a.seq_lens[b];
+  const int qend = max(a.tok_begin, T - a.tok_tail);  // the span this kernel covers ends here
+  const int start = a.tok_begin + split * a.split_len;
+  if (start >= qend) return;
+  const int end = min(qend, start + a.split_len);
+
+  __shared__ float o_s[4][128];  // partial outputs, staged for the workspace stores
+  __shared__ float p_s[NBS][4][32];  // p of a super-block's blocks, per head and token
+  __shared__ float qsum_s[4][4];
+  __shared__ half8 aqk_s[8][64];  // score A operands, re-read from LDS for every block
+
+  // lane roles: scores use (hQ, nQ) = (lane / 32, lane % 32): heads 2hQ, 2hQ+1 of token nQ;
+  // values use (q4, r16) = (lane / 16, lane % 16): A row r16 = 4g + jj, tokens 8q4..8q4+7,
+  // B column r16.
+  const int hQ = lane >> 5, nQ = lane & 31;
+  const int q4 = lane >> 4, r16 = lane & 15;
+  const int jjV = r16 & 3, gV = r16 >> 2;
+  const int gVc = gV < NG ? gV : NG - 1;
+  // -1 the compiler cannot see: keeps fma(f16 -> f32 x, -1, y) a single mixed-precision FMA
+  float neg1 = -1.0f;
+  asm("" : "+s"(neg1));
+
+  // ---- where the partition's blocks live ----
+  // nfull full 32-token blocks, then possibly one partial block
+  const int nblk = (end - start + 31) >> 5;
+  const int nfull = (end - start) >> 5;
+  const int P = c.page;
+  const int pg_first = start / P;
+  const int pg_last = (end - 1) / P;
+  // contiguous case: the whole partition in one page, token t in row row_base + t
+  const bool one_page = pg_last == pg_first;
+  const int32_t* bt = a.block_table + static_cast<int64_t>(b) * a.max_pages;
+  const int64_t row_base =
+      (static_cast<int64_t>(bt[pg_first]) * c.hkv + hk) * P - static_cast<int64_t>(pg_first) * P;
+  // Blocks are loaded in order, each kind through its own cursor: block index, the
+  // page and in-page offset of its first token, and (paged case) a window of 64
+  // block-table entries in a register, lane i holding logical page wbase + i. Past the
+  // last block the cursor stays (the load re-reads the last block; nothing is computed
+  // from it).
+  struct Cursor {
+    int blk, pg, off, wbase;
+    int32_t bt_w;
+  };
+  auto window = [&](int first) -> int32_t { return (first + lane <= pg_last) ? bt[first + lane] : 0; };
+  const Cursor cur0 = {0, pg_first, start - pg_first * P, pg_first, one_page ? 0 : window(pg_first)};
+  auto page_row = [&](Cursor& cu, int pg, int off) -> int64_t {  // row of token pg * P + off
+    if (pg - cu.wbase >= 64) {  // a cursor visits pages in increasing order
+      cu.wbase = pg;
+      cu.bt_w = window(pg);
+    }
+    const int32_t phys = __builtin_amdgcn_readlane(cu.bt_w, pg - cu.wbase);
+    return (static_cast<int64_t>(phys) * c.hkv + hk) * P + off;
+  };
+  auto advance = [&](Cursor& cu) {
+    if (cu.blk + 1 < nblk) {
+      ++cu.blk;
+      cu.off += 32;
+      while (cu.off >= P) {
+        cu.off -= P;
+        ++cu.pg;
+      }
+    }
+  };
+  // rows of the cursor block's two 16-token tiles (a tile past the partition end: the
+  // first tile again)
+  auto tile_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
+    const int t0 = start + 32 * cu.blk;
+    if (one_page) {
+      row0 = row_base + t0;
+      row1 = (t0 + 16 < end) ? row0 + 16 : row0;
+      return;
+    }
+    row0 = page_row(cu, cu.pg, cu.off);
+    if (t0 + 16 >= end) {
+      row1 = row0;
+    } else if (cu.off + 16 < P) {
+      row1 = row0 + 16;
+    } else {
+      row1 = page_row(cu, cu.pg + 1, cu.off + 16 - P);
+    }
+  };
+
+  // This lane's pieces of a block, relative to the first token row (tile_row) of its
+  // tile: key codes, the 16-byte chunk(s) of channels 64 hQ .. 64 hQ + 63 of token nQ
+  // (tiles are chunk-major, so one load instruction reads whole cache lines); value code
+  // words r16 and r16 + 16 of tokens 8 (q4 % 2) ..; value {scale, zero} of group gVc,
+  // tokens 8 (q4 % 2) + 0..3 (part 0) and + 4..7 (part 1).
+  constexpr int KCH = BITS == 4 ? 2 : 1;  // key code chunks per lane
+  const uint32_t kc_lane = static_cast<uint32_t>((KCH * hQ * 16 + (nQ & 15)) * 16);
+  const uint32_t vc_lane = static_cast<uint32_t>((r16 * 16 + 8 * (q4 & 1)) * 2);
+  const uint32_t vm_lane = static_cast<uint32_t>((gVc * 2 + (q4 & 1)) * 4 * 4);
+  // the same for a full block of a contiguous partition, relative to the block's first row
+  const uint32_t koff = static_cast<uint32_t>((nQ >> 4) * 16 * RB) + kc_lane;
+  const uint32_t kmoff = static_cast<uint32_t>(nQ * NG * 4);
+  const uint32_t voff = static_cast<uint32_t>(q4 < 2 ? 0 : 16 * RB) + vc_lane;
+  const uint32_t vmoff = static_cast<uint32_t>(q4 < 2 ? 0 : NG * 64) + vm_lane;
+  // Key and value streams are read once: non-temporal loads. V meta loads cover whole
+  // cache lines only with 4 groups; with fewer they read half lines and stay cached.
+  auto ld16 = [](const uint8_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); };
+
+  // kept key chunks (bit j = chunk j); every chunk until the query has been ranked
+  constexpr int NCH = RB / 16;
+  int kmask = (1 << NCH) - 1;
+
+  auto load_k = [&](Cursor& cu) {
+    KBlock<BITS, NG> kb;
+    const uint8_t* src;
+    const uint8_t* msrc;
+    if (one_page && start + 32 * cu.blk + 32 <= end) {
+      const int64_t r0 = row_base + start + 32 * cu.blk;  // a multiple of 16
+      src = c.kc + r0 * RB + koff;
+      msrc = reinterpret_cast<const uint8_t*>(c.km) + r0 * (NG * 4) + kmoff;
+    } else {
+      int64_t row0, row1;
+      tile_rows(cu, row0, row1);
+      const int64_t trow = (nQ < 16) ? row0 : row1;
+      src = c.kc + trow * RB + kc_lane;
+      msrc = reinterpret_cast<const uint8_t*>(c.km + (trow + (nQ & 15)) * NG);
+    }
+    advance(cu);
+    u32x4 x0 = {0u, 0u, 0u, 0u};
+    if (!PRUNE || ((kmask >> (KCH * hQ)) & 1)) x0 = ld16(src);
+    kb.kc[0] = x0[0]; kb.kc[1] = x0[1]; kb.kc[2] = x0[2]; kb.kc[3] = x0[3];
+    if (BITS == 4) {
+      u32x4 x1 = {0u, 0u, 0u, 0u};
+      if (!PRUNE || ((kmask >> (KCH * hQ + 1)) & 1)) x1 = ld16(src + 16 * 16);  // the next chunk of the token
+      kb.kc[4] = x1[0]; kb.kc[5] = x1[1]; kb.kc[6] = x1[2]; kb.kc[7] = x1[3];
+    }
+    if (NG == 4) {
+      const u32x4 mm = ld16(msrc);
+      kb.km[0] = mm[0]; kb.km[1] = mm[1]; kb.km[2 % NG] = mm[2]; kb.km[3 % NG] = mm[3];
+    } else if (NG == 2) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 mm = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(msrc));
+      kb.km[0] = mm[0]; kb.km[1 % NG] = mm[1];
+    } else {
+      kb.km[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(msrc));
+    }
+    return kb;
+  };
+  auto load_v = [&](Cursor& cu) {
+    VBlock<BITS> vb;
+    const uint8_t* src;   // this lane's first code word of its 8 tokens
+    const uint8_t* msrc;  // this lane's value {scale, zero}, part 0
+    if (one_page && start + 32 * cu.blk + 32 <= end) {
+      const int64_t r0 = row_base + start + 32 * cu.blk;  // a multiple of 16
+      src = c.vc + r0 * RB + voff;
+      msrc = reinterpret_cast<const uint8_t*>(c.vm) + (r0 / 16) * (NG * 64) + vmoff;
+    } else {
+      int64_t row0, row1;
+      tile_rows(cu, row0, row1);
+      const int64_t trow = (q4 < 2) ? row0 : row1;  // value tile of tokens 8q4..8q4+7
+      src = c.vc + trow * RB + vc_lane;
+      msrc = reinterpret_cast<const uint8_t*>(c.vm) + (trow / 16) * (NG * 64) + vm_lane;
+    }
+    advance(cu);
+    const u32x4 w0 = ld16(src);
+    vb.vc[0] = w0[0]; vb.vc[1] = w0[1]; vb.vc[2] = w0[2]; vb.vc[3] = w0[3];
+    if (BITS == 4) {
+      const u32x4 w1 = ld16(src + 16 * 16 * 2);
+      vb.vc[4] = w1[0]; vb.vc[5] = w1[1]; vb.vc[6] = w1[2]; vb.vc[7] = w1[3];
+    }
+    const uint8_t* msrc1 = msrc + NG * 8 * 4;  // part 1
+    const u32x4 m0 = NG == 4 ? ld16(msrc) : *reinterpret_cast<const u32x4*>(msrc);
+    const u32x4 m1 = NG == 4 ? ld16(msrc1) : *reinterpret_cast<const u32x4*>(msrc1);
+    vb.vm[0] = m0[0]; vb.vm[1] = m0[1]; vb.vm[2] = m0[2]; vb.vm[3] = m0[3];
+    vb.vm[4] = m1[0]; vb.vm[5] = m1[1]; vb.vm[6] = m1[2]; vb.vm[7] = m1[3];
+    return vb;
+  };
+
+  // the first key blocks are in flight while the query is prepared
+  KBlock<BITS, NG> kb[PF + 1];
+  VBlock<BITS> vb[PF + 1];
+  Cursor kcur = cur0, vcur = cur0;
+#pragma unroll
+  for (int j = 0; j < PF; ++j) kb[j] = load_k(kcur);
+
+  // ---- rotated, scaled query of the R heads: score A operands and group sums ----
+  // Lane (head jq = lane / 16, chunk c16 = lane % 16) holds channels 8 c16 .. 8 c16 + 7.
+  // The Walsh-Hadamard butterfly runs in registers: strides 1, 2, 4 in the lane, 8..64
+  // across the 16 lanes of the head. A chunk is exactly the channel set of score MFMA
+  // p = c16 % 8 in lane half c16 / 8, so each lane writes its own two A rows (hi and lo
+  // digit of head jq, group of the chunk); every other row of an A operand is zero.
+  {
+    const int jq = lane >> 4, c16 = lane & 15;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (jq < R) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(
+          a.q + (static_cast<int64_t>(b) * a.num_q_heads + hk * R + jq) * 128 + 8 * c16);
+      x[0] = bf16_lo(raw.x); x[1] = bf16_hi(raw.x); x[2] = bf16_lo(raw.y); x[3] = bf16_hi(raw.y);
+      x[4] = bf16_lo(raw.z); x[5] = bf16_hi(raw.z); x[6] = bf16_lo(raw.w); x[7] = bf16_hi(raw.w);
+    }
+    const int hb = a.hblock;
+#pragma unroll
+    for (int s = 1; s < 8; s <<= 1) {
+      if (s < hb) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (!(e & s)) {
+            const float u = x[e], v = x[e + s];
+            x[e] = u + v;
+            x[e + s] = u - v;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      if (8 * m < hb) {
+        const bool upper = (c16 & m) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float y = __shfl_xor(x[e], m, 64);
+          x[e] = upper ? (y - x[e]) : (x[e] + y);
+        }
+      }
+    }
+    if (PRUNE) {
+      // chunk energies: the lane's squared channels, summed over the chunk's lanes and the
+      // heads, then read from the lanes of head 0 that open each chunk
+      constexpr int LPC = 128 / BITS / 8;  // lanes per chunk
+      float e2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) e2 = __builtin_fmaf(x[e], x[e], e2);
+#pragma unroll
+      for (int m = 1; m < LPC; m <<= 1) e2 += __shfl_xor(e2, m, 64);
+      e2 += __shfl_xor(e2, 16, 64);
+      e2 += __shfl_xor(e2, 32, 64);
+      float en[NCH];
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) en[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e2), j * LPC));
+      int keep = 0;
+#pragma unroll
+      for (int j = 0; j < NCH; ++j) {
+        int rank = 0;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) rank += (en[i] > en[j] || (en[i] == en[j] && i < j)) ? 1 : 0;
+        if (rank < a.keep_chunks) keep |= 1 << j;
+      }
+      kmask = keep;
+      if (!((kmask >> (c16 / LPC)) & 1)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+      }
+      if (split == 0 && lane == 0 && a.chunk_mask != nullptr) a.chunk_mask[static_cast<int64_t>(b) * c.hkv + hk] = kmask;
+    }
+    const float qmul = (hb > 0 ? a.rot_c : 1.0f) * a.qscale;
+    _Float16 hi[8], lo[8];
+    float part = 0.f;  // group sum of the query as the MFMA sees it (hi + lo)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = x[e] * qmul;
+      hi[e] = static_cast<_Float16>(v);
+      lo[e] = static_cast<_Float16>(v - static_cast<float>(hi[e]));
+      part += static_cast<float>(hi[e]) + static_cast<float>(lo[e]);
+    }
+#pragma unroll
+    for (int p = 0; p < 8; ++p) aqk_s[p][lane] = half8{};
+    __syncthreads();
+    if (jq < R) {
+      const int p = c16 & 7, hA = c16 >> 3, g = (8 * c16) / G;
+      const int rho = 8 * g + 4 * (jq >> 1) + 2 * (jq & 1);
+      half8 vh, vl;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        vh[k] = hi[qk_slot_channel<BITS>(k)];
+        vl[k] = lo[qk_slot_channel<BITS>(k)];
+      }
+      aqk_s[p][32 * hA + rho] = vh;
+      aqk_s[p][32 * hA + rho + 1] = vl;
+    }
+#pragma unroll
+    for (int m = 1; m < G / 8; m <<= 1) part += __shfl_xor(part, m, 64);
+    if (jq < R && (c16 % (G / 8)) == 0) qsum_s[jq][(8 * c16) / G] = part;
+  }
+  __syncthreads();
+
+  float qsum[2][NG];
+#pragma unroll
+  for (int j2 = 0; j2 < 2; ++j2)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) qsum[j2][g] = (2 * hQ + j2 < R) ? qsum_s[2 * hQ + j2][g] : 0.f;
+
+  // ---- state (exp2 domain) ----
+  // p = 2^(logit - mref) with mref = mrun - shift, mrun the running max: the value
+  // weights carry 2^shift (shift = 8), which keeps the f16 split of p * scale clear of the
+  // f16 subnormal range; written partials hold mref, so the factor cancels in the
+  // combine. A value scale >= 128 could push the weights past the f16 maximum: the
+  // partition is then recomputed with shift = 0.
+  float mrun[2], mref[2], lsum[2], zacc;
+  floatx4 acc[8];
+
+  // scores of one block: logits of heads 2hQ, 2hQ+1 for token nQ
+  auto qk = [&](const KBlock<BITS, NG>& kb, int t0, auto tail, float (&logit)[2]) {
+    constexpr bool TAIL = decltype(tail)::value;
+    half8 a_next[2] = {aqk_s[0][lane], aqk_s[1][lane]};
+    floatx16 cs;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      // keep each unpack next to its MFMA (bounds the live operand registers); the A
+      // operand is read from LDS two MFMAs ahead
+      __builtin_amdgcn_sched_barrier(0);
+      const half8 ap = a_next[p & 1];
+      if (p + 2 < 8) a_next[p & 1] = aqk_s[p + 2][lane];
+      cs = __builtin_amdgcn_mfma_f32_32x32x16_f16(ap, unpack_k<BITS>(kb.kc, p), p == 0 ? floatx16{} : cs, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+      float sa = 0.f, zb = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        // fp16 scale/zero feed the fused mixed-precision FMAs directly
+        sa = __builtin_fmaf(lo_f16(kb.km[g]), cs[4 * g + 2 * j2], sa);
+        sa = __builtin_fmaf(lo_f16(kb.km[g]), cs[4 * g + 2 * j2 + 1], sa);
+        zb = __builtin_fmaf(hi_f16(kb.km[g]), qsum[j2][g], zb);
+      }
+      logit[j2] = sa + zb;
+      if (TAIL) logit[j2] = (t0 + nQ < end) ? logit[j2] : -INFINITY;
+    }
+    // materialise the logits here: left to the compiler, the fold sinks to the logits'
+    // later use and every block's 16 score registers stay live until then
+    asm volatile("" : "+v"(logit[0]), "+v"(logit[1]));
+  };
+
+  // new running max from the lane-local maxima bm of a group of blocks; rescales the
+  // state to the new reference (unconditionally: alpha = 1 when the max is unchanged)
+  auto advance_max = [&](float bm0, float bm1, float shift) {
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) {
+      bm0 = fmaxf(bm0, __shfl_xor(bm0, m, 64));
+      bm1 = fmaxf(bm1, __shfl_xor(bm1, m, 64));
+    }
+    const float n0 = fmaxf(mrun[0], bm0), n1 = fmaxf(mrun[1], bm1);
+    const float r0 = n0 - shift, r1 = n1 - shift;
+    const float al0 = __builtin_amdgcn_exp2f(mref[0] - r0), al1 = __builtin_amdgcn_exp2f(mref[1] - r1);
+    mrun[0] = n0;
+    mrun[1] = n1;
+    mref[0] = r0;
+    mref[1] = r1;
+    lsum[0] *= al0;
+    lsum[1] *= al1;
+    // scale factors of all four heads, everywhere (heads 0,1 live in lanes 0..31)
+    const float alpha[4] = {__shfl(al0, 0, 64), __shfl(al1, 0, 64), __shfl(al0, 32, 64), __shfl(al1, 32, 64)};
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[nt][r] *= alpha[r];
+    zacc *= alpha[jjV];
+  };
+
+  // p = 2^(logit - mref) of the super-block's first n blocks: summed into l and published
+  // in LDS for the value steps (lane (hQ, nQ) holds heads 2hQ, 2hQ + 1 of token nQ; a
+  // value lane needs 8 tokens of one head)
+  auto publish_p = [&](const float (&lg)[NBS][2], int n, auto guard) {
+    constexpr bool GUARD = decltype(guard)::value;
+    // A single wavefront owns this LDS: its DS instructions complete in program order,
+    // so reads of the previous super-block's p are done before these writes land, and
+    // the exchange needs no barrier, only compiler fences.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < NBS; ++j) {
+      if (!GUARD || j < n) {
+        const float p0 = __builtin_amdgcn_exp2f(lg[j][0] - mref[0]);
+        const float p1 = __builtin_amdgcn_exp2f(lg[j][1] - mref[1]);
+        lsum[0] += p0;
+        lsum[1] += p1;
+        p_s[j][2 * hQ][nQ] = p0;
+        p_s[j][2 * hQ + 1][nQ] = p1;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // values of block j of the super-block; false if a value scale is too large for the
+  // f16 weights at this shift (nothing is accumulated then)
+  auto pv = [&](const VBlock<BITS>& vb, int j, int t0, auto tail, bool check_big) -> bool {
+    constexpr bool TAIL = decltype(tail)::value;
+    if (check_big) {
+      _Float16 smax = 0;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) smax = __builtin_fmaxf16(smax, f16_lo(vb.vm[kk]));
+      if (__any(smax >= static_cast<_Float16>(128.0f))) return false;
+    }
+    float pv[8];
+    {
+      const floatx4* src = reinterpret_cast<const floatx4*>(&p_s[j][jjV][8 * q4]);
+      const floatx4 x0 = src[0], x1 = src[1];
+      pv[0] = x0[0]; pv[1] = x0[1]; pv[2] = x0[2]; pv[3] = x0[3];
+      pv[4] = x1[0]; pv[5] = x1[1]; pv[6] = x1[2]; pv[7] = x1[3];
+    }
+    // w = p * scale (masked tokens have p = 0 exactly); w = hi + lo with hi = w's top 11
+    // significant bits (exact in f16) and lo the exact remainder, rounded toward zero to f16
+    uint32_t ahi[4], alo[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float w[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int kk = 2 * k + e;
+        w[e] = __builtin_fmaf(lo_f16(vb.vm[kk]), pv[kk], 0.f);
+        float zp = hi_f16(vb.vm[kk]);
+        if (TAIL && t0 + 8 * q4 + kk >= end) {  // slots past the end may hold anything
+          w[e] = 0.f;
+          zp = 0.f;
+        }
+        zacc = __builtin_fmaf(zp, pv[kk], zacc);
+      }
+      // hi = w rounded toward zero to f16 (w's top 11 significant bits), lo = the exact
+      // remainder w - hi, rounded toward zero to f16
+      ahi[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w[0], w[1]));
+      const float lo0 = __builtin_fmaf(lo_f16(ahi[k]), neg1, w[0]);
+      const float lo1 = __builtin_fmaf(hi_f16(ahi[k]), neg1, w[1]);
+      alo[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo0, lo1));
+    }
+    const half8 Ahi = as_half8(ahi[0], ahi[1], ahi[2], ahi[3]);
+    const half8 Alo = as_half8(alo[0], alo[1], alo[2], alo[3]);
+#pragma unroll
+    for (int nt = 0; nt < 8; nt += 2) {
+      // two N-tiles at a time: the hi and lo products of one tile are not back to back
+      __builtin_amdgcn_sched_barrier(0);
+      const half8 bv0 = unpack_v<BITS>(vb.vc, nt);
+      const half8 bv1 = unpack_v<BITS>(vb.vc, nt + 1);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, bv0, acc[nt], 0, 0, 0);
+      acc[nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ahi, bv1, acc[nt + 1], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, bv0, acc[nt], 0, 0, 0);
+      acc[nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(Alo, bv1, acc[nt + 1], 0, 0, 0);
+    }
+    return true;
+  };
+
+  // The partition in super-blocks of NBS blocks, each in two passes: the scores of all
+  // its blocks (logits stay in registers), one max update, then the values. Loads run
+  // two blocks ahead through the sequence K(0..NBS-1), V(0..NBS-1), K of the next
+  // super-block, ... into three rotating buffers per kind (static slots: the super-block
+  // body is fully unrolled). Super-blocks of NBS full blocks run without guards or
+  // masks; the rest of the partition (fewer than NBS full blocks and a partial block)
+  // forms one last, guarded and masked super-block.
+  auto super_block = [&](int base, int n, auto guard, bool check_big) -> bool {
+    constexpr bool GUARD = decltype(guard)::value;
+    float lg[NBS][2];
+    float bm0 = -INFINITY, bm1 = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NBS; ++j) {
+      if (j + PF < NBS)
+        kb[(j + PF) % (PF + 1)] = load_k(kcur);
+      else
+        vb[(j + PF - NBS) % (PF + 1)] = load_v(vcur);
+      if (!GUARD || j < n) {
+        qk(kb[j % (PF + 1)], start + 32 * (base + j), guard, lg[j]);
+        bm0 = fmaxf(bm0, lg[j][0]);
+        bm1 = fmaxf(bm1, lg[j][1]);
+      }
+    }
+    advance_max(bm0, bm1, check_big ? 8.0f : 0.0f);
+    publish_p(lg, n, guard);
+#pragma unroll
+    for (int j = 0; j < NBS; ++j) {
+      if (j + PF < NBS)
+        vb[(j + PF) % (PF + 1)] = load_v(vcur);
+      else
+        kb[(j + PF - NBS) % (PF + 1)] = load_k(kcur);
+      if (!GUARD || j < n) {
+        if (!pv(vb[j % (PF + 1)], j, start + 32 * (base + j), guard, check_big)) return false;
+      }
+    }
+    return true;
+  };
+  // p carries 2^8 (check_big) unless a value scale >= 128 shows up: the partition is
+  // then recomputed with p unscaled
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    const bool check_big = attempt == 0;
+    mrun[0] = mrun[1] = -INFINITY;
+    mref[0] = mref[1] = -INFINITY;
+    lsum[0] = lsum[1] = 0.f;
+    zacc = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (attempt > 0) {
+      kcur = cur0;
+      vcur = cur0;
+#pragma unroll
+      for (int j = 0; j < PF; ++j) kb[j] = load_k(kcur);
+    }
+    const int nsbf = nfull / NBS;
+    bool ok = true;
+    for (int sb = 0; sb < nsbf && ok; ++sb) ok = super_block(sb * NBS, NBS, std::false_type{}, check_big);
+    const int rem = nblk - nsbf * NBS;
+    if (ok && rem > 0) ok = super_block(nsbf * NBS, rem, std::true_type{}, check_big);
+    if (ok) break;
+  }
+
+  // ---- partials: o[jj][ch] = acc + Z[jj][g(ch)], m = mref, l ----
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) {
+    lsum[0] += __shfl_xor(lsum[0], m, 64);
+    lsum[1] += __shfl_xor(lsum[1], m, 64);
+  }
+  zacc += __shfl_xor(zacc, 16, 64);
+  zacc += __shfl_xor(zacc, 32, 64);  // every lane r16 now holds Z of row (jjV, gV)
+  float* part = a.partials + (static_cast<int64_t>(b) * a.num_q_heads + hk * R) * a.part_stride * 130 +
+                static_cast<int64_t>(split) * 130;
+  const int64_t head_stride = static_cast<int64_t>(a.part_stride) * 130;
+  // lane (q4, r16) owns accumulator rows 4*q4 + r = (jj = r, g = q4) at column r16; the
+  // rows of group q4 hold head jj's output for the channels of that group. Staged in LDS
+  // so the workspace is written with 8-byte stores.
+  float zrow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) zrow[r] = __shfl(zacc, 4 * (q4 < NG ? q4 : 0) + r, 64);
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const int ch = pv_channel<BITS>(nt, r16);
+    if (ch / G == q4) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) o_s[r][ch] = acc[nt][r] + zrow[r];
+    }
+  }
+  __syncthreads();
+  {
+    const int jo = lane >> 4, c8 = 8 * (lane & 15);
+    if (jo < R) {
+      float2* dst = reinterpret_cast<float2*>(part + jo * head_stride + c8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = make_float2(o_s[jo][c8 + 2 * e], o_s[jo][c8 + 2 * e + 1]);
+    }
+  }
+  if (nQ == 0) {
+#pragma unroll
+    for (int j2 = 0; j2 < 2; ++j2) {
+      const int jj = 2 * hQ + j2;
+      if (jj < R) {
+        part[jj * head_stride + 128] = mref[j2];
+        part[jj * head_stride + 129] = lsum[j2];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+}  // namespace kvq

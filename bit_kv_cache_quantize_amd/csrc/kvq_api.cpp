@@ -62,6 +62,8 @@ DecodeArgs decode_args(const kvq_cache* cache, const Geometry& g, const void* q,
   a.tok_tail = 0;
   a.part_stride = sp.num_splits;
   a.window = 0;
+  a.keep_chunks = 0;
+  a.chunk_mask = nullptr;
   a.hblock = g.hblock;
   a.rot_c = g.hblock > 0 ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(g.hblock))) : 1.0f;
   const double scale = softmax_scale > 0.f ? softmax_scale : 1.0 / std::sqrt(static_cast<double>(g.d));
@@ -230,6 +232,32 @@ kvq_status kvq_decode_attention_window(const kvq_cache* cache, const kvq_window*
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_decode_split(a, g, s) != hipSuccess) return KVQ_ERR_HIP;
   if (launch_decode_window(a, dev_window(window), g, s) != hipSuccess) return KVQ_ERR_HIP;
+  return launch_combine(a, g, s) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_decode_attention_pruned(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                                       const int32_t* block_table, int32_t max_pages_per_seq,
+                                       const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                                       int32_t num_splits, int32_t keep_chunks, int32_t* chunk_mask,
+                                       void* workspace, size_t workspace_bytes_given, float* out, void* stream,
+                                       void* split_begin, void* split_end) {
+  Geometry g;
+  kvq_status st = check_decode(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                               max_seq_len, num_splits, workspace, out, &g);
+  if (st != KVQ_OK) return st;
+  if (keep_chunks < 1 || keep_chunks > g.row_bytes / 16) return KVQ_ERR_INVALID;
+  if (chunk_mask && !aligned(chunk_mask, 4)) return KVQ_ERR_INVALID;
+  if (batch == 0) return KVQ_OK;
+  const Splits sp = splits_for(g, batch, num_q_heads, max_seq_len, num_splits);
+  if (workspace_bytes_given < workspace_bytes(g, batch, num_q_heads, sp)) return KVQ_ERR_WORKSPACE;
+  DecodeArgs a = decode_args(cache, g, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                             softmax_scale, sp, workspace, out);
+  a.keep_chunks = keep_chunks;
+  a.chunk_mask = chunk_mask;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (split_begin && hipEventRecord(static_cast<hipEvent_t>(split_begin), s) != hipSuccess) return KVQ_ERR_HIP;
+  if (launch_decode_split_pruned(a, g, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (split_end && hipEventRecord(static_cast<hipEvent_t>(split_end), s) != hipSuccess) return KVQ_ERR_HIP;
   return launch_combine(a, g, s) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

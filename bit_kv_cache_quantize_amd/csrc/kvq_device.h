@@ -107,12 +107,17 @@ struct DecodeArgs {
   // partial (slot num_splits) when `window` is set
   int part_stride;
   int window;
+  // query-channel pruning (pruned kernel only): key chunks kept per (sequence, kv head),
+  // and where the chosen masks go ([batch][Hkv], may be null)
+  int keep_chunks;
+  int32_t* chunk_mask;
   int hblock;
   float rot_c;    // float nearest 1/sqrt(hblock)
   float qscale;   // softmax scale * log2(e): logits are kept in the exp2 domain
 };
 
 hipError_t launch_decode_split(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
+hipError_t launch_decode_split_pruned(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_split_reference(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_window(const DecodeArgs& a, const DevWindow& w, const Geometry& g, hipStream_t stream);

@@ -186,6 +186,31 @@ kvq_status kvq_decode_attention_reference(const kvq_cache* cache, const void* q,
                                           void* workspace, size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * Decode attention with dynamic query-channel pruning of key reads (Dual-QK, Abstract:
+ * query-channel pruning further reduces key-cache reads). Arguments as
+ * kvq_decode_attention (same workspace size), plus:
+ *   keep_chunks : 1 .. head_dim * bits / 128 (4 at INT4, 2 at INT2). Packed key rows are
+ *                 read in 16-byte chunks of 128 / bits channels (32 at INT4, 64 at INT2).
+ *                 Per (sequence, kv head) the rotated query keeps the keep_chunks chunks
+ *                 with the largest sum of squared rotated-query channels over the kv
+ *                 head's query heads (fp32; ties keep the lower chunk); every other
+ *                 channel counts as zero in the scores, and those key chunks are not read
+ *                 (except in the first three 32-token blocks of each partition, read
+ *                 before the query is ranked). Values are not pruned.
+ *   chunk_mask  : int32 [batch][Hkv] device array or NULL; receives the kept chunks
+ *                 (bit j = chunk j) of every sequence with seq_len > 0.
+ *   split_begin, split_end : hipEvent_t recorded around the split-K kernel, or NULL.
+ * out = softmax(scale * (R q restricted to the kept channels) . khat_t) weighted sum of
+ * vhat_t. keep_chunks equal to the number of chunks gives kvq_decode_attention's result.
+ */
+kvq_status kvq_decode_attention_pruned(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                                       const int32_t* block_table, int32_t max_pages_per_seq,
+                                       const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                                       int32_t num_splits, int32_t keep_chunks, int32_t* chunk_mask,
+                                       void* workspace, size_t workspace_bytes, float* out, void* stream,
+                                       void* split_begin, void* split_end);
+
+/*
  * Dequantize n stored rows: out fp32 [n][Hkv][d] = fma(code, scale, zero) per
  * element, read from the rows at `slots` (int64 device array). which = 0 reads K
  * (in the rotated basis), 1 reads V. Bit-exact. For checks and export.

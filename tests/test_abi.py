@@ -244,3 +244,25 @@ def test_decode_window_argument_checks():
     assert _decode_window(d, w, q=FAKE + 8) == kvq.ERR_INVALID
     assert _decode_window(d, w, wsb=100) == kvq.ERR_WORKSPACE
     assert _decode_window(d, w, batch=0) == kvq.OK  # empty: no launch
+
+
+def _decode_pruned(d, **kw):
+    a = dict(q=FAKE, batch=2, hq=32, bt=FAKE, maxp=64, lens=FAKE, maxlen=1000, scale=0.0, splits=0, keep=3,
+             mask=FAKE, ws=FAKE, wsb=1 << 40, out=FAKE)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return kvq.lib().kvq_decode_attention_pruned(
+        ctypes.byref(d), v(a["q"]), a["batch"], a["hq"], v(a["bt"]), a["maxp"], v(a["lens"]), a["maxlen"],
+        a["scale"], a["splits"], a["keep"], v(a["mask"]), v(a["ws"]), a["wsb"], v(a["out"]), None, None, None)
+
+
+def test_decode_pruned_argument_checks():
+    d4, d2 = _desc(), _desc(bits=2, group_size=128)
+    assert _decode_pruned(d4, keep=0) == kvq.ERR_INVALID
+    assert _decode_pruned(d4, keep=5) == kvq.ERR_INVALID    # INT4 rows have 4 chunks
+    assert _decode_pruned(d2, keep=3) == kvq.ERR_INVALID    # INT2 rows have 2 chunks
+    assert _decode_pruned(d4, mask=FAKE + 2) == kvq.ERR_INVALID
+    assert _decode_pruned(d4, q=FAKE + 8) == kvq.ERR_INVALID
+    assert _decode_pruned(d4, wsb=100) == kvq.ERR_WORKSPACE
+    assert _decode_pruned(d4, batch=0) == kvq.OK            # empty: no launch
+    assert _decode_pruned(d2, keep=2, batch=0, mask=0) == kvq.OK
