@@ -49,6 +49,7 @@ class _Cache(ctypes.Structure):
         ("v_codes", ctypes.c_void_p),
         ("v_meta", ctypes.c_void_p),
         ("quant_mode", ctypes.c_int32),
+        ("v_grouping", ctypes.c_int32),
     ]
 
 
@@ -219,6 +220,7 @@ class Cache:
     page_size: int
     num_pages: int
     quant_mode: int = 0  # 0 = asymmetric min/max, 1 = hybrid symmetric/asymmetric
+    v_grouping: int = 0  # 0 = V groups of G channels per token, 1 = of G tokens per channel
 
     def __post_init__(self):
         desc = self._desc(None)
@@ -236,6 +238,7 @@ class Cache:
         d = _Cache(self.head_dim, self.num_kv_heads, self.bits, self.group_size, self.hadamard_block,
                    self.page_size, self.num_pages)
         d.quant_mode = self.quant_mode
+        d.v_grouping = self.v_grouping
         if planes is not None:
             d.k_codes, d.k_meta, d.v_codes, d.v_meta = [p.ctypes.data for p in planes]
         return d
@@ -308,18 +311,21 @@ class _Window(ctypes.Structure):
         ("batch", ctypes.c_int32),
         ("k", ctypes.c_void_p),
         ("v", ctypes.c_void_p),
+        ("residual", ctypes.c_int32),
     ]
 
 
 @dataclass
 class Window:
-    """bf16 high-precision windows (first `sink`, last `recent` tokens per sequence)."""
+    """bf16 high-precision windows (first `sink`, last `recent` tokens per sequence), or
+    with residual=1 the bf16 residual of the incomplete last group of `recent` tokens."""
 
     head_dim: int
     num_kv_heads: int
     sink: int
     recent: int
     batch: int
+    residual: int = 0
 
     def __post_init__(self):
         shape = (self.batch, self.sink + self.recent, self.num_kv_heads, self.head_dim)
@@ -329,7 +335,7 @@ class Window:
     @property
     def desc(self) -> _Window:
         return _Window(self.head_dim, self.num_kv_heads, self.sink, self.recent, self.batch, self.k.ctypes.data,
-                       self.v.ctypes.data)
+                       self.v.ctypes.data, self.residual)
 
     def slot(self, t: int) -> int:
         return load().orc_window_slot(ctypes.byref(self.desc), t)

@@ -303,6 +303,8 @@ int orc_check_cache(const orc_cache* c) {
   if (c->page_size <= 0 || c->page_size % 16) return 5;
   if ((c->head_dim * c->bits) % 128) return 6; /* whole 16-byte chunks per row */
   if (c->quant_mode != 0 && c->quant_mode != 1) return 7;
+  if (c->v_grouping != 0 && c->v_grouping != 1) return 8;
+  if (c->v_grouping == 1 && (c->head_dim != 128 || c->group_size % 32 || c->page_size % c->group_size)) return 8;
   return 0;
 }
 
@@ -337,6 +339,27 @@ static int64_t v_meta_off(const orc_cache* c, int64_t page, int h, int off, int 
   return (t * n_groups(c) * 16 + (((int64_t)part * n_groups(c) + g) * 2 + half) * 4 + i) * 4;
 }
 
+/* V token groups (v_grouping 1): {scale, zero} per (group of G tokens of a page, channel),
+   128 entries per group; channel c sits at entry 8n + t with
+   c = 4(n + 16(t >> 2)) + 2(t & 1) + ((t >> 1) & 1) at INT4 and c = 8n + (t >> 1) + 4(t & 1)
+   at INT2 (n = 0..15, t = 0..7), so that the 8 channels one decode lane needs are
+   adjacent. */
+static int vt_entry(int bits, int ch) {
+  int n, t;
+  if (bits == 4) {
+    n = (ch / 4) % 16;
+    t = 4 * (ch / 64) + 2 * (ch % 2) + (ch % 4) / 2;
+  } else {
+    n = ch / 8;
+    t = 2 * (ch % 4) + (ch % 8) / 4;
+  }
+  return 8 * n + t;
+}
+static int64_t vt_meta_off(const orc_cache* c, int64_t page, int h, int gi, int ch) {
+  int64_t groups = c->page_size / c->group_size;
+  return (((page * c->num_kv_heads + h) * groups + gi) * 128 + vt_entry(c->bits, ch)) * 4;
+}
+
 static void put_u16(uint8_t* p, uint16_t v) {
   p[0] = (uint8_t)(v & 0xFF);
   p[1] = (uint8_t)(v >> 8);
@@ -355,6 +378,7 @@ static void store_row(const orc_cache* c, int which, int64_t page, int h, int of
     }
   } else {
     for (int k = 0; k < rb; ++k) c->v_codes[v_byte_off(c, page, h, off, k)] = packed[k];
+    if (c->v_grouping == 1) return; /* token groups store their {scale, zero} per group */
     for (int g = 0; g < n_groups(c); ++g) {
       uint8_t* m = c->v_meta + v_meta_off(c, page, h, off, g);
       put_u16(m, scale[g]);
@@ -375,6 +399,14 @@ static void load_row(const orc_cache* c, int which, int64_t page, int h, int off
     }
   } else {
     for (int k = 0; k < rb; ++k) packed[k] = c->v_codes[v_byte_off(c, page, h, off, k)];
+    if (c->v_grouping == 1) { /* per channel: scale[i], zero[i] for channel i */
+      for (int i = 0; i < c->head_dim; ++i) {
+        const uint8_t* m = c->v_meta + vt_meta_off(c, page, h, off / c->group_size, i);
+        scale[i] = get_u16(m);
+        zero[i] = get_u16(m + 2);
+      }
+      return;
+    }
     for (int g = 0; g < n_groups(c); ++g) {
       const uint8_t* m = c->v_meta + v_meta_off(c, page, h, off, g);
       scale[g] = get_u16(m);
@@ -392,31 +424,28 @@ static void dequant_row(const orc_cache* c, int which, int64_t page, int h, int 
   uint16_t sc[4096], ze[4096];
   load_row(c, which, page, h, off, packed, sc, ze);
   orc_unpack_row(packed, d, c->bits, codes);
+  int per_channel = which == 1 && c->v_grouping == 1;
   for (int i = 0; i < d; ++i) {
-    float s = orc_f16_to_f32(sc[i / G]);
-    float z = orc_f16_to_f32(ze[i / G]);
+    float s = orc_f16_to_f32(sc[per_channel ? i : i / G]);
+    float z = orc_f16_to_f32(ze[per_channel ? i : i / G]);
     out[i] = fmaf((float)codes[i], s, z);
   }
 }
 
-/* Quantize the bf16 K and V rows of kv head h and store them at `slot` (K rotated). */
-static void quantize_store_pair(const orc_cache* c, const uint16_t* krow, const uint16_t* vrow, int64_t slot, int h) {
+/* Quantize one bf16 row of kv head h (K rotated first, or V with channel groups) and
+   store it at `slot`. */
+static void quantize_store_row_one(const orc_cache* c, int which, const uint16_t* row, int64_t slot, int h) {
   int d = c->head_dim;
   float* x = (float*)malloc(sizeof(float) * (size_t)d);
   uint8_t* codes = (uint8_t*)malloc((size_t)d);
   uint8_t* packed = (uint8_t*)malloc((size_t)d);
   uint16_t* sc = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)d);
   uint16_t* ze = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)d);
-  int64_t page = slot / c->page_size;
-  int off = (int)(slot % c->page_size);
-  for (int which = 0; which < 2; ++which) {
-    const uint16_t* src = which == 0 ? krow : vrow;
-    for (int i = 0; i < d; ++i) x[i] = orc_bf16_to_f32(src[i]);
-    if (which == 0) orc_rotate(x, d, c->hadamard_block); /* keys only */
-    quantize_row_mode(x, d, c->bits, c->group_size, c->quant_mode == 1, codes, sc, ze);
-    orc_pack_row(codes, d, c->bits, packed);
-    store_row(c, which, page, h, off, packed, sc, ze);
-  }
+  for (int i = 0; i < d; ++i) x[i] = orc_bf16_to_f32(row[i]);
+  if (which == 0) orc_rotate(x, d, c->hadamard_block); /* keys only */
+  quantize_row_mode(x, d, c->bits, c->group_size, c->quant_mode == 1, codes, sc, ze);
+  orc_pack_row(codes, d, c->bits, packed);
+  store_row(c, which, slot / c->page_size, h, (int)(slot % c->page_size), packed, sc, ze);
   free(x);
   free(codes);
   free(packed);
@@ -424,9 +453,69 @@ static void quantize_store_pair(const orc_cache* c, const uint16_t* krow, const 
   free(ze);
 }
 
+/* V token groups (InnerQ, Abstract: groups along the inner dimension of the value
+   product). Reading: channel ch of the G tokens slot0 .. slot0 + G - 1 (one page,
+   slot0 a multiple of G) forms one group, quantized by the same formula as a row group
+   (min/max, or hybrid); rows[i] is the bf16 V row of token slot0 + i. */
+static void quantize_store_v_group(const orc_cache* c, const uint16_t* const* rows, int64_t slot0, int h) {
+  int d = c->head_dim, G = c->group_size;
+  int64_t page = slot0 / c->page_size;
+  int off0 = (int)(slot0 % c->page_size);
+  float* col = (float*)malloc(sizeof(float) * (size_t)G);
+  uint8_t* ccodes = (uint8_t*)malloc((size_t)G);
+  uint8_t* codes = (uint8_t*)malloc((size_t)G * (size_t)d); /* [token][channel] */
+  uint8_t* packed = (uint8_t*)malloc((size_t)d);
+  for (int ch = 0; ch < d; ++ch) {
+    uint16_t sc, ze;
+    for (int i = 0; i < G; ++i) col[i] = orc_bf16_to_f32(rows[i][ch]);
+    quantize_row_mode(col, G, c->bits, G, c->quant_mode == 1, ccodes, &sc, &ze);
+    uint8_t* m = c->v_meta + vt_meta_off(c, page, h, off0 / G, ch);
+    put_u16(m, sc);
+    put_u16(m + 2, ze);
+    for (int i = 0; i < G; ++i) codes[(size_t)i * d + ch] = ccodes[i];
+  }
+  for (int i = 0; i < G; ++i) {
+    orc_pack_row(codes + (size_t)i * d, d, c->bits, packed);
+    for (int k = 0; k < row_bytes(c); ++k) c->v_codes[v_byte_off(c, page, h, off0 + i, k)] = packed[k];
+  }
+  free(col);
+  free(ccodes);
+  free(codes);
+  free(packed);
+}
+
+/* Quantize the bf16 K and V rows of kv head h and store them at `slot` (channel groups). */
+static void quantize_store_pair(const orc_cache* c, const uint16_t* krow, const uint16_t* vrow, int64_t slot, int h) {
+  quantize_store_row_one(c, 0, krow, slot, h);
+  quantize_store_row_one(c, 1, vrow, slot, h);
+}
+
+/* G tokens whose V rows form token groups: keys row by row at slots[i], values as one
+   group per kv head at slots[0] .. slots[0] + G - 1. k, v: bf16 [G][Hkv][d]. */
+static void quantize_store_token_group(const orc_cache* c, const uint16_t* k, const uint16_t* v, const int64_t* slots,
+                                       int64_t krow_stride, int64_t vrow_stride) {
+  int d = c->head_dim, H = c->num_kv_heads, G = c->group_size;
+  const uint16_t** rows = (const uint16_t**)malloc(sizeof(uint16_t*) * (size_t)G);
+  for (int h = 0; h < H; ++h) {
+    for (int i = 0; i < G; ++i) {
+      quantize_store_row_one(c, 0, k + i * krow_stride + (int64_t)h * d, slots[i], h);
+      rows[i] = v + i * vrow_stride + (int64_t)h * d;
+    }
+    quantize_store_v_group(c, rows, slots[0], h);
+  }
+  free(rows);
+}
+
 void orc_quantize_append(const orc_cache* c, const uint16_t* k_new, const uint16_t* v_new,
                          const int64_t* slots, int64_t n) {
   int d = c->head_dim;
+  if (c->v_grouping == 1) { /* whole token groups of G consecutive rows */
+    int G = c->group_size;
+    int64_t stride = (int64_t)c->num_kv_heads * d;
+    for (int64_t r = 0; r + G <= n; r += G)
+      quantize_store_token_group(c, k_new + r * stride, v_new + r * stride, slots + r, stride, stride);
+    return;
+  }
   for (int64_t r = 0; r < n; ++r)
     for (int h = 0; h < c->num_kv_heads; ++h)
       quantize_store_pair(c, k_new + (r * c->num_kv_heads + h) * d, v_new + (r * c->num_kv_heads + h) * d, slots[r],
@@ -551,6 +640,12 @@ void orc_prune_energy(const orc_cache* c, const uint16_t* q, int32_t batch, int3
 
 int orc_window_slot(const orc_window* w, int t) { return t < w->sink ? t : w->sink + (t - w->sink) % w->recent; }
 
+/* is token t of a sequence of T tokens a window token? */
+static int in_window(const orc_window* w, int t, int T) {
+  if (w->residual) return t >= T - T % w->recent; /* the incomplete last group */
+  return t < w->sink || t >= T - w->recent;
+}
+
 void orc_window_append(const orc_cache* c, const orc_window* w, const uint16_t* k_new, const uint16_t* v_new,
                        const int32_t* seqs, const int32_t* positions, const int64_t* evict_slots, int64_t n) {
   int d = w->head_dim, H = w->num_kv_heads, S = w->sink, R = w->recent;
@@ -561,9 +656,25 @@ void orc_window_append(const orc_cache* c, const orc_window* w, const uint16_t* 
       uint16_t* kw = w->k + (((int64_t)b * (S + R) + ws) * H + h) * d;
       uint16_t* vw = w->v + (((int64_t)b * (S + R) + ws) * H + h) * d;
       /* the recent ring is full: its slot holds token t - R, which now leaves the window */
-      if (t >= S && t - R >= S) quantize_store_pair(c, kw, vw, evict_slots[r], h);
+      if (!w->residual && t >= S && t - R >= S) quantize_store_pair(c, kw, vw, evict_slots[r], h);
       memcpy(kw, k_new + (r * H + h) * d, sizeof(uint16_t) * (size_t)d);
       memcpy(vw, v_new + (r * H + h) * d, sizeof(uint16_t) * (size_t)d);
+    }
+    /* residual: token t completes the group t - R + 1 .. t (ring rows 0 .. R-1), which is
+       quantized into the cache at evict_slots[r] .. evict_slots[r] + R - 1 */
+    if (w->residual && (t + 1) % R == 0) {
+      const uint16_t* kg = w->k + (int64_t)b * R * H * d;
+      const uint16_t* vg = w->v + (int64_t)b * R * H * d;
+      int64_t* gs = (int64_t*)malloc(sizeof(int64_t) * (size_t)R);
+      for (int i = 0; i < R; ++i) gs[i] = evict_slots[r] + i;
+      if (c->v_grouping == 1) {
+        quantize_store_token_group(c, kg, vg, gs, (int64_t)H * d, (int64_t)H * d);
+      } else {
+        for (int i = 0; i < R; ++i)
+          for (int h = 0; h < H; ++h)
+            quantize_store_pair(c, kg + ((int64_t)i * H + h) * d, vg + ((int64_t)i * H + h) * d, gs[i], h);
+      }
+      free(gs);
     }
   }
 }
@@ -593,7 +704,7 @@ void orc_decode_attention_window(const orc_cache* c, const orc_window* w, const 
       double m = -INFINITY;
       for (int t = 0; t < T; ++t) {
         double dot = 0.0;
-        if (t < S || t >= T - R) { /* window token: original bf16 key, original query */
+        if (in_window(w, t, T)) { /* window token: original bf16 key, original query */
           const uint16_t* kw = w->k + (((int64_t)b * (S + R) + orc_window_slot(w, t)) * H + h) * d;
           for (int i = 0; i < d; ++i) dot += qv[i] * (double)orc_bf16_to_f32(kw[i]);
         } else {
@@ -609,7 +720,7 @@ void orc_decode_attention_window(const orc_cache* c, const orc_window* w, const 
       for (int t = 0; t < T; ++t) {
         double wt = exp(logit[t] - m);
         den += wt;
-        if (t < S || t >= T - R) {
+        if (in_window(w, t, T)) {
           const uint16_t* vw = w->v + (((int64_t)b * (S + R) + orc_window_slot(w, t)) * H + h) * d;
           for (int i = 0; i < d; ++i) acc[i] += wt * (double)orc_bf16_to_f32(vw[i]);
         } else {

@@ -53,6 +53,10 @@
  *   V meta        [u][P/16][2][NG][2][4] x {u16 scale, u16 zero}: token
  *                                             o = 8*half + 4*part + i of group g at
  *                                             entry ((part*NG + g)*2 + half)*4 + i.
+ *   V meta, token groups (v_grouping 1, head_dim 128, P a multiple of G):
+ *                 [u][P/G][128] x {u16 scale, u16 zero}: channel c of token group j of
+ *                 the page at entry 8n + t, c = 4(n + 16(t>>2)) + 2(t&1) + ((t>>1)&1)
+ *                 (INT4) or 8n + (t>>1) + 4(t&1) (INT2).
  */
 #ifndef KVQ_ORACLE_H
 #define KVQ_ORACLE_H
@@ -104,6 +108,7 @@ typedef struct {
   uint8_t* v_codes;
   uint8_t* v_meta;
   int32_t quant_mode; /* 0 = asymmetric min/max, 1 = hybrid symmetric/asymmetric */
+  int32_t v_grouping; /* 0 = V groups of G channels of a token; 1 = of G tokens of a channel */
 } orc_cache;
 
 /* bytes of each plane: 0 = K codes, 1 = K meta, 2 = V codes, 3 = V meta */
@@ -111,7 +116,9 @@ int64_t orc_plane_bytes(const orc_cache* c, int plane);
 /* returns 0 on success, nonzero when the description is outside the oracle's domain */
 int orc_check_cache(const orc_cache* c);
 
-/* k_new, v_new: bf16 [n][Hkv][d]; slots[r] = page*P + offset */
+/* k_new, v_new: bf16 [n][Hkv][d]; slots[r] = page*P + offset. With v_grouping 1, rows come
+   in whole groups of G consecutive tokens (slots[r..r+G-1] = slots[r] + 0..G-1, slots[r] a
+   multiple of G): keys per token, values per (group, channel). */
 void orc_quantize_append(const orc_cache* c, const uint16_t* k_new, const uint16_t* v_new,
                          const int64_t* slots, int64_t n);
 /* which: 0 = K, 1 = V; out: float [n][Hkv][d] */
@@ -142,6 +149,9 @@ typedef struct {
   int32_t batch;
   uint16_t* k; /* bf16 [batch][sink + recent][Hkv][d] */
   uint16_t* v;
+  int32_t residual; /* 1: sink 0, a ring of `recent` rows holding the incomplete last group
+                       of `recent` tokens (T mod recent of them); a group is quantized when
+                       its last token arrives */
 } orc_window;
 
 int orc_window_slot(const orc_window* w, int t);

@@ -668,6 +668,186 @@ def check_prune_energy():
         assert np.allclose(e, want, rtol=1e-12, atol=0), bits
 
 
+# ----------------------------------------------------------------------------- V token groups
+
+def _vt_entry(bits, ch):
+    """Entry of channel ch in a token group's {scale, zero} list: the documented formula
+    c = 4(n + 16(t>>2)) + 2(t&1) + ((t>>1)&1) (INT4) / 8n + (t>>1) + 4(t&1) (INT2) at 8n + t,
+    evaluated forward over all (n, t) and inverted here."""
+    table = {}
+    for n in range(16):
+        for t in range(8):
+            c = 4 * (n + 16 * (t >> 2)) + 2 * (t & 1) + ((t >> 1) & 1) if bits == 4 else 8 * n + (t >> 1) + 4 * (t & 1)
+            table[c] = 8 * n + t
+    return table[ch]
+
+
+def check_vt_entry_is_a_permutation():
+    for bits in (2, 4):
+        assert sorted(_vt_entry(bits, c) for c in range(128)) == list(range(128))
+
+
+def _vt_cache(P, pages, bits=4, G=32, hb=128, mode=0):
+    return oracle.Cache(128, 2, bits, G, hb, P, pages, quant_mode=mode, v_grouping=1)
+
+
+def check_vt_worked_example_and_layout():
+    """V channel 37 of kv head 1 holds the ramp 0..31 across the 32 tokens of a group (the
+    golden ramp: scale 0x4022, zero 0, codes 0,0,1,1,..,15,15), every other channel a
+    constant; read back at the documented byte offsets (V codes: 16-token tiles of 16-bit
+    words, token pairs interleaved; V meta: [u][P/G][128] entries)."""
+    golden = {n: (x, c, sb, zb) for n, _, _, x, c, sb, zb in _golden_cases()}
+    x, codes, sb, zb = golden["ramp_0_to_31_int4_g32"]
+    P, pages, H, d = 64, 3, 2, 128
+    c = _vt_cache(P, pages)
+    v = np.full((32, H, d), 1.25, np.float32)
+    v[:, 1, 37] = x
+    k = np.zeros((32, H, d), np.float32)
+    page, gi = 2, 1                              # token group 1 of page 2: slots 160..191
+    slots = np.arange(32, dtype=np.int64) + page * P + gi * 32
+    c.append(_bf16(k), _bf16(v), slots)
+    u = page * H + 1
+    meta = c.v_meta.view(np.uint16).reshape(-1, 2)
+    e = (u * (P // 32) + gi) * 128 + _vt_entry(4, 37)
+    assert meta[e, 0] == sb and meta[e, 1] == zb, (hex(meta[e, 0]), hex(meta[e, 1]))
+    e1 = (u * (P // 32) + gi) * 128 + _vt_entry(4, 36)   # a constant channel: scale 0, zero 1.25
+    assert meta[e1, 0] == 0 and meta[e1, 1] == np.float16(1.25).view(np.uint16)
+    for i in range(32):
+        off = gi * 32 + i
+        tile = (u * P + off - off % 16) * 64
+        o = off % 16
+        byte = c.v_codes[tile + (37 // 2 // 2) * 32 + (o // 2) * 4 + ((37 // 2) % 2) * 2 + o % 2]
+        assert (byte >> 4) & 15 == codes[i], (i, byte, codes[i])   # channel 37: high nibble of byte 18
+
+
+def check_vt_groups_run_along_tokens():
+    """A V that is constant along tokens but varies across channels is reproduced exactly
+    (every token group of a channel is constant: scale 0, zero = the value), which
+    channel groups would not do."""
+    rng = np.random.default_rng(71)
+    P = 32
+    c = _vt_cache(P, 2, bits=2, G=32)
+    ch_vals = _bf16(rng.standard_normal((2, 128)))
+    v = np.broadcast_to(ch_vals, (64, 2, 128)).copy()
+    k = _bf16(rng.standard_normal((64, 2, 128)))
+    slots = np.arange(64, dtype=np.int64)
+    c.append(k, v, slots)
+    got = c.dequantize(1, slots)
+    want = np.broadcast_to(oracle.bf16_to_f32(ch_vals), got.shape)
+    assert np.array_equal(got, want)
+    cc = oracle.Cache(128, 2, 2, 32, 128, P, 2)
+    cc.append(k, v, slots)
+    assert not np.array_equal(cc.dequantize(1, slots), want)
+
+
+def check_vt_round_trip_per_channel():
+    """Per token group and channel: the group's min maps within one level of code 0, and
+    every element is within half a step (plus the zero's rounding and ulps) of its value."""
+    rng = np.random.default_rng(72)
+    for bits, G in ((4, 32), (2, 64), (4, 128)):
+        P = 128
+        c = _vt_cache(P, 2, bits=bits, G=G)
+        v = _bf16(rng.standard_normal((128, 2, 128)) * np.exp(rng.standard_normal((1, 2, 128))))
+        k = _bf16(rng.standard_normal((128, 2, 128)))
+        slots = np.arange(128, dtype=np.int64) + P
+        c.append(k, v, slots)
+        got = c.dequantize(1, slots).astype(np.float64)
+        x = oracle.bf16_to_f32(v).astype(np.float64)
+        meta = c.v_meta.view(np.uint16).reshape(-1, 2)
+        for h in range(2):
+            for gi in range(128 // G):
+                for ch in range(128):
+                    e = ((1 * 2 + h) * (P // G) + gi) * 128 + _vt_entry(bits, ch)
+                    sc = float(np.uint16(meta[e, 0]).view(np.float16))
+                    ze = float(np.uint16(meta[e, 1]).view(np.float16))
+                    xs = x[gi * G:(gi + 1) * G, h, ch]
+                    err = np.abs(got[gi * G:(gi + 1) * G, h, ch] - xs)
+                    assert err.max() <= sc / 2 + abs(xs.min() - ze) + 4 * np.spacing(np.abs(xs).max()), \
+                        (bits, G, h, gi, ch)
+
+
+def check_vt_attention_matches_sdpa():
+    rng = np.random.default_rng(73)
+    for bits, G, hb, mode in ((4, 32, 128, 0), (2, 64, 0, 1), (4, 128, 64, 0)):
+        B, Hq, Hkv, d, P = 2, 8, 2, 128, 128
+        T = 256
+        pages_per = T // P
+        perm = rng.permutation(B * pages_per)
+        bt = perm.reshape(B, pages_per).astype(np.int32)
+        c = oracle.Cache(d, Hkv, bits, G, hb, P, B * pages_per, quant_mode=mode, v_grouping=1)
+        k = _bf16(rng.standard_normal((B, T, Hkv, d)))
+        v = _bf16(rng.standard_normal((B, T, Hkv, d)))
+        for b in range(B):
+            t = np.arange(T)
+            c.append(k[b], v[b], bt[b][t // P].astype(np.int64) * P + t % P)
+        q = _bf16(rng.standard_normal((B, Hq, d)))
+        lens = np.array([T, 3 * G if 3 * G <= T else G], np.int32)
+        out = c.decode(q, bt, lens, 0.0)
+        Rm = np.kron(np.eye(d // hb), scipy.linalg.hadamard(hb) / np.sqrt(hb)) if hb else np.eye(d)
+        for b in range(B):
+            t = np.arange(lens[b])
+            slots = bt[b][t // P].astype(np.int64) * P + t % P
+            kh = torch.from_numpy(c.dequantize(0, slots).astype(np.float64))
+            vh = torch.from_numpy(c.dequantize(1, slots).astype(np.float64))
+            qf = oracle.bf16_to_f32(q[b]).astype(np.float64) @ Rm.T
+            qt = torch.from_numpy(qf).reshape(Hkv, Hq // Hkv, 1, d)
+            kt = kh.permute(1, 0, 2).reshape(Hkv, 1, -1, d).contiguous()
+            vt = vh.permute(1, 0, 2).reshape(Hkv, 1, -1, d).contiguous()
+            ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).reshape(Hq, d).numpy()
+            assert np.max(np.abs(out[b] - ref)) < 1e-12, (bits, G, hb, b)
+
+
+def check_residual_stream():
+    """Tokens streamed through a residual of G rows: every completed group is in the cache
+    exactly as a direct append of it writes it (token groups or channel groups), the
+    residual holds the incomplete last group at rows t % G, and a decode equals a softmax
+    written out over dequantized cache tokens (rotated query) and raw residual rows
+    (original query)."""
+    rng = np.random.default_rng(74)
+    for vg, T in ((1, 100), (0, 77), (1, 64)):
+        B, H, d, G, P = 2, 2, 128, 32, 64
+        cap = (T + P - 1) // P * P
+        c = oracle.Cache(d, H, 4, G, 128, cap, B, v_grouping=vg)
+        w = oracle.Window(d, H, 0, G, B, residual=1)
+        k = _bf16(rng.standard_normal((B, T, H, d)) * np.exp(rng.standard_normal((1, 1, H, d))))
+        v = _bf16(rng.standard_normal((B, T, H, d)))
+        for t in range(T):
+            first = t - G + 1
+            ev = np.array([b * cap + max(first, 0) for b in range(B)], np.int64)
+            w.append(c, k[:, t], v[:, t], np.arange(B), np.full(B, t), ev)
+        done = T - T % G
+        ref = oracle.Cache(d, H, 4, G, 128, cap, B, v_grouping=vg)
+        for b in range(B):
+            if done:
+                ref.append(k[b, :done], v[b, :done], b * cap + np.arange(done, dtype=np.int64))
+        for g_, r_ in zip(c.planes(), ref.planes()):
+            assert np.array_equal(g_, r_), (vg, T)
+        for b in range(B):
+            for t in range(done, T):
+                assert np.array_equal(w.k[b, t % G], k[b, t]) and np.array_equal(w.v[b, t % G], v[b, t])
+        q = _bf16(rng.standard_normal((B, 8, d)))
+        bt = np.arange(B, dtype=np.int32).reshape(B, 1)
+        out = w.decode(c, q, bt, np.array([T, T], np.int32))
+        Rm = scipy.linalg.hadamard(d) / np.sqrt(d)
+        for b in range(B):
+            qf = oracle.bf16_to_f32(q[b]).astype(np.float64)
+            logits = np.empty((8, T))
+            vals = np.empty((T, H, d))
+            for t in range(T):
+                if t >= done:
+                    kt = oracle.bf16_to_f32(k[b, t]).astype(np.float64)
+                    vals[t] = oracle.bf16_to_f32(v[b, t]).astype(np.float64)
+                    logits[:, t] = np.einsum("jd,jd->j", qf, np.repeat(kt, 4, axis=0))
+                else:
+                    kt = c.dequantize(0, np.array([b * cap + t]))[0].astype(np.float64)
+                    vals[t] = c.dequantize(1, np.array([b * cap + t]))[0].astype(np.float64)
+                    logits[:, t] = np.einsum("jd,jd->j", qf @ Rm.T, np.repeat(kt, 4, axis=0))
+            logits /= np.sqrt(d)
+            p = np.exp(logits - logits.max(1, keepdims=True))
+            want = np.einsum("jt,jtd->jd", p, np.repeat(vals, 4, axis=1).transpose(1, 0, 2)) / p.sum(1, keepdims=True)
+            assert np.max(np.abs(out[b] - want)) < 1e-12, (vg, T, b)
+
+
 ALL_CHECKS = [
     check_hadamard_is_sylvester,
     check_hadamard_orthogonal,
@@ -699,4 +879,10 @@ ALL_CHECKS = [
     check_pruned_all_kept_equals_plain,
     check_pruned_matches_restricted_sdpa,
     check_prune_energy,
+    check_vt_entry_is_a_permutation,
+    check_vt_worked_example_and_layout,
+    check_vt_groups_run_along_tokens,
+    check_vt_round_trip_per_channel,
+    check_vt_attention_matches_sdpa,
+    check_residual_stream,
 ]

@@ -47,12 +47,11 @@ MUTANTS = [
      "return base + tile + (int64_t)o * row_bytes(c) + k;"),
     ("v_meta_parts_swapped", "(((int64_t)part * n_groups(c) + g) * 2 + half) * 4 + i) * 4;",
      "(((int64_t)half * n_groups(c) + g) * 2 + part) * 4 + i) * 4;"),
-    ("window_evict_late", "if (t >= S && t - R >= S) quantize_store_pair(c, kw, vw, evict_slots[r], h);",
-     "if (t >= S && t - R > S) quantize_store_pair(c, kw, vw, evict_slots[r], h);"),
+    ("window_evict_late", "if (!w->residual && t >= S && t - R >= S) quantize_store_pair(c, kw, vw, evict_slots[r], h);",
+     "if (!w->residual && t >= S && t - R > S) quantize_store_pair(c, kw, vw, evict_slots[r], h);"),
     ("window_ring_index", "return t < w->sink ? t : w->sink + (t - w->sink) % w->recent;",
      "return t < w->sink ? t : w->sink + (t - w->sink + 1) % w->recent;"),
-    ("window_recent_edge", "if (t < S || t >= T - R) { /* window token: original bf16 key, original query */",
-     "if (t < S || t > T - R) { /* window token: original bf16 key, original query */"),
+    ("window_recent_edge", "return t < w->sink || t >= T - w->recent;", "return t < w->sink || t > T - w->recent;"),
     ("window_query_rotated", "for (int i = 0; i < d; ++i) dot += qv[i] * (double)orc_bf16_to_f32(kw[i]);",
      "for (int i = 0; i < d; ++i) dot += qr[i] * (double)orc_bf16_to_f32(kw[i]);"),
     ("meta_swapped", "      put_u16(m, scale[g]);\n      put_u16(m + 2, zero[g]);\n    }\n  } else {",
@@ -69,6 +68,12 @@ MUTANTS = [
     ("prune_bit_order", "if (!((mask >> (i / width)) & 1)) qr[i] = 0.0;", "if (!((mask >> (d / width - 1 - i / width)) & 1)) qr[i] = 0.0;"),
     ("prune_mask_ignored", "if (!((mask >> (i / width)) & 1)) qr[i] = 0.0;", "(void)mask;"),
     ("prune_energy_abs", "+= qr[i] * qr[i];", "+= fabs(qr[i]);"),
+    ("vt_entry_bits_swapped", "t = 4 * (ch / 64) + 2 * (ch % 2) + (ch % 4) / 2;", "t = 4 * (ch / 64) + (ch % 2) + 2 * ((ch % 4) / 2);"),
+    ("vt_groups_along_channels", "      quantize_store_token_group(c, k_new + r * stride, v_new + r * stride, slots + r, stride, stride);",
+     "      for (int i = 0; i < G; ++i) for (int h = 0; h < c->num_kv_heads; ++h) quantize_store_pair(c, k_new + (r + i) * stride + h * d, v_new + (r + i) * stride + h * d, slots[r + i], h);"),
+    ("vt_meta_wrong_group", "c->v_meta + vt_meta_off(c, page, h, off / c->group_size, i);", "c->v_meta + vt_meta_off(c, page, h, 0, i);"),
+    ("residual_whole_ring", "if (w->residual) return t >= T - T % w->recent;", "if (w->residual) return t >= T - w->recent;"),
+    ("residual_group_early", "if (w->residual && (t + 1) % R == 0) {", "if (w->residual && t % R == 0) {"),
 ]
 
 RUNNER = r"""
