@@ -41,6 +41,7 @@ class _Desc(ctypes.Structure):
         ("v_codes", ctypes.c_void_p),
         ("v_meta", ctypes.c_void_p),
         ("quant_mode", ctypes.c_int32),
+        ("v_grouping", ctypes.c_int32),
     ]
 
 
@@ -51,6 +52,7 @@ class _Window(ctypes.Structure):
         ("batch", ctypes.c_int32),
         ("k", ctypes.c_void_p),
         ("v", ctypes.c_void_p),
+        ("residual", ctypes.c_int32),
     ]
 
 
@@ -156,6 +158,7 @@ class KVCache:
     v_codes: torch.Tensor
     v_meta: torch.Tensor
     quant_mode: int = 0  # 0 = asymmetric min/max groups, 1 = hybrid symmetric/asymmetric
+    v_grouping: int = 0  # 0 = value groups of G channels per token, 1 = of G tokens per channel
 
     @staticmethod
     def plane_bytes(head_dim, num_kv_heads, bits, group_size, hadamard_block, page_size, num_pages) -> list[int]:
@@ -167,22 +170,23 @@ class KVCache:
 
     @classmethod
     def allocate(cls, head_dim: int, num_kv_heads: int, bits: int, group_size: int, hadamard_block: int,
-                 page_size: int, num_pages: int, device="cuda", quant_mode: int = 0) -> "KVCache":
+                 page_size: int, num_pages: int, device="cuda", quant_mode: int = 0,
+                 v_grouping: int = 0) -> "KVCache":
         sizes = cls.plane_bytes(head_dim, num_kv_heads, bits, group_size, hadamard_block, page_size, num_pages)
         planes = [torch.zeros(n, dtype=torch.uint8, device=device) for n in sizes]
         return cls(head_dim, num_kv_heads, bits, group_size, hadamard_block, page_size, num_pages, *planes,
-                   quant_mode=quant_mode)
+                   quant_mode=quant_mode, v_grouping=v_grouping)
 
     def clone(self) -> "KVCache":
         return KVCache(self.head_dim, self.num_kv_heads, self.bits, self.group_size, self.hadamard_block,
                        self.page_size, self.num_pages, *[p.clone() for p in self.planes()],
-                       quant_mode=self.quant_mode)
+                       quant_mode=self.quant_mode, v_grouping=self.v_grouping)
 
     @property
     def desc(self) -> _Desc:
         return _Desc(self.head_dim, self.num_kv_heads, self.bits, self.group_size, self.hadamard_block,
                      self.page_size, self.num_pages, self.k_codes.data_ptr(), self.k_meta.data_ptr(),
-                     self.v_codes.data_ptr(), self.v_meta.data_ptr(), self.quant_mode)
+                     self.v_codes.data_ptr(), self.v_meta.data_ptr(), self.quant_mode, self.v_grouping)
 
     def planes(self):
         return self.k_codes, self.k_meta, self.v_codes, self.v_meta
@@ -303,10 +307,12 @@ class KVWindow:
     batch: int
     k: torch.Tensor
     v: torch.Tensor
+    residual: int = 0  # 1: sink 0, the ring holds the incomplete last group of `recent` tokens
 
     @classmethod
-    def allocate(cls, cache: KVCache, sink: int, recent: int, batch: int, device="cuda") -> "KVWindow":
-        w = _Window(sink, recent, batch)
+    def allocate(cls, cache: KVCache, sink: int, recent: int, batch: int, device="cuda",
+                 residual: int = 0) -> "KVWindow":
+        w = _Window(sink, recent, batch, None, None, residual)
         n = lib().kvq_window_plane_bytes(ctypes.byref(cache.desc), ctypes.byref(w))
         if n < 0:
             raise KVQError(ERR_INVALID, "window description")
@@ -314,11 +320,11 @@ class KVWindow:
         k = torch.zeros(shape, dtype=torch.bfloat16, device=device)
         v = torch.zeros(shape, dtype=torch.bfloat16, device=device)
         assert k.numel() * 2 == n
-        return cls(sink, recent, batch, k, v)
+        return cls(sink, recent, batch, k, v, residual)
 
     @property
     def desc(self) -> _Window:
-        return _Window(self.sink, self.recent, self.batch, self.k.data_ptr(), self.v.data_ptr())
+        return _Window(self.sink, self.recent, self.batch, self.k.data_ptr(), self.v.data_ptr(), self.residual)
 
     def row(self, t: int) -> int:
         return t if t < self.sink else self.sink + (t - self.sink) % self.recent

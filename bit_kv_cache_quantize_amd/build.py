@@ -17,7 +17,7 @@ OUT = os.path.join(PKG, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "kvq")
 
 SOURCES = ["kvq_validate.cpp", "kvq_api.cpp", "quant.hip", "decode_ref.hip", "decode_mfma.hip", "decode_pruned.hip",
-           "decode_window.hip"]
+           "decode_vgroup.hip", "decode_window.hip"]
 
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 # -packed-fp32-ops: never emit packed fp32 VALU forms (v_pk_fma_f32 and friends).
@@ -34,7 +34,8 @@ def hipcc() -> str:
 
 # per-source extra flags: keep MFMA accumulators in ordinary VGPRs (the decode kernel
 # reads and rescales them with VALU code; AGPR placement would add copies)
-EXTRA = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "decode_pruned.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+_MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {"decode_mfma.hip": _MFMA_FLAGS, "decode_pruned.hip": _MFMA_FLAGS, "decode_vgroup.hip": _MFMA_FLAGS}
 
 
 def _compile(src: str) -> str:

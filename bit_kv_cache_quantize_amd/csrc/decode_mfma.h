@@ -142,7 +142,13 @@ constexpr int PF = 3;   // blocks loaded ahead
 // the largest summed squared query over the kv head's query heads (ties: lower chunk);
 // the other channels are zeroed in the query and their key chunks are never loaded
 // (the first PF blocks, loaded before the query is known, read every chunk).
-template <int BITS, int G, int R, bool PRUNE>
+// VT: value token groups (InnerQ, Abstract: dequantization aligned with the value
+// vector-matrix product). A block's 32 tokens lie in one group of G tokens, whose
+// {scale, zero} is per channel: the value MFMAs take p itself (A rows = (head, f16 digit
+// of p), B = the codes), and each block's product C is folded per channel as
+// o += scale * (C_hi + C_lo) + zero * sum_t p, so the scale multiplies a finished partial
+// sum instead of every element.
+template <int BITS, int G, int R, bool PRUNE, bool VT>
 __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   constexpr int NG = 128 / G;
   constexpr int RB = 128 * BITS / 8;
@@ -154,7 +160,8 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   const int hk = bh % c.hkv;
   const int b = bh / c.hkv;
   const int T = a.seq_lens[b];
-  const int qend = max(a.tok_begin, T - a.tok_tail);  // the span this kernel covers ends here
+  // the span this kernel covers ends here (with a residual: at the last whole group)
+  const int qend = a.tail_mod ? T - T % a.tail_mod : max(a.tok_begin, T - a.tok_tail);
   const int start = a.tok_begin + split * a.split_len;
   if (start >= qend) return;
   const int end = min(qend, start + a.split_len);
@@ -297,18 +304,37 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     VBlock<BITS> vb;
     const uint8_t* src;   // this lane's first code word of its 8 tokens
     const uint8_t* msrc;  // this lane's value {scale, zero}, part 0
+    int64_t brow;         // row of the block's first token
     if (one_page && start + 32 * cu.blk + 32 <= end) {
       const int64_t r0 = row_base + start + 32 * cu.blk;  // a multiple of 16
       src = c.vc + r0 * RB + voff;
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (r0 / 16) * (NG * 64) + vmoff;
+      brow = r0;
     } else {
       int64_t row0, row1;
       tile_rows(cu, row0, row1);
       const int64_t trow = (q4 < 2) ? row0 : row1;  // value tile of tokens 8q4..8q4+7
       src = c.vc + trow * RB + vc_lane;
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (trow / 16) * (NG * 64) + vm_lane;
+      brow = row0;
     }
     advance(cu);
+    if (VT) {
+      // {scale, zero} of channels pv_channel(0..7, r16): entries 8 r16 .. 8 r16 + 7 of the
+      // block's token group (row / G: pages hold whole groups); re-read by the group's
+      // blocks, so ordinary cached loads
+      const u32x4* gm = reinterpret_cast<const u32x4*>(c.vm + (brow / G) * 128 + 8 * r16);
+      const u32x4 g0 = gm[0], g1 = gm[1];
+      vb.vm[0] = g0[0]; vb.vm[1] = g0[1]; vb.vm[2] = g0[2]; vb.vm[3] = g0[3];
+      vb.vm[4] = g1[0]; vb.vm[5] = g1[1]; vb.vm[6] = g1[2]; vb.vm[7] = g1[3];
+      const u32x4 w0 = ld16(src);
+      vb.vc[0] = w0[0]; vb.vc[1] = w0[1]; vb.vc[2] = w0[2]; vb.vc[3] = w0[3];
+      if (BITS == 4) {
+        const u32x4 w1 = ld16(src + 16 * 16 * 2);
+        vb.vc[4] = w1[0]; vb.vc[5] = w1[1]; vb.vc[6] = w1[2]; vb.vc[7] = w1[3];
+      }
+      return vb;
+    }
     const u32x4 w0 = ld16(src);
     vb.vc[0] = w0[0]; vb.vc[1] = w0[1]; vb.vc[2] = w0[2]; vb.vc[3] = w0[3];
     if (BITS == 4) {
@@ -497,6 +523,15 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     lsum[1] *= al1;
     // scale factors of all four heads, everywhere (heads 0,1 live in lanes 0..31)
     const float alpha[4] = {__shfl(al0, 0, 64), __shfl(al1, 0, 64), __shfl(al0, 32, 64), __shfl(al1, 32, 64)};
+    if (VT) {  // lane (q4 < 2) holds heads 2 q4, 2 q4 + 1 in acc[nt][0], acc[nt][1]
+      const float a0 = alpha[2 * (q4 & 1)], a1 = alpha[2 * (q4 & 1) + 1];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        acc[nt][0] *= a0;
+        acc[nt][1] *= a1;
+      }
+      return;
+    }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
@@ -587,6 +622,53 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     return true;
   };
 
+  // values of block j with value token groups: A rows 2 jj + digit hold the f16 hi / lo
+  // parts of head jj's p (rows >= 2R zero), one MFMA per N-tile; lane (q4 < 2, r16) then
+  // folds rows 4 q4 .. 4 q4 + 3 (heads 2 q4, 2 q4 + 1, both digits) of channel
+  // pv_channel(nt, r16) with that channel's scale and zero
+  auto pv_vt = [&](const VBlock<BITS>& vb, int j) {
+    const int jjA = r16 >> 1;
+    float pv[8];
+    {
+      const floatx4* src = reinterpret_cast<const floatx4*>(&p_s[j][jjA < R ? jjA : 0][8 * q4]);
+      const floatx4 x0 = src[0], x1 = src[1];
+      pv[0] = x0[0]; pv[1] = x0[1]; pv[2] = x0[2]; pv[3] = x0[3];
+      pv[4] = x1[0]; pv[5] = x1[1]; pv[6] = x1[2]; pv[7] = x1[3];
+    }
+    uint32_t ad[4];
+    float ps = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ps += pv[2 * k] + pv[2 * k + 1];
+      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[2 * k], pv[2 * k + 1]));
+      const float lo0 = __builtin_fmaf(lo_f16(hi), neg1, pv[2 * k]);
+      const float lo1 = __builtin_fmaf(hi_f16(hi), neg1, pv[2 * k + 1]);
+      const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo0, lo1));
+      ad[k] = jjA < R ? ((r16 & 1) ? lo : hi) : 0u;
+    }
+    const half8 A = as_half8(ad[0], ad[1], ad[2], ad[3]);
+    // sum of the block's p per head: the lane's 8 tokens, then the 4 token quarters
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    const float P0 = __shfl(ps, 4 * (q4 & 1), 64), P1 = __shfl(ps, 4 * (q4 & 1) + 2, 64);
+#pragma unroll
+    for (int nt = 0; nt < 8; nt += 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      // the products start from zeros that depend on the running sums: each block's MFMAs
+      // stay behind the previous block's fold (from constant zeros the scheduler hoists
+      // every block's products and holds them all, past 400 registers)
+      const floatx4 c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, unpack_v<BITS>(vb.vc, nt), acc[nt] * 0.0f, 0, 0, 0);
+      const floatx4 c1 =
+          __builtin_amdgcn_mfma_f32_16x16x32_f16(A, unpack_v<BITS>(vb.vc, nt + 1), acc[nt + 1] * 0.0f, 0, 0, 0);
+      const float s0 = lo_f16(vb.vm[nt]), z0 = hi_f16(vb.vm[nt]);
+      const float s1 = lo_f16(vb.vm[nt + 1]), z1 = hi_f16(vb.vm[nt + 1]);
+      acc[nt][0] = __builtin_fmaf(s0, c0[0] + c0[1], __builtin_fmaf(z0, P0, acc[nt][0]));
+      acc[nt][1] = __builtin_fmaf(s0, c0[2] + c0[3], __builtin_fmaf(z0, P1, acc[nt][1]));
+      acc[nt + 1][0] = __builtin_fmaf(s1, c1[0] + c1[1], __builtin_fmaf(z1, P0, acc[nt + 1][0]));
+      acc[nt + 1][1] = __builtin_fmaf(s1, c1[2] + c1[3], __builtin_fmaf(z1, P1, acc[nt + 1][1]));
+    }
+  };
+
   // The partition in super-blocks of NBS blocks, each in two passes: the scores of all
   // its blocks (logits stay in registers), one max update, then the values. Loads run
   // two blocks ahead through the sequence K(0..NBS-1), V(0..NBS-1), K of the next
@@ -619,7 +701,10 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       else
         kb[(j + PF - NBS) % (PF + 1)] = load_k(kcur);
       if (!GUARD || j < n) {
-        if (!pv(vb[j % (PF + 1)], j, start + 32 * (base + j), guard, check_big)) return false;
+        if (VT)
+          pv_vt(vb[j % (PF + 1)], j);
+        else if (!pv(vb[j % (PF + 1)], j, start + 32 * (base + j), guard, check_big))
+          return false;
       }
     }
     return true;
@@ -662,15 +747,26 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   // lane (q4, r16) owns accumulator rows 4*q4 + r = (jj = r, g = q4) at column r16; the
   // rows of group q4 hold head jj's output for the channels of that group. Staged in LDS
   // so the workspace is written with 8-byte stores.
-  float zrow[4];
+  if (VT) {
+    if (q4 < 2) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) zrow[r] = __shfl(zacc, 4 * (q4 < NG ? q4 : 0) + r, 64);
+      for (int nt = 0; nt < 8; ++nt) {
+        const int ch = pv_channel<BITS>(nt, r16);
+        if (2 * q4 < R) o_s[2 * q4][ch] = acc[nt][0];
+        if (2 * q4 + 1 < R) o_s[2 * q4 + 1][ch] = acc[nt][1];
+      }
+    }
+  } else {
+    float zrow[4];
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    const int ch = pv_channel<BITS>(nt, r16);
-    if (ch / G == q4) {
+    for (int r = 0; r < 4; ++r) zrow[r] = __shfl(zacc, 4 * (q4 < NG ? q4 : 0) + r, 64);
 #pragma unroll
-      for (int r = 0; r < R; ++r) o_s[r][ch] = acc[nt][r] + zrow[r];
+    for (int nt = 0; nt < 8; ++nt) {
+      const int ch = pv_channel<BITS>(nt, r16);
+      if (ch / G == q4) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) o_s[r][ch] = acc[nt][r] + zrow[r];
+      }
     }
   }
   __syncthreads();

@@ -10,7 +10,7 @@ hipError_t launch_decode_split_pruned(const DecodeArgs& a, const Geometry& g, hi
   dim3 grid(static_cast<unsigned>(units)), block(64);
 #define KVQ_DM(B, GS, RR)                                                                              \
   if (g.bits == B && g.group == GS && a.ratio == RR) {                                                 \
-    hipLaunchKernelGGL((decode_split_mfma_kernel<B, GS, RR, true>), grid, block, 0, stream, a);       \
+    hipLaunchKernelGGL((decode_split_mfma_kernel<B, GS, RR, true, false>), grid, block, 0, stream, a);       \
     return hipGetLastError();                                                                          \
   }
 #define KVQ_DM_R(B, GS) KVQ_DM(B, GS, 1) KVQ_DM(B, GS, 2) KVQ_DM(B, GS, 4)

@@ -17,6 +17,18 @@ namespace kvq {
 namespace {
 
 constexpr int kMaxSplit = 2048;  // tokens per partition this kernel stages in LDS
+
+// Entry of channel ch among a value token group's 128 {scale, zero} entries (caches with
+// value token groups): 8n + t for ch = 4(n + 16(t>>2)) + 2(t&1) + ((t>>1)&1) at INT4,
+// 8n + (t>>1) + 4(t&1) at INT2; found here by searching the documented forward map.
+__device__ __forceinline__ int vt_entry_ref(int bits, int ch) {
+  for (int n = 0; n < 16; ++n)
+    for (int t = 0; t < 8; ++t) {
+      const int c = bits == 4 ? 4 * (n + 16 * (t >> 2)) + 2 * (t & 1) + ((t >> 1) & 1) : 8 * n + (t >> 1) + 4 * (t & 1);
+      if (c == ch) return 8 * n + t;
+    }
+  return 0;
+}
 constexpr int kThreads = 256;
 
 template <int BITS, int G>
@@ -30,7 +42,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
   const int h = bh % c.hkv;
   const int b = bh / c.hkv;
   const int T = a.seq_lens[b];
-  const int qend = max(a.tok_begin, T - a.tok_tail);  // the span this kernel covers ends here
+  // the span this kernel covers ends here (with a residual: at the last whole group)
+  const int qend = a.tail_mod ? T - T % a.tail_mod : max(a.tok_begin, T - a.tok_tail);
   const int start = a.tok_begin + split * a.split_len;
   if (start >= qend) return;
   const int end = min(qend, start + a.split_len);
@@ -122,6 +135,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
     const int j = idx / kD, i = idx % kD;
     const int byte = i * BITS / 8;          // byte of the packed row holding channel i
     const int sh = (i * BITS) % 8;
+    const int vte = c.v_grouping ? vt_entry_ref(BITS, i) : 0;  // channel i's entry in a token group
     float o = 0.f;
     for (int t = start; t < end; ++t) {
       const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + t / c.page];
@@ -129,7 +143,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
       const int64_t u = page * c.hkv + h;
       const int64_t tile_row = u * c.page + (off & ~15);
       const uint32_t code = (static_cast<uint32_t>(c.vc[v_code_byte(tile_row, c.row_bytes, off & 15, byte)]) >> sh) & kMask;
-      const uint32_t m = c.vm[v_meta_entry(tile_row >> 4, c.ngroups, i / G, off & 15)];
+      const uint32_t m = c.v_grouping ? c.vm[((u * c.page + off) / G) * 128 + vte]
+                                      : c.vm[v_meta_entry(tile_row >> 4, c.ngroups, i / G, off & 15)];
       const float vhat = __builtin_fmaf(static_cast<float>(code), f16_bits_to_float(m & 0xFFFFu),
                                         f16_bits_to_float(m >> 16));
       o = __builtin_fmaf(sc[j][t - start], vhat, o);
@@ -150,7 +165,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
 __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ partials,
                                                       const int32_t* __restrict__ seq_lens, int num_q_heads,
                                                       int num_splits, int split_len, int tok_begin, int tok_tail,
-                                                      int part_stride, int window, float* __restrict__ out) {
+                                                      int tail_mod, int part_stride, int window,
+                                                      float* __restrict__ out) {
   constexpr int kD = 128;
   constexpr int kChunk = 16;
   const int bj = blockIdx.x;
@@ -161,7 +177,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
     out[static_cast<int64_t>(bj) * kD + i] = 0.f;
     return;
   }
-  const int span = max(tok_begin, T - tok_tail) - tok_begin;
+  const int span = (tail_mod ? T - T % tail_mod : max(tok_begin, T - tok_tail)) - tok_begin;
   const int nq = min(num_splits, (span + split_len - 1) / split_len);
   const int ns = nq + window;  // >= 1: a sequence with T > 0 has a split or window token
   const float* base = partials + static_cast<int64_t>(bj) * part_stride * (kD + 2);
@@ -218,7 +234,7 @@ hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t st
   (void)g;
   dim3 grid(static_cast<unsigned>(a.batch * a.num_q_heads)), block(128);
   hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, a.partials, a.seq_lens, a.num_q_heads, a.num_splits,
-                     a.split_len, a.tok_begin, a.tok_tail, a.part_stride, a.window, a.out);
+                     a.split_len, a.tok_begin, a.tok_tail, a.tail_mod, a.part_stride, a.window, a.out);
   return hipGetLastError();
 }
 

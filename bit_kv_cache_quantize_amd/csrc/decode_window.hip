@@ -50,10 +50,19 @@ __global__ __launch_bounds__(kWThreads) void decode_window_kernel(DecodeArgs a, 
   const int T = a.seq_lens[b];
   if (T <= 0) return;
   const int S = w.sink, RW = w.recent;
-  // window tokens: sink 0..ns-1, then recent rbeg..T-1
-  const int ns = min(S, T);
-  const int rbeg = max(S, T - RW);
-  const int n = ns + max(0, T - rbeg);  // 1 .. S + RW
+  // window tokens: sink 0..ns-1, then recent rbeg..T-1 (a residual: the incomplete last
+  // group rbeg..T-1, possibly empty)
+  const int ns = w.residual ? 0 : min(S, T);
+  const int rbeg = w.residual ? T - T % RW : max(S, T - RW);
+  const int n = ns + max(0, T - rbeg);  // 1 .. S + RW; 0 for an empty residual
+  if (n == 0) {  // an empty partial: m = -inf, l = 0, o = 0
+    for (int idx = threadIdx.x; idx < R * (kD + 2); idx += kWThreads) {
+      const int j = idx / (kD + 2), e = idx % (kD + 2);
+      a.partials[((static_cast<int64_t>(b) * a.num_q_heads + hk * R + j) * a.part_stride + a.num_splits) * (kD + 2) +
+                 e] = e == kD ? -INFINITY : 0.f;
+    }
+    return;
+  }
 
   __shared__ float red_o[kGroups][R][kD];
   __shared__ float red_ml[kGroups][R][2];
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(kWThreads) void decode_window_kernel(DecodeArgs a, 
     float o = 0.f, L = 0.f;
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
-      const float f = exp2f(red_ml[g][j][0] - M);  // M is finite: group 0 holds token 0
+      const float f = exp2f(red_ml[g][j][0] - M);  // M is finite: group 0 holds window token 0
       o = __builtin_fmaf(red_o[g][j][ch], f, o);
       L = __builtin_fmaf(red_ml[g][j][1], f, L);
     }

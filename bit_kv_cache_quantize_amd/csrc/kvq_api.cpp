@@ -60,6 +60,7 @@ DecodeArgs decode_args(const kvq_cache* cache, const Geometry& g, const void* q,
   a.num_splits = sp.num_splits;
   a.tok_begin = 0;
   a.tok_tail = 0;
+  a.tail_mod = 0;
   a.part_stride = sp.num_splits;
   a.window = 0;
   a.keep_chunks = 0;
@@ -69,6 +70,11 @@ DecodeArgs decode_args(const kvq_cache* cache, const Geometry& g, const void* q,
   const double scale = softmax_scale > 0.f ? softmax_scale : 1.0 / std::sqrt(static_cast<double>(g.d));
   a.qscale = static_cast<float>(scale * 1.4426950408889634);  // log2(e)
   return a;
+}
+
+// the matrix-core split kernel for this cache's value grouping
+hipError_t split_kernel(const DecodeArgs& a, const Geometry& g, hipStream_t s) {
+  return g.v_grouping ? launch_decode_split_vgroup(a, g, s) : launch_decode_split(a, g, s);
 }
 
 kvq_status decode_impl(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
@@ -89,7 +95,7 @@ kvq_status decode_impl(const kvq_cache* cache, const void* q, int32_t batch, int
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return KVQ_ERR_HIP;
-  hipError_t e = reference ? launch_decode_split_reference(a, g, s) : launch_decode_split(a, g, s);
+  hipError_t e = reference ? launch_decode_split_reference(a, g, s) : split_kernel(a, g, s);
   if (e != hipSuccess) return KVQ_ERR_HIP;
   if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return KVQ_ERR_HIP;
   e = launch_combine(a, g, s);
@@ -102,6 +108,7 @@ DevWindow dev_window(const kvq_window* w) {
   d.v = static_cast<uint16_t*>(w->v);
   d.sink = w->sink;
   d.recent = w->recent;
+  d.residual = w->residual;
   return d;
 }
 
@@ -126,6 +133,7 @@ int64_t kvq_cache_plane_bytes(const kvq_cache* cache, int32_t plane) {
   g.row_bytes = cache->head_dim * cache->bits / 8;
   g.num_pages = cache->num_pages;
   g.quant_mode = 0;
+  g.v_grouping = 0;
   return plane_bytes(g, plane);
 }
 
@@ -226,11 +234,12 @@ kvq_status kvq_decode_attention_window(const kvq_cache* cache, const kvq_window*
   DecodeArgs a = decode_args(cache, g, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                              softmax_scale, sp, workspace, out);
   a.tok_begin = window->sink;
-  a.tok_tail = window->recent;
+  a.tok_tail = window->residual ? 0 : window->recent;
+  a.tail_mod = window->residual ? window->recent : 0;
   a.part_stride = sp.num_splits + 1;
   a.window = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_decode_split(a, g, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (split_kernel(a, g, s) != hipSuccess) return KVQ_ERR_HIP;
   if (launch_decode_window(a, dev_window(window), g, s) != hipSuccess) return KVQ_ERR_HIP;
   return launch_combine(a, g, s) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
@@ -246,6 +255,7 @@ kvq_status kvq_decode_attention_pruned(const kvq_cache* cache, const void* q, in
                                max_seq_len, num_splits, workspace, out, &g);
   if (st != KVQ_OK) return st;
   if (keep_chunks < 1 || keep_chunks > g.row_bytes / 16) return KVQ_ERR_INVALID;
+  if (g.v_grouping) return KVQ_ERR_UNSUPPORTED;  // the pruned kernel reads value groups per token
   if (chunk_mask && !aligned(chunk_mask, 4)) return KVQ_ERR_INVALID;
   if (batch == 0) return KVQ_OK;
   const Splits sp = splits_for(g, batch, num_q_heads, max_seq_len, num_splits);

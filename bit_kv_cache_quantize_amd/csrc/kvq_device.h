@@ -20,6 +20,7 @@ struct DevCache {
   int row_bytes;
   int ngroups;
   int quant_mode;  // 0 = asymmetric min/max, 1 = hybrid symmetric/asymmetric per group
+  int v_grouping;  // 0 = value groups of G channels per token, 1 = of G tokens per channel
 };
 
 inline DevCache dev_cache(const kvq_cache* c, const Geometry& g) {
@@ -33,6 +34,7 @@ inline DevCache dev_cache(const kvq_cache* c, const Geometry& g) {
   d.row_bytes = g.row_bytes;
   d.ngroups = g.ngroups;
   d.quant_mode = g.quant_mode;
+  d.v_grouping = g.v_grouping;
   return d;
 }
 
@@ -74,6 +76,7 @@ struct DevWindow {
   uint16_t* v;
   int sink;
   int recent;
+  int residual;  // 1: sink 0 and the ring holds the incomplete last group of `recent` tokens
 };
 
 // ---- host launchers (defined in the .hip files) ----
@@ -103,6 +106,9 @@ struct DecodeArgs {
   // sequence (0, 0 without windows); partition p starts at tok_begin + p * split_len.
   int tok_begin;
   int tok_tail;
+  // with a residual of whole groups of tail_mod tokens (else 0): the span ends at
+  // T - T % tail_mod instead
+  int tail_mod;
   // partial slots per (sequence, query head): num_splits, plus one for the window
   // partial (slot num_splits) when `window` is set
   int part_stride;
@@ -118,6 +124,7 @@ struct DecodeArgs {
 
 hipError_t launch_decode_split(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_split_pruned(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
+hipError_t launch_decode_split_vgroup(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_split_reference(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_window(const DecodeArgs& a, const DevWindow& w, const Geometry& g, hipStream_t stream);

@@ -21,6 +21,9 @@ kvq_status check_cache(const kvq_cache* c, bool planes, Geometry* g) {
   if (c->page_size <= 0 || c->page_size % kTile != 0) return KVQ_ERR_INVALID;
   if ((static_cast<int64_t>(c->head_dim) * c->bits) % 16 != 0) return KVQ_ERR_INVALID;
   if (c->quant_mode != 0 && c->quant_mode != 1) return KVQ_ERR_INVALID;
+  if (c->v_grouping != 0 && c->v_grouping != 1) return KVQ_ERR_INVALID;
+  // value token groups live inside one page
+  if (c->v_grouping == 1 && c->page_size % c->group_size != 0) return KVQ_ERR_INVALID;
   if (planes) {
     const void* p[4] = {c->k_codes, c->k_meta, c->v_codes, c->v_meta};
     for (const void* x : p)
@@ -37,6 +40,7 @@ kvq_status check_cache(const kvq_cache* c, bool planes, Geometry* g) {
   t.row_bytes = c->head_dim * c->bits / 8;
   t.num_pages = c->num_pages;
   t.quant_mode = c->quant_mode;
+  t.v_grouping = c->v_grouping;
   if (g) *g = t;
   return cache_supported(t) ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
 }
@@ -127,6 +131,7 @@ kvq_status check_append(const kvq_cache* c, const void* k_new, const void* v_new
   kvq_status st = check_cache(c, true, g);
   if (st != KVQ_OK) return st;
   if (n_new < 0) return KVQ_ERR_INVALID;
+  if (c->v_grouping == 1 && n_new % c->group_size != 0) return KVQ_ERR_INVALID;  // whole token groups
   if (n_new == 0) return KVQ_OK;
   if (!k_new || !v_new || !slots) return KVQ_ERR_INVALID;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slots, 8)) return KVQ_ERR_INVALID;
@@ -136,6 +141,12 @@ kvq_status check_append(const kvq_cache* c, const void* k_new, const void* v_new
 kvq_status check_window(const kvq_cache* c, const kvq_window* w, bool planes) {
   if (!c || !w) return KVQ_ERR_INVALID;
   if (w->sink < 0 || w->recent < 1 || w->batch < 0) return KVQ_ERR_INVALID;
+  if (w->residual != 0 && w->residual != 1) return KVQ_ERR_INVALID;
+  if (w->residual == 1 && w->sink != 0) return KVQ_ERR_INVALID;
+  // a completed group goes to its tokens' consecutive slots: groups must not cross pages
+  if (w->residual == 1 && c->page_size % w->recent != 0) return KVQ_ERR_INVALID;
+  // value token groups come whole out of a residual of one group
+  if (c->v_grouping == 1 && (w->residual != 1 || w->recent != c->group_size)) return KVQ_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(w->sink) + w->recent > kMaxWindow) return KVQ_ERR_UNSUPPORTED;
   // the quantized span starts at `sink`, which the decode kernels need on a tile boundary
   if (w->sink % kTile != 0) return KVQ_ERR_UNSUPPORTED;
@@ -165,6 +176,7 @@ kvq_status check_window_append(const kvq_cache* c, const kvq_window* w, const vo
 }
 
 int32_t window_span(const kvq_window* w, int32_t max_seq_len) {
+  if (w->residual) return max_seq_len;  // up to max_seq_len - (max_seq_len % recent)
   const int64_t n = static_cast<int64_t>(max_seq_len) - w->sink - w->recent;
   return n > 0 ? static_cast<int32_t>(n) : 0;
 }

@@ -15,7 +15,7 @@ constexpr int kTile = 16;
 constexpr int kBlock = 32;
 
 struct Geometry {
-  int d, hkv, bits, group, ngroups, hblock, page, row_bytes, quant_mode;
+  int d, hkv, bits, group, ngroups, hblock, page, row_bytes, quant_mode, v_grouping;
   int64_t num_pages;
 };
 

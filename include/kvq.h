@@ -70,6 +70,14 @@ typedef enum kvq_status {
  *            o = 8*half + 4*part + i of group g at entry ((part*NG + g)*2 + half)*4 + i
  *            of the tile
  *
+ * With v_grouping 1 (InnerQ, Abstract: groups along the inner dimension of the value
+ * product) the value codes keep the layout above and v_meta holds one {scale, zero} per
+ * (group of G tokens of a page, channel):
+ *   v_meta   half2 [u][page_size/G][128]: channel c of token group j at entry 8n + t,
+ *            c = 4(n + 16(t>>2)) + 2(t&1) + ((t>>1)&1) at INT4, 8n + (t>>1) + 4(t&1) at
+ *            INT2 (n = 0..15, t = 0..7); the plane has the same size.
+ * Keys keep their per-token groups.
+ *
  * Packed rows are little-endian: INT4 channel 2k in the low nibble of byte k and
  * 2k+1 in the high nibble; INT2 channel 4k+e in bits 2e..2e+1 of byte k.
  * A contiguous cache is the special case of one page of capacity tokens per
@@ -89,6 +97,8 @@ typedef struct kvq_cache {
   void* v_codes;
   void* v_meta;
   int32_t quant_mode;     /* 0 = asymmetric min/max groups; 1 = hybrid (below) */
+  int32_t v_grouping;     /* 0 = value groups of G channels of a token; 1 = of G tokens of a
+                             channel (InnerQ, below; page_size a multiple of G) */
 } kvq_cache;
 
 /* Bytes of one plane: 0 = k_codes, 1 = k_meta, 2 = v_codes, 3 = v_meta.
@@ -111,6 +121,11 @@ int64_t kvq_cache_plane_bytes(const kvq_cache* cache, int32_t plane);
 kvq_status kvq_quantize_append(const kvq_cache* cache, const void* k_new, const void* v_new,
                                const int64_t* slots, int64_t n_new, void* stream);
 /*
+ * v_grouping 1: n_new must be a multiple of G (else KVQ_ERR_INVALID); rows come in whole
+ * token groups, rows j*G .. j*G+G-1 at the consecutive slots slots[j*G] + 0 .. G-1 of one
+ * page, slots[j*G] a multiple of G (device contents, not checked). Keys are quantized per
+ * token; each channel of a group's values forms one group, by the same formula.
+ *
  * quant_mode 1, hybrid groups (InnerQ, Abstract: each group chooses symmetric or
  * asymmetric quantization from its own statistics): besides the pair above, a symmetric
  * pair scale = fp16(fl32(max|x| / (2^(bits-1) - 1))), zero = -2^(bits-1) * scale (exact)
@@ -237,7 +252,18 @@ typedef struct kvq_window {
   int32_t batch;  /* sequences the planes hold */
   void* k;
   void* v;
+  int32_t residual; /* 0 = sink and recent windows as above; 1 = residual (below) */
 } kvq_window;
+
+/*
+ * residual 1 (sink must be 0, page_size a multiple of R): the ring of R rows holds the incomplete last group of R
+ * tokens in bf16, token t in row t % R, T % R tokens of them; the tokens before are in
+ * the cache. Appending token t with (t + 1) % R == 0 completes the group t-R+1 .. t,
+ * which is then quantized from the ring into the cache at evict_slots[r] + 0 .. R-1
+ * (its tokens' consecutive slots); no token is evicted otherwise. Decode scores the
+ * residual tokens like window tokens. A cache with v_grouping 1 needs a residual window
+ * with R == group_size (other windows return KVQ_ERR_UNSUPPORTED).
+ */
 
 /* Bytes of one window plane (k or v) for this cache's d and Hkv; -1 if invalid. */
 int64_t kvq_window_plane_bytes(const kvq_cache* cache, const kvq_window* window);

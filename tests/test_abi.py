@@ -27,6 +27,7 @@ def _desc(**kw):
     for f in ("k_codes", "k_meta", "v_codes", "v_meta"):
         setattr(d, f, kw.get(f, FAKE))
     d.quant_mode = kw.get("quant_mode", 0)
+    d.v_grouping = kw.get("v_grouping", 0)
     return d
 
 
@@ -73,6 +74,8 @@ INVALID_CACHES = [
     (dict(k_codes=0), kvq.ERR_INVALID),
     (dict(v_meta=FAKE + 4), kvq.ERR_INVALID),        # misaligned plane
     (dict(quant_mode=2), kvq.ERR_INVALID),            # neither asymmetric nor hybrid
+    (dict(v_grouping=2), kvq.ERR_INVALID),
+    (dict(v_grouping=1, page_size=16), kvq.ERR_INVALID),   # token groups of 32 do not fit a page
     (dict(quant_mode=-1), kvq.ERR_INVALID),
 ]
 
@@ -169,9 +172,9 @@ def test_split_sizing_and_workspace():
 
 
 def _win(**kw):
-    base = dict(sink=32, recent=128, batch=4, k=FAKE, v=FAKE)
+    base = dict(sink=32, recent=128, batch=4, k=FAKE, v=FAKE, residual=0)
     base.update(kw)
-    return kvq._Window(base["sink"], base["recent"], base["batch"], base["k"], base["v"])
+    return kvq._Window(base["sink"], base["recent"], base["batch"], base["k"], base["v"], base.get("residual", 0))
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -266,3 +269,24 @@ def test_decode_pruned_argument_checks():
     assert _decode_pruned(d4, wsb=100) == kvq.ERR_WORKSPACE
     assert _decode_pruned(d4, batch=0) == kvq.OK            # empty: no launch
     assert _decode_pruned(d2, keep=2, batch=0, mask=0) == kvq.OK
+
+
+def test_vgroup_argument_checks():
+    """Value token groups: appends of whole groups only; windows must be a residual of one
+    group; the pruned kernel does not take them."""
+    L, v = kvq.lib(), ctypes.c_void_p
+    d = _desc(v_grouping=1, page_size=64)
+    assert L.kvq_quantize_append(ctypes.byref(d), v(FAKE), v(FAKE), v(FAKE), 33, None) == kvq.ERR_INVALID
+    assert L.kvq_quantize_append(ctypes.byref(d), v(FAKE), v(FAKE), v(FAKE), 0, None) == kvq.OK
+    args = [v(FAKE)] * 5
+    assert L.kvq_window_append(ctypes.byref(d), ctypes.byref(_win()), *args, 1, None) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_window_append(ctypes.byref(d), ctypes.byref(_win(sink=0, recent=64, residual=1)), *args, 1,
+                               None) == kvq.ERR_UNSUPPORTED  # ring of 64 rows, groups of 32
+    assert L.kvq_window_append(ctypes.byref(d), ctypes.byref(_win(sink=0, recent=32, residual=1)), *args, 0,
+                               None) == kvq.OK
+    assert L.kvq_window_append(ctypes.byref(_desc()), ctypes.byref(_win(sink=16, residual=1)), *args, 1,
+                               None) == kvq.ERR_INVALID  # a residual has no sink
+    assert L.kvq_window_append(ctypes.byref(_desc()), ctypes.byref(_win(residual=2)), *args, 1, None) == kvq.ERR_INVALID
+    assert L.kvq_window_append(ctypes.byref(_desc(page_size=16)), ctypes.byref(_win(sink=0, recent=32, residual=1)),
+                               *args, 1, None) == kvq.ERR_INVALID  # a group would cross pages
+    assert _decode_pruned(d) == kvq.ERR_UNSUPPORTED
