@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--parity-seqs", type=int, default=2, help="sequences checked against the oracle")
     ap.add_argument("--window", default="", help="S,R: bf16 sink and recent windows of S and R tokens")
     ap.add_argument("--hybrid", action="store_true", help="hybrid symmetric/asymmetric groups (quant_mode 1)")
+    ap.add_argument("--vgroup", action="store_true",
+                    help="values grouped along tokens (v_grouping 1) with a bf16 residual of one group")
     ap.add_argument("--prune", type=int, default=0,
                     help="query-channel pruning: key chunks kept per (sequence, kv head), of bits * head_dim / 128")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
@@ -133,17 +135,30 @@ def main():
     geo = wl.geometry(w, extra_tokens=0, lens=lens)
     win_S, win_R = (int(x) for x in args.window.split(",")) if args.window else (0, 0)
     windowed = bool(args.window)
+    residual = args.vgroup  # a window with sink 0 whose ring holds the incomplete last group
+    if residual:
+        if windowed:
+            sys.exit("bench.py: --vgroup brings its own residual window")
+        win_S, win_R, windowed = 0, w.group_size, True
     maxlen = int(lens.max())
     t0 = time.time()
     cache = kvq.KVCache.allocate(d, Hkv, w.bits, w.group_size, w.hadamard_block, geo.page_size, geo.num_pages,
-                                 device=dev, quant_mode=1 if args.hybrid else 0)
+                                 device=dev, quant_mode=1 if args.hybrid else 0, v_grouping=1 if args.vgroup else 0)
     log(f"[bench] {w.name}: cache {cache.nbytes / 1e9:.2f} GB, B={B} Hq={Hq} Hkv={Hkv} T<= {maxlen}")
-    window = kvq.KVWindow.allocate(cache, win_S, win_R, B, device=dev) if windowed else None
+    window = kvq.KVWindow.allocate(cache, win_S, win_R, B, device=dev, residual=int(residual)) if windowed else None
     for b in range(B):
         T = int(lens[b])
         k, v = wl.keys(w, b, 0, T, device=dev), wl.values(w, b, 0, T, device=dev)
         if not windowed:
             kvq.quantize_append(cache, k, v, geo.slots(b, 0, T).to(dev))
+        elif residual:
+            # state before the step's token T-1: whole groups quantized, the rest in the ring
+            done = (T - 1) - (T - 1) % win_R
+            if done:
+                kvq.quantize_append(cache, k[:done].contiguous(), v[:done].contiguous(), geo.slots(b, 0, done).to(dev))
+            for t in range(done, T - 1):
+                window.k[b, t % win_R] = k[t]
+                window.v[b, t % win_R] = v[t]
         else:
             # state before the step's token T-1: sink rows, the ring holding T-1-R..T-2,
             # and the tokens between quantized
@@ -165,7 +180,8 @@ def main():
     windows = [window]
     for _ in range(ring - 1):
         caches.append(cache.clone())
-        windows.append(kvq.KVWindow(win_S, win_R, B, window.k.clone(), window.v.clone()) if windowed else None)
+        windows.append(kvq.KVWindow(win_S, win_R, B, window.k.clone(), window.v.clone(), int(residual))
+                       if windowed else None)
 
     n_inputs = 4
     qs = [wl.queries(w, step=s, device=dev) for s in range(n_inputs)]
@@ -178,7 +194,10 @@ def main():
         num_splits = kvq.decode_num_splits(cache, B, Hq, max(maxlen - win_S - win_R, 0), args.num_splits)
         seqs_d = torch.arange(B, dtype=torch.int32, device=dev)
         pos_d = (lens - 1).to(dev)
-        evict_d = torch.stack([geo.slots(b, max(int(lens[b]) - 1 - win_R, 0), 1)[0] for b in range(B)]).to(dev)
+        # the evicted token's slot, or with a residual the first slot of the group the
+        # step's token completes
+        first = (lambda T: T - win_R) if residual else (lambda T: T - 1 - win_R)
+        evict_d = torch.stack([geo.slots(b, max(first(int(lens[b])), 0), 1)[0] for b in range(B)]).to(dev)
     else:
         ws_bytes = kvq.decode_workspace_bytes(cache, B, Hq, maxlen, args.num_splits)
         num_splits = kvq.decode_num_splits(cache, B, Hq, maxlen, args.num_splits)
@@ -247,7 +266,14 @@ def main():
         # pruned key chunks are not read: per token and kv head the K codes shrink to
         # keep / n_chunks of a row
         kv_bytes -= int(lens.to(torch.int64).sum()) * Hkv * (d * w.bits // 8) * (n_chunks - args.prune) // n_chunks
-    if windowed:
+    if residual:
+        # the residual holds T % G tokens at decode time; the append writes the token and,
+        # when it completes a group, reads the G ring rows and writes their quantized form
+        n_win = sum(int(T) % win_R for T in lens)
+        kv_bytes = (int(lens.to(torch.int64).sum()) - n_win) * Hkv * per_tok_head + n_win * Hkv * 2 * d * 2
+        completing = sum(1 for T in lens if int(T) % win_R == 0)
+        append_bytes = B * Hkv * 2 * (2 * d * 2) + completing * Hkv * win_R * (2 * d * 2 + per_tok_head)
+    elif windowed:
         # window tokens are read as bf16 K and V rows; the append reads the new token,
         # writes it to the ring, reads the evicted row and writes its quantized form
         n_win = sum(min(win_S, int(T)) + min(win_R, max(int(T) - win_S, 0)) for T in lens)
@@ -304,24 +330,35 @@ def main():
         for s_i, b in enumerate(seqs):
             T = int(lens[b])
             # a one-sequence oracle cache holding sequence b (contiguous layout)
-            P = int(math.ceil(T / 16) * 16)
-            ref = oracle.Cache(d, Hkv, w.bits, w.group_size, w.hadamard_block, P, 1, quant_mode=cache.quant_mode)
+            unit = w.group_size if args.vgroup else 16  # pages hold whole value token groups
+            P = int(math.ceil(T / unit) * unit)
+            ref = oracle.Cache(d, Hkv, w.bits, w.group_size, w.hadamard_block, P, 1, quant_mode=cache.quant_mode,
+                               v_grouping=cache.v_grouping)
             k = wl.keys(w, b, 0, T, device=dev)
             v = wl.values(w, b, 0, T, device=dev)
             if windowed:
                 # prefill state, then the last two steps applied to this cache: each step
-                # rewrites the same ring row and evicted slot, so they fix the final state
-                rw = oracle.Window(d, Hkv, win_S, win_R, 1)
-                lo, hi = win_S, T - 1 - win_R
-                if hi > lo:
-                    ref.append(wl.bf16_bits(k[lo:hi]), wl.bf16_bits(v[lo:hi]), np.arange(lo, hi))
-                for t in list(range(min(win_S, T - 1))) + list(range(max(win_S, T - 1 - win_R), T - 1)):
+                # rewrites the same ring row and evicted slot (or completed group), so they
+                # fix the final state
+                rw = oracle.Window(d, Hkv, win_S, win_R, 1, residual=int(residual))
+                if residual:
+                    done = (T - 1) - (T - 1) % win_R
+                    if done:
+                        ref.append(wl.bf16_bits(k[:done]), wl.bf16_bits(v[:done]), np.arange(done))
+                    win_tokens = list(range(done, T - 1))
+                else:
+                    lo, hi = win_S, T - 1 - win_R
+                    if hi > lo:
+                        ref.append(wl.bf16_bits(k[lo:hi]), wl.bf16_bits(v[lo:hi]), np.arange(lo, hi))
+                    win_tokens = list(range(min(win_S, T - 1))) + list(range(max(win_S, T - 1 - win_R), T - 1))
+                for t in win_tokens:
                     rw.k[0, window.row(t)] = wl.bf16_bits(k[t])
                     rw.v[0, window.row(t)] = wl.bf16_bits(v[t])
+                ev = max(T - win_R, 0) if residual else max(T - 1 - win_R, 0)
                 for j in applied0[-2:]:
                     kj, vj = news[j]
                     rw.append(ref, wl.bf16_bits(kj[b:b + 1]), wl.bf16_bits(vj[b:b + 1]), np.zeros(1, np.int32),
-                              np.array([T - 1], np.int32), np.array([max(T - 1 - win_R, 0)], np.int64))
+                              np.array([T - 1], np.int32), np.array([ev], np.int64))
                 o = rw.decode(ref, wl.bf16_bits(q_last[b:b + 1]), np.zeros((1, 1), np.int32),
                               np.array([T], np.int32))
                 worst = max(worst, float(np.max(np.abs(o[0] - out_h[b]))))
@@ -372,12 +409,12 @@ def main():
                    "context": maxlen, "bits": w.bits, "group_size": w.group_size,
                    "hadamard_block": w.hadamard_block, "page_size": geo.page_size, "num_splits": num_splits,
                    "kernel": "reference" if args.reference else "mfma", "layer_ring": ring,
-                   "step_bytes": step_bytes, "quant_mode": cache.quant_mode,
+                   "step_bytes": step_bytes, "quant_mode": cache.quant_mode, "v_grouping": cache.v_grouping,
                    **({"keep_chunks": args.prune, "chunks": n_chunks,
                        "kv_bits_capacity": round(per_tok_head * 8 / (2 * d), 4),
                        "kv_bits_bandwidth": round(kv_bytes * 8 / (2 * d * Hkv * int(lens.to(torch.int64).sum())), 4)}
                       if args.prune else {}),
-                   **({"window_sink": win_S, "window_recent": win_R} if windowed else {})},
+                   **({"window_sink": win_S, "window_recent": win_R, "residual": int(residual)} if windowed else {})},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,

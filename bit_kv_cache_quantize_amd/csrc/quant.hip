@@ -261,8 +261,13 @@ __device__ __forceinline__ void vgroup_quantize(const DevCache& c, const uint16_
   constexpr int kQmax = (1 << BITS) - 1;
   constexpr int kPerByte = 8 / BITS;
   const int ch = threadIdx.x;
-  auto val = [&](int i) { return __uint_as_float(static_cast<uint32_t>(src[i * row_stride + ch]) << 16); };
+  // the group's G values of this channel, all loads in flight together
+  float xs[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) xs[i] = __uint_as_float(static_cast<uint32_t>(src[i * row_stride + ch]) << 16);
+  auto val = [&](int i) { return xs[i]; };
   float mn = val(0), mx = mn;
+#pragma unroll
   for (int i = 1; i < G; ++i) {
     const float v = val(i);
     mn = fminf(mn, v);
@@ -286,6 +291,7 @@ __device__ __forceinline__ void vgroup_quantize(const DevCache& c, const uint16_
       const float s = f16_bits_to_float(sb), z = f16_bits_to_float(zb);
       const float inv = s != 0.0f ? 1.0f / s : 0.0f;
       float err = 0.0f;
+#pragma unroll
       for (int i = 0; i < G; ++i) {
         const float x = val(i);
         err = fmaxf(err, fabsf(x - __builtin_fmaf(static_cast<float>(code_of(x, s, z, inv)), s, z)));
@@ -303,6 +309,7 @@ __device__ __forceinline__ void vgroup_quantize(const DevCache& c, const uint16_
   c.vm[(u * (c.page / G) + off0 / G) * 128 + vt_entry<BITS>(ch)] = s16 | (z16 << 16);
   const float s = f16_bits_to_float(s16), z = f16_bits_to_float(z16);
   const float inv = s != 0.0f ? 1.0f / s : 0.0f;
+#pragma unroll
   for (int i = 0; i < G; ++i) {
     uint32_t byte = code_of(val(i), s, z, inv);
 #pragma unroll
