@@ -134,16 +134,17 @@ def test_vgroup_split_counts():
         assert err <= TOL
 
 
-@pytest.mark.parametrize("name,steps", [("int4_g32", 70), ("int2_g128", 140), ("int4_g64_gqa2", 70)])
-def test_vgroup_residual_stream(name, steps):
+@pytest.mark.parametrize("name,steps,mode", [("int4_g32", 70, 0), ("int2_g128", 140, 0), ("int4_g64_gqa2", 70, 0),
+                                             ("int4_g32", 40, 1)])
+def test_vgroup_residual_stream(name, steps, mode):
     """Decode-time tokens through the residual: groups complete and are quantized as the
     stream crosses multiples of G; planes bit-exact and decode within tolerance at
     several points (residual empty, partly and almost full)."""
     w, lens = CASES[name]
     G = w.group_size
     lens = [n + (5 if i == 0 else G - 3) for i, n in enumerate(lens)]  # start with a partial group
-    print(f"[vgroup] residual {name}: lens={lens} steps={steps}", flush=True)
-    p = VPair(w, lens, steps=steps, residual=True)
+    print(f"[vgroup] residual {name}: lens={lens} steps={steps} mode={mode}", flush=True)
+    p = VPair(w, lens, steps=steps, mode=mode, residual=True)
     for s in range(steps):
         p.step(s)
         if s % 23 == 0 or s == steps - 1 or int(p.lens[0]) % G == 0:
