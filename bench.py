@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--parity-seqs", type=int, default=2, help="sequences checked against the oracle")
     ap.add_argument("--window", default="", help="S,R: bf16 sink and recent windows of S and R tokens")
     ap.add_argument("--hybrid", action="store_true", help="hybrid symmetric/asymmetric groups (quant_mode 1)")
+    ap.add_argument("--hadamard-block", type=int, default=-1,
+                    help="override the workload's rotation block (0 = no rotation), e.g. to time rotation on/off")
     ap.add_argument("--vgroup", action="store_true",
                     help="values grouped along tokens (v_grouping 1) with a bf16 residual of one group")
     ap.add_argument("--prune", type=int, default=0,
@@ -125,6 +127,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = wl.get(args.workload)
+    if args.hadamard_block >= 0:
+        w = w.with_(hadamard_block=args.hadamard_block)
     if w.ragged is not None:
         lens = wl.seq_lens(w)
     else:

@@ -12,6 +12,7 @@
 // step is a separate IEEE round-to-nearest-even operation in the order the library
 // documents, so the codes and fp16 scale/zero are bit-exact functions of the input.
 #include <cmath>
+#include <type_traits>
 
 #include "kvq_device.h"
 
@@ -22,12 +23,28 @@ namespace kvq {
 namespace {
 
 constexpr int kRowsPerBlock = 16;  // 256 threads, 16 lanes per row
+constexpr int64_t kTileAppendMin = 256;  // appends of at least this many tokens go tile by tile
 
-// One 128-channel K (which = 0, rotated first) or V row of kv head h, 8 channels per lane
-// in x, 16 lanes per row: group parameters, codes, packing, and the stores at `slot`.
+// The value of lane (lane ^ M) of the same 16-lane row, by DPP row permutes instead of
+// LDS-routed shuffles: quad swaps for M = 1, 2; a rotation by 8 of the row for M = 8;
+// for M = 4 the rotations by 4 and by 12, one of which holds lane ^ 4 for each lane.
+template <int M>
+__device__ __forceinline__ float lane_xor16(float v, int lane) {
+  const int iv = __float_as_int(v);
+  if (M == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+  if (M == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+  if (M == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, iv, 0x128, 0xF, 0xF, false));  // row_ror:8
+  const int a = __builtin_amdgcn_update_dpp(0, iv, 0x124, 0xF, 0xF, false);  // row_ror:4, lane i <- i - 4
+  const int b = __builtin_amdgcn_update_dpp(0, iv, 0x12C, 0xF, 0xF, false);  // row_ror:12, lane i <- i + 4
+  return __int_as_float((lane & 4) ? a : b);
+}
+
+// One 128-channel K (which = 0, rotated first) or V row, 8 channels per lane in x, 16
+// lanes per row: group parameters and codes. packed = the lane's packed codes (8 channels,
+// BITS * 8 bits), meta = its group's {scale | zero << 16}.
 template <int BITS, int G>
-__device__ __forceinline__ void quantize_store_row(const DevCache& c, int which, int h, int64_t slot, float (&x)[8],
-                                                   int lane, int hblock, float rot_c) {
+__device__ __forceinline__ void quantize_row_codes(const DevCache& c, int which, float (&x)[8], int lane, int hblock,
+                                                   float rot_c, uint32_t& packed_out, uint32_t& meta_out) {
   const bool hybrid = c.quant_mode == 1;
   constexpr int kQmax = (1 << BITS) - 1;
   constexpr int kLanesPerGroup = G / 8;
@@ -47,17 +64,21 @@ __device__ __forceinline__ void quantize_store_row(const DevCache& c, int which,
       }
     }
     // cross-lane strides 8..64: partner lane = lane ^ (stride / 8)
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
+    auto stage = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
       if (8 * m < hblock) {
         const bool upper = (lane & m) != 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float y = __shfl_xor(x[e], m, 16);
+          const float y = lane_xor16<m>(x[e], lane);
           x[e] = upper ? (y - x[e]) : (x[e] + y);
         }
       }
-    }
+    };
+    stage(std::integral_constant<int, 1>{});
+    stage(std::integral_constant<int, 2>{});
+    stage(std::integral_constant<int, 4>{});
+    stage(std::integral_constant<int, 8>{});
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = x[e] * rot_c;
   }
@@ -68,10 +89,18 @@ __device__ __forceinline__ void quantize_store_row(const DevCache& c, int which,
     mn = fminf(mn, x[e]);
     mx = fmaxf(mx, x[e]);
   }
-#pragma unroll
-  for (int m = 1; m < kLanesPerGroup; m <<= 1) {
-    mn = fminf(mn, __shfl_xor(mn, m, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, m, 16));
+  // over the group's lanes (4, 8 or 16)
+  mn = fminf(mn, lane_xor16<1>(mn, lane));
+  mx = fmaxf(mx, lane_xor16<1>(mx, lane));
+  mn = fminf(mn, lane_xor16<2>(mn, lane));
+  mx = fmaxf(mx, lane_xor16<2>(mx, lane));
+  if (kLanesPerGroup > 4) {
+    mn = fminf(mn, lane_xor16<4>(mn, lane));
+    mx = fmaxf(mx, lane_xor16<4>(mx, lane));
+  }
+  if (kLanesPerGroup > 8) {
+    mn = fminf(mn, lane_xor16<8>(mn, lane));
+    mx = fmaxf(mx, lane_xor16<8>(mx, lane));
   }
   const float range = (mx - mn) + 0.0f;  // +0.0f: a -0 range (mixed-sign zeros) becomes +0
   const float s32 = range / static_cast<float>(kQmax);
@@ -108,8 +137,10 @@ __device__ __forceinline__ void quantize_store_row(const DevCache& c, int which,
       float err = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) err = fmaxf(err, fabsf(x[e] - __builtin_fmaf(static_cast<float>(c8[e]), s, z)));
-#pragma unroll
-      for (int m = 1; m < kLanesPerGroup; m <<= 1) err = fmaxf(err, __shfl_xor(err, m, 16));
+      err = fmaxf(err, lane_xor16<1>(err, lane));
+      err = fmaxf(err, lane_xor16<2>(err, lane));
+      if (kLanesPerGroup > 4) err = fmaxf(err, lane_xor16<4>(err, lane));
+      if (kLanesPerGroup > 8) err = fmaxf(err, lane_xor16<8>(err, lane));
       return err;
     };
     const float amax = fmaxf(fabsf(mn), fabsf(mx));
@@ -128,12 +159,21 @@ __device__ __forceinline__ void quantize_store_row(const DevCache& c, int which,
   uint32_t packed = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) packed |= cd[e] << (BITS * e);
+  packed_out = packed;
+  meta_out = s16 | (z16 << 16);
+}
 
+// The row quantizer plus its stores at `slot` (kv head h).
+template <int BITS, int G>
+__device__ __forceinline__ void quantize_store_row(const DevCache& c, int which, int h, int64_t slot, float (&x)[8],
+                                                   int lane, int hblock, float rot_c) {
+  constexpr int kLanesPerGroup = G / 8;
+  uint32_t packed, meta;
+  quantize_row_codes<BITS, G>(c, which, x, lane, hblock, rot_c, packed, meta);
   const int64_t page = slot / c.page;
   const int off = static_cast<int>(slot - page * c.page);
   const int64_t u = page * c.hkv + h;
   const int g = lane / kLanesPerGroup;
-  const uint32_t meta = s16 | (z16 << 16);
   const bool group_leader = (lane % kLanesPerGroup) == 0;
 
   const int64_t tile_row = u * c.page + (off & ~15);  // first token row of the 16-token tile
@@ -179,6 +219,75 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(DevCache c, const 
   float x[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
                 bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
   quantize_store_row<BITS, G>(c, which, h, slots[r], x, lane, hblock, rot_c);
+}
+
+// Bulk appends: a workgroup takes rows 16j .. 16j+15 of one kv head and one kind (K or V;
+// kinds 1 = keys only). When those rows are one whole 16-token tile (consecutive slots
+// from a tile boundary), the tile is assembled in LDS in its cache layout and written
+// with whole-line 16-byte stores; otherwise every row is stored on its own, as the
+// per-row kernel does. The codes are the same either way.
+template <int BITS, int G>
+__global__ __launch_bounds__(256) void quantize_tiles_kernel(DevCache c, const uint16_t* __restrict__ k_new,
+                                                             const uint16_t* __restrict__ v_new,
+                                                             const int64_t* __restrict__ slots, int64_t n_new,
+                                                             int kinds, int hblock, float rot_c) {
+  constexpr int RB = 128 * BITS / 8;
+  constexpr int NG = 128 / G;
+  constexpr int kLanesPerGroup = G / 8;
+  constexpr int kBytes = BITS;  // packed bytes per lane (8 channels)
+  __shared__ uint32_t codes_s[16 * RB / 4];
+  __shared__ uint32_t meta_s[16 * NG];
+  const int which = kinds == 2 ? static_cast<int>(blockIdx.x & 1) : 0;
+  const int64_t jh = kinds == 2 ? blockIdx.x >> 1 : blockIdx.x;
+  const int h = static_cast<int>(jh % c.hkv);
+  const int64_t j = jh / c.hkv;
+  const int lane = threadIdx.x & 15, o = threadIdx.x >> 4;
+  const int64_t r = 16 * j + o;
+  const bool valid = r < n_new;
+  // the row's data and the slots are independent loads: both in flight before the check
+  uint4 raw = {0u, 0u, 0u, 0u};
+  if (valid) raw = *reinterpret_cast<const uint4*>((which ? v_new : k_new) + (r * c.hkv + h) * 128 + lane * 8);
+  const int64_t slot = valid ? slots[r] : 0;
+  const int64_t s0 = slots[16 * j];
+  const bool tile = __syncthreads_and(valid && slot == s0 + o && (s0 & 15) == 0 && (s0 % c.page) + 15 < c.page);
+  if (!valid) return;  // only when not a whole tile: no barrier follows then
+  float x[8] = {bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y),
+                bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w)};
+  if (!tile) {
+    quantize_store_row<BITS, G>(c, which, h, slot, x, lane, hblock, rot_c);
+    return;
+  }
+  uint32_t packed, meta;
+  quantize_row_codes<BITS, G>(c, which, x, lane, hblock, rot_c, packed, meta);
+  uint8_t* cs = reinterpret_cast<uint8_t*>(codes_s);
+  const int g = lane / kLanesPerGroup;
+  const bool group_leader = (lane % kLanesPerGroup) == 0;
+  if (which == 0) {
+    uint8_t* dst = cs + k_code_byte(0, RB, o, lane * kBytes);
+    if (BITS == 4)
+      *reinterpret_cast<uint32_t*>(dst) = packed;
+    else
+      *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
+    if (group_leader) meta_s[o * NG + g] = meta;
+  } else {
+#pragma unroll
+    for (int k = 0; k < kBytes; ++k) cs[v_code_byte(0, RB, o, lane * kBytes + k)] = static_cast<uint8_t>(packed >> (8 * k));
+    if (group_leader) meta_s[v_meta_entry(0, NG, g, o)] = meta;
+  }
+  __syncthreads();
+  const int64_t page = s0 / c.page;
+  const int64_t tile_row = (page * c.hkv + h) * c.page + (s0 - page * c.page);
+  const int t = threadIdx.x;
+  if (t < 16 * RB / 16) {
+    uint4* dst = reinterpret_cast<uint4*>((which ? c.vc : c.kc) + tile_row * RB);
+    dst[t] = reinterpret_cast<const uint4*>(codes_s)[t];
+  } else if (t - 16 * RB / 16 < 16 * NG / 4) {
+    const int m = t - 16 * RB / 16;
+    // K meta is token-major [u][P][NG]; V meta is tile-major: both are this tile's
+    // 16 NG consecutive entries
+    uint32_t* mdst = which ? c.vm + (tile_row >> 4) * NG * 16 : c.km + tile_row * NG;
+    reinterpret_cast<uint4*>(mdst)[m] = reinterpret_cast<const uint4*>(meta_s)[m];
+  }
 }
 
 // High-precision windows (InnerQ, Abstract): one new token per row of (seqs, positions).
@@ -399,10 +508,18 @@ hipError_t launch_quantize_append(const DevCache& c, const Geometry& g, const vo
   const auto* k = static_cast<const uint16_t*>(k_new);
   const auto* v = static_cast<const uint16_t*>(v_new);
   dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  // bulk appends (prefill): whole tiles at a time
+  const bool tiles = n_new >= kTileAppendMin;
+  const int64_t tile_blocks = (n_new + 15) / 16 * g.hkv * rows_per_token;
+  if (tiles && tile_blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
 #define KVQ_QA(B, GS)                                                                                      \
   if (g.bits == B && g.group == GS) {                                                                      \
-    hipLaunchKernelGGL((quantize_append_kernel<B, GS>), grid, block, 0, stream, c, k, v, slots, n_rows,   \
-                       rows_per_token, g.hblock, rot_c);                                                    \
+    if (tiles)                                                                                             \
+      hipLaunchKernelGGL((quantize_tiles_kernel<B, GS>), dim3(static_cast<unsigned>(tile_blocks)), block, 0, \
+                         stream, c, k, v, slots, n_new, rows_per_token, g.hblock, rot_c);                  \
+    else                                                                                                   \
+      hipLaunchKernelGGL((quantize_append_kernel<B, GS>), grid, block, 0, stream, c, k, v, slots, n_rows, \
+                         rows_per_token, g.hblock, rot_c);                                                  \
     if (c.v_grouping) {                                                                                    \
       const int64_t units = n_new / GS * g.hkv;                                                            \
       if (units > 0)                                                                                       \
