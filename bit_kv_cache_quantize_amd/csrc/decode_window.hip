@@ -70,9 +70,12 @@ __global__ __launch_bounds__(kWThreads) void decode_window_kernel(DecodeArgs a, 
   const int tid = threadIdx.x;
   const int lane16 = tid & 15, grp = tid >> 4;
   const int64_t rows = static_cast<int64_t>(b) * (S + RW);
+  // window row of every window token, computed once (the ring index is a modulo)
+  __shared__ uint16_t wrow_s[kMaxWindow];
+  for (int i = tid; i < n; i += kWThreads) wrow_s[i] = static_cast<uint16_t>(i < ns ? i : S + (rbeg + (i - ns) - S) % RW);
+  __syncthreads();
   auto row_of = [&](int i) -> int64_t {  // element offset of this lane's 8 channels
-    const int wr = i < ns ? i : S + (rbeg + (i - ns) - S) % RW;
-    return ((rows + wr) * hkv + hk) * kD + 8 * lane16;
+    return ((rows + wrow_s[i]) * hkv + hk) * kD + 8 * lane16;
   };
 
   // the R query heads, channels 8 lane16 .. 8 lane16 + 7, scaled
@@ -95,18 +98,21 @@ __global__ __launch_bounds__(kWThreads) void decode_window_kernel(DecodeArgs a, 
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
   }
 
-  for (int i0 = grp; i0 < n; i0 += kGroups * kNB) {
-    uint4 kr[kNB], vr[kNB];
+  // rounds of NB tokens per group: kNB while at least kNB remain, then pairs, so that at
+  // most one token slot per group is idle
+  auto round = [&](int i0, auto nb) {
+    constexpr int NB = decltype(nb)::value;
+    uint4 kr[NB], vr[NB];
 #pragma unroll
-    for (int u = 0; u < kNB; ++u) {  // every load of the round in flight together
+    for (int u = 0; u < NB; ++u) {  // every load of the round in flight together
       const int i = i0 + kGroups * u;
       const int64_t off = row_of(i < n ? i : i0);
       kr[u] = *reinterpret_cast<const uint4*>(w.k + off);
       vr[u] = *reinterpret_cast<const uint4*>(w.v + off);
     }
-    float s[R][kNB];
+    float s[R][NB];
 #pragma unroll
-    for (int u = 0; u < kNB; ++u) {
+    for (int u = 0; u < NB; ++u) {
       float k[8];
       bf16x8(kr[u], k);
 #pragma unroll
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(kWThreads) void decode_window_kernel(DecodeArgs a, 
     for (int j = 0; j < R; ++j) {
       float mn = m[j];
 #pragma unroll
-      for (int u = 0; u < kNB; ++u) mn = fmaxf(mn, s[j][u]);  // finite: token i0 is valid
+      for (int u = 0; u < NB; ++u) mn = fmaxf(mn, s[j][u]);  // finite: token i0 is valid
       const float alpha = exp2f(m[j] - mn);                   // 0 on the first round
       l[j] *= alpha;
 #pragma unroll
@@ -130,7 +136,7 @@ __global__ __launch_bounds__(kWThreads) void decode_window_kernel(DecodeArgs a, 
       m[j] = mn;
     }
 #pragma unroll
-    for (int u = 0; u < kNB; ++u) {
+    for (int u = 0; u < NB; ++u) {
       float v[8];
       bf16x8(vr[u], v);
 #pragma unroll
@@ -141,7 +147,10 @@ __global__ __launch_bounds__(kWThreads) void decode_window_kernel(DecodeArgs a, 
         for (int e = 0; e < 8; ++e) acc[j][e] = __builtin_fmaf(p, v[e], acc[j][e]);
       }
     }
-  }
+  };
+  int i0 = grp;
+  for (; i0 + kGroups * (kNB - 1) < n; i0 += kGroups * kNB) round(i0, std::integral_constant<int, kNB>{});
+  for (; i0 < n; i0 += kGroups * 2) round(i0, std::integral_constant<int, 2>{});
 
   // merge the groups (a group without tokens has m = -inf, l = 0, o = 0)
 #pragma unroll
