@@ -158,38 +158,41 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
   }
 }
 
-// Log-sum-exp merge of the partials of one (sequence, query head): thread i owns
-// channel i and reads each partial's (m, l) and o[i], 16 partials per round trip. The
-// partials present are the split kernel's partitions that hold tokens of the covered
+// Log-sum-exp merge of the partials of one (sequence, query head). The workgroup has
+// 128 * NGRP threads: group gp (threads 128 gp .. 128 gp + 127, thread = channel) merges
+// partials gp, gp + NGRP, ... 16 at a time (one pass, every load of a chunk issued
+// together: the running reference M moves up chunk by chunk and rescales (L, o) like the
+// online softmax inside a partition); the groups' (M, L, o) are then merged through LDS.
+// The partials present are the split kernel's partitions that hold tokens of the covered
 // span, then (with windows) the window partial in slot num_splits.
-__global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ partials,
-                                                      const int32_t* __restrict__ seq_lens, int num_q_heads,
-                                                      int num_splits, int split_len, int tok_begin, int tok_tail,
-                                                      int tail_mod, int part_stride, int window,
-                                                      float* __restrict__ out) {
+template <int NGRP>
+__global__ __launch_bounds__(128 * NGRP) void combine_kernel(const float* __restrict__ partials,
+                                                             const int32_t* __restrict__ seq_lens, int num_q_heads,
+                                                             int num_splits, int split_len, int tok_begin,
+                                                             int tok_tail, int tail_mod, int part_stride, int window,
+                                                             float* __restrict__ out) {
   constexpr int kD = 128;
   constexpr int kChunk = 16;
+  __shared__ float o_s[NGRP][kD];
+  __shared__ float ml_s[NGRP][2];
   const int bj = blockIdx.x;
   const int b = bj / num_q_heads;
-  const int i = threadIdx.x;
+  const int gp = threadIdx.x / kD, i = threadIdx.x % kD;
   const int T = seq_lens[b];
   if (T <= 0) {
-    out[static_cast<int64_t>(bj) * kD + i] = 0.f;
+    if (gp == 0) out[static_cast<int64_t>(bj) * kD + i] = 0.f;
     return;
   }
   const int span = (tail_mod ? T - T % tail_mod : max(tok_begin, T - tok_tail)) - tok_begin;
   const int nq = min(num_splits, (span + split_len - 1) / split_len);
   const int ns = nq + window;  // >= 1: a sequence with T > 0 has a split or window token
   const float* base = partials + static_cast<int64_t>(bj) * part_stride * (kD + 2);
-  // one pass, kChunk partials at a time, every load of a chunk issued together: the
-  // running reference M moves up chunk by chunk and rescales (L, o) exactly like the
-  // online softmax inside a partition
   float M = -INFINITY, L = 0.f, o = 0.f;
-  for (int s0 = 0; s0 < ns; s0 += kChunk) {
+  for (int s0 = gp; s0 < ns; s0 += kChunk * NGRP) {
     float m[kChunk], l[kChunk], v[kChunk];
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) {
-      const int idx = s0 + k;
+      const int idx = s0 + k * NGRP;
       const bool ok = idx < ns;
       const float* p = base + (idx < nq ? idx : num_splits) * (kD + 2);
       m[k] = ok ? p[kD] : -INFINITY;
@@ -199,6 +202,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
     float Mn = M;
 #pragma unroll
     for (int k = 0; k < kChunk; ++k) Mn = fmaxf(Mn, m[k]);
+    if (Mn == -INFINITY) continue;  // only empty partials so far (an empty window residual)
     const float r = exp2f(M - Mn);  // 0 on the first chunk (M = -inf), 1 when M holds
     L *= r;
     o *= r;
@@ -210,7 +214,29 @@ __global__ __launch_bounds__(128) void combine_kernel(const float* __restrict__ 
     }
     M = Mn;
   }
-  out[static_cast<int64_t>(bj) * kD + i] = o / L;
+  if (NGRP == 1) {
+    out[static_cast<int64_t>(bj) * kD + i] = o / L;
+    return;
+  }
+  o_s[gp][i] = o;
+  if (i == 0) {
+    ml_s[gp][0] = M;
+    ml_s[gp][1] = L;
+  }
+  __syncthreads();
+  if (gp == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < NGRP; ++g) Mt = fmaxf(Mt, ml_s[g][0]);
+    float Lt = 0.f, ot = 0.f;
+#pragma unroll
+    for (int g = 0; g < NGRP; ++g) {
+      const float w = exp2f(ml_s[g][0] - Mt);  // 0 for a group without partials
+      Lt = __builtin_fmaf(ml_s[g][1], w, Lt);
+      ot = __builtin_fmaf(o_s[g][i], w, ot);
+    }
+    out[static_cast<int64_t>(bj) * kD + i] = ot / Lt;
+  }
 }
 
 }  // namespace
@@ -232,10 +258,21 @@ hipError_t launch_decode_split_reference(const DecodeArgs& a, const Geometry& g,
 
 hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t stream) {
   (void)g;
-  dim3 grid(static_cast<unsigned>(a.batch * a.num_q_heads)), block(128);
-  hipLaunchKernelGGL(combine_kernel, grid, block, 0, stream, a.partials, a.seq_lens, a.num_q_heads, a.num_splits,
-                     a.split_len, a.tok_begin, a.tok_tail, a.tail_mod, a.part_stride, a.window, a.out);
-  return hipGetLastError();
+  // one group of 128 threads per 32 partials, up to 8 groups (long sequences in many
+  // partitions merge in parallel)
+  const int parts = a.num_splits + a.window;
+  const int ngrp = parts > 128 ? 8 : parts > 64 ? 4 : parts > 32 ? 2 : 1;
+  dim3 grid(static_cast<unsigned>(a.batch * a.num_q_heads));
+#define KVQ_CB(NG)                                                                                          \
+  if (ngrp == NG) {                                                                                         \
+    hipLaunchKernelGGL(combine_kernel<NG>, grid, dim3(128 * NG), 0, stream, a.partials, a.seq_lens,          \
+                       a.num_q_heads, a.num_splits, a.split_len, a.tok_begin, a.tok_tail, a.tail_mod,       \
+                       a.part_stride, a.window, a.out);                                                     \
+    return hipGetLastError();                                                                               \
+  }
+  KVQ_CB(1) KVQ_CB(2) KVQ_CB(4) KVQ_CB(8)
+#undef KVQ_CB
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvq
