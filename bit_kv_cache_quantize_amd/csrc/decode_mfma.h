@@ -155,16 +155,32 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   const DevCache& c = a.c;
   const int lane = threadIdx.x;
   const int unit = blockIdx.x;
-  const int split = unit % a.num_splits;
-  const int bh = unit / a.num_splits;
-  const int hk = bh % c.hkv;
-  const int b = bh / c.hkv;
+  // this unit's (sequence, kv head, partition); `slot` indexes its partials
+  int b, hk, split, split_len;
+  int64_t slot;
+  if (a.balanced) {
+    hk = unit % c.hkv;
+    const int u = unit / c.hkv;
+    split_len = balanced_len(a, lane);
+    const PlanPart pp = balanced_part(a, u, split_len, lane);
+    if (pp.b < 0) return;  // past the batch's last partition
+    b = pp.b;
+    split = pp.p;
+    slot = static_cast<int64_t>(hk) * R * a.unit_slots + u;
+  } else {
+    split = unit % a.num_splits;
+    const int bh = unit / a.num_splits;
+    hk = bh % c.hkv;
+    b = bh / c.hkv;
+    split_len = a.split_len;
+    slot = (static_cast<int64_t>(b) * a.num_q_heads + hk * R) * a.num_splits + split;
+  }
   const int T = a.seq_lens[b];
   // the span this kernel covers ends here (with a residual: at the last whole group)
-  const int qend = a.tail_mod ? T - T % a.tail_mod : max(a.tok_begin, T - a.tok_tail);
-  const int start = a.tok_begin + split * a.split_len;
+  const int qend = covered_end(a, T);
+  const int start = a.tok_begin + split * split_len;
   if (start >= qend) return;
-  const int end = min(qend, start + a.split_len);
+  const int end = min(qend, start + split_len);
 
   __shared__ float o_s[4][128];  // partial outputs, staged for the workspace stores
   __shared__ float p_s[NBS][4][32];  // p of a super-block's blocks, per head and token
@@ -741,9 +757,8 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   }
   zacc += __shfl_xor(zacc, 16, 64);
   zacc += __shfl_xor(zacc, 32, 64);  // every lane r16 now holds Z of row (jjV, gV)
-  float* part = a.partials + (static_cast<int64_t>(b) * a.num_q_heads + hk * R) * a.part_stride * 130 +
-                static_cast<int64_t>(split) * 130;
-  const int64_t head_stride = static_cast<int64_t>(a.part_stride) * 130;
+  float* part = a.partials + slot * 130;
+  const int64_t head_stride = static_cast<int64_t>(a.balanced ? a.unit_slots : a.num_splits) * 130;
   // lane (q4, r16) owns accumulator rows 4*q4 + r = (jj = r, g = q4) at column r16; the
   // rows of group q4 hold head jj's output for the channels of that group. Staged in LDS
   // so the workspace is written with 8-byte stores.

@@ -5,7 +5,7 @@
 namespace kvq {
 
 hipError_t launch_decode_split_pruned(const DecodeArgs& a, const Geometry& g, hipStream_t stream) {
-  const int64_t units = static_cast<int64_t>(a.batch) * g.hkv * a.num_splits;
+  const int64_t units = split_units(a, g);
   if (units > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(units)), block(64);
 #define KVQ_DM(B, GS, RR)                                                                              \

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
   const int b = bh / c.hkv;
   const int T = a.seq_lens[b];
   // the span this kernel covers ends here (with a residual: at the last whole group)
-  const int qend = a.tail_mod ? T - T % a.tail_mod : max(a.tok_begin, T - a.tok_tail);
+  const int qend = covered_end(a, T);
   const int start = a.tok_begin + split * a.split_len;
   if (start >= qend) return;
   const int end = min(qend, start + a.split_len);
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
                                         f16_bits_to_float(m >> 16));
       o = __builtin_fmaf(sc[j][t - start], vhat, o);
     }
-    float* part = a.partials + ((static_cast<int64_t>(b) * a.num_q_heads + h * R + j) * a.part_stride + split) * (kD + 2);
+    float* part = a.partials + ((static_cast<int64_t>(b) * a.num_q_heads + h * R + j) * a.num_splits + split) * (kD + 2);
     part[i] = o;
     if (i == 0) {
       part[kD] = stat[0][j];
@@ -164,29 +164,47 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
 // together: the running reference M moves up chunk by chunk and rescales (L, o) like the
 // online softmax inside a partition); the groups' (M, L, o) are then merged through LDS.
 // The partials present are the split kernel's partitions that hold tokens of the covered
-// span, then (with windows) the window partial in slot num_splits.
+// span (fixed partitions: slots 0.. of the sequence's row; balanced: the sequence's units,
+// found from the same plan the split kernel computed), then (with windows) the window
+// partial.
 template <int NGRP>
-__global__ __launch_bounds__(128 * NGRP) void combine_kernel(const float* __restrict__ partials,
-                                                             const int32_t* __restrict__ seq_lens, int num_q_heads,
-                                                             int num_splits, int split_len, int tok_begin,
-                                                             int tok_tail, int tail_mod, int part_stride, int window,
-                                                             float* __restrict__ out) {
+__global__ __launch_bounds__(128 * NGRP) void combine_kernel(DecodeArgs a) {
   constexpr int kD = 128;
   constexpr int kChunk = 16;
   __shared__ float o_s[NGRP][kD];
   __shared__ float ml_s[NGRP][2];
+  __shared__ int plan_s[2];
   const int bj = blockIdx.x;
-  const int b = bj / num_q_heads;
+  const int b = bj / a.num_q_heads, j = bj % a.num_q_heads;
   const int gp = threadIdx.x / kD, i = threadIdx.x % kD;
-  const int T = seq_lens[b];
+  const int T = a.seq_lens[b];
   if (T <= 0) {
-    if (gp == 0) out[static_cast<int64_t>(bj) * kD + i] = 0.f;
+    if (gp == 0) a.out[static_cast<int64_t>(bj) * kD + i] = 0.f;
     return;
   }
-  const int span = (tail_mod ? T - T % tail_mod : max(tok_begin, T - tok_tail)) - tok_begin;
-  const int nq = min(num_splits, (span + split_len - 1) / split_len);
-  const int ns = nq + window;  // >= 1: a sequence with T > 0 has a split or window token
-  const float* base = partials + static_cast<int64_t>(bj) * part_stride * (kD + 2);
+  const int span = covered_span(a, T);
+  const float* base;
+  int nq;
+  if (a.balanced) {
+    if (threadIdx.x < 64) {  // wavefront 0 recomputes the plan
+      const int L = balanced_len(a, threadIdx.x);
+      const int first = balanced_first(a, b, L, threadIdx.x);
+      if (threadIdx.x == 0) {
+        plan_s[0] = first;
+        plan_s[1] = (span + L - 1) / L;
+      }
+    }
+    __syncthreads();
+    const int first = plan_s[0];
+    // units beyond the grid (seq_lens above max_seq_len) were never computed
+    nq = max(0, min(plan_s[1], a.unit_slots - first));
+    base = a.partials + (static_cast<int64_t>(j) * a.unit_slots + first) * (kD + 2);
+  } else {
+    nq = min(a.num_splits, (span + a.split_len - 1) / a.split_len);
+    base = a.partials + static_cast<int64_t>(bj) * a.num_splits * (kD + 2);
+  }
+  const int ns = nq + a.window;  // >= 1: a sequence with T > 0 has a split or window token
+  const float* win = a.window ? a.win_partials + static_cast<int64_t>(bj) * (kD + 2) : base;
   float M = -INFINITY, L = 0.f, o = 0.f;
   for (int s0 = gp; s0 < ns; s0 += kChunk * NGRP) {
     float m[kChunk], l[kChunk], v[kChunk];
@@ -194,7 +212,7 @@ __global__ __launch_bounds__(128 * NGRP) void combine_kernel(const float* __rest
     for (int k = 0; k < kChunk; ++k) {
       const int idx = s0 + k * NGRP;
       const bool ok = idx < ns;
-      const float* p = base + (idx < nq ? idx : num_splits) * (kD + 2);
+      const float* p = idx < nq ? base + idx * (kD + 2) : win;
       m[k] = ok ? p[kD] : -INFINITY;
       l[k] = ok ? p[kD + 1] : 0.f;
       v[k] = ok ? p[i] : 0.f;
@@ -215,7 +233,7 @@ __global__ __launch_bounds__(128 * NGRP) void combine_kernel(const float* __rest
     M = Mn;
   }
   if (NGRP == 1) {
-    out[static_cast<int64_t>(bj) * kD + i] = o / L;
+    a.out[static_cast<int64_t>(bj) * kD + i] = o / L;
     return;
   }
   o_s[gp][i] = o;
@@ -235,7 +253,7 @@ __global__ __launch_bounds__(128 * NGRP) void combine_kernel(const float* __rest
       Lt = __builtin_fmaf(ml_s[g][1], w, Lt);
       ot = __builtin_fmaf(o_s[g][i], w, ot);
     }
-    out[static_cast<int64_t>(bj) * kD + i] = ot / Lt;
+    a.out[static_cast<int64_t>(bj) * kD + i] = ot / Lt;
   }
 }
 
@@ -259,16 +277,15 @@ hipError_t launch_decode_split_reference(const DecodeArgs& a, const Geometry& g,
 hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t stream) {
   (void)g;
   // one group of 128 threads per 32 partials, up to 8 groups (long sequences in many
-  // partitions merge in parallel)
+  // partitions merge in parallel); balanced plans are sized for max_seq_len-long
+  // sequences (longer partition lists of a ragged batch take more passes)
   const int parts = a.num_splits + a.window;
   const int ngrp = parts > 128 ? 8 : parts > 64 ? 4 : parts > 32 ? 2 : 1;
   dim3 grid(static_cast<unsigned>(a.batch * a.num_q_heads));
-#define KVQ_CB(NG)                                                                                          \
-  if (ngrp == NG) {                                                                                         \
-    hipLaunchKernelGGL(combine_kernel<NG>, grid, dim3(128 * NG), 0, stream, a.partials, a.seq_lens,          \
-                       a.num_q_heads, a.num_splits, a.split_len, a.tok_begin, a.tok_tail, a.tail_mod,       \
-                       a.part_stride, a.window, a.out);                                                     \
-    return hipGetLastError();                                                                               \
+#define KVQ_CB(NG)                                                          \
+  if (ngrp == NG) {                                                         \
+    hipLaunchKernelGGL(combine_kernel<NG>, grid, dim3(128 * NG), 0, stream, a); \
+    return hipGetLastError();                                               \
   }
   KVQ_CB(1) KVQ_CB(2) KVQ_CB(4) KVQ_CB(8)
 #undef KVQ_CB

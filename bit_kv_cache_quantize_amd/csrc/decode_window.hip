@@ -3,7 +3,8 @@
 // InnerQ (Abstract): the attention-sink tokens and a window of recent tokens stay in
 // high precision. Here they are bf16 rows in the original basis, so the query takes no
 // rotation; its scale is the split kernels' (softmax scale * log2 e, exp2 domain), and
-// the partial (o, m, l) is merged with the quantized partitions' by the combine kernel.
+// the partial (o, m, l) goes to the window partials, merged with the quantized partitions'
+// by the combine kernel.
 //
 // One workgroup of 256 threads per (sequence, kv head), 16 groups of 16 lanes, 8
 // channels (16 bytes of a row) per lane. Group g takes window tokens g, g + 16, ...,
@@ -58,8 +59,7 @@ __global__ __launch_bounds__(kWThreads) void decode_window_kernel(DecodeArgs a, 
   if (n == 0) {  // an empty partial: m = -inf, l = 0, o = 0
     for (int idx = threadIdx.x; idx < R * (kD + 2); idx += kWThreads) {
       const int j = idx / (kD + 2), e = idx % (kD + 2);
-      a.partials[((static_cast<int64_t>(b) * a.num_q_heads + hk * R + j) * a.part_stride + a.num_splits) * (kD + 2) +
-                 e] = e == kD ? -INFINITY : 0.f;
+      a.win_partials[(static_cast<int64_t>(b) * a.num_q_heads + hk * R + j) * (kD + 2) + e] = e == kD ? -INFINITY : 0.f;
     }
     return;
   }
@@ -175,8 +175,7 @@ __global__ __launch_bounds__(kWThreads) void decode_window_kernel(DecodeArgs a, 
       o = __builtin_fmaf(red_o[g][j][ch], f, o);
       L = __builtin_fmaf(red_ml[g][j][1], f, L);
     }
-    float* part = a.partials +
-                  ((static_cast<int64_t>(b) * a.num_q_heads + hk * R + j) * a.part_stride + a.num_splits) * (kD + 2);
+    float* part = a.win_partials + (static_cast<int64_t>(b) * a.num_q_heads + hk * R + j) * (kD + 2);
     part[ch] = o;
     if (ch == 0) {
       part[kD] = M;

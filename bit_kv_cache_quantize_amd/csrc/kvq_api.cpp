@@ -61,7 +61,10 @@ DecodeArgs decode_args(const kvq_cache* cache, const Geometry& g, const void* q,
   a.tok_begin = 0;
   a.tok_tail = 0;
   a.tail_mod = 0;
-  a.part_stride = sp.num_splits;
+  a.balanced = sp.balanced;
+  a.units_per_head = sp.units_per_head;
+  a.unit_slots = sp.unit_slots;
+  a.win_partials = nullptr;
   a.window = 0;
   a.keep_chunks = 0;
   a.chunk_mask = nullptr;
@@ -236,7 +239,7 @@ kvq_status kvq_decode_attention_window(const kvq_cache* cache, const kvq_window*
   a.tok_begin = window->sink;
   a.tok_tail = window->residual ? 0 : window->recent;
   a.tail_mod = window->residual ? window->recent : 0;
-  a.part_stride = sp.num_splits + 1;
+  a.win_partials = a.partials + workspace_bytes(g, batch, num_q_heads, sp) / sizeof(float);
   a.window = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (split_kernel(a, g, s) != hipSuccess) return KVQ_ERR_HIP;

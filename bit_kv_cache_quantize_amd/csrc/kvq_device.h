@@ -109,9 +109,17 @@ struct DecodeArgs {
   // with a residual of whole groups of tail_mod tokens (else 0): the span ends at
   // T - T % tail_mod instead
   int tail_mod;
-  // partial slots per (sequence, query head): num_splits, plus one for the window
-  // partial (slot num_splits) when `window` is set
-  int part_stride;
+  // Where partials go. Fixed partitions (split_len from the host): partition p of
+  // sequence b, query head j at partials[((b * Hq + j) * num_splits + p) * (d + 2)].
+  // Balanced partitions (balanced = 1): the length L comes from the batch's total
+  // covered span on the device (balanced_len); each kv head's units u = 0, 1, ... take
+  // the partitions of sequence 0, then sequence 1, ..., and unit u of kv head hk
+  // (blockIdx = u * Hkv + hk) writes partials[(j * unit_slots + u) * (d + 2)].
+  int balanced;
+  int units_per_head;  // balanced: target partitions per kv head
+  int unit_slots;      // balanced: units per kv head in the grid, partial slots per query head
+  // window partials [batch][Hq][d + 2], when `window` is set
+  float* win_partials;
   int window;
   // query-channel pruning (pruned kernel only): key chunks kept per (sequence, kv head),
   // and where the chosen masks go ([batch][Hkv], may be null)
@@ -121,6 +129,82 @@ struct DecodeArgs {
   float rot_c;    // float nearest 1/sqrt(hblock)
   float qscale;   // softmax scale * log2(e): logits are kept in the exp2 domain
 };
+
+// ---- partition plan ----
+
+// Tokens of sequence b (seq_len T) the split kernels cover: [tok_begin, qend).
+__device__ __forceinline__ int covered_end(const DecodeArgs& a, int T) {
+  return a.tail_mod ? T - T % a.tail_mod : max(a.tok_begin, T - a.tok_tail);
+}
+__device__ __forceinline__ int covered_span(const DecodeArgs& a, int T) {
+  return T > 0 ? max(0, covered_end(a, T) - a.tok_begin) : 0;
+}
+
+// Balanced partition length: the batch's total covered span over units_per_head,
+// rounded up to whole 8-block super-blocks, within [kBalancedMinLen, kBalancedMaxLen].
+// Called by a full wavefront (lane = 0..63); every lane, every workgroup and every
+// kernel gets the same value from the same seq_lens.
+__device__ __forceinline__ int balanced_len(const DecodeArgs& a, int lane) {
+  long long w = 0;
+  for (int b = lane; b < a.batch; b += 64) w += covered_span(a, a.seq_lens[b]);
+#pragma unroll
+  for (int m = 32; m > 0; m >>= 1) w += __shfl_xor(w, m, 64);
+  long long L = (w + a.units_per_head - 1) / a.units_per_head;
+  L = (L + kBalancedMinLen - 1) / kBalancedMinLen * kBalancedMinLen;
+  // the same in every lane: made visibly uniform so what derives from it stays scalar
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<int>(L < kBalancedMinLen ? kBalancedMinLen : L > kBalancedMaxLen ? kBalancedMaxLen : L));
+}
+
+// Partitions of sequence b in a plan of length L.
+__device__ __forceinline__ int balanced_count(const DecodeArgs& a, int b, int L) {
+  return (covered_span(a, a.seq_lens[b]) + L - 1) / L;
+}
+
+// Unit u of a kv head in the balanced plan of length L: its sequence (-1 past the last
+// partition) and partition index within the sequence. Wave-uniform; a full wavefront.
+struct PlanPart {
+  int b, p;
+};
+__device__ __forceinline__ PlanPart balanced_part(const DecodeArgs& a, int u, int L, int lane) {
+  int base = 0;  // partitions of the sequences before this group of 64
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    const int n = b0 + lane < a.batch ? balanced_count(a, b0 + lane, L) : 0;
+    int incl = n;  // inclusive prefix sum over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    if (u < base + total) {
+      const unsigned long long hit = __ballot(base + incl > u);  // lane 63 is set
+      const int l = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit)));
+      return {b0 + l, u - base - __builtin_amdgcn_readlane(incl - n, l)};
+    }
+    base += total;
+  }
+  return {-1, 0};
+}
+
+// First unit and unit count of sequence b in the balanced plan of length L. A full
+// wavefront; wave-uniform.
+__device__ __forceinline__ int balanced_first(const DecodeArgs& a, int b, int L, int lane) {
+  int off = 0;
+  for (int b0 = 0; b0 < b; b0 += 64) {
+    int n = b0 + lane < b ? balanced_count(a, b0 + lane, L) : 0;
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) n += __shfl_xor(n, m, 64);
+    off += __builtin_amdgcn_readfirstlane(n);
+  }
+  return off;
+}
+
+// Workgroups of a split-K launch.
+inline int64_t split_units(const DecodeArgs& a, const Geometry& g) {
+  return a.balanced ? static_cast<int64_t>(g.hkv) * a.unit_slots
+                    : static_cast<int64_t>(a.batch) * g.hkv * a.num_splits;
+}
 
 hipError_t launch_decode_split(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_split_pruned(const DecodeArgs& a, const Geometry& g, hipStream_t stream);

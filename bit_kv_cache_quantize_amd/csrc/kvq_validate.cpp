@@ -69,10 +69,32 @@ int64_t plane_bytes(const Geometry& g, int plane) {
 Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
                      int32_t requested, int cus, SplitKernel kernel) {
   (void)num_q_heads;
-  Splits s{1, kBlock};
+  Splits s{1, kBlock, 0, 0, 0};
   const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
   const int64_t blocks = (len + kBlock - 1) / kBlock;
   const bool matrix = kernel == SplitKernel::kMatrix;
+  if (requested == 0 && matrix) {
+    // Balanced: about 16 partitions per CU over all kv heads (several waves of work per
+    // SIMD), of one length from the total span (the device recomputes it from seq_lens;
+    // here every sequence is taken as max_seq_len long).
+    const int64_t nb = batch > 0 ? batch : 1;
+    const int64_t uph = (16LL * (cus > 0 ? cus : 256) + g.hkv - 1) / g.hkv;
+    int64_t L = (nb * len + uph - 1) / uph;
+    L = (L + kBalancedMinLen - 1) / kBalancedMinLen * kBalancedMinLen;
+    L = L < kBalancedMinLen ? kBalancedMinLen : L > kBalancedMaxLen ? kBalancedMaxLen : L;
+    s.split_len = static_cast<int32_t>(L);
+    s.num_splits = static_cast<int32_t>((len + L - 1) / L);
+    s.balanced = 1;
+    s.units_per_head = static_cast<int32_t>(uph);
+    // partitions of one kv head: sum_b ceil(span_b / L) <= total / L + batch, where
+    // total / L <= uph unless L is held at kBalancedMaxLen, and every span <= len
+    const int64_t most = (nb * len + kBalancedMaxLen - 1) / kBalancedMaxLen;
+    int64_t slots = (most > uph ? most : uph) + nb;
+    const int64_t cap = nb * ((len + kBalancedMinLen - 1) / kBalancedMinLen);
+    if (slots > cap) slots = cap;
+    s.unit_slots = static_cast<int32_t>(slots);
+    return s;
+  }
   int64_t n;
   int64_t per;  // blocks per partition
   if (requested > 0) {
@@ -102,6 +124,7 @@ Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int3
 }
 
 size_t workspace_bytes(const Geometry& g, int32_t batch, int32_t num_q_heads, const Splits& s) {
+  if (s.balanced) return static_cast<size_t>(num_q_heads) * s.unit_slots * (g.d + 2) * sizeof(float);
   return static_cast<size_t>(batch) * num_q_heads * s.num_splits * (g.d + 2) * sizeof(float);
 }
 
@@ -182,7 +205,8 @@ int32_t window_span(const kvq_window* w, int32_t max_seq_len) {
 }
 
 size_t window_workspace_bytes(const Geometry& g, int32_t batch, int32_t num_q_heads, const Splits& s) {
-  return static_cast<size_t>(batch) * num_q_heads * (s.num_splits + 1) * (g.d + 2) * sizeof(float);
+  return workspace_bytes(g, batch, num_q_heads, s) +
+         static_cast<size_t>(batch) * num_q_heads * (g.d + 2) * sizeof(float);
 }
 
 kvq_status check_dequantize(const kvq_cache* c, int32_t which, const int64_t* slots, int64_t n,

@@ -31,10 +31,21 @@ bool aligned(const void* p, size_t a);
 int64_t plane_bytes(const Geometry& g, int plane);
 
 // Split-K sizing. `cus` is the device's compute-unit count (256 on MI355X).
+// Fixed partitions: every sequence is cut into split_len-token partitions (a caller's
+// num_splits, and the reference kernel). Balanced partitions (the matrix kernels'
+// automatic choice): one length for the whole batch, chosen on the device from the
+// total covered span so that every kv head gets about units_per_head partitions of equal
+// length whatever the mix of sequence lengths; num_splits and split_len then describe a
+// batch whose sequences all have max_seq_len tokens.
 struct Splits {
   int32_t num_splits;  // partitions of a max_seq_len sequence
   int32_t split_len;   // tokens per partition, a multiple of kBlock
+  int32_t balanced;
+  int32_t units_per_head;  // balanced: target partitions per kv head
+  int32_t unit_slots;      // balanced: bound on the partitions of one kv head (grid units)
 };
+constexpr int kBalancedMinLen = 256;   // 8 blocks
+constexpr int kBalancedMaxLen = 4096;  // 128 blocks
 // Automatic choices differ per decode kernel: the matrix-core kernel takes partitions of
 // up to 128 blocks in whole 8-block super-blocks; the plain reference kernel keeps a
 // partition's scores in LDS and takes at most 64 blocks.

@@ -147,22 +147,35 @@ def test_dequantize_argument_checks():
     assert L.kvq_dequantize(ctypes.byref(d), 1, None, 0, None, None) == kvq.OK
 
 
+def _balanced_slots(B, T, cus=256, hkv=8):
+    """Units per kv head the balanced plan's grid holds: at most total / L + B partitions,
+    total / L <= 16 * CUs / Hkv unless L is held at 4096 tokens; at most B * ceil(T / 256)."""
+    uph = -(-16 * cus // hkv)
+    n = max(T, 1)
+    return min(B * -(-n // 256), max(uph, -(-(B * n) // 4096)) + B)
+
+
 def test_split_sizing_and_workspace():
-    """Automatic split-K sizing: whole 32-token blocks, 256..4096 tokens per partition in
-    whole 8-block super-blocks for the matrix kernel (the reference kernel: at most 2048),
-    and the workspace formula [B][Hq][S][d+2] fp32 for the larger of the two choices.
+    """Automatic split-K sizing. The matrix kernel's partitions are balanced: one length
+    for the batch, 256..4096 tokens in whole 8-block super-blocks, from the total span over
+    16 partitions per CU (reported for a batch of max_seq_len sequences); its workspace is
+    [Hq][units per kv head][d+2] fp32. The reference kernel keeps fixed partitions of at
+    most 2048 tokens, workspace [B][Hq][S][d+2]; the automatic size covers both.
     (Off a GPU the library assumes 256 compute units, the MI355X count.)"""
     L = kvq.lib()
     d = _desc(page_size=32768, num_pages=64)
     cases = {  # (B, T) -> (matrix splits, reference splits)
-        (64, 32768): (8, 16),   # 512 units: 4096-token partitions (2048 for the reference)
-        (16, 8192): (32, 32),   # 128 units x 32, 256-token partitions
+        (64, 32768): (8, 16),   # 4096-token partitions (2048 for the reference)
+        (16, 8192): (32, 32),   # 256-token partitions
         (1, 1024): (4, 4),
-        (3, 5000): (20, 18),    # 157 blocks: 8 per partition (9 for the reference)
+        (3, 5000): (20, 18),    # 256-token partitions (9 blocks for the reference)
     }
     for (B, T), (want, want_ref) in cases.items():
         assert L.kvq_decode_num_splits(ctypes.byref(d), B, 32, T, 0) == want
-        assert L.kvq_decode_workspace_bytes(ctypes.byref(d), B, 32, T, 0) == B * 32 * max(want, want_ref) * 130 * 4
+        balanced = 32 * _balanced_slots(B, T) * 130 * 4
+        assert L.kvq_decode_workspace_bytes(ctypes.byref(d), B, 32, T, 0) == max(balanced, B * 32 * want_ref * 130 * 4)
+    # an explicit count: fixed partitions for both kernels
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 4, 32, 8192, 6) == 4 * 32 * 6 * 130 * 4
     d3 = _desc(group_size=64, page_size=131072, num_pages=1)
     assert L.kvq_decode_num_splits(ctypes.byref(d3), 1, 32, 131072, 0) >= 256
     # explicit requests are honoured up to one partition per 32-token block
@@ -216,11 +229,14 @@ def test_window_sizes():
     assert L.kvq_window_plane_bytes(ctypes.byref(d), ctypes.byref(w)) == 3 * 128 * 8 * 128 * 2
     assert L.kvq_window_plane_bytes(ctypes.byref(d), ctypes.byref(_win(recent=0))) == -1
     # the split count follows the quantized span (max_seq_len - sink - recent), plus one
-    # partial for the windows
+    # window partial per (sequence, query head)
     for B, T in ((64, 32768), (3, 5000), (2, 100)):
         span = max(T - 128, 0)
-        s = L.kvq_decode_num_splits(ctypes.byref(d), B, 32, span, 0)
+        slots = _balanced_slots(B, span)
         assert L.kvq_decode_window_workspace_bytes(ctypes.byref(d), ctypes.byref(w), B, 32, T, 0) == \
+            (32 * slots + B * 32) * 130 * 4
+        s = L.kvq_decode_num_splits(ctypes.byref(d), B, 32, span, 5)
+        assert L.kvq_decode_window_workspace_bytes(ctypes.byref(d), ctypes.byref(w), B, 32, T, 5) == \
             B * 32 * (s + 1) * 130 * 4
     assert L.kvq_decode_window_workspace_bytes(ctypes.byref(d), ctypes.byref(_win(sink=8)), 1, 32, 100, 0) == 0
 

@@ -175,6 +175,40 @@ def test_decode_split_count_independence():
         assert dev <= 1e-4
 
 
+BALANCED_CASES = {
+    # more than 64 sequences: the plan's prefix sums run over several groups of 64
+    "b70_ragged_zeros": (_small("c5", batch=70, ragged=(0, 400)), None),
+    "b130_short": (_small("c5", batch=130, ragged=(1, 120)), None),
+    # one long sequence among short and empty ones: it takes most partitions
+    "dominant": (_small("c5", batch=5, ragged=(1, 9000)), [9000, 3, 0, 40, 700]),
+    # every sequence empty but one token
+    "single_token": (_small("c5", batch=3, ragged=(0, 1)), [0, 1, 0]),
+}
+
+
+@pytest.mark.parametrize("name", list(BALANCED_CASES))
+def test_decode_balanced_plan_ragged_batches(name):
+    """Automatic partitions are planned on the device from the batch's lengths (one length
+    for all sequences, each sequence's partitions found by prefix sums); the result must
+    match the oracle and a fixed-partition decode of the same cache."""
+    w, lens = BALANCED_CASES[name]
+    lens = wl.seq_lens(w) if lens is None else torch.tensor(lens, dtype=torch.int32)
+    if name == "b70_ragged_zeros":
+        lens[::9] = 0
+    print(f"[decode] balanced plan {name}: B={w.batch} lens sum {int(lens.sum())} max {int(lens.max())}", flush=True)
+    p = make_pair(w, DEV, lens=lens)
+    q = wl.queries(w)
+    got, want = decode_both(p, DEV, q=q)
+    err = max_err(got, want)
+    record(f"balanced/{name}", err)
+    print(f"  max-abs err {err:.3e}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert err <= TOL
+    assert np.all(got[lens.numpy() == 0] == 0)
+    fixed, _ = decode_both(p, DEV, q=q, num_splits=3)
+    assert float(np.max(np.abs(got - fixed))) <= 1e-4
+
+
 def test_decode_page_permutation_invariance():
     """Same logical content under two different physical page placements."""
     print("[decode] page permutation", flush=True)
