@@ -137,16 +137,27 @@ kvq_status kvq_quantize_append(const kvq_cache* cache, const void* k_new, const 
 
 /*
  * Workspace bytes kvq_decode_attention (and kvq_decode_attention_reference) need for
- * these sizes: fp32 split partials [batch][num_q_heads][splits][d + 2]. num_splits 0 =
- * the library's choice, made the same way for the same arguments on the same device
- * (up to 4096 tokens per partition for kvq_decode_attention, up to 2048 for the
- * reference kernel; the size covers both). Returns 0 for an invalid description.
+ * these sizes. num_splits > 0 (fixed partitions): fp32 split partials
+ * [batch][num_q_heads][splits][d + 2]. num_splits 0 = the library's choice, made the
+ * same way for the same arguments on the same device: kvq_decode_attention then plans
+ * balanced partitions on the device (below), partials [num_q_heads][U][d + 2] with U a
+ * bound on one kv head's partitions; the reference kernel takes fixed partitions of up
+ * to 2048 tokens; the size covers both. Returns 0 for an invalid description.
+ *
+ * Balanced partitions (kvq_decode_attention, _timed, _pruned and _window with
+ * num_splits 0): one partition length L for the whole call, computed on the device
+ * from seq_lens: L = the total covered span of the batch divided by 16 * CUs / Hkv,
+ * rounded up to a multiple of 256 tokens, within [256, 4096]; sequence b gets
+ * ceil(span_b / L) partitions. Equal-length partitions keep the GPU evenly loaded
+ * whatever the mix of sequence lengths, with no host-side knowledge of the lengths.
  */
 size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
                                   int32_t max_seq_len, int32_t num_splits);
 
 /* The number of split-K partitions (per sequence of max_seq_len tokens) that
-   kvq_decode_attention uses with these arguments; 0 for an invalid description. */
+   kvq_decode_attention uses with these arguments; with num_splits 0, the count for a
+   batch whose sequences all have max_seq_len tokens (a ragged batch's long sequences
+   get more, shorter partitions). 0 for an invalid description. */
 int32_t kvq_decode_num_splits(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
                               int32_t max_seq_len, int32_t num_splits);
 
@@ -157,10 +168,14 @@ int32_t kvq_decode_num_splits(const kvq_cache* cache, int32_t batch, int32_t num
  *                 kernel applies the keys' rotation to it (Dual-QK, Abstract).
  *   block_table : int32 [batch][max_pages_per_seq], physical page of each logical page.
  *   seq_lens    : int32 [batch] on the device: tokens to attend (0 gives a zero row).
- *   max_seq_len : host upper bound of seq_lens, used to size the split-K grid.
+ *   max_seq_len : host upper bound of seq_lens, used to size the split-K grid
+ *                 (seq_lens above it give undefined output rows, but no access outside
+ *                 the buffers).
  *   softmax_scale: 0 means 1/sqrt(d).
- *   num_splits  : 0 = automatic; otherwise the number of token partitions of a
- *                 max_seq_len sequence (rounded to the kernel's 32-token granularity).
+ *   num_splits  : 0 = automatic (balanced partitions planned on the device, see
+ *                 kvq_decode_workspace_bytes); otherwise the number of token partitions
+ *                 of a max_seq_len sequence (rounded to the kernel's 32-token
+ *                 granularity), the same length for every sequence.
  *   workspace   : device scratch of at least kvq_decode_workspace_bytes() bytes,
  *                 16-byte aligned; overwritten.
  *   out         : fp32 [batch][num_q_heads][d]:
@@ -285,8 +300,9 @@ kvq_status kvq_window_append(const kvq_cache* cache, const kvq_window* window, c
                              const void* v_new, const int32_t* seqs, const int32_t* positions,
                              const int64_t* evict_slots, int64_t n_new, void* stream);
 
-/* Workspace bytes of kvq_decode_attention_window: fp32 partials
-   [batch][num_q_heads][splits + 1][d + 2]; 0 for an invalid description. */
+/* Workspace bytes of kvq_decode_attention_window: the split partials of the quantized
+   span (as kvq_decode_workspace_bytes describes, for the matrix kernel), then the window
+   partials [batch][num_q_heads][d + 2] fp32; 0 for an invalid description. */
 size_t kvq_decode_window_workspace_bytes(const kvq_cache* cache, const kvq_window* window, int32_t batch,
                                          int32_t num_q_heads, int32_t max_seq_len, int32_t num_splits);
 
