@@ -219,7 +219,14 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     int blk, pg, off, wbase;
     int32_t bt_w;
   };
-  auto window = [&](int first) -> int32_t { return (first + lane <= pg_last) ? bt[first + lane] : 0; };
+  // The refill is consumed where it is loaded: a load still pending where a refilled and a
+  // kept window meet would make every later lookup wait for all loads in flight (the
+  // prefetched blocks included), not just for this one.
+  auto window = [&](int first) -> int32_t {
+    int32_t w = (first + lane <= pg_last) ? bt[first + lane] : 0;
+    asm volatile("" : "+v"(w));
+    return w;
+  };
   const Cursor cur0 = {0, pg_first, start - pg_first * P, pg_first, one_page ? 0 : window(pg_first)};
   auto page_row = [&](Cursor& cu, int pg, int off) -> int64_t {  // row of token pg * P + off
     if (pg - cu.wbase >= 64) {  // a cursor visits pages in increasing order
