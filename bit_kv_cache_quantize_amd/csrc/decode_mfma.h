@@ -156,16 +156,17 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   const int lane = threadIdx.x;
   const int unit = blockIdx.x;
   // this unit's (sequence, kv head, partition); `slot` indexes its partials
-  int b, hk, split, split_len;
+  int b, hk, split, split_len, T;
   int64_t slot;
   if (a.balanced) {
     hk = unit % c.hkv;
     const int u = unit / c.hkv;
-    split_len = balanced_len(a, lane);
-    const PlanPart pp = balanced_part(a, u, split_len, lane);
-    if (pp.b < 0) return;  // past the batch's last partition
-    b = pp.b;
-    split = pp.p;
+    const PlanUnit pu = balanced_unit(a, u, lane);
+    if (pu.b < 0) return;  // past the batch's last partition
+    b = pu.b;
+    split = pu.p;
+    split_len = pu.L;
+    T = pu.T;
     slot = static_cast<int64_t>(hk) * R * a.unit_slots + u;
   } else {
     split = unit % a.num_splits;
@@ -173,9 +174,9 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     hk = bh % c.hkv;
     b = bh / c.hkv;
     split_len = a.split_len;
+    T = a.seq_lens[b];
     slot = (static_cast<int64_t>(b) * a.num_q_heads + hk * R) * a.num_splits + split;
   }
-  const int T = a.seq_lens[b];
   // the span this kernel covers ends here (with a residual: at the last whole group)
   const int qend = covered_end(a, T);
   const int start = a.tok_begin + split * split_len;

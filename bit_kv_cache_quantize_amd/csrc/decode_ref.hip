@@ -187,11 +187,10 @@ __global__ __launch_bounds__(128 * NGRP) void combine_kernel(DecodeArgs a) {
   int nq;
   if (a.balanced) {
     if (threadIdx.x < 64) {  // wavefront 0 recomputes the plan
-      const int L = balanced_len(a, threadIdx.x);
-      const int first = balanced_first(a, b, L, threadIdx.x);
+      const PlanSeq ps = balanced_seq(a, b, threadIdx.x);
       if (threadIdx.x == 0) {
-        plan_s[0] = first;
-        plan_s[1] = (span + L - 1) / L;
+        plan_s[0] = ps.first;
+        plan_s[1] = (span + ps.L - 1) / ps.L;
       }
     }
     __syncthreads();

@@ -112,9 +112,9 @@ struct DecodeArgs {
   // Where partials go. Fixed partitions (split_len from the host): partition p of
   // sequence b, query head j at partials[((b * Hq + j) * num_splits + p) * (d + 2)].
   // Balanced partitions (balanced = 1): the length L comes from the batch's total
-  // covered span on the device (balanced_len); each kv head's units u = 0, 1, ... take
-  // the partitions of sequence 0, then sequence 1, ..., and unit u of kv head hk
-  // (blockIdx = u * Hkv + hk) writes partials[(j * unit_slots + u) * (d + 2)].
+  // covered span on the device (the balanced plan below); each kv head's units
+  // u = 0, 1, ... take the partitions of sequence 0, then sequence 1, ..., and unit u of
+  // kv head hk (blockIdx = u * Hkv + hk) writes partials[(j * unit_slots + u) * (d + 2)].
   int balanced;
   int units_per_head;  // balanced: target partitions per kv head
   int unit_slots;      // balanced: units per kv head in the grid, partial slots per query head
@@ -140,64 +140,92 @@ __device__ __forceinline__ int covered_span(const DecodeArgs& a, int T) {
   return T > 0 ? max(0, covered_end(a, T) - a.tok_begin) : 0;
 }
 
-// Balanced partition length: the batch's total covered span over units_per_head,
-// rounded up to whole 8-block super-blocks, within [kBalancedMinLen, kBalancedMaxLen].
-// Called by a full wavefront (lane = 0..63); every lane, every workgroup and every
-// kernel gets the same value from the same seq_lens.
-__device__ __forceinline__ int balanced_len(const DecodeArgs& a, int lane) {
-  long long w = 0;
-  for (int b = lane; b < a.batch; b += 64) w += covered_span(a, a.seq_lens[b]);
-#pragma unroll
-  for (int m = 32; m > 0; m >>= 1) w += __shfl_xor(w, m, 64);
-  long long L = (w + a.units_per_head - 1) / a.units_per_head;
-  L = (L + kBalancedMinLen - 1) / kBalancedMinLen * kBalancedMinLen;
-  // the same in every lane: made visibly uniform so what derives from it stays scalar
-  return __builtin_amdgcn_readfirstlane(
-      static_cast<int>(L < kBalancedMinLen ? kBalancedMinLen : L > kBalancedMaxLen ? kBalancedMaxLen : L));
+// Balanced plan, in units of 256 tokens (kBalancedMinLen): c_b = ceil(span_b / 256),
+// C = sum_b c_b; the partition length is L = 256 k with k = ceil(C / units_per_head)
+// within [1, 16] (at most kBalancedMaxLen tokens), and sequence b gets ceil(c_b / k)
+// partitions, the same as ceil(span_b / L). Every function below runs on a full
+// wavefront (lane = 0..63, all active) and returns wave-uniform values (made visibly
+// uniform, so what derives from them stays scalar); every workgroup and kernel gets the
+// same plan from the same seq_lens. Lane l keeps seq_lens[l] (the first 64 sequences)
+// from a single load.
+static_assert(kBalancedMaxLen == 16 * kBalancedMinLen, "the plan's k runs over 1..16");
+
+// Inclusive prefix sum over the 64 lanes: DPP row shifts (zeros shifted in) within each
+// row of 16 lanes, then the totals of the rows below.
+template <int CTRL>
+__device__ __forceinline__ int dpp_shifted(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+  x += dpp_shifted<0x111>(x);  // row_shr:1
+  x += dpp_shifted<0x112>(x);  // row_shr:2
+  x += dpp_shifted<0x114>(x);  // row_shr:4
+  x += dpp_shifted<0x118>(x);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
-// Partitions of sequence b in a plan of length L.
-__device__ __forceinline__ int balanced_count(const DecodeArgs& a, int b, int L) {
-  return (covered_span(a, a.seq_lens[b]) + L - 1) / L;
+__device__ __forceinline__ int span_units(const DecodeArgs& a, int T) {
+  return (covered_span(a, T) + kBalancedMinLen - 1) / kBalancedMinLen;
 }
 
-// Unit u of a kv head in the balanced plan of length L: its sequence (-1 past the last
-// partition) and partition index within the sequence. Wave-uniform; a full wavefront.
-struct PlanPart {
-  int b, p;
+__device__ __forceinline__ int first_lens(const DecodeArgs& a, int lane) {
+  return lane < a.batch ? a.seq_lens[lane] : 0;
+}
+
+// k of the plan (L = 256 k). Lane sums saturate at 2^24 (>= 16 units_per_head, so the
+// result is unchanged) to keep the 64-lane total within 32 bits.
+__device__ __forceinline__ int balanced_k(const DecodeArgs& a, int lane, int T0) {
+  constexpr int kCap = 1 << 24;
+  int c = span_units(a, T0);
+  for (int b = 64 + lane; b < a.batch; b += 64) c = min(kCap, c + span_units(a, a.seq_lens[b]));
+  const int C = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(wave_incl_scan(c, lane), 63));
+  const int U = a.units_per_head;
+  if (C >= 16 * U) return 16;
+  return C > U ? (C + U - 1) / U : 1;
+}
+
+// Unit u of a kv head: its sequence b (-1 past the last partition), partition index p
+// within the sequence, the plan's length L and seq_lens[b].
+struct PlanUnit {
+  int b, p, L, T;
 };
-__device__ __forceinline__ PlanPart balanced_part(const DecodeArgs& a, int u, int L, int lane) {
+__device__ __forceinline__ PlanUnit balanced_unit(const DecodeArgs& a, int u, int lane) {
+  const int T0 = first_lens(a, lane);
+  const int k = balanced_k(a, lane, T0);
   int base = 0;  // partitions of the sequences before this group of 64
   for (int b0 = 0; b0 < a.batch; b0 += 64) {
-    const int n = b0 + lane < a.batch ? balanced_count(a, b0 + lane, L) : 0;
-    int incl = n;  // inclusive prefix sum over the lanes
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
+    const int Tl = b0 == 0 ? T0 : (b0 + lane < a.batch ? a.seq_lens[b0 + lane] : 0);
+    const int n = (span_units(a, Tl) + k - 1) / k;
+    const int incl = wave_incl_scan(n, lane);
     const int total = __builtin_amdgcn_readlane(incl, 63);
     if (u < base + total) {
       const unsigned long long hit = __ballot(base + incl > u);  // lane 63 is set
       const int l = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit)));
-      return {b0 + l, u - base - __builtin_amdgcn_readlane(incl - n, l)};
+      return {b0 + l, u - base - __builtin_amdgcn_readlane(incl - n, l), kBalancedMinLen * k,
+              __builtin_amdgcn_readlane(Tl, l)};
     }
     base += total;
   }
-  return {-1, 0};
+  return {-1, 0, kBalancedMinLen * k, 0};
 }
 
-// First unit and unit count of sequence b in the balanced plan of length L. A full
-// wavefront; wave-uniform.
-__device__ __forceinline__ int balanced_first(const DecodeArgs& a, int b, int L, int lane) {
+// First unit of sequence b and the plan's length L.
+struct PlanSeq {
+  int first, L;
+};
+__device__ __forceinline__ PlanSeq balanced_seq(const DecodeArgs& a, int b, int lane) {
+  const int T0 = first_lens(a, lane);
+  const int k = balanced_k(a, lane, T0);
   int off = 0;
   for (int b0 = 0; b0 < b; b0 += 64) {
-    int n = b0 + lane < b ? balanced_count(a, b0 + lane, L) : 0;
-#pragma unroll
-    for (int m = 32; m > 0; m >>= 1) n += __shfl_xor(n, m, 64);
-    off += __builtin_amdgcn_readfirstlane(n);
+    const int Tl = b0 == 0 ? T0 : (b0 + lane < a.batch ? a.seq_lens[b0 + lane] : 0);
+    const int n = b0 + lane < b ? (span_units(a, Tl) + k - 1) / k : 0;
+    off += __builtin_amdgcn_readlane(wave_incl_scan(n, lane), 63);
   }
-  return off;
+  return {__builtin_amdgcn_readfirstlane(off), kBalancedMinLen * k};
 }
 
 // Workgroups of a split-K launch.

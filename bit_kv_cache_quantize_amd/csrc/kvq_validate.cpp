@@ -73,25 +73,26 @@ Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int3
   const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
   const int64_t blocks = (len + kBlock - 1) / kBlock;
   const bool matrix = kernel == SplitKernel::kMatrix;
-  if (requested == 0 && matrix) {
+  if (requested == 0 && matrix && batch > 1) {
     // Balanced: about 16 partitions per CU over all kv heads (several waves of work per
-    // SIMD), of one length from the total span (the device recomputes it from seq_lens;
-    // here every sequence is taken as max_seq_len long).
+    // SIMD), of one length from the total span in 256-token units (the device recomputes
+    // it from seq_lens; here every sequence is taken as max_seq_len long). A single
+    // sequence has nothing to balance: it takes the fixed partitions below (the same
+    // length for a max_seq_len sequence, without the device-side plan).
     const int64_t nb = batch > 0 ? batch : 1;
     const int64_t uph = (16LL * (cus > 0 ? cus : 256) + g.hkv - 1) / g.hkv;
-    int64_t L = (nb * len + uph - 1) / uph;
-    L = (L + kBalancedMinLen - 1) / kBalancedMinLen * kBalancedMinLen;
-    L = L < kBalancedMinLen ? kBalancedMinLen : L > kBalancedMaxLen ? kBalancedMaxLen : L;
-    s.split_len = static_cast<int32_t>(L);
-    s.num_splits = static_cast<int32_t>((len + L - 1) / L);
+    const int64_t cu = (len + kBalancedMinLen - 1) / kBalancedMinLen;  // units of one sequence
+    const int64_t C = nb * cu;
+    const int64_t k = C >= 16 * uph ? 16 : C > uph ? (C + uph - 1) / uph : 1;
+    s.split_len = static_cast<int32_t>(kBalancedMinLen * k);
+    s.num_splits = static_cast<int32_t>((cu + k - 1) / k);
     s.balanced = 1;
     s.units_per_head = static_cast<int32_t>(uph);
-    // partitions of one kv head: sum_b ceil(span_b / L) <= total / L + batch, where
-    // total / L <= uph unless L is held at kBalancedMaxLen, and every span <= len
-    const int64_t most = (nb * len + kBalancedMaxLen - 1) / kBalancedMaxLen;
+    // partitions of one kv head: sum_b ceil(c_b / k) <= C / k + batch, where C / k <= uph
+    // unless k is held at 16, and every c_b <= cu
+    const int64_t most = (C + 15) / 16;
     int64_t slots = (most > uph ? most : uph) + nb;
-    const int64_t cap = nb * ((len + kBalancedMinLen - 1) / kBalancedMinLen);
-    if (slots > cap) slots = cap;
+    if (slots > C) slots = C;
     s.unit_slots = static_cast<int32_t>(slots);
     return s;
   }

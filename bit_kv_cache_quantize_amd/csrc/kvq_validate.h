@@ -32,8 +32,8 @@ int64_t plane_bytes(const Geometry& g, int plane);
 
 // Split-K sizing. `cus` is the device's compute-unit count (256 on MI355X).
 // Fixed partitions: every sequence is cut into split_len-token partitions (a caller's
-// num_splits, and the reference kernel). Balanced partitions (the matrix kernels'
-// automatic choice): one length for the whole batch, chosen on the device from the
+// num_splits, the reference kernel, a batch of one). Balanced partitions (the matrix
+// kernels' automatic choice): one length for the whole batch, chosen on the device from the
 // total covered span so that every kv head gets about units_per_head partitions of equal
 // length whatever the mix of sequence lengths; num_splits and split_len then describe a
 // batch whose sequences all have max_seq_len tokens.

@@ -148,11 +148,12 @@ def test_dequantize_argument_checks():
 
 
 def _balanced_slots(B, T, cus=256, hkv=8):
-    """Units per kv head the balanced plan's grid holds: at most total / L + B partitions,
-    total / L <= 16 * CUs / Hkv unless L is held at 4096 tokens; at most B * ceil(T / 256)."""
+    """Units per kv head the balanced plan's grid holds, in 256-token units C = B *
+    ceil(T / 256): at most C / k + B partitions, C / k <= 16 * CUs / Hkv unless k is held
+    at 16 (4096 tokens); at most C."""
     uph = -(-16 * cus // hkv)
-    n = max(T, 1)
-    return min(B * -(-n // 256), max(uph, -(-(B * n) // 4096)) + B)
+    C = B * -(-max(T, 1) // 256)
+    return min(C, max(uph, -(-C // 16)) + B)
 
 
 def test_split_sizing_and_workspace():
@@ -172,8 +173,9 @@ def test_split_sizing_and_workspace():
     }
     for (B, T), (want, want_ref) in cases.items():
         assert L.kvq_decode_num_splits(ctypes.byref(d), B, 32, T, 0) == want
-        balanced = 32 * _balanced_slots(B, T) * 130 * 4
-        assert L.kvq_decode_workspace_bytes(ctypes.byref(d), B, 32, T, 0) == max(balanced, B * 32 * want_ref * 130 * 4)
+        # a batch of one takes fixed partitions (nothing to balance)
+        mine = 32 * _balanced_slots(B, T) * 130 * 4 if B > 1 else B * 32 * want * 130 * 4
+        assert L.kvq_decode_workspace_bytes(ctypes.byref(d), B, 32, T, 0) == max(mine, B * 32 * want_ref * 130 * 4)
     # an explicit count: fixed partitions for both kernels
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 4, 32, 8192, 6) == 4 * 32 * 6 * 130 * 4
     d3 = _desc(group_size=64, page_size=131072, num_pages=1)
@@ -238,6 +240,10 @@ def test_window_sizes():
         s = L.kvq_decode_num_splits(ctypes.byref(d), B, 32, span, 5)
         assert L.kvq_decode_window_workspace_bytes(ctypes.byref(d), ctypes.byref(w), B, 32, T, 5) == \
             B * 32 * (s + 1) * 130 * 4
+    # a batch of one: fixed partitions
+    s = L.kvq_decode_num_splits(ctypes.byref(d), 1, 32, 5000 - 128, 0)
+    assert L.kvq_decode_window_workspace_bytes(ctypes.byref(d), ctypes.byref(w), 1, 32, 5000, 0) == \
+        32 * (s + 1) * 130 * 4
     assert L.kvq_decode_window_workspace_bytes(ctypes.byref(d), ctypes.byref(_win(sink=8)), 1, 32, 100, 0) == 0
 
 
