@@ -186,6 +186,48 @@ def test_split_sizing_and_workspace():
     assert L.kvq_decode_workspace_bytes(ctypes.byref(_desc(bits=3)), 1, 32, 100, 0) == 0
 
 
+def _plan_partitions(lens, cus=256, hkv=8):
+    """The balanced plan written out (decode over the whole span, no windows): spans in
+    256-token units c_b, k = ceil(C / units_per_head) within [1, 16], ceil(c_b / k)
+    partitions per sequence."""
+    uph = -(-16 * cus // hkv)
+    c = [-(-max(int(t), 0) // 256) for t in lens]
+    C = sum(c)
+    k = 16 if C >= 16 * uph else (-(-C // uph) if C > uph else 1)
+    return k, sum(-(-x // k) for x in c)
+
+
+def test_balanced_plan_fits_the_grid():
+    """Whatever the lengths (all <= max_seq_len), the plan's partitions per kv head never
+    exceed the units the grid and the workspace provide (the workspace size is
+    Hq * U * 130 * 4 bytes, U the bound), so no partition is dropped; for a uniform batch
+    the reported split count is the plan's."""
+    import random
+    L = kvq.lib()
+    d = _desc(page_size=65536, num_pages=4096)
+    rnd = random.Random(7)
+    for trial in range(400):
+        B = rnd.choice([2, 3, 16, 63, 64, 65, 130, 500])
+        maxlen = rnd.choice([1, 255, 256, 257, 4096, 8191, 32768, 65536, 200000])
+        kind = trial % 4
+        if kind == 0:
+            lens = [maxlen] * B
+        elif kind == 1:
+            lens = [rnd.randint(0, maxlen) for _ in range(B)]
+        elif kind == 2:  # one long, the rest tiny
+            lens = [maxlen] + [rnd.randint(0, 3) for _ in range(B - 1)]
+        else:  # most at the maximum, a few empty
+            lens = [maxlen if rnd.random() < 0.8 else 0 for _ in range(B)]
+        ws = L.kvq_decode_workspace_bytes(ctypes.byref(d), B, 32, maxlen, 0)
+        ref = L.kvq_decode_num_splits(ctypes.byref(d), B, 32, maxlen, 0)
+        U = _balanced_slots(B, maxlen)
+        assert ws >= 32 * U * 130 * 4
+        k, n = _plan_partitions(lens)
+        assert n <= U, (B, maxlen, kind, k, n, U)
+        if kind == 0:
+            assert ref == -(-(-(-maxlen // 256)) // k)
+
+
 def _win(**kw):
     base = dict(sink=32, recent=128, batch=4, k=FAKE, v=FAKE, residual=0)
     base.update(kw)
