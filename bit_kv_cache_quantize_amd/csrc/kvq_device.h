@@ -141,14 +141,14 @@ __device__ __forceinline__ int covered_span(const DecodeArgs& a, int T) {
 }
 
 // Balanced plan, in units of 256 tokens (kBalancedMinLen): c_b = ceil(span_b / 256),
-// C = sum_b c_b; the partition length is L = 256 k with k = ceil(C / units_per_head)
-// within [1, 16] (at most kBalancedMaxLen tokens), and sequence b gets ceil(c_b / k)
-// partitions, the same as ceil(span_b / L). Every function below runs on a full
-// wavefront (lane = 0..63, all active) and returns wave-uniform values (made visibly
-// uniform, so what derives from them stays scalar); every workgroup and kernel gets the
-// same plan from the same seq_lens. Lane l keeps seq_lens[l] (the first 64 sequences)
-// from a single load.
-static_assert(kBalancedMaxLen == 16 * kBalancedMinLen, "the plan's k runs over 1..16");
+// C = sum_b c_b, U = units_per_head (one round of waves over the kv heads). The
+// partition length is L = 256 k: k starts at ceil(C / U) and grows until the partitions,
+// sum_b ceil(c_b / k), fit in U (at most kBalancedMaxK; past that, several rounds);
+// sequence b gets ceil(c_b / k) partitions, the same as ceil(span_b / L). Every function
+// below runs on a full wavefront (lane = 0..63, all active) and returns wave-uniform
+// values (made visibly uniform, so what derives from them stays scalar); every workgroup
+// and kernel gets the same plan from the same seq_lens. Lane l keeps seq_lens[l] (the
+// first 64 sequences) from a single load.
 
 // Inclusive prefix sum over the 64 lanes: DPP row shifts (zeros shifted in) within each
 // row of 16 lanes, then the totals of the rows below.
@@ -166,6 +166,9 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   const int row = lane >> 4;
   return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
+__device__ __forceinline__ int wave_sum(int x, int lane) {
+  return __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(wave_incl_scan(x, lane), 63));
+}
 
 __device__ __forceinline__ int span_units(const DecodeArgs& a, int T) {
   return (covered_span(a, T) + kBalancedMinLen - 1) / kBalancedMinLen;
@@ -175,16 +178,26 @@ __device__ __forceinline__ int first_lens(const DecodeArgs& a, int lane) {
   return lane < a.batch ? a.seq_lens[lane] : 0;
 }
 
-// k of the plan (L = 256 k). Lane sums saturate at 2^24 (>= 16 units_per_head, so the
-// result is unchanged) to keep the 64-lane total within 32 bits.
+// Partitions of all sequences for a given k.
+__device__ __forceinline__ int balanced_count(const DecodeArgs& a, int lane, int c0, int k) {
+  int n = (c0 + k - 1) / k;
+  for (int b = 64 + lane; b < a.batch; b += 64) n += (span_units(a, a.seq_lens[b]) + k - 1) / k;
+  return wave_sum(n, lane);
+}
+
+// k of the plan (L = 256 k). Lane sums of C saturate at 2^24 (>= kBalancedMaxK * U, so
+// the result is unchanged) to keep the 64-lane total within 32 bits.
 __device__ __forceinline__ int balanced_k(const DecodeArgs& a, int lane, int T0) {
   constexpr int kCap = 1 << 24;
-  int c = span_units(a, T0);
+  const int c0 = span_units(a, T0);
+  int c = c0;
   for (int b = 64 + lane; b < a.batch; b += 64) c = min(kCap, c + span_units(a, a.seq_lens[b]));
-  const int C = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(wave_incl_scan(c, lane), 63));
+  const int C = wave_sum(c, lane);
   const int U = a.units_per_head;
-  if (C >= 16 * U) return 16;
-  return C > U ? (C + U - 1) / U : 1;
+  if (C >= kBalancedMaxK * U) return kBalancedMaxK;
+  int k = C > U ? (C + U - 1) / U : 1;
+  while (k < kBalancedMaxK && balanced_count(a, lane, c0, k) > U) ++k;
+  return k;
 }
 
 // Unit u of a kv head: its sequence b (-1 past the last partition), partition index p

@@ -74,23 +74,23 @@ Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int3
   const int64_t blocks = (len + kBlock - 1) / kBlock;
   const bool matrix = kernel == SplitKernel::kMatrix;
   if (requested == 0 && matrix && batch > 1) {
-    // Balanced: about 16 partitions per CU over all kv heads (several waves of work per
-    // SIMD), of one length from the total span in 256-token units (the device recomputes
-    // it from seq_lens; here every sequence is taken as max_seq_len long). A single
-    // sequence has nothing to balance: it takes the fixed partitions below (the same
-    // length for a max_seq_len sequence, without the device-side plan).
-    const int64_t nb = batch > 0 ? batch : 1;
-    const int64_t uph = (16LL * (cus > 0 ? cus : 256) + g.hkv - 1) / g.hkv;
+    // Balanced: one round of equal partitions, as many as the GPU holds waves (kWavesPerCU
+    // per CU, over all kv heads), of one length from the total span in 256-token units;
+    // the device recomputes the plan from seq_lens (here every sequence is taken as
+    // max_seq_len long).
+    const int64_t nb = batch;
+    const int64_t uph = (static_cast<int64_t>(kWavesPerCU) * (cus > 0 ? cus : 256) + g.hkv - 1) / g.hkv;
     const int64_t cu = (len + kBalancedMinLen - 1) / kBalancedMinLen;  // units of one sequence
     const int64_t C = nb * cu;
-    const int64_t k = C >= 16 * uph ? 16 : C > uph ? (C + uph - 1) / uph : 1;
+    int64_t k = C >= kBalancedMaxK * uph ? kBalancedMaxK : C > uph ? (C + uph - 1) / uph : 1;
+    while (k < kBalancedMaxK && nb * ((cu + k - 1) / k) > uph) ++k;  // the device's fitting search
     s.split_len = static_cast<int32_t>(kBalancedMinLen * k);
     s.num_splits = static_cast<int32_t>((cu + k - 1) / k);
     s.balanced = 1;
     s.units_per_head = static_cast<int32_t>(uph);
     // partitions of one kv head: sum_b ceil(c_b / k) <= C / k + batch, where C / k <= uph
-    // unless k is held at 16, and every c_b <= cu
-    const int64_t most = (C + 15) / 16;
+    // unless k is held at kBalancedMaxK, and every c_b <= cu
+    const int64_t most = (C + kBalancedMaxK - 1) / kBalancedMaxK;
     int64_t slots = (most > uph ? most : uph) + nb;
     if (slots > C) slots = C;
     s.unit_slots = static_cast<int32_t>(slots);
@@ -102,12 +102,13 @@ Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int3
     n = requested < blocks ? requested : blocks;
     per = (blocks + n - 1) / n;
   } else {
-    // Enough independent work units to keep every CU busy several times over
-    // (16 per CU), without partitions shorter than 8 blocks (256 tokens), whose
-    // partial results would cost more than they balance, nor longer than the kernel's
-    // limit (128 blocks for the matrix kernel, 64 for the reference kernel).
+    // Enough independent work units to fill every CU: one round of the matrix kernel's
+    // waves (kWavesPerCU per CU; fewer, longer partitions measured faster than two
+    // rounds), 16 per CU for the reference kernel; without partitions shorter than 8
+    // blocks (256 tokens), whose partial results would cost more than they balance, nor
+    // longer than 128 blocks (the reference kernel: 64, its LDS limit).
     const int64_t units = static_cast<int64_t>(batch) * g.hkv;
-    const int64_t target = 16LL * (cus > 0 ? cus : 256);
+    const int64_t target = static_cast<int64_t>(matrix ? kWavesPerCU : 16) * (cus > 0 ? cus : 256);
     n = (target + units - 1) / (units > 0 ? units : 1);
     int64_t cap = blocks / 8;
     if (cap < 1) cap = 1;

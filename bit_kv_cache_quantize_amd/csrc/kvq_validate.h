@@ -44,8 +44,9 @@ struct Splits {
   int32_t units_per_head;  // balanced: target partitions per kv head
   int32_t unit_slots;      // balanced: bound on the partitions of one kv head (grid units)
 };
-constexpr int kBalancedMinLen = 256;   // 8 blocks
-constexpr int kBalancedMaxLen = 4096;  // 128 blocks
+constexpr int kBalancedMinLen = 256;     // 8 blocks
+constexpr int kBalancedMaxK = 64;        // longest balanced partition: 64 * 256 tokens
+constexpr int kWavesPerCU = 8;           // the matrix kernels' occupancy: 2 waves per SIMD
 // Automatic choices differ per decode kernel: the matrix-core kernel takes partitions of
 // up to 128 blocks in whole 8-block super-blocks; the plain reference kernel keeps a
 // partition's scores in LDS and takes at most 64 blocks.

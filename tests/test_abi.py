@@ -149,27 +149,28 @@ def test_dequantize_argument_checks():
 
 def _balanced_slots(B, T, cus=256, hkv=8):
     """Units per kv head the balanced plan's grid holds, in 256-token units C = B *
-    ceil(T / 256): at most C / k + B partitions, C / k <= 16 * CUs / Hkv unless k is held
-    at 16 (4096 tokens); at most C."""
-    uph = -(-16 * cus // hkv)
+    ceil(T / 256): at most C / k + B partitions, C / k <= 8 * CUs / Hkv (one round of
+    waves) unless k is held at 64; at most C."""
+    uph = -(-8 * cus // hkv)
     C = B * -(-max(T, 1) // 256)
-    return min(C, max(uph, -(-C // 16)) + B)
+    return min(C, max(uph, -(-C // 64)) + B)
 
 
 def test_split_sizing_and_workspace():
     """Automatic split-K sizing. The matrix kernel's partitions are balanced: one length
-    for the batch, 256..4096 tokens in whole 8-block super-blocks, from the total span over
-    16 partitions per CU (reported for a batch of max_seq_len sequences); its workspace is
-    [Hq][units per kv head][d+2] fp32. The reference kernel keeps fixed partitions of at
-    most 2048 tokens, workspace [B][Hq][S][d+2]; the automatic size covers both.
-    (Off a GPU the library assumes 256 compute units, the MI355X count.)"""
+    for the batch in whole 256-token units, as long as it takes for the partitions to fit
+    one round of waves (8 per CU over the kv heads; reported for a batch of max_seq_len
+    sequences); its workspace is [Hq][units per kv head][d+2] fp32. The reference kernel
+    keeps fixed partitions of at most 2048 tokens, workspace [B][Hq][S][d+2]; the automatic
+    size covers both. (Off a GPU the library assumes 256 compute units, the MI355X count.)"""
     L = kvq.lib()
     d = _desc(page_size=32768, num_pages=64)
     cases = {  # (B, T) -> (matrix splits, reference splits)
-        (64, 32768): (8, 16),   # 4096-token partitions (2048 for the reference)
-        (16, 8192): (32, 32),   # 256-token partitions
-        (1, 1024): (4, 4),
+        (64, 32768): (4, 16),   # 8192-token partitions: 2048 units, one round (reference: 2048 tokens)
+        (16, 8192): (16, 32),   # 512-token partitions (reference: 256)
+        (1, 1024): (4, 4),      # one sequence: fixed partitions, at least 256 tokens
         (3, 5000): (20, 18),    # 256-token partitions (9 blocks for the reference)
+        (48, 32768): (5, 16),   # k = 24 gives 48 * 6 partitions > 256: k = 26, 6656 tokens
     }
     for (B, T), (want, want_ref) in cases.items():
         assert L.kvq_decode_num_splits(ctypes.byref(d), B, 32, T, 0) == want
@@ -188,13 +189,16 @@ def test_split_sizing_and_workspace():
 
 def _plan_partitions(lens, cus=256, hkv=8):
     """The balanced plan written out (decode over the whole span, no windows): spans in
-    256-token units c_b, k = ceil(C / units_per_head) within [1, 16], ceil(c_b / k)
-    partitions per sequence."""
-    uph = -(-16 * cus // hkv)
+    256-token units c_b, k from ceil(C / U) up until sum ceil(c_b / k) <= U (U = one round
+    of waves per kv head, k at most 64); ceil(c_b / k) partitions per sequence."""
+    uph = -(-8 * cus // hkv)
     c = [-(-max(int(t), 0) // 256) for t in lens]
     C = sum(c)
-    k = 16 if C >= 16 * uph else (-(-C // uph) if C > uph else 1)
-    return k, sum(-(-x // k) for x in c)
+    count = lambda k: sum(-(-x // k) for x in c)
+    k = 64 if C >= 64 * uph else (-(-C // uph) if C > uph else 1)
+    while k < 64 and count(k) > uph:
+        k += 1
+    return k, count(k)
 
 
 def test_balanced_plan_fits_the_grid():
