@@ -145,12 +145,13 @@ kvq_status kvq_quantize_append(const kvq_cache* cache, const void* k_new, const 
  * to 2048 tokens; the size covers both. Returns 0 for an invalid description.
  *
  * Balanced partitions (kvq_decode_attention, _timed, _pruned and _window with
- * num_splits 0 and batch > 1): one partition length L for the whole call, computed on the device
- * from seq_lens: with C = sum_b ceil(span_b / 256) (span_b = the tokens of sequence b
- * the split kernel covers), L = 256 k, k = ceil(C / ceil(16 * CUs / Hkv)) within
- * [1, 16]; sequence b gets ceil(span_b / L) partitions. Equal-length partitions keep
- * the GPU evenly loaded whatever the mix of sequence lengths, with no host-side
- * knowledge of the lengths.
+ * num_splits 0 and batch > 1): one partition length L for the whole call, computed on
+ * the device from seq_lens: with c_b = ceil(span_b / 256) (span_b = the tokens of
+ * sequence b the split kernel covers), C = sum_b c_b and U = ceil(8 * CUs / Hkv) (one
+ * round of the kernel's waves per kv head), L = 256 k where k starts at ceil(C / U)
+ * (at least 1) and grows until sum_b ceil(c_b / k) <= U, at most 64; sequence b gets
+ * ceil(span_b / L) partitions. Equal-length partitions keep the GPU evenly loaded
+ * whatever the mix of sequence lengths, with no host-side knowledge of the lengths.
  */
 size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
                                   int32_t max_seq_len, int32_t num_splits);
