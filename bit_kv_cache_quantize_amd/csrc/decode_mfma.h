@@ -213,29 +213,30 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       (static_cast<int64_t>(bt[pg_first]) * c.hkv + hk) * P - static_cast<int64_t>(pg_first) * P;
   // Blocks are loaded in order, each kind through its own cursor: block index, the
   // page and in-page offset of its first token, and (paged case) a window of 64
-  // block-table entries in a register, lane i holding logical page wbase + i. Past the
-  // last block the cursor stays (the load re-reads the last block; nothing is computed
-  // from it).
+  // block-table entries in a register, lane i holding phys * Hkv + hk for logical page
+  // wbase + i (the page's tile-row block of this kv head: fewer than 2^32, checked on the
+  // host), so a lookup is one readlane and one 32 x 32-bit multiply. Past the last block
+  // the cursor stays (the load re-reads the last block; nothing is computed from it).
   struct Cursor {
     int blk, pg, off, wbase;
-    int32_t bt_w;
+    uint32_t bt_w;
   };
   // The refill is consumed where it is loaded: a load still pending where a refilled and a
   // kept window meet would make every later lookup wait for all loads in flight (the
   // prefetched blocks included), not just for this one.
-  auto window = [&](int first) -> int32_t {
+  auto window = [&](int first) -> uint32_t {
     int32_t w = (first + lane <= pg_last) ? bt[first + lane] : 0;
     asm volatile("" : "+v"(w));
-    return w;
+    return static_cast<uint32_t>(w) * static_cast<uint32_t>(c.hkv) + static_cast<uint32_t>(hk);
   };
-  const Cursor cur0 = {0, pg_first, start - pg_first * P, pg_first, one_page ? 0 : window(pg_first)};
+  const Cursor cur0 = {0, pg_first, start - pg_first * P, pg_first, one_page ? 0u : window(pg_first)};
   auto page_row = [&](Cursor& cu, int pg, int off) -> int64_t {  // row of token pg * P + off
     if (pg - cu.wbase >= 64) {  // a cursor visits pages in increasing order
       cu.wbase = pg;
       cu.bt_w = window(pg);
     }
-    const int32_t phys = __builtin_amdgcn_readlane(cu.bt_w, pg - cu.wbase);
-    return (static_cast<int64_t>(phys) * c.hkv + hk) * P + off;
+    const uint32_t u = __builtin_amdgcn_readlane(cu.bt_w, pg - cu.wbase);
+    return static_cast<int64_t>(static_cast<uint64_t>(u) * static_cast<uint32_t>(P)) + off;
   };
   auto advance = [&](Cursor& cu) {
     if (cu.blk + 1 < nblk) {

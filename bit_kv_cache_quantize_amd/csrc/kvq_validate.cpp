@@ -47,6 +47,8 @@ kvq_status check_cache(const kvq_cache* c, bool planes, Geometry* g) {
 
 bool cache_supported(const Geometry& g) {
   if (g.d != 128) return false;
+  // the decode kernels index a page's rows of one kv head as page * Hkv + head in 32 bits
+  if (g.num_pages * g.hkv > 0xFFFFFFFFLL) return false;
   if (g.group != 32 && g.group != 64 && g.group != 128) return false;
   if (g.hblock != 0 && (g.hblock < 2 || g.hblock > 128)) return false;
   return true;
