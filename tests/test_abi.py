@@ -232,6 +232,18 @@ def test_balanced_plan_fits_the_grid():
             assert ref == -(-(-(-maxlen // 256)) // k)
 
 
+def test_page_index_limit():
+    """The decode kernels index a page's rows of one kv head as page * Hkv + head in 32
+    bits: a pool whose num_pages * Hkv passes 2^32 is reported unsupported before any
+    launch (the device pointers here are never touched)."""
+    L, v = kvq.lib(), ctypes.c_void_p
+    big = _desc(num_pages=(1 << 29) + 1)  # x 8 kv heads > 2^32
+    ok = _desc(num_pages=(1 << 29) - 1)
+    args = [v(FAKE), 2, 32, v(FAKE), 4, v(FAKE), 64, 0.0, 0, v(FAKE), 1 << 40, v(FAKE), None]
+    assert L.kvq_decode_attention(ctypes.byref(big), *args) == kvq.ERR_UNSUPPORTED
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(ok), 2, 32, 64, 0) > 0
+
+
 def _win(**kw):
     base = dict(sink=32, recent=128, batch=4, k=FAKE, v=FAKE, residual=0)
     base.update(kw)

@@ -31,6 +31,8 @@ CASES = {
     "int2_g32_gqa1_hb0": _small("c2", batch=2, context=333, bits=2, num_q_heads=8, hadamard_block=0),
     "paged_ragged": _small("c5", batch=5, ragged=(1, 800)),
     "int4_g128_hb32": _small("c2", batch=2, context=400, group_size=128, hadamard_block=32),
+    # more than 64 sequences, some empty: the balanced plan over several groups of 64
+    "b70_ragged": _small("c5", batch=70, ragged=(0, 300)),
 }
 
 

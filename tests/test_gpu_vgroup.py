@@ -103,6 +103,8 @@ CASES = {
     "int2_g128": (_w("c4", batch=2, context=1280, page_size=128), [1280, 384]),
     "int2_g32_gqa1": (_w("c2", batch=2, context=512, page_size=64, bits=2, num_q_heads=8), [512, 96]),
     "int4_g32_sink_outliers": (_w("c3", context=4096, group_size=32, page_size=512), [4096]),
+    # more than 64 sequences: the balanced plan over several groups of 64
+    "b66_int4_g32": (_w("c2", batch=66, context=256, page_size=64), [32 * (1 + (5 * b) % 8) for b in range(66)]),
 }
 
 

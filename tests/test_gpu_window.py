@@ -114,6 +114,9 @@ CASES = {
     "gqa1": (_w("c2", batch=2, context=800, num_q_heads=8), 32, 64, [800, 300], 2),
     "gqa2": (_w("c2", batch=2, context=800, num_q_heads=16), 32, 64, [800, 300], 2),
     "max_window": (_w("c2", batch=2, context=2500), 512, 512, [2500, 1100], 2),
+    # more than 64 sequences: the balanced plan's prefix sums over several groups of 64
+    "b70_ragged": (_w("c2", batch=70, context=700), 16, 32,
+                   [(37 * b) % 700 if b % 9 else 0 for b in range(70)], 2),
 }
 
 
