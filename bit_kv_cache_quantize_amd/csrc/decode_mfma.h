@@ -59,13 +59,21 @@ __device__ __forceinline__ uint32_t codes_f16x2(uint32_t bytes) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(bytes, 512.0f, HI_WORD));
 }
 
+// Two 2-bit codes c (0..3), the low and high nibble of byte SEL of `nibbles`, -> f16x2
+// holding them exactly: nibbles 0..3 read as fp4-e2m1 are c / 2 (0, 0.5, 1, 1.5), which
+// the scaled fp4->f16 conversion with scale 2 turns into c.
+template <int SEL>
+__device__ __forceinline__ uint32_t crumbs_f16x2(uint32_t nibbles) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nibbles, 2.0f, SEL));
+}
+
 // Score MFMA p, lane half h covers the 8 channels 64h + 8p .. 64h + 8p + 7; its K-slot
 // kappa (0..7) holds the channel at this position within them, the order in which
 // unpack_k() below lays codes into the B operand.
 template <int BITS>
 __device__ __forceinline__ int qk_slot_channel(int kappa) {
   if (BITS == 4) return 2 * (kappa & 3) + (kappa >> 2);
-  return (kappa >> 1) + 4 * (kappa & 1);
+  return 2 * (kappa & 1) + 4 * ((kappa >> 1) & 1) + (kappa >> 2);
 }
 
 // B operand of score MFMA p from the lane's packed key codes (kc: 8 dwords at INT4 =
@@ -77,12 +85,13 @@ __device__ __forceinline__ half8 unpack_k(const uint32_t* kc, int p) {
     const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;  // nibbles 0,2,4,6 / 1,3,5,7
     return as_half8(codes_f16x2<false>(lo), codes_f16x2<true>(lo), codes_f16x2<false>(hi), codes_f16x2<true>(hi));
   }
+  // byte j of w holds channels 4j .. 4j + 3 (crumb i = channel 4j + i); m0 keeps crumbs
+  // 0 and 2 of every byte in its nibbles, m1 crumbs 1 and 3: two masks feed all four bytes
   const uint32_t w = kc[p >> 1];
-  const uint32_t b0 = w & 0x03030303u, b1 = (w >> 2) & 0x03030303u;  // crumbs j, j+4, j+8, j+12
-  const uint32_t b2 = (w >> 4) & 0x03030303u, b3 = (w >> 6) & 0x03030303u;
+  const uint32_t m0 = w & 0x33333333u, m1 = (w >> 2) & 0x33333333u;
   if (p & 1)
-    return as_half8(codes_f16x2<true>(b0), codes_f16x2<true>(b1), codes_f16x2<true>(b2), codes_f16x2<true>(b3));
-  return as_half8(codes_f16x2<false>(b0), codes_f16x2<false>(b1), codes_f16x2<false>(b2), codes_f16x2<false>(b3));
+    return as_half8(crumbs_f16x2<2>(m0), crumbs_f16x2<3>(m0), crumbs_f16x2<2>(m1), crumbs_f16x2<3>(m1));
+  return as_half8(crumbs_f16x2<0>(m0), crumbs_f16x2<1>(m0), crumbs_f16x2<0>(m1), crumbs_f16x2<1>(m1));
 }
 
 // Channel of column n (0..15) of value N-tile nt (0..7), matching unpack_v().
