@@ -412,6 +412,11 @@ def main():
         "config": {"workload": w.name, "batch": B, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": d,
                    "context": maxlen, "bits": w.bits, "group_size": w.group_size,
                    "hadamard_block": w.hadamard_block, "page_size": geo.page_size, "num_splits": num_splits,
+                   # automatic split count with more than one sequence: one partition length for
+                   # the batch, planned on the device from seq_lens (num_splits = the count for a
+                   # max_seq_len sequence of a uniform batch)
+                   "partitions": "balanced" if (args.num_splits == 0 and B > 1 and not args.reference)
+                   else "fixed",
                    "kernel": "reference" if args.reference else "mfma", "layer_ring": ring,
                    "step_bytes": step_bytes, "quant_mode": cache.quant_mode, "v_grouping": cache.v_grouping,
                    **({"keep_chunks": args.prune, "chunks": n_chunks,
