@@ -92,8 +92,8 @@ def traffic_from_profile(workload: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="h1")
     ap.add_argument("--reference", action="store_true", help="time the plain-VALU decode kernel instead")
     ap.add_argument("--num-splits", type=int, default=0)
