@@ -168,15 +168,14 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   int b, hk, split, split_len, T;
   int64_t slot;
   if (a.balanced) {
-    hk = unit % c.hkv;
-    const int u = unit / c.hkv;
-    const PlanUnit pu = balanced_unit(a, u, lane);
+    const PlanUnit pu = balanced_unit(a, unit, c.hkv, lane);
     if (pu.b < 0) return;  // past the batch's last partition
     b = pu.b;
+    hk = pu.hk;
     split = pu.p;
     split_len = pu.L;
     T = pu.T;
-    slot = static_cast<int64_t>(hk) * R * a.unit_slots + u;
+    slot = static_cast<int64_t>(hk) * R * a.unit_slots + pu.u;
   } else {
     split = unit % a.num_splits;
     const int bh = unit / a.num_splits;

@@ -112,9 +112,10 @@ struct DecodeArgs {
   // Where partials go. Fixed partitions (split_len from the host): partition p of
   // sequence b, query head j at partials[((b * Hq + j) * num_splits + p) * (d + 2)].
   // Balanced partitions (balanced = 1): the length L comes from the batch's total
-  // covered span on the device (the balanced plan below); each kv head's units
-  // u = 0, 1, ... take the partitions of sequence 0, then sequence 1, ..., and unit u of
-  // kv head hk (blockIdx = u * Hkv + hk) writes partials[(j * unit_slots + u) * (d + 2)].
+  // covered span on the device (the balanced plan below); units u = 0, 1, ... number the
+  // partitions of sequence 0, then sequence 1, ...; workgroups run them in the order
+  // (sequence, kv head, partition), and unit u of kv head hk writes
+  // partials[(j * unit_slots + u) * (d + 2)] for its query heads j.
   int balanced;
   int units_per_head;  // balanced: target partitions per kv head
   int unit_slots;      // balanced: units per kv head in the grid, partial slots per query head
@@ -200,12 +201,15 @@ __device__ __forceinline__ int balanced_k(const DecodeArgs& a, int lane, int T0)
   return k;
 }
 
-// Unit u of a kv head: its sequence b (-1 past the last partition), partition index p
-// within the sequence, the plan's length L and seq_lens[b].
+// Workgroup g of the split launch in the order (sequence, kv head, partition) — each
+// sequence's n_b partitions for kv head 0, then for kv head 1, ... — as the fixed
+// partitions are ordered: its sequence b (-1 past the last partition), kv head hk,
+// partition index p within the sequence, the plan's length L, seq_lens[b], and its unit
+// u = (first unit of b) + p, the partial slot shared by all kv heads' layouts.
 struct PlanUnit {
-  int b, p, L, T;
+  int b, hk, p, u, L, T;
 };
-__device__ __forceinline__ PlanUnit balanced_unit(const DecodeArgs& a, int u, int lane) {
+__device__ __forceinline__ PlanUnit balanced_unit(const DecodeArgs& a, int g, int hkv, int lane) {
   const int T0 = first_lens(a, lane);
   const int k = balanced_k(a, lane, T0);
   int base = 0;  // partitions of the sequences before this group of 64
@@ -214,15 +218,18 @@ __device__ __forceinline__ PlanUnit balanced_unit(const DecodeArgs& a, int u, in
     const int n = (span_units(a, Tl) + k - 1) / k;
     const int incl = wave_incl_scan(n, lane);
     const int total = __builtin_amdgcn_readlane(incl, 63);
-    if (u < base + total) {
-      const unsigned long long hit = __ballot(base + incl > u);  // lane 63 is set
+    if (g < (base + total) * hkv) {
+      const unsigned long long hit = __ballot((base + incl) * hkv > g);  // lane 63 is set
       const int l = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(hit)));
-      return {b0 + l, u - base - __builtin_amdgcn_readlane(incl - n, l), kBalancedMinLen * k,
-              __builtin_amdgcn_readlane(Tl, l)};
+      const int first = base + __builtin_amdgcn_readlane(incl - n, l);
+      const int nb = __builtin_amdgcn_readlane(n, l);  // >= 1: workgroup g falls in it
+      const int r = g - first * hkv;
+      const int hk = r / nb, p = r - hk * nb;
+      return {b0 + l, hk, p, first + p, kBalancedMinLen * k, __builtin_amdgcn_readlane(Tl, l)};
     }
     base += total;
   }
-  return {-1, 0, kBalancedMinLen * k, 0};
+  return {-1, 0, 0, 0, kBalancedMinLen * k, 0};
 }
 
 // First unit of sequence b and the plan's length L.
