@@ -47,9 +47,9 @@ struct Splits {
 constexpr int kBalancedMinLen = 256;     // 8 blocks
 constexpr int kBalancedMaxK = 64;        // longest balanced partition: 64 * 256 tokens
 constexpr int kWavesPerCU = 8;           // the matrix kernels' occupancy: 2 waves per SIMD
-// Automatic choices differ per decode kernel: the matrix-core kernel takes partitions of
-// up to 128 blocks in whole 8-block super-blocks; the plain reference kernel keeps a
-// partition's scores in LDS and takes at most 64 blocks.
+// Automatic choices differ per decode kernel: the matrix-core kernel takes balanced
+// partitions (batch > 1) or fixed ones of up to 128 blocks (one sequence); the plain
+// reference kernel keeps a partition's scores in LDS and takes at most 64 blocks.
 enum class SplitKernel { kMatrix, kReference };
 Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
                      int32_t requested, int cus, SplitKernel kernel);
