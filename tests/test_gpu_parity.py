@@ -183,6 +183,8 @@ BALANCED_CASES = {
     "dominant": (_small("c5", batch=5, ragged=(1, 9000)), [9000, 3, 0, 40, 700]),
     # every sequence empty but one token
     "single_token": (_small("c5", batch=3, ragged=(0, 1)), [0, 1, 0]),
+    # every sequence empty: no partitions at all, zero rows
+    "all_empty": (_small("c5", batch=5, ragged=(0, 1)), [0, 0, 0, 0, 0]),
 }
 
 
