@@ -158,25 +158,30 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
   }
 }
 
-// Log-sum-exp merge of the partials of one (sequence, query head). The workgroup has
-// 128 * NGRP threads: group gp (threads 128 gp .. 128 gp + 127, thread = channel) merges
-// partials gp, gp + NGRP, ... 16 at a time (one pass, every load of a chunk issued
-// together: the running reference M moves up chunk by chunk and rescales (L, o) like the
-// online softmax inside a partition); the groups' (M, L, o) are then merged through LDS.
+// Log-sum-exp merge of the partials of one (sequence, query head), or of CW of its 128
+// channels (the grid then holds 128 / CW workgroups per pair). The workgroup has CW * NGRP
+// threads: group gp (threads CW gp .. CW gp + CW - 1, thread = channel) merges partials gp,
+// gp + NGRP, ... 16 at a time (one pass, every load of a chunk issued together: the
+// running reference M moves up chunk by chunk and rescales (L, o) like the online softmax
+// inside a partition); the groups' (M, L, o) are then merged through LDS. Many partials
+// take many groups of fewer channels, so the loads spread over more CUs in one pass.
 // The partials present are the split kernel's partitions that hold tokens of the covered
 // span (fixed partitions: slots 0.. of the sequence's row; balanced: the sequence's units,
 // found from the same plan the split kernel computed), then (with windows) the window
 // partial.
-template <int NGRP>
-__global__ __launch_bounds__(128 * NGRP) void combine_kernel(DecodeArgs a) {
+template <int NGRP, int CW>
+__global__ __launch_bounds__(CW * NGRP) void combine_kernel(DecodeArgs a) {
   constexpr int kD = 128;
   constexpr int kChunk = 16;
-  __shared__ float o_s[NGRP][kD];
+  constexpr int kParts = kD / CW;
+  static_assert(CW * NGRP >= 64 && CW * NGRP <= 1024, "one to sixteen wavefronts");
+  __shared__ float o_s[NGRP][CW];
   __shared__ float ml_s[NGRP][2];
   __shared__ int plan_s[2];
-  const int bj = blockIdx.x;
+  const int bj = blockIdx.x / kParts;
   const int b = bj / a.num_q_heads, j = bj % a.num_q_heads;
-  const int gp = threadIdx.x / kD, i = threadIdx.x % kD;
+  const int gp = threadIdx.x / CW;
+  const int i = (blockIdx.x % kParts) * CW + threadIdx.x % CW;  // channel
   const int T = a.seq_lens[b];
   if (T <= 0) {
     if (gp == 0) a.out[static_cast<int64_t>(bj) * kD + i] = 0.f;
@@ -235,8 +240,8 @@ __global__ __launch_bounds__(128 * NGRP) void combine_kernel(DecodeArgs a) {
     a.out[static_cast<int64_t>(bj) * kD + i] = o / L;
     return;
   }
-  o_s[gp][i] = o;
-  if (i == 0) {
+  o_s[gp][threadIdx.x % CW] = o;
+  if (threadIdx.x % CW == 0) {
     ml_s[gp][0] = M;
     ml_s[gp][1] = L;
   }
@@ -250,7 +255,7 @@ __global__ __launch_bounds__(128 * NGRP) void combine_kernel(DecodeArgs a) {
     for (int g = 0; g < NGRP; ++g) {
       const float w = exp2f(ml_s[g][0] - Mt);  // 0 for a group without partials
       Lt = __builtin_fmaf(ml_s[g][1], w, Lt);
-      ot = __builtin_fmaf(o_s[g][i], w, ot);
+      ot = __builtin_fmaf(o_s[g][threadIdx.x], w, ot);
     }
     a.out[static_cast<int64_t>(bj) * kD + i] = ot / Lt;
   }
@@ -275,20 +280,24 @@ hipError_t launch_decode_split_reference(const DecodeArgs& a, const Geometry& g,
 
 hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t stream) {
   (void)g;
-  // one group of 128 threads per 32 partials, up to 8 groups (long sequences in many
-  // partitions merge in parallel); balanced plans are sized for max_seq_len-long
-  // sequences (longer partition lists of a ragged batch take more passes)
+  // One group of threads per up to 16 partials, each thread one channel; a pair's partials
+  // beyond 128 are spread over 32 groups of 32 channels (four workgroups per pair), so
+  // long sequences in many partitions merge in one pass over more CUs. Balanced plans are
+  // sized for max_seq_len-long sequences (longer partition lists of a ragged batch take
+  // more passes).
   const int parts = a.num_splits + a.window;
-  const int ngrp = parts > 128 ? 8 : parts > 64 ? 4 : parts > 32 ? 2 : 1;
-  dim3 grid(static_cast<unsigned>(a.batch * a.num_q_heads));
-#define KVQ_CB(NG)                                                          \
-  if (ngrp == NG) {                                                         \
-    hipLaunchKernelGGL(combine_kernel<NG>, grid, dim3(128 * NG), 0, stream, a); \
-    return hipGetLastError();                                               \
+  const unsigned pairs = static_cast<unsigned>(a.batch * a.num_q_heads);
+#define KVQ_CB(NG, CW)                                                                          \
+  {                                                                                             \
+    hipLaunchKernelGGL((combine_kernel<NG, CW>), dim3(pairs * (128 / CW)), dim3(NG * CW), 0, stream, a); \
+    return hipGetLastError();                                                                   \
   }
-  KVQ_CB(1) KVQ_CB(2) KVQ_CB(4) KVQ_CB(8)
+  if (parts > 128) KVQ_CB(32, 32)
+  if (parts > 64) KVQ_CB(8, 128)
+  if (parts > 32) KVQ_CB(4, 128)
+  if (parts > 16) KVQ_CB(2, 128)
+  KVQ_CB(1, 128)
 #undef KVQ_CB
-  return hipErrorInvalidValue;
 }
 
 }  // namespace kvq
