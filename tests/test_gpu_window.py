@@ -166,6 +166,18 @@ def test_window_decode_explicit_splits_and_scale():
         assert err <= TOL, (splits, scale, err)
 
 
+def test_window_decode_many_partials():
+    """More than 128 partials per (sequence, query head) plus the window partial: the
+    combine's shape with four workgroups of 32 groups x 32 channels per pair."""
+    w = _w("c2", batch=2, context=5200)
+    p = WinPair(w, 32, 64, torch.tensor([5200, 4700], dtype=torch.int32), 0)
+    for splits in (150, 0):
+        got, want = p.decode(5, num_splits=splits)
+        err = max_err(got, want)
+        print(f"[window] many partials, splits={splits}: max err {err:.3e}", flush=True)
+        assert err <= TOL, (splits, err)
+
+
 def test_window_zero_length_rows():
     """seq_len 0 gives a zero row; other sequences are unaffected."""
     w = _w("c2", batch=3, context=400)
