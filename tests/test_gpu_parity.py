@@ -211,6 +211,41 @@ def test_decode_balanced_plan_ragged_batches(name):
     assert float(np.max(np.abs(got - fixed))) <= 1e-4
 
 
+def test_decode_balanced_plan_random_batches():
+    """Seeded random batches (2..200 sequences, lengths 0..1500 with empty ones, 16- or
+    48-token pages or contiguous, INT4/INT2): the balanced plan's output equals a fixed
+    partition decode of the same cache within 1e-4 (fp32 accumulation order only), and
+    every third batch matches the oracle within the parity bound."""
+    import random
+    rnd = random.Random(11)
+    for trial in range(12):
+        B = rnd.choice([2, 3, 17, 64, 65, 130, 200])
+        hi = rnd.choice([40, 300, 1500])
+        page = rnd.choice([16, 48, 0])
+        bits, G = rnd.choice([(4, 32), (4, 64), (2, 128)])
+        base = "c4" if bits == 2 else "c5"
+        w = _small(base, batch=B, ragged=(0, hi), page_size=page, bits=bits, group_size=G, seed=100 + trial)
+        lens = wl.seq_lens(w)
+        lens[torch.randperm(B, generator=torch.Generator().manual_seed(trial))[: B // 7]] = 0
+        with_oracle = trial % 3 == 0
+        print(f"[decode] random balanced batch {trial}: B={B} max={int(lens.max())} page={page} "
+              f"INT{bits} g{G} oracle={with_oracle}", flush=True)
+        p = make_pair(w, DEV, lens=lens, with_oracle=with_oracle)
+        q = wl.queries(w).to(DEV)
+        bt, ln = p.geo.block_table.to(DEV), p.lens.to(DEV)
+        maxlen = max(int(p.lens.max()), 1)
+        got = kvq.decode_attention(p.gpu, q, bt, ln, maxlen).cpu().numpy().astype(np.float64)
+        fixed = kvq.decode_attention(p.gpu, q, bt, ln, maxlen, num_splits=3).cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got))
+        assert np.all(got[p.lens.numpy() == 0] == 0)
+        assert float(np.max(np.abs(got - fixed))) <= 1e-4, trial
+        if with_oracle:
+            want = p.ref.decode(wl.bf16_bits(wl.queries(w)), p.geo.block_table.numpy(), p.lens.numpy())
+            err = max_err(got, want)
+            record(f"balanced/random{trial}", err)
+            assert err <= TOL, (trial, err)
+
+
 def test_decode_page_permutation_invariance():
     """Same logical content under two different physical page placements."""
     print("[decode] page permutation", flush=True)
