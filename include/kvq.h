@@ -29,8 +29,10 @@
  *    or non-finite inputs give undefined results.
  *  - Supported today: head_dim 128; bits 4 or 2; group_size 32, 64 or 128;
  *    hadamard_block 0 (off) or a power of two from 2 to 128; GQA ratio
- *    num_q_heads / num_kv_heads of 1, 2 or 4; page_size a multiple of 16.
- *    Other well-formed descriptions return KVQ_ERR_UNSUPPORTED.
+ *    num_q_heads / num_kv_heads of 1, 2 or 4; page_size a multiple of 16;
+ *    num_pages * num_kv_heads below 2^32 (the decode kernels index a page's rows of
+ *    one kv head in 32 bits). Other well-formed descriptions return
+ *    KVQ_ERR_UNSUPPORTED.
  */
 #ifndef KVQ_H
 #define KVQ_H
