@@ -75,7 +75,7 @@ Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int3
   const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
   const int64_t blocks = (len + kBlock - 1) / kBlock;
   const bool matrix = kernel == SplitKernel::kMatrix;
-  if (requested == 0 && matrix && batch > 1) {
+  if (requested == 0 && matrix && batch > 1 && batch <= kBalancedMaxBatch) {
     // Balanced: one round of equal partitions, as many as the GPU holds waves (kWavesPerCU
     // per CU, over all kv heads), of one length from the total span in 256-token units;
     // the device recomputes the plan from seq_lens (here every sequence is taken as

@@ -47,6 +47,10 @@ struct Splits {
 constexpr int kBalancedMinLen = 256;     // 8 blocks
 constexpr int kBalancedMaxK = 64;        // longest balanced partition: 64 * 256 tokens
 constexpr int kWavesPerCU = 8;           // the matrix kernels' occupancy: 2 waves per SIMD
+// Every split and combine workgroup recomputes the plan from all of seq_lens (64 per
+// step); past this many sequences the batch alone gives enough partitions to balance,
+// and fixed partitions are used.
+constexpr int kBalancedMaxBatch = 256;
 // Automatic choices differ per decode kernel: the matrix-core kernel takes balanced
 // partitions (batch > 1) or fixed ones of up to 128 blocks (one sequence); the plain
 // reference kernel keeps a partition's scores in LDS and takes at most 64 blocks.

@@ -147,7 +147,7 @@ kvq_status kvq_quantize_append(const kvq_cache* cache, const void* k_new, const 
  * to 2048 tokens; the size covers both. Returns 0 for an invalid description.
  *
  * Balanced partitions (kvq_decode_attention, _timed, _pruned and _window with
- * num_splits 0 and batch > 1): one partition length L for the whole call, computed on
+ * num_splits 0 and 2 <= batch <= 256): one partition length L for the whole call, computed on
  * the device from seq_lens: with c_b = ceil(span_b / 256) (span_b = the tokens of
  * sequence b the split kernel covers), C = sum_b c_b and U = ceil(8 * CUs / Hkv) (one
  * round of the kernel's waves per kv head), L = 256 k where k starts at ceil(C / U)

@@ -179,6 +179,11 @@ def test_split_sizing_and_workspace():
         assert L.kvq_decode_workspace_bytes(ctypes.byref(d), B, 32, T, 0) == max(mine, B * 32 * want_ref * 130 * 4)
     # an explicit count: fixed partitions for both kernels
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 4, 32, 8192, 6) == 4 * 32 * 6 * 130 * 4
+    # past 256 sequences the plan would cost every workgroup too much: fixed partitions
+    # (matrix kernel: one 2048-token partition per sequence, 2400 units already fill a
+    # round; reference kernel: two of 1024; the workspace covers the larger)
+    assert L.kvq_decode_num_splits(ctypes.byref(d), 300, 32, 2048, 0) == 1
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 300, 32, 2048, 0) == 300 * 32 * 2 * 130 * 4
     d3 = _desc(group_size=64, page_size=131072, num_pages=1)
     assert L.kvq_decode_num_splits(ctypes.byref(d3), 1, 32, 131072, 0) >= 256
     # explicit requests are honoured up to one partition per 32-token block
@@ -211,7 +216,7 @@ def test_balanced_plan_fits_the_grid():
     d = _desc(page_size=65536, num_pages=4096)
     rnd = random.Random(7)
     for trial in range(400):
-        B = rnd.choice([2, 3, 16, 63, 64, 65, 130, 500])
+        B = rnd.choice([2, 3, 16, 63, 64, 65, 130, 256])
         maxlen = rnd.choice([1, 255, 256, 257, 4096, 8191, 32768, 65536, 200000])
         kind = trial % 4
         if kind == 0:
