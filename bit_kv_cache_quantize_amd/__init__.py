@@ -225,6 +225,9 @@ def decode_attention(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor,
                      events=None, reference: bool = False) -> torch.Tensor:
     """Split-K GQA decode attention; q bf16 [B][Hq][d] (original basis) -> fp32 [B][Hq][d].
 
+    `num_splits` 0 lets the library choose: for 2..256 sequences one partition length
+    for the whole batch, planned on the device from `seq_lens` (see include/kvq.h);
+    otherwise a fixed number of partitions per max_seq_len sequence.
     `events` = (begin, end) raw hipEvent_t handles (ints) recorded around the split-K kernel.
     `reference` routes to the plain-VALU kernel (for cross-checks).
     """
