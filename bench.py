@@ -8,7 +8,9 @@ combine). Inputs are seeded synthetic tensors resident in HBM before timing star
 
 Prints one JSON line. `value` is effective KV GB/s of the whole step (algorithmic
 bytes / step time); `roofline` covers the dominant kernel (the split-K decode), timed
-with HIP events recorded on its own stream around every launch.
+with HIP events recorded on its own stream around every launch. Before the W warmup
+steps the step runs untimed for --settle-s seconds (default 0.25): the GPU's clocks
+need some 50-100 ms of sustained load to settle.
 
   python bench.py [--steps K] [--warmup W] [--workload h1] [--gpus 1] [--window S,R]
 
@@ -97,6 +99,8 @@ def main():
     ap.add_argument("--workload", default="h1")
     ap.add_argument("--reference", action="store_true", help="time the plain-VALU decode kernel instead")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--settle-s", type=float, default=0.25,
+                    help="seconds of untimed steps before the warmup steps (the clocks settle under load)")
     ap.add_argument("--cpu-sample-seqs", type=int, default=3, help="sequences in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--parity-seqs", type=int, default=2, help="sequences checked against the oracle")
@@ -220,7 +224,6 @@ def main():
         del src, dst
         log(f"[bench] calibration copy: {args.calibration_copy_mb} MiB read + written")
 
-    total_steps = args.warmup + args.steps
     hip_events = HipEvents(args.steps)
 
     applied0 = []  # input indices of the steps applied to caches[0], in order
@@ -244,14 +247,26 @@ def main():
         kvq.decode_attention(c, qs[i % n_inputs], bt, lens_d, maxlen, num_splits=args.num_splits, workspace=ws,
                              out=out, events=events, reference=args.reference)
 
+    # The GPU needs some 50-100 ms of sustained load before its clocks settle: untimed
+    # steps for settle_s seconds (checked every 20 steps), then the warmup steps.
+    n_settle = 0
+    t_settle = time.perf_counter()
+    while args.settle_s > 0:
+        for _ in range(20):
+            step(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_settle >= args.settle_s:
+            break
     for i in range(args.warmup):
-        step(i)
+        step(n_settle + i)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(args.steps):
-        step(args.warmup + i, events=None if (args.reference or windowed) else hip_events.pair(i))
+        step(n_settle + args.warmup + i, events=None if (args.reference or windowed) else hip_events.pair(i))
     end.record()
+    total_steps = n_settle + args.warmup + args.steps
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     split_ms = None
@@ -418,6 +433,7 @@ def main():
                    "partitions": "balanced" if (args.num_splits == 0 and B > 1 and not args.reference)
                    else "fixed",
                    "kernel": "reference" if args.reference else "mfma", "layer_ring": ring,
+                   "settle_steps": n_settle,
                    "step_bytes": step_bytes, "quant_mode": cache.quant_mode, "v_grouping": cache.v_grouping,
                    **({"keep_chunks": args.prune, "chunks": n_chunks,
                        "kv_bits_capacity": round(per_tok_head * 8 / (2 * d), 4),
