@@ -170,6 +170,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   if (a.balanced) {
     const PlanUnit pu = balanced_unit(a, unit, c.hkv, lane);
     if (pu.b < 0) return;  // past the batch's last partition
+    if (pu.hk == 0 && pu.p == 0 && lane == 0) a.seq_plan[pu.b] = make_int2(pu.u, pu.n);
     b = pu.b;
     hk = pu.hk;
     split = pu.p;

@@ -167,8 +167,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
 // take many groups of fewer channels, so the loads spread over more CUs in one pass.
 // The partials present are the split kernel's partitions that hold tokens of the covered
 // span (fixed partitions: slots 0.. of the sequence's row; balanced: the sequence's units,
-// found from the same plan the split kernel computed), then (with windows) the window
-// partial.
+// from the table the split kernel wrote), then (with windows) the window partial.
 template <int NGRP, int CW>
 __global__ __launch_bounds__(CW * NGRP) void combine_kernel(DecodeArgs a) {
   constexpr int kD = 128;
@@ -177,7 +176,6 @@ __global__ __launch_bounds__(CW * NGRP) void combine_kernel(DecodeArgs a) {
   static_assert(CW * NGRP >= 64 && CW * NGRP <= 1024, "one to sixteen wavefronts");
   __shared__ float o_s[NGRP][CW];
   __shared__ float ml_s[NGRP][2];
-  __shared__ int plan_s[2];
   const int bj = blockIdx.x / kParts;
   const int b = bj / a.num_q_heads, j = bj % a.num_q_heads;
   const int gp = threadIdx.x / CW;
@@ -191,17 +189,15 @@ __global__ __launch_bounds__(CW * NGRP) void combine_kernel(DecodeArgs a) {
   const float* base;
   int nq;
   if (a.balanced) {
-    if (threadIdx.x < 64) {  // wavefront 0 recomputes the plan
-      const PlanSeq ps = balanced_seq(a, b, threadIdx.x);
-      if (threadIdx.x == 0) {
-        plan_s[0] = ps.first;
-        plan_s[1] = (span + ps.L - 1) / ps.L;
-      }
+    // the split kernel's table (an entry exists for every sequence with tokens to cover);
+    // clamped to the grid's units, so seq_lens above max_seq_len cannot read outside it
+    int first = 0;
+    nq = 0;
+    if (span > 0) {
+      const int2 e = a.seq_plan[b];
+      first = min(max(e.x, 0), a.unit_slots);
+      nq = max(0, min(e.y, a.unit_slots - first));
     }
-    __syncthreads();
-    const int first = plan_s[0];
-    // units beyond the grid (seq_lens above max_seq_len) were never computed
-    nq = max(0, min(plan_s[1], a.unit_slots - first));
     base = a.partials + (static_cast<int64_t>(j) * a.unit_slots + first) * (kD + 2);
   } else {
     nq = min(a.num_splits, (span + a.split_len - 1) / a.split_len);

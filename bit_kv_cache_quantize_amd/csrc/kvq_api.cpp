@@ -64,6 +64,9 @@ DecodeArgs decode_args(const kvq_cache* cache, const Geometry& g, const void* q,
   a.balanced = sp.balanced;
   a.units_per_head = sp.units_per_head;
   a.unit_slots = sp.unit_slots;
+  a.seq_plan = sp.balanced ? reinterpret_cast<int2*>(static_cast<char*>(workspace) +
+                                                     balanced_partials_bytes(g, num_q_heads, sp))
+                           : nullptr;
   a.win_partials = nullptr;
   a.window = 0;
   a.keep_chunks = 0;

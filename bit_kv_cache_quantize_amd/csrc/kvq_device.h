@@ -119,6 +119,9 @@ struct DecodeArgs {
   int balanced;
   int units_per_head;  // balanced: target partitions per kv head
   int unit_slots;      // balanced: units per kv head in the grid, partial slots per query head
+  // balanced: per sequence {first unit, partitions}, written by the split kernel's unit
+  // (kv head 0, partition 0) of each sequence with tokens, read by the combine
+  int2* seq_plan;
   // window partials [batch][Hq][d + 2], when `window` is set
   float* win_partials;
   int window;
@@ -207,7 +210,7 @@ __device__ __forceinline__ int balanced_k(const DecodeArgs& a, int lane, int T0)
 // partition index p within the sequence, the plan's length L, seq_lens[b], and its unit
 // u = (first unit of b) + p, the partial slot shared by all kv heads' layouts.
 struct PlanUnit {
-  int b, hk, p, u, L, T;
+  int b, hk, p, u, L, T, n;
 };
 __device__ __forceinline__ PlanUnit balanced_unit(const DecodeArgs& a, int g, int hkv, int lane) {
   const int T0 = first_lens(a, lane);
@@ -225,27 +228,11 @@ __device__ __forceinline__ PlanUnit balanced_unit(const DecodeArgs& a, int g, in
       const int nb = __builtin_amdgcn_readlane(n, l);  // >= 1: workgroup g falls in it
       const int r = g - first * hkv;
       const int hk = r / nb, p = r - hk * nb;
-      return {b0 + l, hk, p, first + p, kBalancedMinLen * k, __builtin_amdgcn_readlane(Tl, l)};
+      return {b0 + l, hk, p, first + p, kBalancedMinLen * k, __builtin_amdgcn_readlane(Tl, l), nb};
     }
     base += total;
   }
-  return {-1, 0, 0, 0, kBalancedMinLen * k, 0};
-}
-
-// First unit of sequence b and the plan's length L.
-struct PlanSeq {
-  int first, L;
-};
-__device__ __forceinline__ PlanSeq balanced_seq(const DecodeArgs& a, int b, int lane) {
-  const int T0 = first_lens(a, lane);
-  const int k = balanced_k(a, lane, T0);
-  int off = 0;
-  for (int b0 = 0; b0 < b; b0 += 64) {
-    const int Tl = b0 == 0 ? T0 : (b0 + lane < a.batch ? a.seq_lens[b0 + lane] : 0);
-    const int n = b0 + lane < b ? (span_units(a, Tl) + k - 1) / k : 0;
-    off += __builtin_amdgcn_readlane(wave_incl_scan(n, lane), 63);
-  }
-  return {__builtin_amdgcn_readfirstlane(off), kBalancedMinLen * k};
+  return {-1, 0, 0, 0, kBalancedMinLen * k, 0, 0};
 }
 
 // Workgroups of a split-K launch.

@@ -128,8 +128,13 @@ Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int3
 }
 
 size_t workspace_bytes(const Geometry& g, int32_t batch, int32_t num_q_heads, const Splits& s) {
-  if (s.balanced) return static_cast<size_t>(num_q_heads) * s.unit_slots * (g.d + 2) * sizeof(float);
+  if (s.balanced)
+    return balanced_partials_bytes(g, num_q_heads, s) + (static_cast<size_t>(batch) * 8 + 255) / 256 * 256;
   return static_cast<size_t>(batch) * num_q_heads * s.num_splits * (g.d + 2) * sizeof(float);
+}
+
+size_t balanced_partials_bytes(const Geometry& g, int32_t num_q_heads, const Splits& s) {
+  return static_cast<size_t>(num_q_heads) * s.unit_slots * (g.d + 2) * sizeof(float);
 }
 
 kvq_status check_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t num_q_heads,

@@ -59,6 +59,9 @@ Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int3
                      int32_t requested, int cus, SplitKernel kernel);
 
 size_t workspace_bytes(const Geometry& g, int32_t batch, int32_t num_q_heads, const Splits& s);
+// Balanced layout: the partials [Hq][unit_slots][d + 2] fp32, then a table of int32 pairs
+// {first unit, partitions} per sequence (written by the split kernel, read by the combine).
+size_t balanced_partials_bytes(const Geometry& g, int32_t num_q_heads, const Splits& s);
 
 // Full check of decode arguments (everything but the workspace size).
 kvq_status check_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t num_q_heads,

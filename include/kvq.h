@@ -143,7 +143,9 @@ kvq_status kvq_quantize_append(const kvq_cache* cache, const void* k_new, const 
  * [batch][num_q_heads][splits][d + 2]. num_splits 0 = the library's choice, made the
  * same way for the same arguments on the same device: kvq_decode_attention then plans
  * balanced partitions on the device (below), partials [num_q_heads][U][d + 2] with U a
- * bound on one kv head's partitions; the reference kernel takes fixed partitions of up
+ * bound on one kv head's partitions, then two int32 per sequence (the split kernel's
+ * record of where each sequence's partials start, for the combine); the reference
+ * kernel takes fixed partitions of up
  * to 2048 tokens; the size covers both. Returns 0 for an invalid description.
  *
  * Balanced partitions (kvq_decode_attention, _timed, _pruned and _window with

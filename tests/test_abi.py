@@ -147,6 +147,12 @@ def test_dequantize_argument_checks():
     assert L.kvq_dequantize(ctypes.byref(d), 1, None, 0, None, None) == kvq.OK
 
 
+def _balanced_table(B):
+    """Bytes of the balanced layout's per-sequence table (two int32 per sequence, in
+    whole 256-byte blocks) after its partials."""
+    return -(-8 * B // 256) * 256
+
+
 def _balanced_slots(B, T, cus=256, hkv=8):
     """Units per kv head the balanced plan's grid holds, in 256-token units C = B *
     ceil(T / 256): at most C / k + B partitions, C / k <= 8 * CUs / Hkv (one round of
@@ -175,7 +181,7 @@ def test_split_sizing_and_workspace():
     for (B, T), (want, want_ref) in cases.items():
         assert L.kvq_decode_num_splits(ctypes.byref(d), B, 32, T, 0) == want
         # a batch of one takes fixed partitions (nothing to balance)
-        mine = 32 * _balanced_slots(B, T) * 130 * 4 if B > 1 else B * 32 * want * 130 * 4
+        mine = 32 * _balanced_slots(B, T) * 130 * 4 + _balanced_table(B) if B > 1 else B * 32 * want * 130 * 4
         assert L.kvq_decode_workspace_bytes(ctypes.byref(d), B, 32, T, 0) == max(mine, B * 32 * want_ref * 130 * 4)
     # an explicit count: fixed partitions for both kernels
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 4, 32, 8192, 6) == 4 * 32 * 6 * 130 * 4
@@ -230,7 +236,7 @@ def test_balanced_plan_fits_the_grid():
         ws = L.kvq_decode_workspace_bytes(ctypes.byref(d), B, 32, maxlen, 0)
         ref = L.kvq_decode_num_splits(ctypes.byref(d), B, 32, maxlen, 0)
         U = _balanced_slots(B, maxlen)
-        assert ws >= 32 * U * 130 * 4
+        assert ws >= 32 * U * 130 * 4 + _balanced_table(B)
         k, n = _plan_partitions(lens)
         assert n <= U, (B, maxlen, kind, k, n, U)
         if kind == 0:
@@ -299,7 +305,7 @@ def test_window_sizes():
         span = max(T - 128, 0)
         slots = _balanced_slots(B, span)
         assert L.kvq_decode_window_workspace_bytes(ctypes.byref(d), ctypes.byref(w), B, 32, T, 0) == \
-            (32 * slots + B * 32) * 130 * 4
+            (32 * slots + B * 32) * 130 * 4 + _balanced_table(B)
         s = L.kvq_decode_num_splits(ctypes.byref(d), B, 32, span, 5)
         assert L.kvq_decode_window_workspace_bytes(ctypes.byref(d), ctypes.byref(w), B, 32, T, 5) == \
             B * 32 * (s + 1) * 130 * 4
