@@ -181,6 +181,9 @@ __global__ __launch_bounds__(CW * NGRP) void combine_kernel(DecodeArgs a) {
   const int gp = threadIdx.x / CW;
   const int i = (blockIdx.x % kParts) * CW + threadIdx.x % CW;  // channel
   const int T = a.seq_lens[b];
+  // the split kernel's table entry (in bounds for every b), loaded alongside T; used only
+  // for a sequence with tokens to cover, whose entry this call's split kernel wrote
+  const int2 plan = a.balanced ? a.seq_plan[b] : make_int2(0, 0);
   if (T <= 0) {
     if (gp == 0) a.out[static_cast<int64_t>(bj) * kD + i] = 0.f;
     return;
@@ -189,14 +192,12 @@ __global__ __launch_bounds__(CW * NGRP) void combine_kernel(DecodeArgs a) {
   const float* base;
   int nq;
   if (a.balanced) {
-    // the split kernel's table (an entry exists for every sequence with tokens to cover);
     // clamped to the grid's units, so seq_lens above max_seq_len cannot read outside it
     int first = 0;
     nq = 0;
     if (span > 0) {
-      const int2 e = a.seq_plan[b];
-      first = min(max(e.x, 0), a.unit_slots);
-      nq = max(0, min(e.y, a.unit_slots - first));
+      first = min(max(plan.x, 0), a.unit_slots);
+      nq = max(0, min(plan.y, a.unit_slots - first));
     }
     base = a.partials + (static_cast<int64_t>(j) * a.unit_slots + first) * (kD + 2);
   } else {
