@@ -78,10 +78,29 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str):
-    """HBM bytes per split-kernel launch from committed rocprofv3 counter runs, or None
-    when absent or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"decode_split_{workload}_traffic.json")
+def profile_key(args) -> str:
+    """Name of a run's split-kernel configuration: the workload and every option that
+    changes what that kernel reads or how it runs (h1, h1_prune2, h1_window32x128, ...)."""
+    key = args.workload
+    if args.prune:
+        key += f"_prune{args.prune}"
+    if args.window:
+        key += "_window" + args.window.replace(",", "x")
+    if args.vgroup:
+        key += "_vgroup"
+    if args.hybrid:
+        key += "_hybrid"
+    if args.hadamard_block >= 0:
+        key += f"_hb{args.hadamard_block}"
+    if args.num_splits:
+        key += f"_splits{args.num_splits}"
+    return key
+
+
+def traffic_from_profile(key: str):
+    """HBM bytes per split-kernel launch from committed rocprofv3 counter runs of the same
+    configuration (profile_key), or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"decode_split_{key}_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -236,7 +255,7 @@ def main():
         if windowed:
             kvq.window_append(c, windows[i % ring], kn, vn, seqs_d, pos_d, evict_d)
             kvq.decode_attention_window(c, windows[i % ring], qs[i % n_inputs], bt, lens_d, maxlen,
-                                        num_splits=args.num_splits, workspace=ws, out=out)
+                                        num_splits=args.num_splits, workspace=ws, out=out, events=events)
             return
         kvq.quantize_append(c, kn, vn, last_slots)
         if args.prune:
@@ -264,13 +283,13 @@ def main():
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(args.steps):
-        step(n_settle + args.warmup + i, events=None if (args.reference or windowed) else hip_events.pair(i))
+        step(n_settle + args.warmup + i, events=None if args.reference else hip_events.pair(i))
     end.record()
     total_steps = n_settle + args.warmup + args.steps
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     split_ms = None
-    if not (args.reference or windowed):
+    if not args.reference:
         split_ms = float(np.mean([hip_events.elapsed_ms(i) for i in range(args.steps)]))
     hip_events.close()
 
@@ -289,26 +308,30 @@ def main():
         # the residual holds T % G tokens at decode time; the append writes the token and,
         # when it completes a group, reads the G ring rows and writes their quantized form
         n_win = sum(int(T) % win_R for T in lens)
-        kv_bytes = (int(lens.to(torch.int64).sum()) - n_win) * Hkv * per_tok_head + n_win * Hkv * 2 * d * 2
+        split_kv_bytes = (int(lens.to(torch.int64).sum()) - n_win) * Hkv * per_tok_head
+        kv_bytes = split_kv_bytes + n_win * Hkv * 2 * d * 2
         completing = sum(1 for T in lens if int(T) % win_R == 0)
         append_bytes = B * Hkv * 2 * (2 * d * 2) + completing * Hkv * win_R * (2 * d * 2 + per_tok_head)
     elif windowed:
         # window tokens are read as bf16 K and V rows; the append reads the new token,
         # writes it to the ring, reads the evicted row and writes its quantized form
         n_win = sum(min(win_S, int(T)) + min(win_R, max(int(T) - win_S, 0)) for T in lens)
-        kv_bytes = (int(lens.to(torch.int64).sum()) - n_win) * Hkv * per_tok_head + n_win * Hkv * 2 * d * 2
+        split_kv_bytes = (int(lens.to(torch.int64).sum()) - n_win) * Hkv * per_tok_head
+        kv_bytes = split_kv_bytes + n_win * Hkv * 2 * d * 2
         append_bytes = B * Hkv * (3 * 2 * d * 2 + per_tok_head)
     step_bytes = kv_bytes + q_bytes + out_bytes + append_bytes
-    split_bytes = kv_bytes + q_bytes
+    # the split kernel reads the quantized span only (window tokens go to the window kernel)
+    split_bytes = (split_kv_bytes if windowed else kv_bytes) + q_bytes
     value = step_bytes / (ms * 1e-3) / 1e9
 
     roofline = None
     if split_ms is not None:
         achieved = split_bytes / (split_ms * 1e-3) / 1e9
-        traffic = traffic_from_profile(args.workload)
+        traffic = traffic_from_profile(profile_key(args))
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "kernel": "decode_split", "algorithmic_bytes_per_launch": split_bytes,
+                    "kernel": "decode_split", "profile_key": profile_key(args),
+                    "algorithmic_bytes_per_launch": split_bytes,
                     "avg_launch_us": round(split_ms * 1e3, 2)}
 
     # ---- parity on sampled sequences (the oracle recomputes them from the same bytes) ----

@@ -78,6 +78,8 @@ SIGNATURES = {
     "kvq_decode_window_workspace_bytes": (_sz, [_DP, _WP, _i32, _i32, _i32, _i32]),
     "kvq_decode_attention_window": (ctypes.c_int, [_DP, _WP, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32,
                                                    _vp, _sz, _vp, _vp]),
+    "kvq_decode_attention_window_timed": (ctypes.c_int, [_DP, _WP, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32,
+                                                         _i32, _vp, _sz, _vp, _vp, _vp, _vp]),
     "kvq_decode_attention_pruned": (ctypes.c_int, [_DP, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32, _i32,
                                                    _vp, _vp, _sz, _vp, _vp, _vp, _vp]),
     "kvq_dequantize": (ctypes.c_int, [_DP, _i32, _vp, _i64, _vp, _vp]),
@@ -361,9 +363,10 @@ def decode_window_workspace_bytes(cache: KVCache, window: KVWindow, batch: int, 
 def decode_attention_window(cache: KVCache, window: KVWindow, q: torch.Tensor, block_table: torch.Tensor,
                             seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float = 0.0,
                             num_splits: int = 0, workspace: torch.Tensor | None = None,
-                            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                            out: torch.Tensor | None = None, stream=None, events=None) -> torch.Tensor:
     """Decode attention over windows (bf16, original query) and cache (rotated query) in one
-    softmax; q bf16 [B][Hq][d] -> fp32 [B][Hq][d]; seq_lens count all tokens."""
+    softmax; q bf16 [B][Hq][d] -> fp32 [B][Hq][d]; seq_lens count all tokens. events: an
+    optional (begin, end) pair of hipEvent_t handles recorded around the split-K kernel."""
     _need(q, torch.bfloat16, "q")
     _need(block_table, torch.int32, "block_table")
     _need(seq_lens, torch.int32, "seq_lens")
@@ -375,9 +378,12 @@ def decode_attention_window(cache: KVCache, window: KVWindow, q: torch.Tensor, b
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     _need(workspace, torch.uint8, "workspace")
-    st = lib().kvq_decode_attention_window(ctypes.byref(cache.desc), ctypes.byref(window.desc), _ptr(q), B, Hq,
-                                           _ptr(block_table), block_table.shape[1], _ptr(seq_lens), max_seq_len,
-                                           softmax_scale, num_splits, _ptr(workspace), workspace.numel(),
-                                           _ptr(out), _stream(stream))
+    args = (ctypes.byref(cache.desc), ctypes.byref(window.desc), _ptr(q), B, Hq, _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), max_seq_len, softmax_scale, num_splits, _ptr(workspace),
+            workspace.numel(), _ptr(out), _stream(stream))
+    if events is None:
+        st = lib().kvq_decode_attention_window(*args)
+    else:
+        st = lib().kvq_decode_attention_window_timed(*args, ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
     _check(st, "kvq_decode_attention_window")
     return out

@@ -222,11 +222,12 @@ size_t kvq_decode_window_workspace_bytes(const kvq_cache* cache, const kvq_windo
   return window_workspace_bytes(g, batch, num_q_heads, sp);
 }
 
-kvq_status kvq_decode_attention_window(const kvq_cache* cache, const kvq_window* window, const void* q,
-                                       int32_t batch, int32_t num_q_heads, const int32_t* block_table,
-                                       int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
-                                       float softmax_scale, int32_t num_splits, void* workspace,
-                                       size_t workspace_bytes_given, float* out, void* stream) {
+kvq_status kvq_decode_attention_window_timed(const kvq_cache* cache, const kvq_window* window, const void* q,
+                                             int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                             int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                             int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                                             void* workspace, size_t workspace_bytes_given, float* out,
+                                             void* stream, void* split_begin, void* split_end) {
   Geometry g;
   kvq_status st = check_decode(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                                max_seq_len, num_splits, workspace, out, &g);
@@ -245,9 +246,21 @@ kvq_status kvq_decode_attention_window(const kvq_cache* cache, const kvq_window*
   a.win_partials = a.partials + workspace_bytes(g, batch, num_q_heads, sp) / sizeof(float);
   a.window = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (split_begin && hipEventRecord(static_cast<hipEvent_t>(split_begin), s) != hipSuccess) return KVQ_ERR_HIP;
   if (split_kernel(a, g, s) != hipSuccess) return KVQ_ERR_HIP;
+  if (split_end && hipEventRecord(static_cast<hipEvent_t>(split_end), s) != hipSuccess) return KVQ_ERR_HIP;
   if (launch_decode_window(a, dev_window(window), g, s) != hipSuccess) return KVQ_ERR_HIP;
   return launch_combine(a, g, s) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_decode_attention_window(const kvq_cache* cache, const kvq_window* window, const void* q,
+                                       int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                       int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                       float softmax_scale, int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes_given, float* out, void* stream) {
+  return kvq_decode_attention_window_timed(cache, window, q, batch, num_q_heads, block_table, max_pages_per_seq,
+                                           seq_lens, max_seq_len, softmax_scale, num_splits, workspace,
+                                           workspace_bytes_given, out, stream, nullptr, nullptr);
 }
 
 kvq_status kvq_decode_attention_pruned(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,

@@ -328,6 +328,19 @@ kvq_status kvq_decode_attention_window(const kvq_cache* cache, const kvq_window*
                                        float softmax_scale, int32_t num_splits, void* workspace,
                                        size_t workspace_bytes, float* out, void* stream);
 
+/*
+ * Same as kvq_decode_attention_window, and additionally records the hipEvent_t
+ * `split_begin` right before and `split_end` right after the split-K kernel over the
+ * quantized span on `stream` (either may be NULL), as kvq_decode_attention_timed does.
+ * For benchmarking.
+ */
+kvq_status kvq_decode_attention_window_timed(const kvq_cache* cache, const kvq_window* window, const void* q,
+                                             int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                             int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                             int32_t max_seq_len, float softmax_scale, int32_t num_splits,
+                                             void* workspace, size_t workspace_bytes, float* out,
+                                             void* stream, void* split_begin, void* split_end);
+
 /* Static description of a status code. */
 const char* kvq_status_string(kvq_status status);
 

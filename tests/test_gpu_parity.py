@@ -13,7 +13,7 @@ import torch
 import bit_kv_cache_quantize_amd as kvq
 import oracle
 import workloads as wl
-from kvq_harness import TOL, append_step, decode_both, make_pair, max_err, planes_equal, record
+from kvq_harness import TOL, EventPair, append_step, decode_both, make_pair, max_err, planes_equal, record
 
 pytestmark = pytest.mark.gpu
 
@@ -275,6 +275,26 @@ def test_decode_deterministic():
     a = kvq.decode_attention(p.gpu, q, p.geo.block_table.to(DEV), p.lens.to(DEV), 900).cpu()
     b = kvq.decode_attention(p.gpu, q, p.geo.block_table.to(DEV), p.lens.to(DEV), 900).cpu()
     assert torch.equal(a, b)
+
+
+
+def test_decode_timed_entry_point():
+    """The timed entry point gives the untimed call's exact output and records a positive
+    interval around the split kernel."""
+    w = _small("c2", batch=3, context=1500)
+    print("[decode] timed entry point", flush=True)
+    p = make_pair(w, DEV, with_oracle=False)
+    q = wl.queries(w).to(DEV)
+    bt, lens = p.geo.block_table.to(DEV), p.lens.to(DEV)
+    plain = kvq.decode_attention(p.gpu, q, bt, lens, 1500).cpu()
+    ev = EventPair()
+    try:
+        timed = kvq.decode_attention(p.gpu, q, bt, lens, 1500, events=ev.handles()).cpu()
+        torch.cuda.synchronize()
+        assert torch.equal(plain, timed)
+        assert ev.elapsed_ms() > 0.0
+    finally:
+        ev.close()
 
 
 def test_decode_custom_softmax_scale():

@@ -13,7 +13,7 @@ import torch
 
 import bit_kv_cache_quantize_amd as kvq
 import workloads as wl
-from kvq_harness import TOL, make_pair, max_err, record
+from kvq_harness import TOL, EventPair, make_pair, max_err, record
 
 pytestmark = pytest.mark.gpu
 
@@ -117,3 +117,22 @@ def test_pruned_fullsize_h1_sampled():
             assert err <= TOL
     del cache
     torch.cuda.empty_cache()
+
+
+def test_pruned_timed_events():
+    """Events passed to the pruned decode give the untimed call's exact output and record a
+    positive interval around the split kernel."""
+    w = _small("c2", batch=3, context=700)
+    print("[pruned] timed entry point", flush=True)
+    p = make_pair(w, DEV, with_oracle=False)
+    q = wl.queries(w, step=3).to(DEV)
+    bt, lens = p.geo.block_table.to(DEV), p.lens.to(DEV)
+    plain = kvq.decode_attention_pruned(p.gpu, q, bt, lens, 700, 2).cpu()
+    ev = EventPair()
+    try:
+        timed = kvq.decode_attention_pruned(p.gpu, q, bt, lens, 700, 2, events=ev.handles()).cpu()
+        torch.cuda.synchronize()
+        assert torch.equal(plain, timed)
+        assert ev.elapsed_ms() > 0.0
+    finally:
+        ev.close()

@@ -16,7 +16,7 @@ import torch
 import bit_kv_cache_quantize_amd as kvq
 import oracle
 import workloads as wl
-from kvq_harness import TOL, max_err, record
+from kvq_harness import TOL, EventPair, max_err, record
 
 pytestmark = pytest.mark.gpu
 
@@ -185,3 +185,23 @@ def test_window_zero_length_rows():
     got, want = p.decode(3)
     assert np.all(got[1] == 0.0)
     assert max_err(got, want) <= TOL
+
+
+def test_window_decode_timed_entry_point():
+    """kvq_decode_attention_window_timed gives the untimed call's exact output and records
+    a positive interval around the split kernel."""
+    w = _w("c2", batch=2, context=3000)
+    print("[window] timed entry point", flush=True)
+    p = WinPair(w, 32, 128, torch.tensor([3000, 2100], dtype=torch.int32), 0)
+    q = wl.queries(w, 7).to(DEV)
+    bt, lens = p.geo.block_table.to(DEV), p.lens.to(DEV)
+    maxlen = int(p.lens.max())
+    plain = kvq.decode_attention_window(p.gpu, p.gwin, q, bt, lens, maxlen).cpu()
+    ev = EventPair()
+    try:
+        timed = kvq.decode_attention_window(p.gpu, p.gwin, q, bt, lens, maxlen, events=ev.handles()).cpu()
+        torch.cuda.synchronize()
+        assert torch.equal(plain, timed)
+        assert ev.elapsed_ms() > 0.0
+    finally:
+        ev.close()
