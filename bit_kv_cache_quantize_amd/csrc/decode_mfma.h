@@ -239,14 +239,6 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     return static_cast<uint32_t>(w) * static_cast<uint32_t>(c.hkv) + static_cast<uint32_t>(hk);
   };
   const Cursor cur0 = {0, pg_first, start - pg_first * P, pg_first, one_page ? 0u : window(pg_first)};
-  auto page_row = [&](Cursor& cu, int pg, int off) -> int64_t {  // row of token pg * P + off
-    if (pg - cu.wbase >= 64) {  // a cursor visits pages in increasing order
-      cu.wbase = pg;
-      cu.bt_w = window(pg);
-    }
-    const uint32_t u = __builtin_amdgcn_readlane(cu.bt_w, pg - cu.wbase);
-    return static_cast<int64_t>(static_cast<uint64_t>(u) * static_cast<uint32_t>(P)) + off;
-  };
   auto advance = [&](Cursor& cu) {
     if (cu.blk + 1 < nblk) {
       ++cu.blk;
@@ -258,7 +250,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     }
   };
   // rows of the cursor block's two 16-token tiles (a tile past the partition end: the
-  // first tile again)
+  // first tile again); one window check per block keeps both of its pages in the window
   auto tile_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
     const int t0 = start + 32 * cu.blk;
     if (one_page) {
@@ -266,13 +258,20 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       row1 = (t0 + 16 < end) ? row0 + 16 : row0;
       return;
     }
-    row0 = page_row(cu, cu.pg, cu.off);
+    if (cu.pg + 1 - cu.wbase >= 64) {  // a cursor visits pages in increasing order
+      cu.wbase = cu.pg;
+      cu.bt_w = window(cu.pg);
+    }
+    const int i0 = cu.pg - cu.wbase;  // 0 .. 62
+    const uint32_t u0 = __builtin_amdgcn_readlane(cu.bt_w, i0);
+    row0 = static_cast<int64_t>(static_cast<uint64_t>(u0) * static_cast<uint32_t>(P)) + cu.off;
     if (t0 + 16 >= end) {
       row1 = row0;
     } else if (cu.off + 16 < P) {
       row1 = row0 + 16;
-    } else {
-      row1 = page_row(cu, cu.pg + 1, cu.off + 16 - P);
+    } else {  // the second tile opens the next page (off = P - 16)
+      const uint32_t u1 = __builtin_amdgcn_readlane(cu.bt_w, i0 + 1);
+      row1 = static_cast<int64_t>(static_cast<uint64_t>(u1) * static_cast<uint32_t>(P));
     }
   };
 
