@@ -110,6 +110,67 @@ def traffic_from_profile(key: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def host_threads() -> int:
+    """Host threads for the oracle's multi-thread timing: the CPUs this process may run
+    on, at most 16 (a one-GPU share of the GPU machine's host) and at most OMP_NUM_THREADS
+    when that is set."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, min(n, 16))
+
+
+def host_description() -> dict:
+    """CPU model (from /proc/cpuinfo) and core counts of the host the oracle ran on."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": aff}
+
+
+def measure_stream_ceiling(kvq, dev, gib: int, reps: int = 10) -> dict:
+    """Read bandwidth of this GPU for the decode kernel's load shape (kvq_stream_read: one
+    16-byte load per lane, whole cache lines per wave instruction) over a `gib` GiB buffer,
+    plain and non-temporal, at 2, 4 and 8 workgroups of 256 threads per CU; mean of `reps`
+    hipEvent-timed launches per setting after one untimed launch. `ceiling` is the best."""
+    import torch
+
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)  # written once, so every page is resident
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    ev = HipEvents(reps)
+    res = {}
+    try:
+        for nt in (1, 0):
+            for wpc in (2, 4, 8):
+                kvq.stream_read(buf, bool(nt), wpc, sink)
+                for i in range(reps):
+                    kvq.stream_read(buf, bool(nt), wpc, sink, events=ev.pair(i))
+                torch.cuda.synchronize()
+                ms = sum(ev.elapsed_ms(i) for i in range(reps)) / reps
+                res[f"{'nontemporal' if nt else 'plain'}_wg{wpc}"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    finally:
+        ev.close()
+        del buf
+    best = max(res.values())
+    return {"ceiling": best, "unit": "GB/s", "bytes": nbytes, "settings": res,
+            "best_setting": max(res, key=res.get), "frac_of_peak": round(best / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,7 +181,9 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--settle-s", type=float, default=0.25,
                     help="seconds of untimed steps before the warmup steps (the clocks settle under load)")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=3, help="sequences in the oracle's timed sample")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=2,
+                    help="sequences in the oracle's one-thread timed sample (the multi-thread sample runs one "
+                         "sequence per host thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--parity-seqs", type=int, default=2, help="sequences checked against the oracle")
     ap.add_argument("--window", default="", help="S,R: bf16 sink and recent windows of S and R tokens")
@@ -131,6 +194,8 @@ def main():
                     help="values grouped along tokens (v_grouping 1) with a bf16 residual of one group")
     ap.add_argument("--prune", type=int, default=0,
                     help="query-channel pruning: key chunks kept per (sequence, kv head), of bits * head_dim / 128")
+    ap.add_argument("--no-stream-probe", action="store_true", help="skip the read-stream ceiling measurement")
+    ap.add_argument("--stream-gib", type=int, default=4, help="GiB read by the read-stream probe")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg, fp32) of this many MiB before timing, "
                          "so hardware byte counters can be scaled against a kernel of known traffic")
@@ -334,6 +399,14 @@ def main():
                     "algorithmic_bytes_per_launch": split_bytes,
                     "avg_launch_us": round(split_ms * 1e3, 2)}
 
+    # ---- read-stream ceiling of this GPU, measured in the same process ----
+    stream = None
+    if not args.no_stream_probe:
+        stream = measure_stream_ceiling(kvq, dev, args.stream_gib)
+        if roofline is not None:
+            roofline["stream_ceiling"] = stream["ceiling"]
+            roofline["pct_of_stream"] = round(100.0 * roofline["achieved"] / stream["ceiling"], 2)
+
     # ---- parity on sampled sequences (the oracle recomputes them from the same bytes) ----
     parity = None
     cpu = None
@@ -341,6 +414,8 @@ def main():
         args.no_cpu_baseline = True  # the CPU baseline is the default (window-free) workload's
     want_oracle = args.parity_seqs > 0 or not args.no_cpu_baseline
     if want_oracle:
+        import concurrent.futures as cf
+
         import oracle
 
         # the last timed step's inputs
@@ -363,22 +438,18 @@ def main():
         torch.cuda.synchronize()
         mask_h = chunk_mask.cpu().numpy()
         out_h = out.cpu().numpy().astype(np.float64)
-        n_samp = max(args.parity_seqs, 0 if args.no_cpu_baseline else args.cpu_sample_seqs)
-        seqs = [int(s) for s in np.linspace(0, B - 1, num=min(n_samp, B)).round()]
         worst = 0.0
-        t_build = 0.0
-        t_step = 0.0
-        bytes_cpu = 0
-        for s_i, b in enumerate(seqs):
-            T = int(lens[b])
-            # a one-sequence oracle cache holding sequence b (contiguous layout)
-            unit = w.group_size if args.vgroup else 16  # pages hold whole value token groups
-            P = int(math.ceil(T / unit) * unit)
-            ref = oracle.Cache(d, Hkv, w.bits, w.group_size, w.hadamard_block, P, 1, quant_mode=cache.quant_mode,
-                               v_grouping=cache.v_grouping)
-            k = wl.keys(w, b, 0, T, device=dev)
-            v = wl.values(w, b, 0, T, device=dev)
-            if windowed:
+
+        if windowed:
+            seqs = [int(s) for s in np.linspace(0, B - 1, num=min(args.parity_seqs, B)).round()]
+            for b in seqs:
+                T = int(lens[b])
+                unit = w.group_size if args.vgroup else 16  # pages hold whole value token groups
+                P = int(math.ceil(T / unit) * unit)
+                ref = oracle.Cache(d, Hkv, w.bits, w.group_size, w.hadamard_block, P, 1,
+                                   quant_mode=cache.quant_mode, v_grouping=cache.v_grouping)
+                k = wl.keys(w, b, 0, T, device=dev)
+                v = wl.values(w, b, 0, T, device=dev)
                 # prefill state, then the last two steps applied to this cache: each step
                 # rewrites the same ring row and evicted slot (or completed group), so they
                 # fix the final state
@@ -405,32 +476,92 @@ def main():
                               np.array([T], np.int32))
                 worst = max(worst, float(np.max(np.abs(o[0] - out_h[b]))))
                 del k, v
-                continue
+            parity = {"max_abs_err": worst, "tolerance": 2e-3, "sequences": seqs, "ok": worst <= 2e-3}
+        else:
+            # Oracle caches of single sequences (contiguous layout), built in host threads:
+            # the oracle is C behind ctypes, which releases the GIL during each call.
+            n_thr = host_threads()
+            n1 = max(args.parity_seqs, 0 if args.no_cpu_baseline else args.cpu_sample_seqs)
+            seqs1 = [int(s) for s in np.linspace(0, B - 1, num=min(max(n1, 1), B)).round()]
+            seqsN = [] if args.no_cpu_baseline or n_thr < 2 else \
+                [int(s) for s in np.linspace(0, B - 1, num=min(n_thr, B)).round()]
+            jobs = seqs1 + [seqsN[i % len(seqsN)] for i in range(n_thr)] if seqsN else list(seqs1)
+            rows = {}
+            for b in sorted(set(jobs)):
+                T = int(lens[b])
+                # the same draw of T tokens the GPU cache was built from (slot T - 1 is then
+                # rewritten by the step's token)
+                k = wl.keys(w, b, 0, T, device=dev)
+                v = wl.values(w, b, 0, T, device=dev)
+                rows[b] = (wl.bf16_bits(k[:T - 1]), wl.bf16_bits(v[:T - 1]))
+                del k, v
+
+            def build_one(b):
+                T = int(lens[b])
+                ref = oracle.Cache(d, Hkv, w.bits, w.group_size, w.hadamard_block, int(math.ceil(T / 16) * 16), 1,
+                                   quant_mode=cache.quant_mode, v_grouping=cache.v_grouping)
+                ref.append(rows[b][0], rows[b][1], np.arange(T - 1))
+                return ref
+
             tb = time.perf_counter()
-            ref.append(wl.bf16_bits(k[:T - 1]), wl.bf16_bits(v[:T - 1]), np.arange(T - 1))
-            t_build += time.perf_counter() - tb
-            del k, v
-            # timed oracle step: append the new token, decode every query head of the sequence
+            with cf.ThreadPoolExecutor(max_workers=max(n_thr, 1)) as ex:
+                refs = list(ex.map(build_one, jobs))
+            t_build = time.perf_counter() - tb
+            rows.clear()
+            kn_h, vn_h, q_h = wl.bf16_bits(kn), wl.bf16_bits(vn), wl.bf16_bits(q_last)
+
+            def oracle_step(i):
+                """One decode step of sequence jobs[i] on its own oracle cache: append the
+                step's token, then fp64 decode of every query head of the sequence."""
+                b = jobs[i]
+                ref, T = refs[i], int(lens[b])
+                ref.append(kn_h[b:b + 1], vn_h[b:b + 1], np.array([T - 1]))
+                one = (np.zeros((1, 1), np.int32), np.array([T], np.int32))
+                if args.prune:  # the oracle takes the kernel's choice of kept chunks
+                    return ref.decode_pruned(q_h[b:b + 1], *one, mask_h[b:b + 1])[0]
+                return ref.decode(q_h[b:b + 1], *one)[0]
+
+            def step_bytes_of(b):
+                return int(lens[b]) * Hkv * per_tok_head + Hq * d * 6 + Hkv * (2 * d * 2 + per_tok_head)
+
+            # one thread, the first len(seqs1) jobs in turn
             ts = time.perf_counter()
-            ref.append(wl.bf16_bits(kn[b:b + 1]), wl.bf16_bits(vn[b:b + 1]), np.array([T - 1]))
-            if args.prune:  # the oracle takes the kernel's choice of kept chunks
-                o = ref.decode_pruned(wl.bf16_bits(q_last[b:b + 1]), np.zeros((1, 1), np.int32),
-                                      np.array([T], np.int32), mask_h[b:b + 1])
-            else:
-                o = ref.decode(wl.bf16_bits(q_last[b:b + 1]), np.zeros((1, 1), np.int32), np.array([T], np.int32))
-            t_step += time.perf_counter() - ts
-            bytes_cpu += T * Hkv * per_tok_head + Hq * d * 6 + Hkv * (2 * d * 2 + per_tok_head)
-            if s_i < args.parity_seqs:
-                worst = max(worst, float(np.max(np.abs(o[0] - out_h[b]))))
-        if args.parity_seqs > 0:
-            parity = {"max_abs_err": worst, "tolerance": 2e-3, "sequences": seqs[:args.parity_seqs],
-                      "ok": worst <= 2e-3}
-        if not args.no_cpu_baseline:
-            cpu = {"value": round(bytes_cpu / t_step / 1e9, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-                   "sample": f"{len(seqs)} of {B} sequences ({Hkv} kv heads, {Hq} q heads, T={int(lens[seqs[0]])}): "
-                             f"oracle append of the step's token + fp64 decode of every query head; "
-                             f"{t_step:.1f}s timed, cache build {t_build:.1f}s untimed",
-                   "cpu": platform.processor() or platform.machine()}
+            outs1 = [oracle_step(i) for i in range(len(seqs1))]
+            t1 = time.perf_counter() - ts
+            checked = list(zip(seqs1, outs1))
+            # n_thr threads, one job each, all started together
+            tN, outsN = None, []
+            if seqsN:
+                idx = list(range(len(seqs1), len(jobs)))
+                ts = time.perf_counter()
+                with cf.ThreadPoolExecutor(max_workers=n_thr) as ex:
+                    outsN = list(ex.map(oracle_step, idx))
+                tN = time.perf_counter() - ts
+                checked += list(zip(jobs[len(seqs1):], outsN))
+            for b, o in checked:
+                worst = max(worst, float(np.max(np.abs(o - out_h[b]))))
+            if args.parity_seqs > 0:
+                parity = {"max_abs_err": worst, "tolerance": 2e-3, "sequences": sorted({b for b, _ in checked}),
+                          "ok": worst <= 2e-3}
+            if not args.no_cpu_baseline:
+                T0 = int(lens[seqs1[0]])
+                bytes1 = sum(step_bytes_of(b) for b in seqs1)
+                one = {"value": round(bytes1 / t1 / 1e9, 6), "unit": "GB/s", "threads": 1,
+                       "sample": f"{len(seqs1)} sequences one after another, {t1:.1f}s"}
+                cpu = {"value": one["value"], "unit": "GB/s", "cores": 1, "kind": "oracle",
+                       "sample": f"{len(seqs1)} of {B} sequences ({Hkv} kv heads, {Hq} q heads, T={T0}): oracle "
+                                 f"append of the step's token + fp64 decode of every query head, one after another; "
+                                 f"{t1:.1f}s timed, cache build {t_build:.1f}s untimed",
+                       "threads_1": one}
+                if tN is not None:
+                    bytesN = sum(step_bytes_of(b) for b in jobs[len(seqs1):])
+                    cpu.update({"value": round(bytesN / tN / 1e9, 6), "cores": n_thr,
+                                "sample": f"{n_thr} sequence steps ({len(set(seqsN))} distinct of {B}; {Hkv} kv "
+                                          f"heads, {Hq} q heads, T={T0}) on {n_thr} host threads at once, each the "
+                                          f"unmodified oracle (append of the step's token + fp64 decode of every "
+                                          f"query head) on its own sequence; {tN:.1f}s timed, cache build "
+                                          f"{t_build:.1f}s untimed"})
+                cpu.update(host_description())
 
     res = {
         "metric": METRIC,
@@ -466,6 +597,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity": parity,
+        "stream": stream,
     }
     print(json.dumps(res), flush=True)
 

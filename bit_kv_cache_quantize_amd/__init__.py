@@ -83,6 +83,7 @@ SIGNATURES = {
     "kvq_decode_attention_pruned": (ctypes.c_int, [_DP, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32, _i32,
                                                    _vp, _vp, _sz, _vp, _vp, _vp, _vp]),
     "kvq_dequantize": (ctypes.c_int, [_DP, _i32, _vp, _i64, _vp, _vp]),
+    "kvq_stream_read": (ctypes.c_int, [_vp, _sz, _vp, _i32, _i32, _vp, _vp, _vp]),
     "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvq_version": (ctypes.c_char_p, []),
 }
@@ -387,3 +388,18 @@ def decode_attention_window(cache: KVCache, window: KVWindow, q: torch.Tensor, b
         st = lib().kvq_decode_attention_window_timed(*args, ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
     _check(st, "kvq_decode_attention_window")
     return out
+
+
+def stream_read(buf: torch.Tensor, nontemporal: bool = True, workgroups_per_cu: int = 8,
+                sink: torch.Tensor | None = None, stream=None, events=None) -> None:
+    """Read-bandwidth probe: read every byte of `buf` (a contiguous device tensor whose
+    size is a multiple of 16 bytes) once with the decode kernel's 16-byte load shape.
+    `events` = (begin, end) raw hipEvent_t handles recorded around the launch."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    ev = events if events is not None else (None, None)
+    st = lib().kvq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(nontemporal),
+                               workgroups_per_cu, _stream(stream), ctypes.c_void_p(ev[0]), ctypes.c_void_p(ev[1]))
+    _check(st, "kvq_stream_read")

@@ -195,6 +195,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   __shared__ float o_s[4][128];  // partial outputs, staged for the workspace stores
   __shared__ float p_s[NBS][4][32];  // p of a super-block's blocks, per head and token
   __shared__ float qsum_s[4][4];
+  __shared__ int qexp_s[4];       // per head: the query carries 2^-qexp in the score MFMAs
   __shared__ half8 aqk_s[8][64];  // score A operands, re-read from LDS for every block
 
   // lane roles: scores use (hQ, nQ) = (lane / 32, lane % 32): heads 2hQ, 2hQ+1 of token nQ;
@@ -459,15 +460,30 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       if (split == 0 && lane == 0 && a.chunk_mask != nullptr) a.chunk_mask[static_cast<int64_t>(b) * c.hkv + hk] = kmask;
     }
     const float qmul = (hb > 0 ? a.rot_c : 1.0f) * a.qscale;
+    // Each head's scaled query is brought to a largest magnitude in [2^13, 2^14) by a
+    // power of two 2^-qe (exact) before the f16 split: no finite query overflows the f16
+    // range, and the lo digit stays clear of the f16 subnormals. The scores multiply the
+    // logits back by 2^qe.
+    float v[8];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      v[e] = x[e] * qmul;
+      amax = fmaxf(amax, fabsf(v[e]));
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));  // the head's 16 lanes
+    const int qe = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 14 : 0;
     _Float16 hi[8], lo[8];
     float part = 0.f;  // group sum of the query as the MFMA sees it (hi + lo)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float v = x[e] * qmul;
-      hi[e] = static_cast<_Float16>(v);
-      lo[e] = static_cast<_Float16>(v - static_cast<float>(hi[e]));
+      const float s = __builtin_amdgcn_ldexpf(v[e], -qe);
+      hi[e] = static_cast<_Float16>(s);
+      lo[e] = static_cast<_Float16>(s - static_cast<float>(hi[e]));
       part += static_cast<float>(hi[e]) + static_cast<float>(lo[e]);
     }
+    if (c16 == 0 && jq < R) qexp_s[jq] = qe;
 #pragma unroll
     for (int p = 0; p < 8; ++p) aqk_s[p][lane] = half8{};
     __syncthreads();
@@ -490,10 +506,13 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   __syncthreads();
 
   float qsum[2][NG];
+  int qexp[2];
 #pragma unroll
-  for (int j2 = 0; j2 < 2; ++j2)
+  for (int j2 = 0; j2 < 2; ++j2) {
+    qexp[j2] = (2 * hQ + j2 < R) ? qexp_s[2 * hQ + j2] : 0;
 #pragma unroll
     for (int g = 0; g < NG; ++g) qsum[j2][g] = (2 * hQ + j2 < R) ? qsum_s[2 * hQ + j2][g] : 0.f;
+  }
 
   // ---- state (exp2 domain) ----
   // p = 2^(logit - mref) with mref = mrun - shift, mrun the running max: the value
@@ -535,7 +554,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
         sa = __builtin_fmaf(lo_f16(kb.km[g]), cs[4 * g + 2 * j2 + 1], sa);
         zb = __builtin_fmaf(hi_f16(kb.km[g]), qsum[j2][g], zb);
       }
-      logit[j2] = sa + zb;
+      logit[j2] = __builtin_amdgcn_ldexpf(sa + zb, qexp[j2]);
       if (TAIL) logit[j2] = (t0 + nQ < end) ? logit[j2] : -INFINITY;
     }
     // materialise the logits here: left to the compiler, the fold sinks to the logits'

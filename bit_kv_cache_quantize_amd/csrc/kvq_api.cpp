@@ -83,7 +83,19 @@ hipError_t split_kernel(const DecodeArgs& a, const Geometry& g, hipStream_t s) {
   return g.v_grouping ? launch_decode_split_vgroup(a, g, s) : launch_decode_split(a, g, s);
 }
 
-kvq_status decode_impl(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+DevWindow dev_window(const kvq_window* w) {
+  DevWindow d;
+  d.k = static_cast<uint16_t*>(w->k);
+  d.v = static_cast<uint16_t*>(w->v);
+  d.sink = w->sink;
+  d.recent = w->recent;
+  d.residual = w->residual;
+  return d;
+}
+
+}  // namespace
+
+kvq_status decode_run(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
                        const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
                        int32_t max_seq_len, float softmax_scale, int32_t num_splits, void* workspace,
                        size_t workspace_bytes_given, float* out, void* stream, void* ev_begin, void* ev_end,
@@ -94,7 +106,9 @@ kvq_status decode_impl(const kvq_cache* cache, const void* q, int32_t batch, int
   if (st != KVQ_OK || batch == 0) return st;
   const Splits sp = splits_for(g, batch, num_q_heads, max_seq_len, num_splits,
                                reference ? SplitKernel::kReference : SplitKernel::kMatrix);
-  if (workspace_bytes_given < workspace_bytes(g, batch, num_q_heads, sp)) return KVQ_ERR_WORKSPACE;
+  const size_t need = workspace_bytes(g, batch, num_q_heads, sp);
+  if (need == SIZE_MAX) return KVQ_ERR_INVALID;  // no such workspace can exist
+  if (workspace_bytes_given < need) return KVQ_ERR_WORKSPACE;
   if (reference && sp.split_len > 2048) return KVQ_ERR_UNSUPPORTED;
   const DecodeArgs a = decode_args(cache, g, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                                    softmax_scale, sp, workspace, out);
@@ -108,40 +122,13 @@ kvq_status decode_impl(const kvq_cache* cache, const void* q, int32_t batch, int
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
-DevWindow dev_window(const kvq_window* w) {
-  DevWindow d;
-  d.k = static_cast<uint16_t*>(w->k);
-  d.v = static_cast<uint16_t*>(w->v);
-  d.sink = w->sink;
-  d.recent = w->recent;
-  d.residual = w->residual;
-  return d;
-}
-
-}  // namespace
 }  // namespace kvq
 
 using namespace kvq;
 
 extern "C" {
 
-int64_t kvq_cache_plane_bytes(const kvq_cache* cache, int32_t plane) {
-  Geometry g;
-  const kvq_status st = check_cache(cache, false, &g);
-  if (st == KVQ_ERR_INVALID || !cache) return -1;
-  if (st == KVQ_ERR_UNSUPPORTED && cache->bits != 2 && cache->bits != 4) return -1;
-  g.d = cache->head_dim;
-  g.hkv = cache->num_kv_heads;
-  g.bits = cache->bits;
-  g.group = cache->group_size;
-  g.ngroups = cache->head_dim / cache->group_size;
-  g.page = cache->page_size;
-  g.row_bytes = cache->head_dim * cache->bits / 8;
-  g.num_pages = cache->num_pages;
-  g.quant_mode = 0;
-  g.v_grouping = 0;
-  return plane_bytes(g, plane);
-}
+int64_t kvq_cache_plane_bytes(const kvq_cache* cache, int32_t plane) { return cache_plane_bytes(cache, plane); }
 
 kvq_status kvq_quantize_append(const kvq_cache* cache, const void* k_new, const void* v_new, const int64_t* slots,
                                int64_t n_new, void* stream) {
@@ -157,15 +144,16 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t
                                   int32_t num_splits) {
   Geometry g;
   if (check_cache(cache, false, &g) != KVQ_OK) return 0;
-  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0) return 0;
-  return workspace_for(g, batch, num_q_heads, max_seq_len, num_splits);
+  if (check_decode_sizes(batch, num_q_heads, max_seq_len, num_splits) != KVQ_OK) return 0;
+  const size_t n = workspace_for(g, batch, num_q_heads, max_seq_len, num_splits);
+  return n == SIZE_MAX ? 0 : n;
 }
 
 int32_t kvq_decode_num_splits(const kvq_cache* cache, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
                               int32_t num_splits) {
   Geometry g;
   if (check_cache(cache, false, &g) != KVQ_OK) return 0;
-  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0) return 0;
+  if (check_decode_sizes(batch, num_q_heads, max_seq_len, num_splits) != KVQ_OK) return 0;
   return splits_for(g, batch, num_q_heads, max_seq_len, num_splits).num_splits;
 }
 
@@ -173,7 +161,7 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t b
                                 const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
                                 int32_t max_seq_len, float softmax_scale, int32_t num_splits, void* workspace,
                                 size_t workspace_bytes, float* out, void* stream) {
-  return decode_impl(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
+  return decode_run(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
                      softmax_scale, num_splits, workspace, workspace_bytes, out, stream, nullptr, nullptr, false);
 }
 
@@ -182,7 +170,7 @@ kvq_status kvq_decode_attention_timed(const kvq_cache* cache, const void* q, int
                                       const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
                                       int32_t num_splits, void* workspace, size_t workspace_bytes, float* out,
                                       void* stream, void* split_begin, void* split_end) {
-  return decode_impl(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
+  return decode_run(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
                      softmax_scale, num_splits, workspace, workspace_bytes, out, stream, split_begin, split_end,
                      false);
 }
@@ -192,7 +180,7 @@ kvq_status kvq_decode_attention_reference(const kvq_cache* cache, const void* q,
                                           int32_t max_pages_per_seq, const int32_t* seq_lens,
                                           int32_t max_seq_len, float softmax_scale, int32_t num_splits,
                                           void* workspace, size_t workspace_bytes, float* out, void* stream) {
-  return decode_impl(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
+  return decode_run(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
                      softmax_scale, num_splits, workspace, workspace_bytes, out, stream, nullptr, nullptr, true);
 }
 
@@ -217,9 +205,10 @@ size_t kvq_decode_window_workspace_bytes(const kvq_cache* cache, const kvq_windo
                                          int32_t num_q_heads, int32_t max_seq_len, int32_t num_splits) {
   Geometry g;
   if (check_cache(cache, false, &g) != KVQ_OK || check_window(cache, window, false) != KVQ_OK) return 0;
-  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0) return 0;
+  if (check_decode_sizes(batch, num_q_heads, max_seq_len, num_splits) != KVQ_OK) return 0;
   const Splits sp = splits_for(g, batch, num_q_heads, window_span(window, max_seq_len), num_splits);
-  return window_workspace_bytes(g, batch, num_q_heads, sp);
+  const size_t n = window_workspace_bytes(g, batch, num_q_heads, sp);
+  return n == SIZE_MAX ? 0 : n;
 }
 
 kvq_status kvq_decode_attention_window_timed(const kvq_cache* cache, const kvq_window* window, const void* q,
@@ -237,7 +226,9 @@ kvq_status kvq_decode_attention_window_timed(const kvq_cache* cache, const kvq_w
   if (batch > window->batch) return KVQ_ERR_INVALID;
   if (batch == 0) return KVQ_OK;
   const Splits sp = splits_for(g, batch, num_q_heads, window_span(window, max_seq_len), num_splits);
-  if (workspace_bytes_given < window_workspace_bytes(g, batch, num_q_heads, sp)) return KVQ_ERR_WORKSPACE;
+  const size_t need = window_workspace_bytes(g, batch, num_q_heads, sp);
+  if (need == SIZE_MAX) return KVQ_ERR_INVALID;
+  if (workspace_bytes_given < need) return KVQ_ERR_WORKSPACE;
   DecodeArgs a = decode_args(cache, g, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                              softmax_scale, sp, workspace, out);
   a.tok_begin = window->sink;
@@ -278,7 +269,9 @@ kvq_status kvq_decode_attention_pruned(const kvq_cache* cache, const void* q, in
   if (chunk_mask && !aligned(chunk_mask, 4)) return KVQ_ERR_INVALID;
   if (batch == 0) return KVQ_OK;
   const Splits sp = splits_for(g, batch, num_q_heads, max_seq_len, num_splits);
-  if (workspace_bytes_given < workspace_bytes(g, batch, num_q_heads, sp)) return KVQ_ERR_WORKSPACE;
+  const size_t need = workspace_bytes(g, batch, num_q_heads, sp);
+  if (need == SIZE_MAX) return KVQ_ERR_INVALID;
+  if (workspace_bytes_given < need) return KVQ_ERR_WORKSPACE;
   DecodeArgs a = decode_args(cache, g, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                              softmax_scale, sp, workspace, out);
   a.keep_chunks = keep_chunks;
@@ -297,6 +290,21 @@ kvq_status kvq_dequantize(const kvq_cache* cache, int32_t which, const int64_t* 
   if (st != KVQ_OK || n == 0) return st;
   const hipError_t e = launch_dequantize(dev_cache(cache, g), g, which, slots, n, out, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t nontemporal,
+                           int32_t workgroups_per_cu, void* stream, void* ev_begin, void* ev_end) {
+  if (!src || !aligned(src, 16) || bytes % 16 != 0 || !sink || !aligned(sink, 4)) return KVQ_ERR_INVALID;
+  if ((nontemporal != 0 && nontemporal != 1) || workgroups_per_cu < 1 || workgroups_per_cu > 32)
+    return KVQ_ERR_INVALID;
+  if (bytes == 0) return KVQ_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return KVQ_ERR_HIP;
+  const int64_t wgs = static_cast<int64_t>(device_cus()) * workgroups_per_cu;
+  if (launch_stream_read(src, static_cast<int64_t>(bytes / 16), sink, nontemporal, wgs, s) != hipSuccess)
+    return KVQ_ERR_HIP;
+  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return KVQ_ERR_HIP;
+  return KVQ_OK;
 }
 
 const char* kvq_status_string(kvq_status status) {

@@ -88,6 +88,9 @@ hipError_t launch_window_append(const DevCache& c, const DevWindow& w, const Geo
                                 const int64_t* evict_slots, int64_t n_new, hipStream_t stream);
 hipError_t launch_dequantize(const DevCache& c, const Geometry& g, int which, const int64_t* slots,
                              int64_t n, float* out, hipStream_t stream);
+// read probe (stream_probe.hip): n16 16-byte pieces at src, `workgroups` of 256 threads
+hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* sink, int nontemporal, int64_t workgroups,
+                              hipStream_t stream);
 
 struct DecodeArgs {
   DevCache c;
@@ -247,5 +250,13 @@ hipError_t launch_decode_split_vgroup(const DecodeArgs& a, const Geometry& g, hi
 hipError_t launch_decode_split_reference(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_window(const DecodeArgs& a, const DevWindow& w, const Geometry& g, hipStream_t stream);
+
+// kvq_decode_attention and its timed and reference variants (kvq_api.cpp): every host check,
+// the split kernel (matrix or reference) and the combine, with the given workspace.
+kvq_status decode_run(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                      const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                      int32_t max_seq_len, float softmax_scale, int32_t num_splits, void* workspace,
+                      size_t workspace_bytes_given, float* out, void* stream, void* ev_begin, void* ev_end,
+                      bool reference);
 
 }  // namespace kvq

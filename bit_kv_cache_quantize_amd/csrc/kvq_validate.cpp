@@ -7,9 +7,26 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 static bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
+// Products of non-negative sizes: -1 (int64) or SIZE_MAX (size_t) when the exact product
+// does not fit, so no size computed here ever wraps.
+static int64_t mul64(int64_t a, int64_t b) {
+  int64_t r;
+  return (a < 0 || b < 0 || __builtin_mul_overflow(a, b, &r)) ? -1 : r;
+}
+static size_t mulsz(size_t a, size_t b) {
+  size_t r;
+  return __builtin_mul_overflow(a, b, &r) ? SIZE_MAX : r;
+}
+static size_t addsz(size_t a, size_t b) {
+  size_t r;
+  return __builtin_add_overflow(a, b, &r) ? SIZE_MAX : r;
+}
+
 kvq_status check_cache(const kvq_cache* c, bool planes, Geometry* g) {
   if (!c) return KVQ_ERR_INVALID;
   if (c->head_dim <= 0 || c->num_kv_heads <= 0 || c->num_pages <= 0) return KVQ_ERR_INVALID;
+  // far beyond any head; keeps every per-row size below in 32 bits
+  if (c->head_dim > kMaxHeadDim) return KVQ_ERR_UNSUPPORTED;
   if (c->bits != 2 && c->bits != 4) {
     // other widths are well formed integers but not a packing this library defines
     return (c->bits > 0 && c->bits <= 8) ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID;
@@ -48,24 +65,35 @@ kvq_status check_cache(const kvq_cache* c, bool planes, Geometry* g) {
 bool cache_supported(const Geometry& g) {
   if (g.d != 128) return false;
   // the decode kernels index a page's rows of one kv head as page * Hkv + head in 32 bits
-  if (g.num_pages * g.hkv > 0xFFFFFFFFLL) return false;
+  if (g.num_pages > 0xFFFFFFFFLL / g.hkv) return false;
   if (g.group != 32 && g.group != 64 && g.group != 128) return false;
   if (g.hblock != 0 && (g.hblock < 2 || g.hblock > 128)) return false;
   return true;
 }
 
 int64_t plane_bytes(const Geometry& g, int plane) {
-  const int64_t tokens = g.num_pages * g.hkv * static_cast<int64_t>(g.page);
+  const int64_t tokens = mul64(mul64(g.num_pages, g.hkv), g.page);
+  if (tokens < 0) return -1;
   switch (plane) {
     case 0:
     case 2:
-      return tokens * g.row_bytes;
+      return mul64(tokens, g.row_bytes);
     case 1:
     case 3:
-      return tokens * g.ngroups * 4;
+      return mul64(tokens, static_cast<int64_t>(g.ngroups) * 4);
     default:
       return -1;
   }
+}
+
+int64_t cache_plane_bytes(const kvq_cache* c, int32_t plane) {
+  Geometry g;
+  const kvq_status st = check_cache(c, false, &g);
+  // well-formed descriptions have sizes whether or not a kernel is built for them; a
+  // width other than 2 or 4 bits has no packing, and an oversized head no geometry
+  if (st == KVQ_ERR_INVALID || !c) return -1;
+  if (st == KVQ_ERR_UNSUPPORTED && ((c->bits != 2 && c->bits != 4) || c->head_dim > kMaxHeadDim)) return -1;
+  return plane_bytes(g, plane);
 }
 
 Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
@@ -129,21 +157,30 @@ Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int3
 
 size_t workspace_bytes(const Geometry& g, int32_t batch, int32_t num_q_heads, const Splits& s) {
   if (s.balanced)
-    return balanced_partials_bytes(g, num_q_heads, s) + (static_cast<size_t>(batch) * 8 + 255) / 256 * 256;
-  return static_cast<size_t>(batch) * num_q_heads * s.num_splits * (g.d + 2) * sizeof(float);
+    return addsz(balanced_partials_bytes(g, num_q_heads, s), (static_cast<size_t>(batch) * 8 + 255) / 256 * 256);
+  return mulsz(mulsz(mulsz(static_cast<size_t>(batch), static_cast<size_t>(num_q_heads)),
+                     static_cast<size_t>(s.num_splits)),
+               static_cast<size_t>(g.d + 2) * sizeof(float));
 }
 
 size_t balanced_partials_bytes(const Geometry& g, int32_t num_q_heads, const Splits& s) {
-  return static_cast<size_t>(num_q_heads) * s.unit_slots * (g.d + 2) * sizeof(float);
+  return mulsz(mulsz(static_cast<size_t>(num_q_heads), static_cast<size_t>(s.unit_slots)),
+               static_cast<size_t>(g.d + 2) * sizeof(float));
 }
 
-kvq_status check_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t num_q_heads,
-                        const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
-                        int32_t max_seq_len, int32_t num_splits, const void* workspace, const float* out,
-                        Geometry* g) {
+kvq_status check_decode_sizes(int32_t batch, int32_t num_q_heads, int32_t max_seq_len, int32_t num_splits) {
+  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0) return KVQ_ERR_INVALID;
+  if (max_seq_len > kMaxSeqLen) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+kvq_status check_decode_args(const kvq_cache* c, const void* q, int32_t batch, int32_t num_q_heads,
+                             const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                             int32_t max_seq_len, int32_t num_splits, const float* out, Geometry* g) {
   kvq_status st = check_cache(c, true, g);
   if (st != KVQ_OK) return st;
-  if (batch < 0 || num_q_heads <= 0 || max_seq_len < 0 || num_splits < 0) return KVQ_ERR_INVALID;
+  st = check_decode_sizes(batch, num_q_heads, max_seq_len, num_splits);
+  if (st != KVQ_OK) return st;
   if (num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID;
   const int ratio = num_q_heads / c->num_kv_heads;
   if (ratio != 1 && ratio != 2 && ratio != 4) return KVQ_ERR_UNSUPPORTED;
@@ -154,6 +191,16 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t batch, int32_
   if (!block_table || !aligned(block_table, 4)) return KVQ_ERR_INVALID;
   if (!seq_lens || !aligned(seq_lens, 4)) return KVQ_ERR_INVALID;
   if (!out || !aligned(out, 16)) return KVQ_ERR_INVALID;
+  return KVQ_OK;
+}
+
+kvq_status check_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t num_q_heads,
+                        const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                        int32_t max_seq_len, int32_t num_splits, const void* workspace, const float* out,
+                        Geometry* g) {
+  const kvq_status st = check_decode_args(c, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                                          max_seq_len, num_splits, out, g);
+  if (st != KVQ_OK || batch == 0) return st;
   if (!workspace || !aligned(workspace, 16)) return KVQ_ERR_INVALID;
   return KVQ_OK;
 }
@@ -187,7 +234,7 @@ kvq_status check_window(const kvq_cache* c, const kvq_window* w, bool planes) {
 }
 
 int64_t window_plane_bytes(const Geometry& g, const kvq_window* w) {
-  return static_cast<int64_t>(w->batch) * (w->sink + w->recent) * g.hkv * g.d * 2;
+  return mul64(mul64(mul64(w->batch, static_cast<int64_t>(w->sink) + w->recent), g.hkv), static_cast<int64_t>(g.d) * 2);
 }
 
 kvq_status check_window_append(const kvq_cache* c, const kvq_window* w, const void* k_new, const void* v_new,
@@ -214,8 +261,9 @@ int32_t window_span(const kvq_window* w, int32_t max_seq_len) {
 }
 
 size_t window_workspace_bytes(const Geometry& g, int32_t batch, int32_t num_q_heads, const Splits& s) {
-  return workspace_bytes(g, batch, num_q_heads, s) +
-         static_cast<size_t>(batch) * num_q_heads * (g.d + 2) * sizeof(float);
+  return addsz(workspace_bytes(g, batch, num_q_heads, s),
+               mulsz(mulsz(static_cast<size_t>(batch), static_cast<size_t>(num_q_heads)),
+                     static_cast<size_t>(g.d + 2) * sizeof(float)));
 }
 
 kvq_status check_dequantize(const kvq_cache* c, int32_t which, const int64_t* slots, int64_t n,

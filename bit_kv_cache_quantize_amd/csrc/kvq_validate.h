@@ -13,6 +13,10 @@ namespace kvq {
 // two 16-token tiles; split-K partitions are whole blocks.
 constexpr int kTile = 16;
 constexpr int kBlock = 32;
+// Size limits of well-formed descriptions: larger values return KVQ_ERR_UNSUPPORTED, so
+// token positions and partition lengths stay far inside 32 bits and per-row sizes too.
+constexpr int32_t kMaxSeqLen = 1 << 30;
+constexpr int32_t kMaxHeadDim = 1 << 16;
 
 struct Geometry {
   int d, hkv, bits, group, ngroups, hblock, page, row_bytes, quant_mode, v_grouping;
@@ -28,7 +32,11 @@ bool cache_supported(const Geometry& g);
 
 bool aligned(const void* p, size_t a);
 
+// Bytes of one cache plane (-1 for a plane index outside 0..3 or a size beyond int64).
 int64_t plane_bytes(const Geometry& g, int plane);
+// kvq_cache_plane_bytes: -1 for an invalid description, a width without a packing
+// (bits other than 2, 4) or a head beyond kMaxHeadDim; sizes also for other unsupported ones.
+int64_t cache_plane_bytes(const kvq_cache* c, int32_t plane);
 
 // Split-K sizing. `cus` is the device's compute-unit count (256 on MI355X).
 // Fixed partitions: every sequence is cut into split_len-token partitions (a caller's
@@ -58,10 +66,20 @@ enum class SplitKernel { kMatrix, kReference };
 Splits choose_splits(const Geometry& g, int32_t batch, int32_t num_q_heads, int32_t max_seq_len,
                      int32_t requested, int cus, SplitKernel kernel);
 
+// Workspace sizes saturate at SIZE_MAX (no configuration that large can be allocated).
 size_t workspace_bytes(const Geometry& g, int32_t batch, int32_t num_q_heads, const Splits& s);
 // Balanced layout: the partials [Hq][unit_slots][d + 2] fp32, then a table of int32 pairs
 // {first unit, partitions} per sequence (written by the split kernel, read by the combine).
 size_t balanced_partials_bytes(const Geometry& g, int32_t num_q_heads, const Splits& s);
+
+// Sizes of a decode call: INVALID for negative counts or no query heads, UNSUPPORTED for
+// max_seq_len beyond kMaxSeqLen.
+kvq_status check_decode_sizes(int32_t batch, int32_t num_q_heads, int32_t max_seq_len, int32_t num_splits);
+
+// Decode arguments other than the workspace (for calls whose workspace is the library's).
+kvq_status check_decode_args(const kvq_cache* c, const void* q, int32_t batch, int32_t num_q_heads,
+                             const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                             int32_t max_seq_len, int32_t num_splits, const float* out, Geometry* g);
 
 // Full check of decode arguments (everything but the workspace size).
 kvq_status check_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t num_q_heads,
@@ -73,6 +91,7 @@ kvq_status check_append(const kvq_cache* c, const void* k_new, const void* v_new
                         int64_t n_new, Geometry* g);
 
 // Window description against the cache (sizes only; `planes` also checks k and v).
+// Plane sizes are -1 when they exceed int64.
 constexpr int kMaxWindow = 1024;  // sink + recent
 kvq_status check_window(const kvq_cache* c, const kvq_window* w, bool planes);
 int64_t window_plane_bytes(const Geometry& g, const kvq_window* w);

@@ -1,0 +1,59 @@
+// Read-bandwidth probe: how fast this GPU streams a buffer out of HBM with the load
+// shape the decode kernel uses (one 16-byte load per lane, consecutive lanes on
+// consecutive 16-byte pieces, so every wave-wide load instruction covers whole 128-byte
+// cache lines). InnerQ (Abstract) and SAW-INT4 (Abstract) both place the cost of decode
+// in moving the KV cache out of memory; this kernel measures the ceiling that movement
+// can reach on the device at hand, next to the decode kernel, in the same process.
+//
+// Each thread reads its pieces with four independent loads in flight per loop trip and
+// folds them into one XOR; the result is written only if it equals a value the caller
+// passes (never, in practice), so the loads stay live and nothing else touches memory.
+#include "kvq_device.h"
+
+namespace kvq {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const u32x4* p) {
+  if (NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <bool NT>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                          uint32_t* __restrict__ sink, uint32_t never) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = load16<NT>(src + i);
+    const u32x4 b = load16<NT>(src + i + stride);
+    const u32x4 c = load16<NT>(src + i + 2 * stride);
+    const u32x4 d = load16<NT>(src + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= load16<NT>(src + i);
+  const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (x == never) sink[0] = x;
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* sink, int nontemporal, int64_t workgroups,
+                              hipStream_t stream) {
+  if (workgroups <= 0 || workgroups > 0x7FFFFFFF) return hipErrorInvalidValue;
+  dim3 grid(static_cast<unsigned>(workgroups)), block(256);
+  const auto* p = static_cast<const u32x4*>(src);
+  // the XOR of random-looking data is never this value in practice; if it were, one
+  // dword of the sink would be written, which the caller provides for that purpose
+  constexpr uint32_t kNever = 0x9E3779B9u;
+  if (nontemporal)
+    hipLaunchKernelGGL((stream_read_kernel<true>), grid, block, 0, stream, p, n16, sink, kNever);
+  else
+    hipLaunchKernelGGL((stream_read_kernel<false>), grid, block, 0, stream, p, n16, sink, kNever);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

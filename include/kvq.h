@@ -26,13 +26,14 @@
  *    than KVQ_OK nothing was launched, except KVQ_ERR_HIP, which reports a failed
  *    launch. Device-side contents are not checked: a slot outside the page pool,
  *    duplicate slots in one append, seq_len beyond the pages of its block-table row,
- *    or non-finite inputs give undefined results.
+ *    or non-finite inputs give undefined results. Finite queries of any magnitude are
+ *    in the domain as long as the logits softmax_scale * (R q) . khat are finite in fp32.
  *  - Supported today: head_dim 128; bits 4 or 2; group_size 32, 64 or 128;
  *    hadamard_block 0 (off) or a power of two from 2 to 128; GQA ratio
  *    num_q_heads / num_kv_heads of 1, 2 or 4; page_size a multiple of 16;
  *    num_pages * num_kv_heads below 2^32 (the decode kernels index a page's rows of
- *    one kv head in 32 bits). Other well-formed descriptions return
- *    KVQ_ERR_UNSUPPORTED.
+ *    one kv head in 32 bits); max_seq_len up to 2^30. Other well-formed descriptions
+ *    return KVQ_ERR_UNSUPPORTED.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -146,7 +147,8 @@ kvq_status kvq_quantize_append(const kvq_cache* cache, const void* k_new, const 
  * bound on one kv head's partitions, then two int32 per sequence (the split kernel's
  * record of where each sequence's partials start, for the combine); the reference
  * kernel takes fixed partitions of up
- * to 2048 tokens; the size covers both. Returns 0 for an invalid description.
+ * to 2048 tokens; the size covers both. Returns 0 for an invalid description and for
+ * sizes that do not fit in size_t (the decode calls then return KVQ_ERR_INVALID).
  *
  * Balanced partitions (kvq_decode_attention, _timed, _pruned and _window with
  * num_splits 0 and 2 <= batch <= 256): one partition length L for the whole call, computed on
@@ -247,9 +249,12 @@ kvq_status kvq_decode_attention_pruned(const kvq_cache* cache, const void* q, in
                                        void* split_begin, void* split_end);
 
 /*
- * Dequantize n stored rows: out fp32 [n][Hkv][d] = fma(code, scale, zero) per
- * element, read from the rows at `slots` (int64 device array). which = 0 reads K
- * (in the rotated basis), 1 reads V. Bit-exact. For checks and export.
+ * Dequantize n stored rows (InnerQ, Abstract: asymmetric group quantization with a scale
+ * and a zero point per group; SAW-INT4, Abstract: token-wise INT4 keys and values):
+ * out fp32 [n][Hkv][d] = fma(code, scale, zero) per element, one fp32 rounding, read from
+ * the rows at `slots` (int64 device array, page * P + offset, not checked). which = 0
+ * reads K (in the rotated basis), 1 reads V (value token groups: each channel's
+ * {scale, zero} of its token group). Bit-exact. For checks and export.
  */
 kvq_status kvq_dequantize(const kvq_cache* cache, int32_t which, const int64_t* slots, int64_t n,
                           float* out, void* stream);
@@ -340,6 +345,21 @@ kvq_status kvq_decode_attention_window_timed(const kvq_cache* cache, const kvq_w
                                              int32_t max_seq_len, float softmax_scale, int32_t num_splits,
                                              void* workspace, size_t workspace_bytes, float* out,
                                              void* stream, void* split_begin, void* split_end);
+
+/*
+ * Read-bandwidth probe, a measurement aid (InnerQ, Abstract, and SAW-INT4, Abstract: the
+ * cost of decode lies in reading the KV cache from memory, so the decode kernel is
+ * measured against the read rate the device sustains). Reads the `bytes` bytes at `src`
+ * (device memory, 16-byte aligned, bytes a multiple of 16) once, with 16-byte loads laid
+ * out as the decode kernel's (consecutive lanes on consecutive 16-byte pieces, so each
+ * wave-wide load covers whole cache lines), non-temporal when `nontemporal` is 1, from
+ * workgroups_per_cu (1..32) workgroups of 256 threads per compute unit. Nothing is
+ * written except, with negligible probability, the first dword of `sink` (a device
+ * word the caller provides). Records the hipEvent_t `ev_begin` / `ev_end` (either may be
+ * NULL) around the launch on `stream`. bytes == 0 is a no-op returning KVQ_OK.
+ */
+kvq_status kvq_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t nontemporal,
+                           int32_t workgroups_per_cu, void* stream, void* ev_begin, void* ev_end);
 
 /* Static description of a status code. */
 const char* kvq_status_string(kvq_status status);

@@ -381,3 +381,43 @@ def test_vgroup_argument_checks():
     assert L.kvq_window_append(ctypes.byref(_desc(page_size=16)), ctypes.byref(_win(sink=0, recent=32, residual=1)),
                                *args, 1, None) == kvq.ERR_INVALID  # a group would cross pages
     assert _decode_pruned(d) == kvq.ERR_UNSUPPORTED
+
+
+def test_stream_read_argument_checks():
+    """The read probe rejects misaligned or odd-sized buffers and out-of-range settings
+    before any launch; an empty read launches nothing."""
+    L, v = kvq.lib(), ctypes.c_void_p
+
+    def call(src=FAKE, nbytes=1 << 20, sink=FAKE, nt=1, wpc=8):
+        return L.kvq_stream_read(v(src), nbytes, v(sink), nt, wpc, None, None, None)
+
+    assert call(src=0) == kvq.ERR_INVALID
+    assert call(src=FAKE + 4) == kvq.ERR_INVALID
+    assert call(nbytes=(1 << 20) + 8) == kvq.ERR_INVALID
+    assert call(sink=0) == kvq.ERR_INVALID
+    assert call(sink=FAKE + 2) == kvq.ERR_INVALID
+    assert call(nt=2) == kvq.ERR_INVALID
+    assert call(wpc=0) == kvq.ERR_INVALID
+    assert call(wpc=33) == kvq.ERR_INVALID
+    assert call(nbytes=0) == kvq.OK
+
+
+def test_size_limits():
+    """Sizes past the documented limits are refused, never wrapped: a context beyond 2^30
+    tokens is unsupported, and workspace sizes that do not fit in size_t are reported as 0
+    (invalid) rather than as a small wrapped number."""
+    L = kvq.lib()
+    d = _desc(num_pages=1 << 20)
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 4, 32, (1 << 30) + 1, 0) == 0
+    assert L.kvq_decode_num_splits(ctypes.byref(d), 4, 32, (1 << 30) + 1, 0) == 0
+    assert _decode(d, maxlen=(1 << 30) + 1, maxp=1 << 20) == kvq.ERR_UNSUPPORTED
+    # batch * heads * splits * 520 B beyond 2^64
+    big = L.kvq_decode_workspace_bytes(ctypes.byref(d), 2 ** 31 - 1, 32, 1 << 30, 2 ** 31 - 1)
+    assert big == 0
+    assert _decode(d, batch=2 ** 31 - 1, hq=32, maxlen=1 << 30, splits=2 ** 31 - 1, maxp=1 << 20,
+                   wsb=2 ** 64 - 1) == kvq.ERR_INVALID
+    # pools whose page count overflows int64 products
+    huge = _desc(num_pages=2 ** 62)
+    assert L.kvq_cache_plane_bytes(ctypes.byref(huge), 0) == -1
+    w = kvq._Window(16, 128, 2 ** 31 - 1, FAKE, FAKE, 0)
+    assert L.kvq_window_plane_bytes(ctypes.byref(_desc(num_kv_heads=2 ** 31 - 1, num_pages=1)), ctypes.byref(w)) == -1
