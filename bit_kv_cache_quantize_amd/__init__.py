@@ -80,6 +80,8 @@ SIGNATURES = {
                                                    _vp, _sz, _vp, _vp]),
     "kvq_decode_attention_window_timed": (ctypes.c_int, [_DP, _WP, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32,
                                                          _i32, _vp, _sz, _vp, _vp, _vp, _vp]),
+    "kvq_decode_attention_noalloc": (ctypes.c_int, [_DP, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32, _vp,
+                                                    _vp]),
     "kvq_decode_attention_pruned": (ctypes.c_int, [_DP, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32, _i32,
                                                    _vp, _vp, _sz, _vp, _vp, _vp, _vp]),
     "kvq_dequantize": (ctypes.c_int, [_DP, _i32, _vp, _i64, _vp, _vp]),
@@ -254,6 +256,27 @@ def decode_attention(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor,
     else:
         st = lib().kvq_decode_attention(*args)
     _check(st, "kvq_decode_attention")
+    return out
+
+
+NOALLOC_WORKSPACE_BYTES = 32 << 20  # KVQ_NOALLOC_WORKSPACE_BYTES
+
+
+def decode_attention_noalloc(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                             max_seq_len: int, out: torch.Tensor, softmax_scale: float = 0.0, num_splits: int = 0,
+                             stream=None) -> torch.Tensor:
+    """decode_attention with the library's own device workspace (kvq_decode_attention_noalloc):
+    the C call allocates nothing, so `out` (fp32 [B][Hq][d]) is the caller's. Calls that
+    overlap on one GPU share that workspace and race."""
+    _need(q, torch.bfloat16, "q")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(out, torch.float32, "out")
+    B, Hq, d = q.shape
+    st = lib().kvq_decode_attention_noalloc(ctypes.byref(cache.desc), _ptr(q), B, Hq, _ptr(block_table),
+                                            block_table.shape[1], _ptr(seq_lens), max_seq_len, softmax_scale,
+                                            num_splits, _ptr(out), _stream(stream))
+    _check(st, "kvq_decode_attention_noalloc")
     return out
 
 

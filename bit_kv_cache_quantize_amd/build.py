@@ -17,7 +17,8 @@ OUT = os.path.join(PKG, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "kvq")
 
 SOURCES = ["kvq_validate.cpp", "kvq_api.cpp", "quant.hip", "decode_ref.hip", "decode_mfma.hip", "decode_pruned.hip",
-           "decode_vgroup.hip", "decode_window.hip", "stream_probe.hip"]
+           "decode_vgroup.hip", "decode_window.hip", "stream_probe.hip",
+           "decode_noalloc.hip"]
 
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 # -packed-fp32-ops: never emit packed fp32 VALU forms (v_pk_fma_f32 and friends).

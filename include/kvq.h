@@ -224,6 +224,25 @@ kvq_status kvq_decode_attention_reference(const kvq_cache* cache, const void* q,
                                           void* workspace, size_t workspace_bytes, float* out, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): kvq_decode_attention without the
+ * workspace arguments. The split partials and the balanced plan's table go to a device
+ * array the library owns, KVQ_NOALLOC_WORKSPACE_BYTES (32 MiB) per device, held from the
+ * first call on a device until the process ends; the call allocates nothing. A call
+ * whose matrix-kernel workspace would exceed it returns KVQ_ERR_WORKSPACE before any
+ * launch (kvq_decode_workspace_bytes() is an upper bound of that size). Every call on a
+ * device shares the one array: calls that overlap on one GPU (other streams or host
+ * threads) race and must be serialised by the caller. Nothing in the array needs to
+ * start at zero: every byte the combine reads is written by the same call's split kernel.
+ * Same arguments and the same result, bit for bit, as kvq_decode_attention otherwise.
+ */
+#define KVQ_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                                        const int32_t* block_table, int32_t max_pages_per_seq,
+                                        const int32_t* seq_lens, int32_t max_seq_len, float softmax_scale,
+                                        int32_t num_splits, float* out, void* stream);
+
+/*
  * Decode attention with dynamic query-channel pruning of key reads (Dual-QK, Abstract:
  * query-channel pruning further reduces key-cache reads). Arguments as
  * kvq_decode_attention (same workspace size), plus:
