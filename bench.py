@@ -195,6 +195,8 @@ def main():
     ap.add_argument("--prune", type=int, default=0,
                     help="query-channel pruning: key chunks kept per (sequence, kv head), of bits * head_dim / 128")
     ap.add_argument("--no-stream-probe", action="store_true", help="skip the read-stream ceiling measurement")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps replayed from a HIP graph (value and ms_per_step then come from it)")
     ap.add_argument("--stream-gib", type=int, default=4, help="GiB read by the read-stream probe")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg, fp32) of this many MiB before timing, "
@@ -357,6 +359,45 @@ def main():
     if not args.reference:
         split_ms = float(np.mean([hip_events.elapsed_ms(i) for i in range(args.steps)]))
     hip_events.close()
+
+    # The same steps replayed from a HIP graph: one launch per graph instead of three
+    # host calls per step, so short steps are not paced by the host. The graph holds one
+    # cycle of the layer ring and the input rotation; its last replayed step must give the
+    # eager step's output bit for bit.
+    graph = None
+    if args.graph:
+        if windowed or args.reference:
+            sys.exit("bench.py: --graph times the plain or pruned decode step")
+        per = ring * n_inputs // math.gcd(ring, n_inputs)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(per):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(per):
+                step(i)
+        reps = max(1, -(-args.steps // per))
+        for _ in range(max(1, -(-args.warmup // per))):
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(reps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / (reps * per)
+        replayed = out.clone()
+        step(per - 1)
+        torch.cuda.synchronize()
+        graph = {"us_per_step": round(graph_ms * 1e3, 2), "steps": reps * per, "steps_per_graph": per,
+                 "matches_eager": bool(torch.equal(replayed, out)), "us_per_step_eager": round(ms * 1e3, 2)}
+        ms = graph_ms
+        del g
 
     # algorithmic bytes (what the method must move; no re-reads, no partials)
     per_tok_head = wl.kv_bytes_per_token_head(d, w.bits, w.group_size)
@@ -598,6 +639,7 @@ def main():
         "cpu_baseline": cpu,
         "parity": parity,
         "stream": stream,
+        "graph": graph,
     }
     print(json.dumps(res), flush=True)
 

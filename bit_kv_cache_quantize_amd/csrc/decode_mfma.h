@@ -33,6 +33,18 @@
 //     yields both tokens' codes for a channel side by side;
 //   the zero term sum_t p * zero_g(t) is accumulated separately in fp32.
 // Partials (unnormalised o, reference max m, sum l) go to the workspace for the combine.
+//
+// Groups of 64 or 128 channels (two or one per head) take a leaner form of both passes:
+// Scores, v_mfma_i32_16x16x64_i8, 4 per block: C[row][token] over 64 channels per K-step
+//   A rows = (query head jj, digit d): the rotated, pre-scaled query of head jj as four
+//     signed int8 digits (base 128, first digit within +-64: 2^-28 of the head's largest
+//     element), so one i32 sum per digit is exact; the lane holding a head's four digit
+//     sums combines them.
+//   B = the codes as int8 bytes, from masks alone. Each K-step lies inside one group; the
+//     two 16-token tiles of a block are the two N-tiles. Lane (head q, token n) receives
+//     the logits of head q for token n of both tiles. A stays in registers.
+// Values: one 16x16x32 product per N-tile: the hi and lo digits of W take separate A rows
+//   (head, digit, group), summed after the partition.
 #pragma once
 
 #include <type_traits>
@@ -43,6 +55,7 @@ namespace kvq {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -123,13 +136,53 @@ __device__ __forceinline__ half8 unpack_v(const uint32_t* vc, int nt) {
                   codes_f16x2<false>(x[3]));
 }
 
+// Narrow groups (G = 64, 128). Channel held by K-slot s (0..15) of K-step k (0, 1) in lane
+// group q (0..3, the lanes 16q..16q+15) of the int8 score MFMAs: the order in which
+// unpack_k_i8() lays a K-step's codes into the B operand (and the prologue the query digits
+// into A). A K-step's 16 channels of lane group q are 2 * BITS contiguous code bytes of the
+// packed row; at G = 64 K-step k covers group k.
+template <int BITS, int G>
+__device__ __forceinline__ int narrow_channel(int k, int q, int s) {
+  const int base = G == 128 ? 32 * q + 16 * k : 64 * k + 16 * q;
+  if (BITS == 4) {
+    const int w = s >> 2, j = s & 3;  // dword w of the operand: low / high nibbles of two dwords
+    return base + 8 * (w >> 1) + 2 * j + (w & 1);
+  }
+  return base + 4 * (s & 3) + (s >> 2);  // dword s / 4 holds crumb s / 4 of the 4 bytes
+}
+// Its inverse: the position 32 q + 16 k + s of channel c in a row of A operands.
+template <int BITS, int G>
+__device__ __forceinline__ int narrow_position(int c) {
+  const int q = G == 128 ? c >> 5 : (c >> 4) & 3;
+  const int k = G == 128 ? (c >> 4) & 1 : c >> 6;
+  const int off = c & 15;
+  const int s = BITS == 4 ? 4 * (2 * (off >> 3) + (off & 1)) + ((off >> 1) & 3) : 4 * (off & 3) + (off >> 2);
+  return 32 * q + 16 * k + s;
+}
+// B operand of one K-step: its BITS / 2 dwords of packed codes spread into 16 int8 codes.
+template <int BITS>
+__device__ __forceinline__ i32x4 unpack_k_i8(const uint32_t* d) {
+  if (BITS == 4)
+    return i32x4{static_cast<int>(d[0] & 0x0F0F0F0Fu), static_cast<int>((d[0] >> 4) & 0x0F0F0F0Fu),
+                 static_cast<int>(d[1] & 0x0F0F0F0Fu), static_cast<int>((d[1] >> 4) & 0x0F0F0F0Fu)};
+  return i32x4{static_cast<int>(d[0] & 0x03030303u), static_cast<int>((d[0] >> 2) & 0x03030303u),
+               static_cast<int>((d[0] >> 4) & 0x03030303u), static_cast<int>((d[0] >> 6) & 0x03030303u)};
+}
+
 __device__ __forceinline__ float lo_f16(uint32_t m) { return f16_bits_to_float(m & 0xFFFFu); }
 __device__ __forceinline__ float hi_f16(uint32_t m) { return f16_bits_to_float(m >> 16); }
 
-template <int BITS, int NG>
+template <int BITS, int NG, bool NARROW>
 struct KBlock {
   uint32_t kc[BITS == 4 ? 8 : 4];  // key codes of the lane's token, channels 64h..64h+63
   uint32_t km[NG];                 // key {scale, zero} of the lane's token
+};
+// narrow groups: per 16-token tile t, the lane's code dwords of both K-steps (BITS / 2 each)
+// and the {scale, zero} of its token in that tile
+template <int BITS, int NG>
+struct KBlock<BITS, NG, true> {
+  uint32_t kc[2][BITS];
+  uint32_t km[2][NG];
 };
 
 template <int BITS>
@@ -161,6 +214,8 @@ template <int BITS, int G, int R, bool PRUNE, bool VT>
 __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   constexpr int NG = 128 / G;
   constexpr int RB = 128 * BITS / 8;
+  // one or two groups per head: int8 score MFMAs and merged value digits (see the top)
+  constexpr bool NARROW = NG <= 2 && !PRUNE && !VT;
   const DevCache& c = a.c;
   const int lane = threadIdx.x;
   const int unit = blockIdx.x;
@@ -197,13 +252,18 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   __shared__ float qsum_s[4][4];
   __shared__ int qexp_s[4];       // per head: the query carries 2^-qexp in the score MFMAs
   __shared__ half8 aqk_s[8][64];  // score A operands, re-read from LDS for every block
+  __shared__ __align__(16) int8_t dig_s[4][4][128];  // narrow: query digits in A-operand order
 
   // lane roles: scores use (hQ, nQ) = (lane / 32, lane % 32): heads 2hQ, 2hQ+1 of token nQ;
   // values use (q4, r16) = (lane / 16, lane % 16): A row r16 = 4g + jj, tokens 8q4..8q4+7,
   // B column r16.
+  // Narrow groups: scores use (qS, nS) = (lane / 16, lane % 16): head qS, token nS of each
+  // tile; value A row r16 = 8g + 4d + jj (d = the digit of W).
   const int hQ = lane >> 5, nQ = lane & 31;
   const int q4 = lane >> 4, r16 = lane & 15;
-  const int jjV = r16 & 3, gV = r16 >> 2;
+  const int qS = q4, nS = r16;
+  const int jjV = r16 & 3, gV = NARROW ? r16 >> 3 : r16 >> 2;
+  const int dV = (r16 >> 2) & 1;
   const int gVc = gV < NG ? gV : NG - 1;
   // -1 the compiler cannot see: keeps fma(f16 -> f32 x, -1, y) a single mixed-precision FMA
   float neg1 = -1.0f;
@@ -298,8 +358,58 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   constexpr int NCH = RB / 16;
   int kmask = (1 << NCH) - 1;
 
-  auto load_k = [&](Cursor& cu) {
-    KBlock<BITS, NG> kb;
+  // narrow: lane group qS's code bytes of K-step k start at byte knb[k] of the packed row
+  // (G = 128: both K-steps in one piece of 4 BITS bytes)
+  int knoff[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int bk = G == 128 ? 4 * qS * BITS + 2 * k * BITS : 8 * k * BITS + 2 * qS * BITS;
+    knoff[k] = ((bk >> 4) * 16 + nS) * 16 + (bk & 15);
+  }
+  auto load_k_narrow = [&](Cursor& cu) {
+    KBlock<BITS, NG, true> kb;
+    int64_t row0, row1;
+    if (one_page && start + 32 * cu.blk + 32 <= end) {
+      row0 = row_base + start + 32 * cu.blk;  // a multiple of 16
+      row1 = row0 + 16;
+    } else {
+      tile_rows(cu, row0, row1);
+    }
+    advance(cu);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t row = t ? row1 : row0;
+      const uint8_t* tile = c.kc + row * RB;
+      if (G == 128 && BITS == 4) {
+        const u32x4 x = ld16(tile + knoff[0]);
+        kb.kc[t][0] = x[0]; kb.kc[t][1] = x[1]; kb.kc[t][2] = x[2]; kb.kc[t][3] = x[3];
+      } else if (G == 128) {
+        const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tile + knoff[0]));
+        kb.kc[t][0] = x[0]; kb.kc[t][1 % BITS] = x[1];
+      } else {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          if (BITS == 4) {
+            const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tile + knoff[k]));
+            kb.kc[t][2 * k] = x[0]; kb.kc[t][(2 * k + 1) % BITS] = x[1];
+          } else {
+            kb.kc[t][k % BITS] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tile + knoff[k]));
+          }
+        }
+      }
+      const uint32_t* m = c.km + (row + nS) * NG;
+      if (NG == 2) {
+        const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(m));
+        kb.km[t][0] = x[0]; kb.km[t][1 % NG] = x[1];
+      } else {
+        kb.km[t][0] = __builtin_nontemporal_load(m);
+      }
+    }
+    return kb;
+  };
+  auto load_k_wide = [&](Cursor& cu) {
+    KBlock<BITS, NG, false> kb;
     const uint8_t* src;
     const uint8_t* msrc;
     if (one_page && start + 32 * cu.blk + 32 <= end) {
@@ -333,6 +443,12 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       kb.km[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(msrc));
     }
     return kb;
+  };
+  auto load_k = [&](Cursor& cu) {
+    if constexpr (NARROW)
+      return load_k_narrow(cu);
+    else
+      return load_k_wide(cu);
   };
   auto load_v = [&](Cursor& cu) {
     VBlock<BITS> vb;
@@ -384,7 +500,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   };
 
   // the first key blocks are in flight while the query is prepared
-  KBlock<BITS, NG> kb[PF + 1];
+  KBlock<BITS, NG, NARROW> kb[PF + 1];
   VBlock<BITS> vb[PF + 1];
   Cursor kcur = cur0, vcur = cur0;
 #pragma unroll
@@ -474,6 +590,35 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));  // the head's 16 lanes
     const int qe = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 14 : 0;
+    if constexpr (NARROW) {
+      // Four int8 digits per channel, base 128: x = v 2^-ne lies in (-64, 64); d0 = rint(x),
+      // then each next digit is rint(128 r) of the previous remainder r (|r| <= 1/2), every
+      // step exact in fp32, so x = d0 + d1 2^-7 + d2 2^-14 + d3 2^-21 up to 2^-22. The score
+      // MFMAs sum each digit against the codes in int32 (exact); the sums are recombined as
+      // D = 2^21 d0 + 2^14 d1 + 2^7 d2 + d3 per channel, and the logits carry 2^(ne - 21).
+      const int ne = amax > 0.f ? __builtin_amdgcn_frexp_expf(amax) - 6 : 0;
+      float part = 0.f;  // the lane's sum of D 2^-21 over its 8 channels
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float r = __builtin_amdgcn_ldexpf(v[e], -ne);
+        float dg[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dg[i] = __builtin_rintf(r);
+          r = (r - dg[i]) * 128.0f;
+        }
+        if (jq < R) {
+          const int pos = narrow_position<BITS, G>(8 * c16 + e);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dig_s[jq][i][pos] = static_cast<int8_t>(dg[i]);
+        }
+        part += dg[0] + dg[1] * 0x1p-7f + dg[2] * 0x1p-14f + dg[3] * 0x1p-21f;
+      }
+#pragma unroll
+      for (int m = 1; m < G / 8; m <<= 1) part += __shfl_xor(part, m, 64);
+      if (jq < R && (c16 % (G / 8)) == 0) qsum_s[jq][(8 * c16) / G] = part * 0x1p21f;
+      if (c16 == 0 && jq < R) qexp_s[jq] = ne - 21;
+    } else {
     _Float16 hi[8], lo[8];
     float part = 0.f;  // group sum of the query as the MFMA sees it (hi + lo)
 #pragma unroll
@@ -502,16 +647,30 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int m = 1; m < G / 8; m <<= 1) part += __shfl_xor(part, m, 64);
     if (jq < R && (c16 % (G / 8)) == 0) qsum_s[jq][(8 * c16) / G] = part;
+    }
   }
   __syncthreads();
 
+  // narrow: the score A operands of both K-steps, held in registers (lane: row r16 = 4 jj + d
+  // of A, K-slots 16 q4 ..; rows of heads beyond R are zero)
+  i32x4 aq[2] = {i32x4{0, 0, 0, 0}, i32x4{0, 0, 0, 0}};
+  if constexpr (NARROW) {
+    const int jjA = r16 >> 2, dA = r16 & 3;
+    if (jjA < R) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) aq[k] = *reinterpret_cast<const i32x4*>(&dig_s[jjA][dA][32 * q4 + 16 * k]);
+    }
+  }
+
+  // the query sums and the power of two of the lane's heads: 2hQ + j2 (narrow: qS only)
   float qsum[2][NG];
   int qexp[2];
 #pragma unroll
   for (int j2 = 0; j2 < 2; ++j2) {
-    qexp[j2] = (2 * hQ + j2 < R) ? qexp_s[2 * hQ + j2] : 0;
+    const int jh = NARROW ? qS : 2 * hQ + j2;
+    qexp[j2] = (jh < R) ? qexp_s[jh] : 0;
 #pragma unroll
-    for (int g = 0; g < NG; ++g) qsum[j2][g] = (2 * hQ + j2 < R) ? qsum_s[2 * hQ + j2][g] : 0.f;
+    for (int g = 0; g < NG; ++g) qsum[j2][g] = (jh < R) ? qsum_s[jh][g] : 0.f;
   }
 
   // ---- state (exp2 domain) ----
@@ -523,8 +682,47 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   float mrun[2], mref[2], lsum[2], zacc;
   floatx4 acc[8];
 
+  // scores of one block, narrow groups: logits of head qS for token nS of tiles 0 and 1
+  auto qk_narrow = [&](const KBlock<BITS, NG, true>& kb, int t0, auto tail, float (&logit)[2]) {
+    constexpr bool TAIL = decltype(tail)::value;
+    i32x4 C[2][NG];
+    __builtin_amdgcn_s_setprio(1);  // the matrix-core cluster (see below)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        __builtin_amdgcn_sched_barrier(0);
+        const i32x4 bk = unpack_k_i8<BITS>(&kb.kc[t][k * (BITS / 2)]);
+        const i32x4 zero = {0, 0, 0, 0};
+        if (NG == 1)
+          C[t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[k], bk, k == 0 ? zero : C[t][0], 0, 0, 0);
+        else
+          C[t][k % NG] = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[k], bk, zero, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float acc = 0.f;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        // rows 4 qS + d of C: head qS, digit d. Pairs of digit sums recombine exactly in
+        // integers below 2^24 (|sum| <= 64 * 15 * 128 per digit), then one fp32 FMA.
+        const int hi = static_cast<int>((static_cast<uint32_t>(C[t][g][0]) << 7) + static_cast<uint32_t>(C[t][g][1]));
+        const int lo = static_cast<int>((static_cast<uint32_t>(C[t][g][2]) << 7) + static_cast<uint32_t>(C[t][g][3]));
+        const float sum = __builtin_fmaf(static_cast<float>(hi), 16384.0f, static_cast<float>(lo));
+        acc = __builtin_fmaf(lo_f16(kb.km[t][g]), sum, acc);
+        acc = __builtin_fmaf(hi_f16(kb.km[t][g]), qsum[0][g], acc);
+      }
+      logit[t] = __builtin_amdgcn_ldexpf(acc, qexp[0]);
+      if (TAIL) logit[t] = (t0 + 16 * t + nS < end) ? logit[t] : -INFINITY;
+    }
+    asm volatile("" : "+v"(logit[0]), "+v"(logit[1]));
+  };
+
   // scores of one block: logits of heads 2hQ, 2hQ+1 for token nQ
-  auto qk = [&](const KBlock<BITS, NG>& kb, int t0, auto tail, float (&logit)[2]) {
+  auto qk_wide = [&](const KBlock<BITS, NG, false>& kb, int t0, auto tail, float (&logit)[2]) {
     constexpr bool TAIL = decltype(tail)::value;
     half8 a_next[2] = {aqk_s[0][lane], aqk_s[1][lane]};
     floatx16 cs;
@@ -561,10 +759,35 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     // later use and every block's 16 score registers stay live until then
     asm volatile("" : "+v"(logit[0]), "+v"(logit[1]));
   };
+  auto qk = [&](const KBlock<BITS, NG, NARROW>& kb, int t0, auto tail, float (&logit)[2]) {
+    if constexpr (NARROW)
+      qk_narrow(kb, t0, tail, logit);
+    else
+      qk_wide(kb, t0, tail, logit);
+  };
 
   // new running max from the lane-local maxima bm of a group of blocks; rescales the
   // state to the new reference (unconditionally: alpha = 1 when the max is unchanged)
   auto advance_max = [&](float bm0, float bm1, float shift) {
+    if constexpr (NARROW) {
+      // both logit slots belong to head qS: one max over the slots and the head's 16 lanes
+      float bm = fmaxf(bm0, bm1);
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1) bm = fmaxf(bm, __shfl_xor(bm, m, 64));
+      const float n0 = fmaxf(mrun[0], bm);
+      const float r0 = n0 - shift;
+      const float al = __builtin_amdgcn_exp2f(mref[0] - r0);
+      mrun[0] = n0;
+      mref[0] = r0;
+      lsum[0] *= al;
+      const float alpha[4] = {__shfl(al, 0, 64), __shfl(al, 16, 64), __shfl(al, 32, 64), __shfl(al, 48, 64)};
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nt][r] *= alpha[r];
+      zacc *= alpha[jjV];
+      return;
+    }
 #pragma unroll
     for (int m = 16; m >= 1; m >>= 1) {
       bm0 = fmaxf(bm0, __shfl_xor(bm0, m, 64));
@@ -610,12 +833,20 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < NBS; ++j) {
       if (!GUARD || j < n) {
-        const float p0 = __builtin_amdgcn_exp2f(lg[j][0] - mref[0]);
-        const float p1 = __builtin_amdgcn_exp2f(lg[j][1] - mref[1]);
-        lsum[0] += p0;
-        lsum[1] += p1;
-        p_s[j][2 * hQ][nQ] = p0;
-        p_s[j][2 * hQ + 1][nQ] = p1;
+        if constexpr (NARROW) {  // head qS, tokens nS and 16 + nS
+          const float p0 = __builtin_amdgcn_exp2f(lg[j][0] - mref[0]);
+          const float p1 = __builtin_amdgcn_exp2f(lg[j][1] - mref[0]);
+          lsum[0] += p0 + p1;
+          p_s[j][qS][nS] = p0;
+          p_s[j][qS][16 + nS] = p1;
+        } else {
+          const float p0 = __builtin_amdgcn_exp2f(lg[j][0] - mref[0]);
+          const float p1 = __builtin_amdgcn_exp2f(lg[j][1] - mref[1]);
+          lsum[0] += p0;
+          lsum[1] += p1;
+          p_s[j][2 * hQ][nQ] = p0;
+          p_s[j][2 * hQ + 1][nQ] = p1;
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -663,6 +894,22 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       const float lo0 = __builtin_fmaf(lo_f16(ahi[k]), neg1, w[0]);
       const float lo1 = __builtin_fmaf(hi_f16(ahi[k]), neg1, w[1]);
       alo[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo0, lo1));
+    }
+    if constexpr (NARROW) {
+      // the lane's A row carries one digit of W (row r16 = 8g + 4d + jj): one product per
+      // N-tile, the two digits' rows summed after the partition
+      const half8 A = dV ? as_half8(alo[0], alo[1], alo[2], alo[3]) : as_half8(ahi[0], ahi[1], ahi[2], ahi[3]);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int nt = 0; nt < 8; nt += 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        const half8 bv0 = unpack_v<BITS>(vb.vc, nt);
+        const half8 bv1 = unpack_v<BITS>(vb.vc, nt + 1);
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bv0, acc[nt], 0, 0, 0);
+        acc[nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bv1, acc[nt + 1], 0, 0, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      return true;
     }
     const half8 Ahi = as_half8(ahi[0], ahi[1], ahi[2], ahi[3]);
     const half8 Alo = as_half8(alo[0], alo[1], alo[2], alo[3]);
@@ -796,10 +1043,15 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   }
 
   // ---- partials: o[jj][ch] = acc + Z[jj][g(ch)], m = mref, l ----
+  if constexpr (NARROW) {
 #pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) {
-    lsum[0] += __shfl_xor(lsum[0], m, 64);
-    lsum[1] += __shfl_xor(lsum[1], m, 64);
+    for (int m = 8; m >= 1; m >>= 1) lsum[0] += __shfl_xor(lsum[0], m, 64);  // head qS's 16 lanes
+  } else {
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) {
+      lsum[0] += __shfl_xor(lsum[0], m, 64);
+      lsum[1] += __shfl_xor(lsum[1], m, 64);
+    }
   }
   zacc += __shfl_xor(zacc, 16, 64);
   zacc += __shfl_xor(zacc, 32, 64);  // every lane r16 now holds Z of row (jjV, gV)
@@ -815,6 +1067,24 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
         const int ch = pv_channel<BITS>(nt, r16);
         if (2 * q4 < R) o_s[2 * q4][ch] = acc[nt][0];
         if (2 * q4 + 1 < R) o_s[2 * q4 + 1][ch] = acc[nt][1];
+      }
+    }
+  } else if (NARROW) {
+    // lane (q4, r16) holds rows 4 q4 + r = (group q4 / 2, digit q4 % 2, head r): the digits
+    // are summed across lanes q4 and q4 ^ 1; Z of row (g, head r) sits in lane 8 g + r
+    const int g = q4 >> 1;
+    float zrow[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) zrow[r] = __shfl(zacc, 8 * (g < NG ? g : 0) + r, 64);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const int ch = pv_channel<BITS>(nt, r16);
+      float o4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o4[r] = acc[nt][r] + __shfl_xor(acc[nt][r], 16, 64);
+      if ((q4 & 1) == 0 && ch / G == g) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) o_s[r][ch] = o4[r] + zrow[r];
       }
     }
   } else {
@@ -839,7 +1109,12 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       for (int e = 0; e < 4; ++e) dst[e] = make_float2(o_s[jo][c8 + 2 * e], o_s[jo][c8 + 2 * e + 1]);
     }
   }
-  if (nQ == 0) {
+  if (NARROW) {
+    if (nS == 0 && qS < R) {
+      part[qS * head_stride + 128] = mref[0];
+      part[qS * head_stride + 129] = lsum[0];
+    }
+  } else if (nQ == 0) {
 #pragma unroll
     for (int j2 = 0; j2 < 2; ++j2) {
       const int jj = 2 * hQ + j2;

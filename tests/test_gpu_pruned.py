@@ -74,8 +74,18 @@ def test_pruned_decode_matches_oracle(name):
         record(f"pruned_{name}_keep{keep}", err)
         print(f"[pruned] {name} keep {keep}/{nch}: max err {err:.3e}", flush=True)
         assert err <= TOL, (keep, err)
-        if keep == nch:  # nothing pruned: the plain kernel's result
-            assert np.max(np.abs(got - plain)) <= 1e-6
+        if keep == nch:  # nothing pruned: the plain decode's result
+            dev = float(np.max(np.abs(got - plain)))
+            record(f"pruned_{name}_all_vs_plain", dev)
+            if w.group_size == 32:
+                # the same arithmetic in both kernels: equal up to summation order
+                assert dev <= 1e-6
+            else:
+                # with 64- or 128-channel groups the plain decode scores with int8 query
+                # digits, the pruned one with f16 digits: each must match the unpruned oracle
+                plain_ref = p.ref.decode(wl.bf16_bits(q), p.geo.block_table.numpy(), p.lens.numpy())
+                assert np.array_equal(want, plain_ref)
+                assert max_err(plain.astype(np.float64), plain_ref) <= TOL
 
 
 def test_pruned_fullsize_h1_sampled():
