@@ -44,7 +44,9 @@
 //     two 16-token tiles of a block are the two N-tiles. Lane (head q, token n) receives
 //     the logits of head q for token n of both tiles. A stays in registers.
 // Values: one 16x16x32 product per N-tile: the hi and lo digits of W take separate A rows
-//   (head, digit, group), summed after the partition.
+//   (head, digit, group), summed after the partition. Each lane forms W = p * scale for two
+//   tokens of one head only (no lane repeats another's), and the A rows are gathered from
+//   a small wave-local LDS table.
 #pragma once
 
 #include <type_traits>
@@ -185,10 +187,16 @@ struct KBlock<BITS, NG, true> {
   uint32_t km[2][NG];
 };
 
-template <int BITS>
+template <int BITS, bool NARROW = false, int NG = 4>
 struct VBlock {
   uint32_t vc[BITS == 4 ? 8 : 4];  // value code words, 8 tokens
   uint32_t vm[8];                  // value {scale, zero} of group g, 8 tokens
+};
+// narrow groups: the {scale, zero} of the lane's two tokens (below) in every group
+template <int BITS, int NG>
+struct VBlock<BITS, true, NG> {
+  uint32_t vc[BITS == 4 ? 8 : 4];
+  uint32_t vm[NG][2];
 };
 
 __device__ __forceinline__ _Float16 f16_lo(uint32_t m) {
@@ -216,6 +224,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   constexpr int RB = 128 * BITS / 8;
   // one or two groups per head: int8 score MFMAs and merged value digits (see the top)
   constexpr bool NARROW = NG <= 2 && !PRUNE && !VT;
+  using VB = std::conditional_t<NARROW, VBlock<BITS, true, NG>, VBlock<BITS>>;
   const DevCache& c = a.c;
   const int lane = threadIdx.x;
   const int unit = blockIdx.x;
@@ -253,6 +262,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   __shared__ int qexp_s[4];       // per head: the query carries 2^-qexp in the score MFMAs
   __shared__ half8 aqk_s[8][64];  // score A operands, re-read from LDS for every block
   __shared__ __align__(16) int8_t dig_s[4][4][128];  // narrow: query digits in A-operand order
+  __shared__ __align__(16) uint32_t w_s[2][2][4][16];  // narrow: W digit pairs [digit][group][head][token pair]
 
   // lane roles: scores use (hQ, nQ) = (lane / 32, lane % 32): heads 2hQ, 2hQ+1 of token nQ;
   // values use (q4, r16) = (lane / 16, lane % 16): A row r16 = 4g + jj, tokens 8q4..8q4+7,
@@ -450,7 +460,42 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     else
       return load_k_wide(cu);
   };
-  auto load_v = [&](Cursor& cu) {
+  // narrow: this lane's two tokens 8 (q4 % 2) + 2 i4 + e (e = 0, 1) of tile q4 / 2, i4 = r16 / 4;
+  // their {scale, zero} entries of group g are adjacent in the tile's meta, part i4 / 2
+  const int i4 = r16 >> 2;
+  const uint32_t vmn_lane = static_cast<uint32_t>((((i4 >> 1) * NG) * 2 + (q4 & 1)) * 16 + 8 * (i4 & 1));
+  auto load_v_narrow = [&](Cursor& cu) {
+    VBlock<BITS, true, NG> vb;
+    const uint8_t* src;
+    const uint8_t* msrc;
+    if (one_page && start + 32 * cu.blk + 32 <= end) {
+      const int64_t r0 = row_base + start + 32 * cu.blk;  // a multiple of 16
+      src = c.vc + r0 * RB + voff;
+      msrc = reinterpret_cast<const uint8_t*>(c.vm) + (r0 / 16 + (q4 >> 1)) * (NG * 64) + vmn_lane;
+    } else {
+      int64_t row0, row1;
+      tile_rows(cu, row0, row1);
+      const int64_t trow = (q4 < 2) ? row0 : row1;
+      src = c.vc + trow * RB + vc_lane;
+      msrc = reinterpret_cast<const uint8_t*>(c.vm) + (trow / 16) * (NG * 64) + vmn_lane;
+    }
+    advance(cu);
+    const u32x4 w0 = ld16(src);
+    vb.vc[0] = w0[0]; vb.vc[1] = w0[1]; vb.vc[2] = w0[2]; vb.vc[3] = w0[3];
+    if (BITS == 4) {
+      const u32x4 w1 = ld16(src + 16 * 16 * 2);
+      vb.vc[4] = w1[0]; vb.vc[5] = w1[1]; vb.vc[6] = w1[2]; vb.vc[7] = w1[3];
+    }
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {  // group g's entries sit 32 bytes after group g - 1's
+      const u32x2 m = *reinterpret_cast<const u32x2*>(msrc + 32 * g);
+      vb.vm[g][0] = m[0];
+      vb.vm[g][1] = m[1];
+    }
+    return vb;
+  };
+  auto load_v_wide = [&](Cursor& cu) {
     VBlock<BITS> vb;
     const uint8_t* src;   // this lane's first code word of its 8 tokens
     const uint8_t* msrc;  // this lane's value {scale, zero}, part 0
@@ -498,10 +543,16 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     vb.vm[4] = m1[0]; vb.vm[5] = m1[1]; vb.vm[6] = m1[2]; vb.vm[7] = m1[3];
     return vb;
   };
+  auto load_v = [&](Cursor& cu) {
+    if constexpr (NARROW)
+      return load_v_narrow(cu);
+    else
+      return load_v_wide(cu);
+  };
 
   // the first key blocks are in flight while the query is prepared
   KBlock<BITS, NG, NARROW> kb[PF + 1];
-  VBlock<BITS> vb[PF + 1];
+  VB vb[PF + 1];
   Cursor kcur = cur0, vcur = cur0;
 #pragma unroll
   for (int j = 0; j < PF; ++j) kb[j] = load_k(kcur);
@@ -680,6 +731,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   // combine. A value scale >= 128 could push the weights past the f16 maximum: the
   // partition is then recomputed with shift = 0.
   float mrun[2], mref[2], lsum[2], zacc;
+  float zaccN[2];  // narrow: the lane's share of sum_t p * zero for head jjV, groups 0 / 1
   floatx4 acc[8];
 
   // scores of one block, narrow groups: logits of head qS for token nS of tiles 0 and 1
@@ -785,7 +837,8 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[nt][r] *= alpha[r];
-      zacc *= alpha[jjV];
+      zaccN[0] *= alpha[jjV];
+      zaccN[1] *= alpha[jjV];
       return;
     }
 #pragma unroll
@@ -854,9 +907,64 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
+  // values of block j, narrow groups: the lane forms the W digits of head jjV for its two
+  // tokens in each group and publishes them; it then reads back its A row (digit dV, group
+  // gVc, head jjV) for tokens 8 q4 .. 8 q4 + 7 and runs one MFMA per N-tile
+  auto pv_narrow = [&](const VBlock<BITS, true, NG>& vb, int j, int t0, auto tail, bool check_big) -> bool {
+    constexpr bool TAIL = decltype(tail)::value;
+    if (check_big) {
+      _Float16 smax = 0;
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) smax = __builtin_fmaxf16(smax, f16_lo(vb.vm[g][e]));
+      if (__any(smax >= static_cast<_Float16>(128.0f))) return false;
+    }
+    typedef float floatx2 __attribute__((ext_vector_type(2)));
+    const floatx2 pp = *reinterpret_cast<const floatx2*>(&p_s[j][jjV][8 * q4 + 2 * i4]);
+    // the previous block's reads of w_s are issued before these writes (one wavefront: its
+    // DS instructions complete in program order), so compiler fences suffice
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      float w[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        w[e] = __builtin_fmaf(lo_f16(vb.vm[g][e]), pp[e], 0.f);
+        float zp = hi_f16(vb.vm[g][e]);
+        if (TAIL && t0 + 8 * q4 + 2 * i4 + e >= end) {  // slots past the end may hold anything
+          w[e] = 0.f;
+          zp = 0.f;
+        }
+        zaccN[g] = __builtin_fmaf(zp, pp[e], zaccN[g]);
+      }
+      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(w[0], w[1]));
+      const float lo0 = __builtin_fmaf(lo_f16(hi), neg1, w[0]);
+      const float lo1 = __builtin_fmaf(hi_f16(hi), neg1, w[1]);
+      w_s[0][g][jjV][4 * q4 + i4] = hi;
+      w_s[1][g][jjV][4 * q4 + i4] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo0, lo1));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const half8 A = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(&w_s[dV][gVc][jjV][4 * q4]));
+    __builtin_amdgcn_s_setprio(1);  // the matrix-core cluster (see qk)
+#pragma unroll
+    for (int nt = 0; nt < 8; nt += 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      const half8 bv0 = unpack_v<BITS>(vb.vc, nt);
+      const half8 bv1 = unpack_v<BITS>(vb.vc, nt + 1);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bv0, acc[nt], 0, 0, 0);
+      acc[nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bv1, acc[nt + 1], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    return true;
+  };
+
   // values of block j of the super-block; false if a value scale is too large for the
   // f16 weights at this shift (nothing is accumulated then)
-  auto pv = [&](const VBlock<BITS>& vb, int j, int t0, auto tail, bool check_big) -> bool {
+  auto pv_wide = [&](const VBlock<BITS>& vb, int j, int t0, auto tail, bool check_big) -> bool {
     constexpr bool TAIL = decltype(tail)::value;
     if (check_big) {
       _Float16 smax = 0;
@@ -895,22 +1003,6 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       const float lo1 = __builtin_fmaf(hi_f16(ahi[k]), neg1, w[1]);
       alo[k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo0, lo1));
     }
-    if constexpr (NARROW) {
-      // the lane's A row carries one digit of W (row r16 = 8g + 4d + jj): one product per
-      // N-tile, the two digits' rows summed after the partition
-      const half8 A = dV ? as_half8(alo[0], alo[1], alo[2], alo[3]) : as_half8(ahi[0], ahi[1], ahi[2], ahi[3]);
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int nt = 0; nt < 8; nt += 2) {
-        __builtin_amdgcn_sched_barrier(0);
-        const half8 bv0 = unpack_v<BITS>(vb.vc, nt);
-        const half8 bv1 = unpack_v<BITS>(vb.vc, nt + 1);
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bv0, acc[nt], 0, 0, 0);
-        acc[nt + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bv1, acc[nt + 1], 0, 0, 0);
-      }
-      __builtin_amdgcn_s_setprio(0);
-      return true;
-    }
     const half8 Ahi = as_half8(ahi[0], ahi[1], ahi[2], ahi[3]);
     const half8 Alo = as_half8(alo[0], alo[1], alo[2], alo[3]);
     __builtin_amdgcn_s_setprio(1);  // the matrix-core cluster (see qk)
@@ -928,12 +1020,18 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     __builtin_amdgcn_s_setprio(0);
     return true;
   };
+  auto pv = [&](const VB& vb, int j, int t0, auto tail, bool check_big) -> bool {
+    if constexpr (NARROW)
+      return pv_narrow(vb, j, t0, tail, check_big);
+    else
+      return pv_wide(vb, j, t0, tail, check_big);
+  };
 
   // values of block j with value token groups: A rows 2 jj + digit hold the f16 hi / lo
   // parts of head jj's p (rows >= 2R zero), one MFMA per N-tile; lane (q4 < 2, r16) then
   // folds rows 4 q4 .. 4 q4 + 3 (heads 2 q4, 2 q4 + 1, both digits) of channel
   // pv_channel(nt, r16) with that channel's scale and zero
-  auto pv_vt = [&](const VBlock<BITS>& vb, int j) {
+  auto pv_vt = [&](const auto& vb, int j) {  // generic: instantiated only where called (VT)
     const int jjA = r16 >> 1;
     float pv[8];
     {
@@ -1010,7 +1108,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       else
         kb[(j + PF - NBS) % (PF + 1)] = load_k(kcur);
       if (!GUARD || j < n) {
-        if (VT)
+        if constexpr (VT)
           pv_vt(vb[j % (PF + 1)], j);
         else if (!pv(vb[j % (PF + 1)], j, start + 32 * (base + j), guard, check_big))
           return false;
@@ -1026,6 +1124,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     mref[0] = mref[1] = -INFINITY;
     lsum[0] = lsum[1] = 0.f;
     zacc = 0.f;
+    zaccN[0] = zaccN[1] = 0.f;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     if (attempt > 0) {
@@ -1071,11 +1170,19 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     }
   } else if (NARROW) {
     // lane (q4, r16) holds rows 4 q4 + r = (group q4 / 2, digit q4 % 2, head r): the digits
-    // are summed across lanes q4 and q4 ^ 1; Z of row (g, head r) sits in lane 8 g + r
+    // are summed across lanes q4 and q4 ^ 1. Z of (head r, group g): the sum of zaccN[g]
+    // over the lanes of head r (after the reduction, lane r holds it)
     const int g = q4 >> 1;
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int m = 4; m <= 32; m <<= 1) zaccN[gg] += __shfl_xor(zaccN[gg], m, 64);
     float zrow[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) zrow[r] = __shfl(zacc, 8 * (g < NG ? g : 0) + r, 64);
+    for (int r = 0; r < 4; ++r) {
+      const float z0 = __shfl(zaccN[0], r, 64), z1 = __shfl(zaccN[1], r, 64);
+      zrow[r] = (g == 1 && NG == 2) ? z1 : z0;
+    }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       const int ch = pv_channel<BITS>(nt, r16);
