@@ -12,7 +12,11 @@ with HIP events recorded on its own stream around every launch. Before the W war
 steps the step runs untimed for --settle-s seconds (default 0.25): the GPU's clocks
 need some 50-100 ms of sustained load to settle.
 
-  python bench.py [--steps K] [--warmup W] [--workload h1] [--gpus 1] [--window S,R]
+  python bench.py [--steps K] [--warmup W] [--workload h1] [--gpus 1] [--window S,R] [--eager]
+
+The timed step is the K steps replayed from one HIP graph (after an untimed replay);
+the eager host-launched K steps run first, and their per-launch events time the split
+kernel for the roofline. --eager reports the host-launched step time instead.
 
 With --window S,R the first S and last R tokens of every sequence stay in bf16
 windows (InnerQ, Abstract): a step appends through the windows (the token leaving the
@@ -195,8 +199,8 @@ def main():
     ap.add_argument("--prune", type=int, default=0,
                     help="query-channel pruning: key chunks kept per (sequence, kv head), of bits * head_dim / 128")
     ap.add_argument("--no-stream-probe", action="store_true", help="skip the read-stream ceiling measurement")
-    ap.add_argument("--graph", action="store_true",
-                    help="time the steps replayed from a HIP graph (value and ms_per_step then come from it)")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the steps as host launches (default: the K steps replayed from one HIP graph)")
     ap.add_argument("--stream-gib", type=int, default=4, help="GiB read by the read-stream probe")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg, fp32) of this many MiB before timing, "
@@ -360,43 +364,42 @@ def main():
         split_ms = float(np.mean([hip_events.elapsed_ms(i) for i in range(args.steps)]))
     hip_events.close()
 
-    # The same steps replayed from a HIP graph: one launch per graph instead of three
-    # host calls per step, so short steps are not paced by the host. The graph holds one
-    # cycle of the layer ring and the input rotation; its last replayed step must give the
-    # eager step's output bit for bit.
+    # The same K steps replayed from one HIP graph: the three kernels of a step then run
+    # back to back without host launches between them (short steps are otherwise paced by
+    # the host). The graph is replayed once untimed, then once timed; the last replayed
+    # step's output must equal the eager step's bit for bit. The split kernel's
+    # event-timed launches above give the roofline either way.
     graph = None
-    if args.graph:
-        if windowed or args.reference:
-            sys.exit("bench.py: --graph times the plain or pruned decode step")
-        per = ring * n_inputs // math.gcd(ring, n_inputs)
+    if not args.eager and not windowed and not args.reference:
+        base = total_steps
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            for i in range(per):
-                step(i)
+            for j in range(min(args.steps, 8)):
+                step(base + j)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for i in range(per):
-                step(i)
-        reps = max(1, -(-args.steps // per))
-        for _ in range(max(1, -(-args.warmup // per))):
-            g.replay()
+            for j in range(args.steps):
+                step(base + j)
+        g.replay()
         torch.cuda.synchronize()
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record()
-        for _ in range(reps):
-            g.replay()
+        g.replay()
         g1.record()
         torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / (reps * per)
+        graph_ms = g0.elapsed_time(g1) / args.steps
         replayed = out.clone()
-        step(per - 1)
+        step(base + args.steps - 1)
         torch.cuda.synchronize()
-        graph = {"us_per_step": round(graph_ms * 1e3, 2), "steps": reps * per, "steps_per_graph": per,
+        graph = {"us_per_step": round(graph_ms * 1e3, 2), "steps": args.steps,
                  "matches_eager": bool(torch.equal(replayed, out)), "us_per_step_eager": round(ms * 1e3, 2)}
+        if not graph["matches_eager"]:
+            sys.exit("bench.py: the graph-replayed step differs from the eager step")
         ms = graph_ms
+        total_steps = base + args.steps
         del g
 
     # algorithmic bytes (what the method must move; no re-reads, no partials)

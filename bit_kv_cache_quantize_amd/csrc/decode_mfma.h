@@ -295,8 +295,8 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   // page and in-page offset of its first token, and (paged case) a window of 64
   // block-table entries in a register, lane i holding phys * Hkv + hk for logical page
   // wbase + i (the page's tile-row block of this kv head: fewer than 2^32, checked on the
-  // host), so a lookup is one readlane and one 32 x 32-bit multiply. Past the last block
-  // the cursor stays (the load re-reads the last block; nothing is computed from it).
+  // host), so a lookup is one readlane and one 32 x 32-bit multiply. A cursor stops at
+  // the last block (no load is issued past it).
   struct Cursor {
     int blk, pg, off, wbase;
     uint32_t bt_w;
@@ -551,11 +551,14 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   };
 
   // the first key blocks are in flight while the query is prepared
-  KBlock<BITS, NG, NARROW> kb[PF + 1];
+  // a buffer whose block lies past the partition's end is zeroed instead of loaded (so
+  // the old contents die at their last use)
+  using KBT = KBlock<BITS, NG, NARROW>;
+  KBT kb[PF + 1];
   VB vb[PF + 1];
   Cursor kcur = cur0, vcur = cur0;
 #pragma unroll
-  for (int j = 0; j < PF; ++j) kb[j] = load_k(kcur);
+  for (int j = 0; j < PF; ++j) kb[j] = j < nblk ? load_k(kcur) : KBT{};
 
   // ---- rotated, scaled query of the R heads: score A operands and group sums ----
   // Lane (head jq = lane / 16, chunk c16 = lane % 16) holds channels 8 c16 .. 8 c16 + 7.
@@ -1082,17 +1085,24 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   // super-block, ... into three rotating buffers per kind (static slots: the super-block
   // body is fully unrolled). Super-blocks of NBS full blocks run without guards or
   // masks; the rest of the partition (fewer than NBS full blocks and a partial block)
-  // forms one last, guarded and masked super-block.
-  auto super_block = [&](int base, int n, auto guard, bool check_big) -> bool {
+  // forms one last, guarded and masked super-block. Loads past the partition's last
+  // block: the last super-block (LASTC when unguarded, any guarded one) prefetches no
+  // keys, and a guarded one loads none of its blocks at or past n. The one left: when the
+  // guarded super-block holds fewer than PF blocks, the key prefetches before it read up
+  // to PF - 1 blocks past the end. (A run-time test on the prefetch instead of a second
+  // unguarded body splits the body into basic blocks and costs the issue-bound INT2
+  // kernels 4 %.)
+  auto super_block = [&](int base, int n, auto guard, auto lastc, bool check_big) -> bool {
     constexpr bool GUARD = decltype(guard)::value;
+    constexpr bool LASTC = decltype(lastc)::value;
     float lg[NBS][2];
     float bm0 = -INFINITY, bm1 = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NBS; ++j) {
       if (j + PF < NBS)
-        kb[(j + PF) % (PF + 1)] = load_k(kcur);
+        kb[(j + PF) % (PF + 1)] = (!GUARD || j + PF < n) ? load_k(kcur) : KBT{};
       else
-        vb[(j + PF - NBS) % (PF + 1)] = load_v(vcur);
+        vb[(j + PF - NBS) % (PF + 1)] = (!GUARD || j + PF - NBS < n) ? load_v(vcur) : VB{};
       if (!GUARD || j < n) {
         qk(kb[j % (PF + 1)], start + 32 * (base + j), guard, lg[j]);
         bm0 = fmaxf(bm0, lg[j][0]);
@@ -1104,8 +1114,8 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < NBS; ++j) {
       if (j + PF < NBS)
-        vb[(j + PF) % (PF + 1)] = load_v(vcur);
-      else
+        vb[(j + PF) % (PF + 1)] = (!GUARD || j + PF < n) ? load_v(vcur) : VB{};
+      else if constexpr (!GUARD && !LASTC)  // the next super-block's keys
         kb[(j + PF - NBS) % (PF + 1)] = load_k(kcur);
       if (!GUARD || j < n) {
         if constexpr (VT)
@@ -1131,13 +1141,21 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       kcur = cur0;
       vcur = cur0;
 #pragma unroll
-      for (int j = 0; j < PF; ++j) kb[j] = load_k(kcur);
+      for (int j = 0; j < PF; ++j) kb[j] = j < nblk ? load_k(kcur) : KBT{};
     }
     const int nsbf = nfull / NBS;
-    bool ok = true;
-    for (int sb = 0; sb < nsbf && ok; ++sb) ok = super_block(sb * NBS, NBS, std::false_type{}, check_big);
     const int rem = nblk - nsbf * NBS;
-    if (ok && rem > 0) ok = super_block(nsbf * NBS, rem, std::true_type{}, check_big);
+    bool ok = true;
+    // (value token groups: no LASTC body, whose registers would cost them a wave per SIMD;
+    // their last super-block prefetches PF key blocks past the end)
+    const int nplain = nsbf - (rem == 0 && !VT ? 1 : 0);
+    for (int sb = 0; sb < nplain && ok; ++sb)
+      ok = super_block(sb * NBS, NBS, std::false_type{}, std::false_type{}, check_big);
+    if constexpr (!VT) {
+      if (ok && rem == 0 && nsbf > 0)
+        ok = super_block((nsbf - 1) * NBS, NBS, std::false_type{}, std::true_type{}, check_big);
+    }
+    if (ok && rem > 0) ok = super_block(nsbf * NBS, rem, std::true_type{}, std::false_type{}, check_big);
     if (ok) break;
   }
 
