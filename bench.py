@@ -4,7 +4,11 @@
 A step is one pass of the whole hot path on one batch: each sequence appends one new
 token (fused Hadamard rotation + INT4 group quantization into the cache), then every
 sequence runs GQA decode attention over its full quantized context (split-K kernel +
-combine). Inputs are seeded synthetic tensors resident in HBM before timing starts.
+combine). By default the step is one kvq_decode_step call, whose split-K launch does the
+append first in the unit that reads the new token; --unfused makes it the two calls
+kvq_quantize_append + kvq_decode_attention (windows, value token groups, pruning and
+the reference kernel always take separate calls). Inputs are seeded synthetic tensors
+resident in HBM before timing starts.
 
 Prints one JSON line. `value` is effective KV GB/s of the whole step (algorithmic
 bytes / step time); `roofline` covers the dominant kernel (the split-K decode), timed
@@ -12,7 +16,7 @@ with HIP events recorded on its own stream around every launch. Before the W war
 steps the step runs untimed for --settle-s seconds (default 0.25): the GPU's clocks
 need some 50-100 ms of sustained load to settle.
 
-  python bench.py [--steps K] [--warmup W] [--workload h1] [--gpus 1] [--window S,R] [--eager]
+  python bench.py [--steps K] [--warmup W] [--workload h1] [--gpus 1] [--window S,R] [--eager] [--unfused]
 
 The timed step is the K steps replayed from one HIP graph (after an untimed replay);
 the eager host-launched K steps run first, and their per-launch events time the split
@@ -98,6 +102,8 @@ def profile_key(args) -> str:
         key += f"_hb{args.hadamard_block}"
     if args.num_splits:
         key += f"_splits{args.num_splits}"
+    if args.unfused:
+        key += "_unfused"
     return key
 
 
@@ -199,6 +205,8 @@ def main():
     ap.add_argument("--prune", type=int, default=0,
                     help="query-channel pruning: key chunks kept per (sequence, kv head), of bits * head_dim / 128")
     ap.add_argument("--no-stream-probe", action="store_true", help="skip the read-stream ceiling measurement")
+    ap.add_argument("--unfused", action="store_true",
+                    help="append and decode as two calls (default: kvq_decode_step where the cache allows it)")
     ap.add_argument("--eager", action="store_true",
                     help="time the steps as host launches (default: the K steps replayed from one HIP graph)")
     ap.add_argument("--stream-gib", type=int, default=4, help="GiB read by the read-stream probe")
@@ -239,6 +247,8 @@ def main():
             sys.exit("bench.py: --vgroup brings its own residual window")
         win_S, win_R, windowed = 0, w.group_size, True
     maxlen = int(lens.max())
+    # the fused step covers plain caches: no windows, value token groups or pruning, the matrix kernel
+    fused = not (args.unfused or windowed or args.prune or args.reference)
     t0 = time.time()
     cache = kvq.KVCache.allocate(d, Hkv, w.bits, w.group_size, w.hadamard_block, geo.page_size, geo.num_pages,
                                  device=dev, quant_mode=1 if args.hybrid else 0, v_grouping=1 if args.vgroup else 0)
@@ -327,6 +337,10 @@ def main():
             kvq.window_append(c, windows[i % ring], kn, vn, seqs_d, pos_d, evict_d)
             kvq.decode_attention_window(c, windows[i % ring], qs[i % n_inputs], bt, lens_d, maxlen,
                                         num_splits=args.num_splits, workspace=ws, out=out, events=events)
+            return
+        if fused:
+            kvq.decode_step(c, kn, vn, qs[i % n_inputs], bt, lens_d, maxlen, num_splits=args.num_splits,
+                            workspace=ws, out=out, events=events)
             return
         kvq.quantize_append(c, kn, vn, last_slots)
         if args.prune:
@@ -429,8 +443,9 @@ def main():
         kv_bytes = split_kv_bytes + n_win * Hkv * 2 * d * 2
         append_bytes = B * Hkv * (3 * 2 * d * 2 + per_tok_head)
     step_bytes = kv_bytes + q_bytes + out_bytes + append_bytes
-    # the split kernel reads the quantized span only (window tokens go to the window kernel)
-    split_bytes = (split_kv_bytes if windowed else kv_bytes) + q_bytes
+    # the split kernel reads the quantized span only (window tokens go to the window kernel);
+    # a fused step's split kernel also does the append
+    split_bytes = (split_kv_bytes if windowed else kv_bytes) + q_bytes + (append_bytes if fused else 0)
     value = step_bytes / (ms * 1e-3) / 1e9
 
     roofline = None
@@ -475,6 +490,9 @@ def main():
             kvq.quantize_append(caches[0], kn, vn, last_slots)
             kvq.decode_attention_pruned(caches[0], q_last, bt, lens_d, maxlen, args.prune,
                                         num_splits=args.num_splits, chunk_mask=chunk_mask, workspace=ws, out=out)
+        elif fused:
+            kvq.decode_step(caches[0], kn, vn, q_last, bt, lens_d, maxlen, num_splits=args.num_splits,
+                            workspace=ws, out=out)
         else:
             kvq.quantize_append(caches[0], kn, vn, last_slots)
             kvq.decode_attention(caches[0], q_last, bt, lens_d, maxlen, num_splits=args.num_splits, workspace=ws,
@@ -631,6 +649,8 @@ def main():
                    "partitions": "balanced" if (args.num_splits == 0 and B > 1 and not args.reference)
                    else "fixed",
                    "kernel": "reference" if args.reference else "mfma", "layer_ring": ring,
+                   # fused: kvq_decode_step (the append inside the split-K launch)
+                   "step": "fused" if fused else "append+decode",
                    "settle_steps": n_settle,
                    "step_bytes": step_bytes, "quant_mode": cache.quant_mode, "v_grouping": cache.v_grouping,
                    **({"keep_chunks": args.prune, "chunks": n_chunks,

@@ -73,6 +73,10 @@ SIGNATURES = {
                                                   _sz, _vp, _vp, _vp, _vp]),
     "kvq_decode_attention_reference": (ctypes.c_int, [_DP, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32,
                                                       _vp, _sz, _vp, _vp]),
+    "kvq_decode_step": (ctypes.c_int, [_DP, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32, _vp, _sz,
+                                       _vp, _vp]),
+    "kvq_decode_step_timed": (ctypes.c_int, [_DP, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _f32, _i32, _vp,
+                                             _sz, _vp, _vp, _vp, _vp]),
     "kvq_window_plane_bytes": (_i64, [_DP, _WP]),
     "kvq_window_append": (ctypes.c_int, [_DP, _WP, _vp, _vp, _vp, _vp, _vp, _i64, _vp]),
     "kvq_decode_window_workspace_bytes": (_sz, [_DP, _WP, _i32, _i32, _i32, _i32]),
@@ -256,6 +260,40 @@ def decode_attention(cache: KVCache, q: torch.Tensor, block_table: torch.Tensor,
     else:
         st = lib().kvq_decode_attention(*args)
     _check(st, "kvq_decode_attention")
+    return out
+
+
+def decode_step(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                block_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, softmax_scale: float = 0.0,
+                num_splits: int = 0, workspace: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                stream=None, events=None) -> torch.Tensor:
+    """One decode step with the append fused into the split-K kernel (kvq_decode_step):
+    k_new/v_new bf16 [B][Hkv][d] are each sequence's new token, written at position
+    seq_lens[b] - 1, then the decode of q over seq_lens[b] tokens. The same cache bytes and
+    output as quantize_append at those slots followed by decode_attention."""
+    _need(k_new, torch.bfloat16, "k_new")
+    _need(v_new, torch.bfloat16, "v_new")
+    _need(q, torch.bfloat16, "q")
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    B, Hq, d = q.shape
+    if k_new.shape != (B, cache.num_kv_heads, cache.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError(f"k_new/v_new must be [{B}][{cache.num_kv_heads}][{cache.head_dim}]")
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, "out")
+    need = decode_workspace_bytes(cache, B, Hq, max_seq_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, torch.uint8, "workspace")
+    args = [ctypes.byref(cache.desc), _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq, _ptr(block_table),
+            block_table.shape[1], _ptr(seq_lens), max_seq_len, softmax_scale, num_splits, _ptr(workspace),
+            workspace.numel(), _ptr(out), _stream(stream)]
+    if events is not None:
+        st = lib().kvq_decode_step_timed(*args, ctypes.c_void_p(events[0]), ctypes.c_void_p(events[1]))
+    else:
+        st = lib().kvq_decode_step(*args)
+    _check(st, "kvq_decode_step")
     return out
 
 

@@ -52,6 +52,7 @@
 #include <type_traits>
 
 #include "kvq_device.h"
+#include "quant_row.h"
 
 namespace kvq {
 namespace {
@@ -255,6 +256,40 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   const int start = a.tok_begin + split * split_len;
   if (start >= qend) return;
   const int end = min(qend, start + split_len);
+
+  // Fused step (kvq_decode_step): the unit whose partition holds the sequence's last
+  // position quantizes that token's key row (lanes 0-15) and value row (lanes 16-31) into
+  // the cache, with the append kernels' row quantizer, and waits for its stores to
+  // complete before it loads the block that holds them (a wave's own stores, read back by
+  // the same wave). The rows are loaded here; the quantizer runs after the first blocks'
+  // loads are issued and the query is prepared, unless the new token lies in one of those
+  // blocks. (A position past the block table's row, seq_lens above max_seq_len: no append.)
+  constexpr bool FUSE = !PRUNE && !VT;
+  const bool appends =
+      FUSE && a.k_new != nullptr && T - 1 >= start && T - 1 < end && (T - 1) / c.page < a.max_pages;
+  uint4 new_raw = {0u, 0u, 0u, 0u};
+  int64_t new_slot = 0;
+  if (appends) {
+    if (lane < 32) {
+      const int64_t rh = static_cast<int64_t>(b) * c.hkv + hk;
+      new_raw = *reinterpret_cast<const uint4*>((lane >= 16 ? a.v_new : a.k_new) + rh * 128 + (lane & 15) * 8);
+    }
+    const int pos = T - 1;
+    new_slot = static_cast<int64_t>(a.block_table[static_cast<int64_t>(b) * a.max_pages + pos / c.page]) * c.page +
+               pos % c.page;
+  }
+  auto append_new = [&]() {
+    if constexpr (FUSE) {
+      if (lane < 32) {
+        float x[8] = {bf16_lo(new_raw.x), bf16_hi(new_raw.x), bf16_lo(new_raw.y), bf16_hi(new_raw.y),
+                      bf16_lo(new_raw.z), bf16_hi(new_raw.z), bf16_lo(new_raw.w), bf16_hi(new_raw.w)};
+        quantize_store_row<BITS, G>(c, lane >> 4, hk, new_slot, x, lane & 15, a.hblock, a.rot_c);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    }
+  };
 
   __shared__ float o_s[4][128];  // partial outputs, staged for the workspace stores
   __shared__ float p_s[NBS][4][32];  // p of a super-block's blocks, per head and token
@@ -550,6 +585,10 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       return load_v_wide(cu);
   };
 
+  // the new token in one of the first PF blocks: appended before they are loaded
+  const bool append_early = appends && (T - 1 - start) / 32 < PF;
+  if (append_early) append_new();
+
   // the first key blocks are in flight while the query is prepared
   // a buffer whose block lies past the partition's end is zeroed instead of loaded (so
   // the old contents die at their last use)
@@ -726,6 +765,8 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int g = 0; g < NG; ++g) qsum[j2][g] = (jh < R) ? qsum_s[jh][g] : 0.f;
   }
+
+  if (appends && !append_early) append_new();
 
   // ---- state (exp2 domain) ----
   // p = 2^(logit - mref) with mref = mrun - shift, mrun the running max: the value

@@ -75,6 +75,8 @@ DecodeArgs decode_args(const kvq_cache* cache, const Geometry& g, const void* q,
   a.rot_c = g.hblock > 0 ? static_cast<float>(1.0 / std::sqrt(static_cast<double>(g.hblock))) : 1.0f;
   const double scale = softmax_scale > 0.f ? softmax_scale : 1.0 / std::sqrt(static_cast<double>(g.d));
   a.qscale = static_cast<float>(scale * 1.4426950408889634);  // log2(e)
+  a.k_new = nullptr;
+  a.v_new = nullptr;
   return a;
 }
 
@@ -99,10 +101,11 @@ kvq_status decode_run(const kvq_cache* cache, const void* q, int32_t batch, int3
                        const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
                        int32_t max_seq_len, float softmax_scale, int32_t num_splits, void* workspace,
                        size_t workspace_bytes_given, float* out, void* stream, void* ev_begin, void* ev_end,
-                       bool reference) {
+                       bool reference, const void* k_new, const void* v_new) {
   Geometry g;
   kvq_status st = check_decode(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
                                max_seq_len, num_splits, workspace, out, &g);
+  if (st == KVQ_OK && (k_new || v_new)) st = check_step_rows(g, k_new, v_new, reference);
   if (st != KVQ_OK || batch == 0) return st;
   const Splits sp = splits_for(g, batch, num_q_heads, max_seq_len, num_splits,
                                reference ? SplitKernel::kReference : SplitKernel::kMatrix);
@@ -110,8 +113,10 @@ kvq_status decode_run(const kvq_cache* cache, const void* q, int32_t batch, int3
   if (need == SIZE_MAX) return KVQ_ERR_INVALID;  // no such workspace can exist
   if (workspace_bytes_given < need) return KVQ_ERR_WORKSPACE;
   if (reference && sp.split_len > 2048) return KVQ_ERR_UNSUPPORTED;
-  const DecodeArgs a = decode_args(cache, g, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
-                                   softmax_scale, sp, workspace, out);
+  DecodeArgs a = decode_args(cache, g, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
+                             softmax_scale, sp, workspace, out);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return KVQ_ERR_HIP;
@@ -173,6 +178,28 @@ kvq_status kvq_decode_attention_timed(const kvq_cache* cache, const void* q, int
   return decode_run(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
                      softmax_scale, num_splits, workspace, workspace_bytes, out, stream, split_begin, split_end,
                      false);
+}
+
+kvq_status kvq_decode_step(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                           int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                           int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                           float softmax_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                           float* out, void* stream) {
+  if (!k_new || !v_new) return KVQ_ERR_INVALID;
+  return decode_run(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
+                     softmax_scale, num_splits, workspace, workspace_bytes, out, stream, nullptr, nullptr, false,
+                     k_new, v_new);
+}
+
+kvq_status kvq_decode_step_timed(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                                 int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                 float softmax_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                 float* out, void* stream, void* split_begin, void* split_end) {
+  if (!k_new || !v_new) return KVQ_ERR_INVALID;
+  return decode_run(cache, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens, max_seq_len,
+                     softmax_scale, num_splits, workspace, workspace_bytes, out, stream, split_begin, split_end,
+                     false, k_new, v_new);
 }
 
 kvq_status kvq_decode_attention_reference(const kvq_cache* cache, const void* q, int32_t batch,

@@ -135,6 +135,11 @@ struct DecodeArgs {
   int hblock;
   float rot_c;    // float nearest 1/sqrt(hblock)
   float qscale;   // softmax scale * log2(e): logits are kept in the exp2 domain
+  // Fused step (kvq_decode_step; null otherwise): the new token of each sequence, K and V
+  // rows [batch][Hkv][128] bf16, quantized into position seq_lens[b] - 1 by the split
+  // kernel's unit whose partition holds that position, before that unit's first load.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
 };
 
 // ---- partition plan ----
@@ -251,12 +256,14 @@ hipError_t launch_decode_split_reference(const DecodeArgs& a, const Geometry& g,
 hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_window(const DecodeArgs& a, const DevWindow& w, const Geometry& g, hipStream_t stream);
 
-// kvq_decode_attention and its timed and reference variants (kvq_api.cpp): every host check,
-// the split kernel (matrix or reference) and the combine, with the given workspace.
+// kvq_decode_attention and its timed and reference variants, and the fused step
+// (kvq_api.cpp): every host check, the split kernel (matrix or reference; with k_new and
+// v_new, the matrix kernel appends each sequence's new token first) and the combine, with
+// the given workspace.
 kvq_status decode_run(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
                       const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
                       int32_t max_seq_len, float softmax_scale, int32_t num_splits, void* workspace,
                       size_t workspace_bytes_given, float* out, void* stream, void* ev_begin, void* ev_end,
-                      bool reference);
+                      bool reference, const void* k_new = nullptr, const void* v_new = nullptr);
 
 }  // namespace kvq

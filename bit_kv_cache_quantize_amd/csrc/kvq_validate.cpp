@@ -217,6 +217,12 @@ kvq_status check_append(const kvq_cache* c, const void* k_new, const void* v_new
   return KVQ_OK;
 }
 
+kvq_status check_step_rows(const Geometry& g, const void* k_new, const void* v_new, bool reference) {
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return KVQ_ERR_INVALID;
+  if (reference || g.v_grouping != 0) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
 kvq_status check_window(const kvq_cache* c, const kvq_window* w, bool planes) {
   if (!c || !w) return KVQ_ERR_INVALID;
   if (w->sink < 0 || w->recent < 1 || w->batch < 0) return KVQ_ERR_INVALID;

@@ -90,6 +90,11 @@ kvq_status check_decode(const kvq_cache* c, const void* q, int32_t batch, int32_
 kvq_status check_append(const kvq_cache* c, const void* k_new, const void* v_new, const int64_t* slots,
                         int64_t n_new, Geometry* g);
 
+// The new-token rows of a fused step (kvq_decode_step) for a cache that passed
+// check_decode: INVALID for a null or misaligned row pointer, UNSUPPORTED for value
+// token groups or the reference kernel.
+kvq_status check_step_rows(const Geometry& g, const void* k_new, const void* v_new, bool reference);
+
 // Window description against the cache (sizes only; `planes` also checks k and v).
 // Plane sizes are -1 when they exceed int64.
 constexpr int kMaxWindow = 1024;  // sink + recent

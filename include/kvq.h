@@ -212,6 +212,36 @@ kvq_status kvq_decode_attention_timed(const kvq_cache* cache, const void* q, int
                                       void* split_begin, void* split_end);
 
 /*
+ * One decode step with the append fused into the split-K kernel (SAW-INT4, Abstract:
+ * rotation and quantization fused into one kernel that writes the paged layout): the
+ * same results as kvq_quantize_append of each sequence's new token at the slot of its
+ * position seq_lens[b] - 1 (page block_table[b][pos / P], offset pos % P), followed by
+ * kvq_decode_attention with the same arguments, in one split-K launch and the combine.
+ *   k_new, v_new : bf16 [batch][Hkv][d], 16-byte aligned, contiguous: row b is the new
+ *                  token of sequence b (sequences with seq_lens[b] <= 0 append nothing).
+ * The unit whose partition holds position seq_lens[b] - 1 quantizes those rows before it
+ * reads its blocks, so the rows are bit-identical to kvq_quantize_append's and the
+ * output bit-identical to the two calls'. Every other argument, the workspace and the
+ * errors are those of kvq_decode_attention; in addition KVQ_ERR_INVALID for a null or
+ * misaligned k_new / v_new, KVQ_ERR_UNSUPPORTED for a cache with v_grouping 1 (value
+ * token groups are appended a group at a time). Requires seq_lens[b] <= max_seq_len for
+ * the append to happen (above it the row is undefined, as is the output).
+ */
+kvq_status kvq_decode_step(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                           int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                           int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                           float softmax_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                           float* out, void* stream);
+
+/* kvq_decode_step with hipEvent_t records around its split-K kernel, as
+   kvq_decode_attention_timed. For benchmarking. */
+kvq_status kvq_decode_step_timed(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                                 int32_t batch, int32_t num_q_heads, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                                 float softmax_scale, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                 float* out, void* stream, void* split_begin, void* split_end);
+
+/*
  * The same computation through a second, plain-VALU split-K kernel (fp32
  * dequantization and dot products, scores staged in LDS) instead of the MFMA
  * kernel. For cross-checking the fast path; partitions longer than 2048 tokens

@@ -136,6 +136,38 @@ def test_decode_bad_cache_and_empty_batch():
     assert _decode(_desc(), batch=0) == kvq.OK  # empty: no launch
 
 
+def _step(d, **kw):
+    a = dict(k=FAKE, v=FAKE, q=FAKE, batch=2, hq=32, bt=FAKE, maxp=64, lens=FAKE, maxlen=1000, scale=0.0,
+             splits=0, ws=FAKE, wsb=1 << 40, out=FAKE)
+    a.update(kw)
+    v = ctypes.c_void_p
+    return kvq.lib().kvq_decode_step(ctypes.byref(d) if d is not None else None, v(a["k"]), v(a["v"]), v(a["q"]),
+                                     a["batch"], a["hq"], v(a["bt"]), a["maxp"], v(a["lens"]), a["maxlen"],
+                                     a["scale"], a["splits"], v(a["ws"]), a["wsb"], v(a["out"]), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), kvq.ERR_INVALID),
+    (dict(v=0), kvq.ERR_INVALID),
+    (dict(k=FAKE + 2), kvq.ERR_INVALID),     # rows are read 16 bytes at a time
+    (dict(v=FAKE + 8), kvq.ERR_INVALID),
+    (dict(hq=12), kvq.ERR_INVALID),          # the decode checks apply as they are
+    (dict(hq=64), kvq.ERR_UNSUPPORTED),
+    (dict(q=FAKE + 8), kvq.ERR_INVALID),
+    (dict(wsb=100), kvq.ERR_WORKSPACE),
+])
+def test_decode_step_argument_checks(kw, status):
+    assert _step(_desc(), **kw) == status
+
+
+def test_decode_step_cache_kinds():
+    assert _step(None) == kvq.ERR_INVALID
+    # value token groups append a whole group at a time: no fused single-token step
+    assert _step(_desc(v_grouping=1, page_size=32)) == kvq.ERR_UNSUPPORTED
+    assert _step(_desc(), batch=0) == kvq.OK  # empty: no launch
+    assert _step(_desc(quant_mode=1), batch=0) == kvq.OK
+
+
 def test_dequantize_argument_checks():
     d = _desc()
     L = kvq.lib()

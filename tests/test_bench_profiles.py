@@ -11,7 +11,8 @@ import bench
 
 
 def _args(**kw):
-    base = dict(workload="h1", prune=0, window="", vgroup=False, hybrid=False, hadamard_block=-1, num_splits=0)
+    base = dict(workload="h1", prune=0, window="", vgroup=False, hybrid=False, hadamard_block=-1, num_splits=0,
+                unfused=False)
     base.update(kw)
     return argparse.Namespace(**base)
 
@@ -26,6 +27,8 @@ def test_profile_keys_name_every_variant():
     assert bench.profile_key(_args(hadamard_block=32)) == "h1_hb32"
     assert bench.profile_key(_args(num_splits=8)) == "h1_splits8"
     assert bench.profile_key(_args(prune=3, num_splits=16)) == "h1_prune3_splits16"
+    assert bench.profile_key(_args(unfused=True)) == "h1_unfused"
+    assert bench.profile_key(_args(workload="c2", unfused=True)) == "c2_unfused"
 
 
 def test_traffic_only_from_matching_profiles():
