@@ -115,6 +115,19 @@ static void documented_statuses() {
   EXPECT(check_append(&ok, p, p, reinterpret_cast<const int64_t*>(p), -1, nullptr) == KVQ_ERR_INVALID);
   EXPECT(check_append(&ok, nullptr, nullptr, nullptr, 0, nullptr) == KVQ_OK);
   EXPECT(check_append(&ok, p + 2, p, reinterpret_cast<const int64_t*>(p), 1, nullptr) == KVQ_ERR_INVALID);
+  // the fused step's new-token rows
+  {
+    Geometry g{};
+    EXPECT(check_cache(&ok, true, &g) == KVQ_OK);
+    EXPECT(check_step_rows(g, p, p, false) == KVQ_OK);
+    EXPECT(check_step_rows(g, nullptr, p, false) == KVQ_ERR_INVALID);
+    EXPECT(check_step_rows(g, p, p + 8, false) == KVQ_ERR_INVALID);
+    EXPECT(check_step_rows(g, p, p, true) == KVQ_ERR_UNSUPPORTED);
+    const kvq_cache vg = desc(128, 8, 4, 32, 128, 32, 64, 0, 1);
+    Geometry gv{};
+    EXPECT(check_cache(&vg, true, &gv) == KVQ_OK);
+    EXPECT(check_step_rows(gv, p, p, false) == KVQ_ERR_UNSUPPORTED);
+  }
   EXPECT(check_dequantize(&ok, 2, reinterpret_cast<const int64_t*>(p), 1, reinterpret_cast<const float*>(p),
                           nullptr) == KVQ_ERR_INVALID);
   EXPECT(check_dequantize(&ok, 1, reinterpret_cast<const int64_t*>(p), 1, reinterpret_cast<const float*>(p),
