@@ -251,8 +251,9 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     T = a.seq_lens[b];
     slot = (static_cast<int64_t>(b) * a.num_q_heads + hk * R) * a.num_splits + split;
   }
-  // the span this kernel covers ends here (with a residual: at the last whole group)
-  const int qend = covered_end(a, T);
+  // the span this kernel covers ends here (with a residual: at the last whole group);
+  // a sequence longer than max_seq_len is taken as max_seq_len long
+  const int qend = covered_end(a, min(T, a.max_len));
   const int start = a.tok_begin + split * split_len;
   if (start >= qend) return;
   const int end = min(qend, start + split_len);

@@ -43,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_reference_kernel(Decode
   const int b = bh / c.hkv;
   const int T = a.seq_lens[b];
   // the span this kernel covers ends here (with a residual: at the last whole group)
-  const int qend = covered_end(a, T);
+  const int qend = covered_end(a, min(T, a.max_len));  // longer sequences: taken as max_len long
   const int start = a.tok_begin + split * a.split_len;
   if (start >= qend) return;
   const int end = min(qend, start + a.split_len);
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(CW * NGRP) void combine_kernel(DecodeArgs a) {
     if (gp == 0) a.out[static_cast<int64_t>(bj) * kD + i] = 0.f;
     return;
   }
-  const int span = covered_span(a, T);
+  const int span = covered_span(a, min(T, a.max_len));  // as the split kernels take it
   const float* base;
   int nq;
   if (a.balanced) {

@@ -44,7 +44,7 @@ size_t workspace_for(const Geometry& g, int32_t batch, int32_t num_q_heads, int3
 
 DecodeArgs decode_args(const kvq_cache* cache, const Geometry& g, const void* q, int32_t batch, int32_t num_q_heads,
                        const int32_t* block_table, int32_t max_pages_per_seq, const int32_t* seq_lens,
-                       float softmax_scale, const Splits& sp, void* workspace, float* out) {
+                       int32_t max_seq_len, float softmax_scale, const Splits& sp, void* workspace, float* out) {
   DecodeArgs a;
   a.c = dev_cache(cache, g);
   a.q = static_cast<const uint16_t*>(q);
@@ -67,6 +67,7 @@ DecodeArgs decode_args(const kvq_cache* cache, const Geometry& g, const void* q,
   a.seq_plan = sp.balanced ? reinterpret_cast<int2*>(static_cast<char*>(workspace) +
                                                      balanced_partials_bytes(g, num_q_heads, sp))
                            : nullptr;
+  a.max_len = max_seq_len;
   a.win_partials = nullptr;
   a.window = 0;
   a.keep_chunks = 0;
@@ -114,7 +115,7 @@ kvq_status decode_run(const kvq_cache* cache, const void* q, int32_t batch, int3
   if (workspace_bytes_given < need) return KVQ_ERR_WORKSPACE;
   if (reference && sp.split_len > 2048) return KVQ_ERR_UNSUPPORTED;
   DecodeArgs a = decode_args(cache, g, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
-                             softmax_scale, sp, workspace, out);
+                             max_seq_len, softmax_scale, sp, workspace, out);
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
 
@@ -257,7 +258,7 @@ kvq_status kvq_decode_attention_window_timed(const kvq_cache* cache, const kvq_w
   if (need == SIZE_MAX) return KVQ_ERR_INVALID;
   if (workspace_bytes_given < need) return KVQ_ERR_WORKSPACE;
   DecodeArgs a = decode_args(cache, g, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
-                             softmax_scale, sp, workspace, out);
+                             max_seq_len, softmax_scale, sp, workspace, out);
   a.tok_begin = window->sink;
   a.tok_tail = window->residual ? 0 : window->recent;
   a.tail_mod = window->residual ? window->recent : 0;
@@ -300,7 +301,7 @@ kvq_status kvq_decode_attention_pruned(const kvq_cache* cache, const void* q, in
   if (need == SIZE_MAX) return KVQ_ERR_INVALID;
   if (workspace_bytes_given < need) return KVQ_ERR_WORKSPACE;
   DecodeArgs a = decode_args(cache, g, q, batch, num_q_heads, block_table, max_pages_per_seq, seq_lens,
-                             softmax_scale, sp, workspace, out);
+                             max_seq_len, softmax_scale, sp, workspace, out);
   a.keep_chunks = keep_chunks;
   a.chunk_mask = chunk_mask;
   hipStream_t s = static_cast<hipStream_t>(stream);

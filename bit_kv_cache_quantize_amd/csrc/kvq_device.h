@@ -125,6 +125,9 @@ struct DecodeArgs {
   // balanced: per sequence {first unit, partitions}, written by the split kernel's unit
   // (kv head 0, partition 0) of each sequence with tokens, read by the combine
   int2* seq_plan;
+  // the host's max_seq_len: the split kernels and their plan take longer sequences as this
+  // long, which keeps every partition within the block table's row and the host's sizing
+  int max_len;
   // window partials [batch][Hq][d + 2], when `window` is set
   float* win_partials;
   int window;
@@ -183,7 +186,7 @@ __device__ __forceinline__ int wave_sum(int x, int lane) {
 }
 
 __device__ __forceinline__ int span_units(const DecodeArgs& a, int T) {
-  return (covered_span(a, T) + kBalancedMinLen - 1) / kBalancedMinLen;
+  return (covered_span(a, min(T, a.max_len)) + kBalancedMinLen - 1) / kBalancedMinLen;
 }
 
 __device__ __forceinline__ int first_lens(const DecodeArgs& a, int lane) {

@@ -411,6 +411,50 @@ def test_decode_custom_softmax_scale():
     assert max_err(got, want) <= TOL
 
 
+def test_sequences_longer_than_max_seq_len():
+    """A sequence whose seq_lens entry exceeds max_seq_len is taken as max_seq_len long: the
+    block table holds only ceil(max_seq_len / P) pages per sequence, and no kernel reads
+    past that row (its own output row is undefined). The other rows match the oracle, the
+    workspace and output canaries stay intact, and the fused step appends nothing for it."""
+    w = _small("c5", batch=3, ragged=(1, 200))
+    lens = torch.tensor([100, 100, 50], dtype=torch.int32)  # what the cache holds
+    p = make_pair(w, DEV, extra_tokens=0, lens=lens)
+    bt = p.geo.block_table.to(DEV)
+    assert bt.shape[1] * p.geo.page_size < 150
+    claimed = torch.tensor([100, 150, 50], dtype=torch.int32).to(DEV)
+    q = wl.queries(w)
+    want = p.ref.decode(wl.bf16_bits(q), p.geo.block_table.numpy(), lens.numpy())
+    B, Hq, d = w.batch, w.num_q_heads, w.head_dim
+    guard = 4096
+    for name, kw in (("balanced", {}), ("fixed", {"num_splits": 2}), ("reference", {"reference": True})):
+        print(f"[decode] seq_lens above max_seq_len: {name}", flush=True)
+        outbuf = torch.full((B * Hq * d + 2 * guard,), 12345.0, device=DEV)
+        out = outbuf[guard:guard + B * Hq * d].view(B, Hq, d)
+        need = kvq.decode_workspace_bytes(p.gpu, B, Hq, 100, kw.get("num_splits", 0))
+        wsbuf = torch.full((need + 2 * guard,), 0xAB, dtype=torch.uint8, device=DEV)
+        kvq.decode_attention(p.gpu, q.to(DEV), bt, claimed, 100, workspace=wsbuf[guard:guard + need], out=out, **kw)
+        torch.cuda.synchronize()
+        assert torch.all(outbuf[:guard] == 12345.0) and torch.all(outbuf[-guard:] == 12345.0)
+        assert torch.all(wsbuf[:guard] == 0xAB) and torch.all(wsbuf[-guard:] == 0xAB)
+        got = out.cpu().numpy().astype(np.float64)
+        assert max_err(got[[0, 2]], want[[0, 2]]) <= TOL, name
+    print("[decode] seq_lens above max_seq_len: fused step", flush=True)
+    before = [t.clone() for t in p.gpu.planes()]
+    k, v = wl.new_tokens(w, 0)
+    kvq.decode_step(p.gpu, k.to(DEV), v.to(DEV), q.to(DEV), bt, torch.tensor([101, 150, 51], dtype=torch.int32).to(DEV),
+                    100)
+    torch.cuda.synchronize()
+    # sequence 0 (101 > 100) and sequence 1 (150) append nothing; sequence 2 writes position 50
+    slot2 = int(p.geo.slots(2, 50, 1)[0])
+    twin = p.gpu.clone()
+    for t, b0 in zip(twin.planes(), before):
+        t.copy_(b0)
+    kvq.quantize_append(twin, k[2:3].to(DEV), v[2:3].to(DEV), torch.tensor([slot2], dtype=torch.int64, device=DEV))
+    torch.cuda.synchronize()
+    for a, b in zip(p.gpu.planes(), twin.planes()):
+        assert torch.equal(a, b)
+
+
 def test_output_guard_bytes_untouched():
     """Canaries around the output and workspace catch out-of-bounds writes."""
     w = _small("c5", batch=3, ragged=(1, 200))
