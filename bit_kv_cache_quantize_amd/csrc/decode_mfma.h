@@ -346,6 +346,9 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     return static_cast<uint32_t>(w) * static_cast<uint32_t>(c.hkv) + static_cast<uint32_t>(hk);
   };
   const Cursor cur0 = {0, pg_first, start - pg_first * P, pg_first, one_page ? 0u : window(pg_first)};
+  // contiguous full blocks need only the block index (step_blk); the paged lookup the page
+  // and offset too (advance)
+  auto step_blk = [&](Cursor& cu) { cu.blk = min(cu.blk + 1, nblk - 1); };
   auto advance = [&](Cursor& cu) {
     if (cu.blk + 1 < nblk) {
       ++cu.blk;
@@ -418,10 +421,11 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     if (one_page && start + 32 * cu.blk + 32 <= end) {
       row0 = row_base + start + 32 * cu.blk;  // a multiple of 16
       row1 = row0 + 16;
+      step_blk(cu);
     } else {
       tile_rows(cu, row0, row1);
+      advance(cu);
     }
-    advance(cu);
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -462,14 +466,15 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       const int64_t r0 = row_base + start + 32 * cu.blk;  // a multiple of 16
       src = c.kc + r0 * RB + koff;
       msrc = reinterpret_cast<const uint8_t*>(c.km) + r0 * (NG * 4) + kmoff;
+      step_blk(cu);
     } else {
       int64_t row0, row1;
       tile_rows(cu, row0, row1);
       const int64_t trow = (nQ < 16) ? row0 : row1;
       src = c.kc + trow * RB + kc_lane;
       msrc = reinterpret_cast<const uint8_t*>(c.km + (trow + (nQ & 15)) * NG);
+      advance(cu);
     }
-    advance(cu);
     u32x4 x0 = {0u, 0u, 0u, 0u};
     if (!PRUNE || ((kmask >> (KCH * hQ)) & 1)) x0 = ld16(src);
     kb.kc[0] = x0[0]; kb.kc[1] = x0[1]; kb.kc[2] = x0[2]; kb.kc[3] = x0[3];
@@ -508,14 +513,15 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       const int64_t r0 = row_base + start + 32 * cu.blk;  // a multiple of 16
       src = c.vc + r0 * RB + voff;
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (r0 / 16 + (q4 >> 1)) * (NG * 64) + vmn_lane;
+      step_blk(cu);
     } else {
       int64_t row0, row1;
       tile_rows(cu, row0, row1);
       const int64_t trow = (q4 < 2) ? row0 : row1;
       src = c.vc + trow * RB + vc_lane;
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (trow / 16) * (NG * 64) + vmn_lane;
+      advance(cu);
     }
-    advance(cu);
     const u32x4 w0 = ld16(src);
     vb.vc[0] = w0[0]; vb.vc[1] = w0[1]; vb.vc[2] = w0[2]; vb.vc[3] = w0[3];
     if (BITS == 4) {
@@ -541,6 +547,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       src = c.vc + r0 * RB + voff;
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (r0 / 16) * (NG * 64) + vmoff;
       brow = r0;
+      step_blk(cu);
     } else {
       int64_t row0, row1;
       tile_rows(cu, row0, row1);
@@ -548,8 +555,8 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       src = c.vc + trow * RB + vc_lane;
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (trow / 16) * (NG * 64) + vm_lane;
       brow = row0;
+      advance(cu);
     }
-    advance(cu);
     if (VT) {
       // {scale, zero} of channels pv_channel(0..7, r16): entries 8 r16 .. 8 r16 + 7 of the
       // block's token group (row / G: pages hold whole groups); re-read by the group's
