@@ -415,10 +415,10 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     const int bk = G == 128 ? 4 * qS * BITS + 2 * k * BITS : 8 * k * BITS + 2 * qS * BITS;
     knoff[k] = ((bk >> 4) * 16 + nS) * 16 + (bk & 15);
   }
-  auto load_k_narrow = [&](Cursor& cu) {
+  auto load_k_narrow = [&](Cursor& cu, auto full) {
     KBlock<BITS, NG, true> kb;
     int64_t row0, row1;
-    if (one_page && start + 32 * cu.blk + 32 <= end) {
+    if (one_page && (decltype(full)::value || start + 32 * cu.blk + 32 <= end)) {
       row0 = row_base + start + 32 * cu.blk;  // a multiple of 16
       row1 = row0 + 16;
       step_blk(cu);
@@ -458,11 +458,11 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     }
     return kb;
   };
-  auto load_k_wide = [&](Cursor& cu) {
+  auto load_k_wide = [&](Cursor& cu, auto full) {
     KBlock<BITS, NG, false> kb;
     const uint8_t* src;
     const uint8_t* msrc;
-    if (one_page && start + 32 * cu.blk + 32 <= end) {
+    if (one_page && (decltype(full)::value || start + 32 * cu.blk + 32 <= end)) {
       const int64_t r0 = row_base + start + 32 * cu.blk;  // a multiple of 16
       src = c.kc + r0 * RB + koff;
       msrc = reinterpret_cast<const uint8_t*>(c.km) + r0 * (NG * 4) + kmoff;
@@ -495,21 +495,22 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     }
     return kb;
   };
-  auto load_k = [&](Cursor& cu) {
+  // `full`: the block is known to be a full one (inside an unguarded super-block)
+  auto load_k = [&](Cursor& cu, auto full) {
     if constexpr (NARROW)
-      return load_k_narrow(cu);
+      return load_k_narrow(cu, full);
     else
-      return load_k_wide(cu);
+      return load_k_wide(cu, full);
   };
   // narrow: this lane's two tokens 8 (q4 % 2) + 2 i4 + e (e = 0, 1) of tile q4 / 2, i4 = r16 / 4;
   // their {scale, zero} entries of group g are adjacent in the tile's meta, part i4 / 2
   const int i4 = r16 >> 2;
   const uint32_t vmn_lane = static_cast<uint32_t>((((i4 >> 1) * NG) * 2 + (q4 & 1)) * 16 + 8 * (i4 & 1));
-  auto load_v_narrow = [&](Cursor& cu) {
+  auto load_v_narrow = [&](Cursor& cu, auto full) {
     VBlock<BITS, true, NG> vb;
     const uint8_t* src;
     const uint8_t* msrc;
-    if (one_page && start + 32 * cu.blk + 32 <= end) {
+    if (one_page && (decltype(full)::value || start + 32 * cu.blk + 32 <= end)) {
       const int64_t r0 = row_base + start + 32 * cu.blk;  // a multiple of 16
       src = c.vc + r0 * RB + voff;
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (r0 / 16 + (q4 >> 1)) * (NG * 64) + vmn_lane;
@@ -537,12 +538,12 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     }
     return vb;
   };
-  auto load_v_wide = [&](Cursor& cu) {
+  auto load_v_wide = [&](Cursor& cu, auto full) {
     VBlock<BITS> vb;
     const uint8_t* src;   // this lane's first code word of its 8 tokens
     const uint8_t* msrc;  // this lane's value {scale, zero}, part 0
     int64_t brow;         // row of the block's first token
-    if (one_page && start + 32 * cu.blk + 32 <= end) {
+    if (one_page && (decltype(full)::value || start + 32 * cu.blk + 32 <= end)) {
       const int64_t r0 = row_base + start + 32 * cu.blk;  // a multiple of 16
       src = c.vc + r0 * RB + voff;
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (r0 / 16) * (NG * 64) + vmoff;
@@ -586,11 +587,11 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     vb.vm[4] = m1[0]; vb.vm[5] = m1[1]; vb.vm[6] = m1[2]; vb.vm[7] = m1[3];
     return vb;
   };
-  auto load_v = [&](Cursor& cu) {
+  auto load_v = [&](Cursor& cu, auto full) {
     if constexpr (NARROW)
-      return load_v_narrow(cu);
+      return load_v_narrow(cu, full);
     else
-      return load_v_wide(cu);
+      return load_v_wide(cu, full);
   };
 
   // the new token in one of the first PF blocks: appended before they are loaded
@@ -605,7 +606,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   VB vb[PF + 1];
   Cursor kcur = cur0, vcur = cur0;
 #pragma unroll
-  for (int j = 0; j < PF; ++j) kb[j] = j < nblk ? load_k(kcur) : KBT{};
+  for (int j = 0; j < PF; ++j) kb[j] = j < nblk ? load_k(kcur, std::false_type{}) : KBT{};
 
   // ---- rotated, scaled query of the R heads: score A operands and group sums ----
   // Lane (head jq = lane / 16, chunk c16 = lane % 16) holds channels 8 c16 .. 8 c16 + 7.
@@ -1149,9 +1150,9 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < NBS; ++j) {
       if (j + PF < NBS)
-        kb[(j + PF) % (PF + 1)] = (!GUARD || j + PF < n) ? load_k(kcur) : KBT{};
+        kb[(j + PF) % (PF + 1)] = (!GUARD || j + PF < n) ? load_k(kcur, std::bool_constant<!GUARD>{}) : KBT{};
       else
-        vb[(j + PF - NBS) % (PF + 1)] = (!GUARD || j + PF - NBS < n) ? load_v(vcur) : VB{};
+        vb[(j + PF - NBS) % (PF + 1)] = (!GUARD || j + PF - NBS < n) ? load_v(vcur, std::bool_constant<!GUARD>{}) : VB{};
       if (!GUARD || j < n) {
         qk(kb[j % (PF + 1)], start + 32 * (base + j), guard, lg[j]);
         bm0 = fmaxf(bm0, lg[j][0]);
@@ -1163,9 +1164,9 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < NBS; ++j) {
       if (j + PF < NBS)
-        vb[(j + PF) % (PF + 1)] = (!GUARD || j + PF < n) ? load_v(vcur) : VB{};
+        vb[(j + PF) % (PF + 1)] = (!GUARD || j + PF < n) ? load_v(vcur, std::bool_constant<!GUARD>{}) : VB{};
       else if constexpr (!GUARD && !LASTC)  // the next super-block's keys
-        kb[(j + PF - NBS) % (PF + 1)] = load_k(kcur);
+        kb[(j + PF - NBS) % (PF + 1)] = load_k(kcur, std::false_type{});
       if (!GUARD || j < n) {
         if constexpr (VT)
           pv_vt(vb[j % (PF + 1)], j);
@@ -1190,7 +1191,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       kcur = cur0;
       vcur = cur0;
 #pragma unroll
-      for (int j = 0; j < PF; ++j) kb[j] = j < nblk ? load_k(kcur) : KBT{};
+      for (int j = 0; j < PF; ++j) kb[j] = j < nblk ? load_k(kcur, std::false_type{}) : KBT{};
     }
     const int nsbf = nfull / NBS;
     const int rem = nblk - nsbf * NBS;
