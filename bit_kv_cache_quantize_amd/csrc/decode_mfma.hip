@@ -4,14 +4,16 @@
 
 namespace kvq {
 
-hipError_t launch_decode_split(const DecodeArgs& a, const Geometry& g, hipStream_t stream) {
+hipError_t launch_decode_split(const DecodeArgs& a, const Geometry& g, hipStream_t stream, hipEvent_t t0,
+                               hipEvent_t t1) {
   const int64_t units = split_units(a, g);
   if (units > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(units)), block(64);
 #define KVQ_DM(B, GS, RR)                                                                              \
   if (g.bits == B && g.group == GS && a.ratio == RR) {                                                 \
-    hipLaunchKernelGGL((decode_split_mfma_kernel<B, GS, RR, false, false>), grid, block, 0, stream, a);      \
-    return hipGetLastError();                                                                          \
+    void* args[] = {const_cast<DecodeArgs*>(&a)};                                                 \
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(&decode_split_mfma_kernel<B, GS, RR, false, false>), grid, \
+                              block, args, 0, stream, t0, t1, 0);                                       \
   }
 #define KVQ_DM_R(B, GS) KVQ_DM(B, GS, 1) KVQ_DM(B, GS, 2) KVQ_DM(B, GS, 4)
   KVQ_DM_R(4, 32) KVQ_DM_R(4, 64) KVQ_DM_R(4, 128) KVQ_DM_R(2, 32) KVQ_DM_R(2, 64) KVQ_DM_R(2, 128)

@@ -82,8 +82,10 @@ DecodeArgs decode_args(const kvq_cache* cache, const Geometry& g, const void* q,
 }
 
 // the matrix-core split kernel for this cache's value grouping
-hipError_t split_kernel(const DecodeArgs& a, const Geometry& g, hipStream_t s) {
-  return g.v_grouping ? launch_decode_split_vgroup(a, g, s) : launch_decode_split(a, g, s);
+hipError_t split_kernel(const DecodeArgs& a, const Geometry& g, hipStream_t s, void* t0 = nullptr,
+                        void* t1 = nullptr) {
+  const auto e0 = static_cast<hipEvent_t>(t0), e1 = static_cast<hipEvent_t>(t1);
+  return g.v_grouping ? launch_decode_split_vgroup(a, g, s, e0, e1) : launch_decode_split(a, g, s, e0, e1);
 }
 
 DevWindow dev_window(const kvq_window* w) {
@@ -120,10 +122,16 @@ kvq_status decode_run(const kvq_cache* cache, const void* q, int32_t batch, int3
   a.v_new = static_cast<const uint16_t*>(v_new);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return KVQ_ERR_HIP;
-  hipError_t e = reference ? launch_decode_split_reference(a, g, s) : split_kernel(a, g, s);
+  hipError_t e;
+  if (reference) {
+    if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return KVQ_ERR_HIP;
+    e = launch_decode_split_reference(a, g, s);
+    if (e == hipSuccess && ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess)
+      return KVQ_ERR_HIP;
+  } else {
+    e = split_kernel(a, g, s, ev_begin, ev_end);
+  }
   if (e != hipSuccess) return KVQ_ERR_HIP;
-  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return KVQ_ERR_HIP;
   e = launch_combine(a, g, s);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
@@ -265,9 +273,7 @@ kvq_status kvq_decode_attention_window_timed(const kvq_cache* cache, const kvq_w
   a.win_partials = a.partials + workspace_bytes(g, batch, num_q_heads, sp) / sizeof(float);
   a.window = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (split_begin && hipEventRecord(static_cast<hipEvent_t>(split_begin), s) != hipSuccess) return KVQ_ERR_HIP;
-  if (split_kernel(a, g, s) != hipSuccess) return KVQ_ERR_HIP;
-  if (split_end && hipEventRecord(static_cast<hipEvent_t>(split_end), s) != hipSuccess) return KVQ_ERR_HIP;
+  if (split_kernel(a, g, s, split_begin, split_end) != hipSuccess) return KVQ_ERR_HIP;
   if (launch_decode_window(a, dev_window(window), g, s) != hipSuccess) return KVQ_ERR_HIP;
   return launch_combine(a, g, s) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
@@ -305,9 +311,9 @@ kvq_status kvq_decode_attention_pruned(const kvq_cache* cache, const void* q, in
   a.keep_chunks = keep_chunks;
   a.chunk_mask = chunk_mask;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (split_begin && hipEventRecord(static_cast<hipEvent_t>(split_begin), s) != hipSuccess) return KVQ_ERR_HIP;
-  if (launch_decode_split_pruned(a, g, s) != hipSuccess) return KVQ_ERR_HIP;
-  if (split_end && hipEventRecord(static_cast<hipEvent_t>(split_end), s) != hipSuccess) return KVQ_ERR_HIP;
+  if (launch_decode_split_pruned(a, g, s, static_cast<hipEvent_t>(split_begin), static_cast<hipEvent_t>(split_end)) !=
+      hipSuccess)
+    return KVQ_ERR_HIP;
   return launch_combine(a, g, s) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
@@ -327,11 +333,10 @@ kvq_status kvq_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_
     return KVQ_ERR_INVALID;
   if (bytes == 0) return KVQ_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (ev_begin && hipEventRecord(static_cast<hipEvent_t>(ev_begin), s) != hipSuccess) return KVQ_ERR_HIP;
   const int64_t wgs = static_cast<int64_t>(device_cus()) * workgroups_per_cu;
-  if (launch_stream_read(src, static_cast<int64_t>(bytes / 16), sink, nontemporal, wgs, s) != hipSuccess)
+  if (launch_stream_read(src, static_cast<int64_t>(bytes / 16), sink, nontemporal, wgs, s,
+                         static_cast<hipEvent_t>(ev_begin), static_cast<hipEvent_t>(ev_end)) != hipSuccess)
     return KVQ_ERR_HIP;
-  if (ev_end && hipEventRecord(static_cast<hipEvent_t>(ev_end), s) != hipSuccess) return KVQ_ERR_HIP;
   return KVQ_OK;
 }
 

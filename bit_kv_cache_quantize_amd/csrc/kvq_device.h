@@ -88,9 +88,10 @@ hipError_t launch_window_append(const DevCache& c, const DevWindow& w, const Geo
                                 const int64_t* evict_slots, int64_t n_new, hipStream_t stream);
 hipError_t launch_dequantize(const DevCache& c, const Geometry& g, int which, const int64_t* slots,
                              int64_t n, float* out, hipStream_t stream);
-// read probe (stream_probe.hip): n16 16-byte pieces at src, `workgroups` of 256 threads
+// read probe (stream_probe.hip): n16 16-byte pieces at src, `workgroups` of 256 threads;
+// t0 / t1 (may be null) recorded as part of the dispatch, as for the split launches
 hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* sink, int nontemporal, int64_t workgroups,
-                              hipStream_t stream);
+                              hipStream_t stream, hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 
 struct DecodeArgs {
   DevCache c;
@@ -252,9 +253,15 @@ inline int64_t split_units(const DecodeArgs& a, const Geometry& g) {
                     : static_cast<int64_t>(a.batch) * g.hkv * a.num_splits;
 }
 
-hipError_t launch_decode_split(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
-hipError_t launch_decode_split_pruned(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
-hipError_t launch_decode_split_vgroup(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
+// The split launches record t0 / t1 (may be null) as part of the kernel's dispatch
+// (hipExtLaunchKernel): their elapsed time is the kernel's own, without the dispatch
+// around it that separately recorded events would also time.
+hipError_t launch_decode_split(const DecodeArgs& a, const Geometry& g, hipStream_t stream, hipEvent_t t0 = nullptr,
+                               hipEvent_t t1 = nullptr);
+hipError_t launch_decode_split_pruned(const DecodeArgs& a, const Geometry& g, hipStream_t stream,
+                                      hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
+hipError_t launch_decode_split_vgroup(const DecodeArgs& a, const Geometry& g, hipStream_t stream,
+                                      hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_decode_split_reference(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_combine(const DecodeArgs& a, const Geometry& g, hipStream_t stream);
 hipError_t launch_decode_window(const DecodeArgs& a, const DevWindow& w, const Geometry& g, hipStream_t stream);

@@ -42,18 +42,18 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 }  // namespace
 
 hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* sink, int nontemporal, int64_t workgroups,
-                              hipStream_t stream) {
+                              hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   if (workgroups <= 0 || workgroups > 0x7FFFFFFF) return hipErrorInvalidValue;
   dim3 grid(static_cast<unsigned>(workgroups)), block(256);
   const auto* p = static_cast<const u32x4*>(src);
   // the XOR of random-looking data is never this value in practice; if it were, one
   // dword of the sink would be written, which the caller provides for that purpose
   constexpr uint32_t kNever = 0x9E3779B9u;
-  if (nontemporal)
-    hipLaunchKernelGGL((stream_read_kernel<true>), grid, block, 0, stream, p, n16, sink, kNever);
-  else
-    hipLaunchKernelGGL((stream_read_kernel<false>), grid, block, 0, stream, p, n16, sink, kNever);
-  return hipGetLastError();
+  uint32_t never = kNever;
+  void* args[] = {&p, &n16, &sink, &never};
+  const void* k = nontemporal ? reinterpret_cast<const void*>(&stream_read_kernel<true>)
+                              : reinterpret_cast<const void*>(&stream_read_kernel<false>);
+  return hipExtLaunchKernel(k, grid, block, args, 0, stream, t0, t1, 0);
 }
 
 }  // namespace kvq
