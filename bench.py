@@ -12,7 +12,8 @@ resident in HBM before timing starts.
 
 Prints one JSON line. `value` is effective KV GB/s of the whole step (algorithmic
 bytes / step time); `roofline` covers the dominant kernel (the split-K decode), timed
-with HIP events recorded on its own stream around every launch. Before the W warmup
+with HIP events the library records on its stream at the start and end of every launch
+(as part of the launch itself). Before the W warmup
 steps the step runs untimed for --settle-s seconds (default 0.25): the GPU's clocks
 need some 50-100 ms of sustained load to settle.
 

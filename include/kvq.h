@@ -200,9 +200,9 @@ kvq_status kvq_decode_attention(const kvq_cache* cache, const void* q, int32_t b
 
 /*
  * Same as kvq_decode_attention, and additionally records the hipEvent_t
- * `split_begin` right before and `split_end` right after the split-K kernel on
- * `stream` (either may be NULL), so a caller can time that kernel alone with
- * hipEventElapsedTime. For benchmarking.
+ * `split_begin` at the start and `split_end` at the end of the split-K kernel on
+ * `stream` (either may be NULL), as part of that kernel's dispatch (hipExtLaunchKernel),
+ * so a caller can time that kernel alone with hipEventElapsedTime. For benchmarking.
  */
 kvq_status kvq_decode_attention_timed(const kvq_cache* cache, const void* q, int32_t batch,
                                       int32_t num_q_heads, const int32_t* block_table,
@@ -286,7 +286,8 @@ kvq_status kvq_decode_attention_noalloc(const kvq_cache* cache, const void* q, i
  *                 before the query is ranked). Values are not pruned.
  *   chunk_mask  : int32 [batch][Hkv] device array or NULL; receives the kept chunks
  *                 (bit j = chunk j) of every sequence with seq_len > 0.
- *   split_begin, split_end : hipEvent_t recorded around the split-K kernel, or NULL.
+ *   split_begin, split_end : hipEvent_t recorded at the start and end of the split-K
+ *                            kernel (as kvq_decode_attention_timed), or NULL.
  * out = softmax(scale * (R q restricted to the kept channels) . khat_t) weighted sum of
  * vhat_t. keep_chunks equal to the number of chunks gives kvq_decode_attention's result.
  */
@@ -384,7 +385,7 @@ kvq_status kvq_decode_attention_window(const kvq_cache* cache, const kvq_window*
 
 /*
  * Same as kvq_decode_attention_window, and additionally records the hipEvent_t
- * `split_begin` right before and `split_end` right after the split-K kernel over the
+ * `split_begin` at the start and `split_end` at the end of the split-K kernel over the
  * quantized span on `stream` (either may be NULL), as kvq_decode_attention_timed does.
  * For benchmarking.
  */
@@ -405,7 +406,8 @@ kvq_status kvq_decode_attention_window_timed(const kvq_cache* cache, const kvq_w
  * workgroups_per_cu (1..32) workgroups of 256 threads per compute unit. Nothing is
  * written except, with negligible probability, the first dword of `sink` (a device
  * word the caller provides). Records the hipEvent_t `ev_begin` / `ev_end` (either may be
- * NULL) around the launch on `stream`. bytes == 0 is a no-op returning KVQ_OK.
+ * NULL) at the start and end of the probe kernel on `stream`, as part of its dispatch.
+ * bytes == 0 is a no-op returning KVQ_OK.
  */
 kvq_status kvq_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t nontemporal,
                            int32_t workgroups_per_cu, void* stream, void* ev_begin, void* ev_end);
