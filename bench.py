@@ -81,7 +81,7 @@ class HipEvents:
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("decode_mfma.h", "decode_mfma.hip", "kvq_device.h"):
+    for f in ("decode_mfma.h", "decode_mfma.hip", "decode_paged.hip", "kvq_device.h"):
         with open(os.path.join(ROOT, "bit_kv_cache_quantize_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -123,7 +123,7 @@ def traffic_from_profile(key: str):
 
 def host_threads() -> int:
     """Host threads for the oracle's multi-thread timing: the CPUs this process may run
-    on, at most 16 (a one-GPU share of the GPU machine's host) and at most OMP_NUM_THREADS
+    on, at most 16 (one GPU's share of a multi-GPU host) and at most OMP_NUM_THREADS
     when that is set."""
     try:
         n = len(os.sched_getaffinity(0))

@@ -16,9 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build", "kvq")
 
-SOURCES = ["kvq_validate.cpp", "kvq_api.cpp", "quant.hip", "decode_ref.hip", "decode_mfma.hip", "decode_pruned.hip",
-           "decode_vgroup.hip", "decode_window.hip", "stream_probe.hip",
-           "decode_noalloc.hip"]
+SOURCES = ["kvq_validate.cpp", "kvq_api.cpp", "quant.hip", "decode_ref.hip", "decode_mfma.hip", "decode_paged.hip",
+           "decode_pruned.hip", "decode_vgroup.hip", "decode_window.hip", "stream_probe.hip", "decode_noalloc.hip"]
 
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 # -packed-fp32-ops: never emit packed fp32 VALU forms (v_pk_fma_f32 and friends).
@@ -36,7 +35,7 @@ def hipcc() -> str:
 # per-source extra flags: keep MFMA accumulators in ordinary VGPRs (the decode kernel
 # reads and rescales them with VALU code; AGPR placement would add copies)
 _MFMA_FLAGS = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA = {"decode_mfma.hip": _MFMA_FLAGS, "decode_pruned.hip": _MFMA_FLAGS, "decode_vgroup.hip": _MFMA_FLAGS}
+EXTRA = {src: _MFMA_FLAGS for src in ("decode_mfma.hip", "decode_paged.hip", "decode_pruned.hip", "decode_vgroup.hip")}
 
 
 def _compile(src: str) -> str:

@@ -219,7 +219,9 @@ constexpr int PF = 3;   // blocks loaded ahead
 // of p), B = the codes), and each block's product C is folded per channel as
 // o += scale * (C_hi + C_lo) + zero * sum_t p, so the scale multiplies a finished partial
 // sum instead of every element.
-template <int BITS, int G, int R, bool PRUNE, bool VT>
+// RING (paged caches): the value cursor takes each block's tile rows from the key cursor
+// through a small LDS ring instead of repeating the block-table lookups.
+template <int BITS, int G, int R, bool PRUNE, bool VT, bool RING = false>
 __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   constexpr int NG = 128 / G;
   constexpr int RB = 128 * BITS / 8;
@@ -385,6 +387,39 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     }
   };
 
+  // RING: on a partition of several pages the key cursor leaves each block's two tile rows
+  // in a 16-entry LDS ring slot (blk mod 16), and the value cursor reads them back. The key
+  // cursor is at most NBS + PF blocks ahead of the value cursor and one wave owns the ring,
+  // whose DS instructions complete in program order: a slot is read after its block's key
+  // lookup wrote it and before the key cursor reaches the block 16 further on.
+  __shared__ int64_t rows_s[RING ? 16 : 1][2];
+  auto key_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
+    tile_rows(cu, row0, row1);
+    if constexpr (RING) {
+      if (!one_page) {
+        rows_s[cu.blk & 15][0] = row0;
+        rows_s[cu.blk & 15][1] = row1;
+      }
+    }
+  };
+  // a value load off the contiguous fast path: its tile rows, and the cursor step after it
+  auto value_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
+    if constexpr (RING) {
+      if (!one_page) {
+        row0 = rows_s[cu.blk & 15][0];
+        row1 = rows_s[cu.blk & 15][1];
+        return;
+      }
+    }
+    tile_rows(cu, row0, row1);
+  };
+  auto value_next = [&](Cursor& cu) {
+    if constexpr (RING)
+      step_blk(cu);  // the ring is indexed by the block alone
+    else
+      advance(cu);
+  };
+
   // This lane's pieces of a block, relative to the first token row (tile_row) of its
   // tile: key codes, the 16-byte chunk(s) of channels 64 hQ .. 64 hQ + 63 of token nQ
   // (tiles are chunk-major, so one load instruction reads whole cache lines); value code
@@ -423,7 +458,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       row1 = row0 + 16;
       step_blk(cu);
     } else {
-      tile_rows(cu, row0, row1);
+      key_rows(cu, row0, row1);
       advance(cu);
     }
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -469,7 +504,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       step_blk(cu);
     } else {
       int64_t row0, row1;
-      tile_rows(cu, row0, row1);
+      key_rows(cu, row0, row1);
       const int64_t trow = (nQ < 16) ? row0 : row1;
       src = c.kc + trow * RB + kc_lane;
       msrc = reinterpret_cast<const uint8_t*>(c.km + (trow + (nQ & 15)) * NG);
@@ -517,11 +552,11 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       step_blk(cu);
     } else {
       int64_t row0, row1;
-      tile_rows(cu, row0, row1);
+      value_rows(cu, row0, row1);
       const int64_t trow = (q4 < 2) ? row0 : row1;
       src = c.vc + trow * RB + vc_lane;
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (trow / 16) * (NG * 64) + vmn_lane;
-      advance(cu);
+      value_next(cu);
     }
     const u32x4 w0 = ld16(src);
     vb.vc[0] = w0[0]; vb.vc[1] = w0[1]; vb.vc[2] = w0[2]; vb.vc[3] = w0[3];
@@ -551,12 +586,12 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       step_blk(cu);
     } else {
       int64_t row0, row1;
-      tile_rows(cu, row0, row1);
+      value_rows(cu, row0, row1);
       const int64_t trow = (q4 < 2) ? row0 : row1;  // value tile of tokens 8q4..8q4+7
       src = c.vc + trow * RB + vc_lane;
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (trow / 16) * (NG * 64) + vm_lane;
       brow = row0;
-      advance(cu);
+      value_next(cu);
     }
     if (VT) {
       // {scale, zero} of channels pv_channel(0..7, r16): entries 8 r16 .. 8 r16 + 7 of the

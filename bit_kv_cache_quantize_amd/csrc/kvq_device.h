@@ -258,6 +258,8 @@ inline int64_t split_units(const DecodeArgs& a, const Geometry& g) {
 // around it that separately recorded events would also time.
 hipError_t launch_decode_split(const DecodeArgs& a, const Geometry& g, hipStream_t stream, hipEvent_t t0 = nullptr,
                                hipEvent_t t1 = nullptr);
+hipError_t launch_decode_split_paged(const DecodeArgs& a, const Geometry& g, hipStream_t stream,
+                                     hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_decode_split_pruned(const DecodeArgs& a, const Geometry& g, hipStream_t stream,
                                       hipEvent_t t0 = nullptr, hipEvent_t t1 = nullptr);
 hipError_t launch_decode_split_vgroup(const DecodeArgs& a, const Geometry& g, hipStream_t stream,
