@@ -259,6 +259,13 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   const int start = a.tok_begin + split * split_len;
   if (start >= qend) return;
   const int end = min(qend, start + split_len);
+  // This lane's 8 query channels (head lane / 16 < R), loaded ahead of the first key
+  // blocks: a wave's loads complete in issue order, so a query load issued after them
+  // would hold the query's preparation until the whole first fill had arrived.
+  uint4 qraw = {0u, 0u, 0u, 0u};
+  if ((lane >> 4) < R)
+    qraw = *reinterpret_cast<const uint4*>(
+        a.q + (static_cast<int64_t>(b) * a.num_q_heads + hk * R + (lane >> 4)) * 128 + 8 * (lane & 15));
 
   // Fused step (kvq_decode_step): the unit whose partition holds the sequence's last
   // position quantizes that token's key row (lanes 0-15) and value row (lanes 16-31) into
@@ -653,8 +660,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     const int jq = lane >> 4, c16 = lane & 15;
     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (jq < R) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(
-          a.q + (static_cast<int64_t>(b) * a.num_q_heads + hk * R + jq) * 128 + 8 * c16);
+      const uint4 raw = qraw;
       x[0] = bf16_lo(raw.x); x[1] = bf16_hi(raw.x); x[2] = bf16_lo(raw.y); x[3] = bf16_hi(raw.y);
       x[4] = bf16_lo(raw.z); x[5] = bf16_hi(raw.z); x[6] = bf16_lo(raw.w); x[7] = bf16_hi(raw.w);
     }
