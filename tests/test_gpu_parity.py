@@ -287,6 +287,10 @@ BALANCED_CASES = {
     "single_token": (_small("c5", batch=3, ragged=(0, 1)), [0, 1, 0]),
     # every sequence empty: no partitions at all, zero rows
     "all_empty": (_small("c5", batch=5, ragged=(0, 1)), [0, 0, 0, 0, 0]),
+    # equal lengths whose partitions fill one round of waves exactly (on 256 CUs: 2 and 4
+    # kv heads, 16 partitions per sequence, the last one shorter), INT4 g32 and INT2 g128
+    "paired_b64_kv2": (_small("c2", batch=64, num_kv_heads=2, num_q_heads=8, context=7900), None),
+    "paired_b32_kv4_int2_g128": (_small("c4", batch=32, num_kv_heads=4, num_q_heads=16, context=11982), None),
 }
 
 
