@@ -19,7 +19,8 @@ need some 50-100 ms of sustained load to settle.
 
   python bench.py [--steps K] [--warmup W] [--workload h1] [--gpus 1] [--window S,R] [--eager] [--unfused]
 
-The timed step is the K steps replayed from one HIP graph (after an untimed replay);
+The timed step is the K steps replayed from one HIP graph (after untimed replays for
+--settle-s seconds, at least one);
 the eager host-launched K steps run first, and their per-launch events time the split
 kernel for the roofline. --eager reports the host-launched step time instead.
 
@@ -381,7 +382,7 @@ def main():
 
     # The same K steps replayed from one HIP graph: the three kernels of a step then run
     # back to back without host launches between them (short steps are otherwise paced by
-    # the host). The graph is replayed once untimed, then once timed; the last replayed
+    # the host). The graph is replayed untimed (see below), then once timed; the last replayed
     # step's output must equal the eager step's bit for bit. The split kernel's
     # event-timed launches above give the roofline either way.
     graph = None
@@ -398,8 +399,17 @@ def main():
         with torch.cuda.graph(g):
             for j in range(args.steps):
                 step(base + j)
-        g.replay()
-        torch.cuda.synchronize()
+        # the capture leaves the GPU idle long enough for its clocks to drop: untimed
+        # replays for settle_s seconds (at least one) before the timed one; a short K
+        # (20 steps of h1 are ~9 ms) would otherwise be timed on unsettled clocks
+        n_untimed = 0
+        t_settle = time.perf_counter()
+        while True:
+            g.replay()
+            n_untimed += 1
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_settle >= args.settle_s:
+                break
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g0.record()
         g.replay()
@@ -410,7 +420,8 @@ def main():
         step(base + args.steps - 1)
         torch.cuda.synchronize()
         graph = {"us_per_step": round(graph_ms * 1e3, 2), "steps": args.steps,
-                 "matches_eager": bool(torch.equal(replayed, out)), "us_per_step_eager": round(ms * 1e3, 2)}
+                 "matches_eager": bool(torch.equal(replayed, out)), "us_per_step_eager": round(ms * 1e3, 2),
+                 "untimed_replays": n_untimed}
         if not graph["matches_eager"]:
             sys.exit("bench.py: the graph-replayed step differs from the eager step")
         ms = graph_ms
