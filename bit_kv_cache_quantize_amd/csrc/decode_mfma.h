@@ -368,13 +368,16 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       }
     }
   };
-  // rows of the cursor block's two 16-token tiles (a tile past the partition end: the
-  // first tile again); one window check per block keeps both of its pages in the window
-  auto tile_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
-    const int t0 = start + 32 * cu.blk;
+  // The cursor block's two 16-token tiles as tile indices: a tile of one kv head starts at
+  // row 16 t, and t stays below 2^32 (num_pages * Hkv * page / 16, checked on the host), so
+  // the first tile t0 and the step d to the second (t0 + d; d = 0 when the second lies past
+  // the partition end: the first tile again) are 32-bit. One window check per block keeps
+  // both of its pages in the window.
+  auto tile_ids = [&](Cursor& cu, uint32_t& t0, uint32_t& d) {
+    const int tok = start + 32 * cu.blk;
     if (one_page) {
-      row0 = row_base + t0;
-      row1 = (t0 + 16 < end) ? row0 + 16 : row0;
+      t0 = static_cast<uint32_t>((row_base + tok) >> 4);
+      d = tok + 16 < end ? 1u : 0u;
       return;
     }
     if (cu.pg + 1 - cu.wbase >= 64) {  // a cursor visits pages in increasing order
@@ -382,43 +385,54 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       cu.bt_w = window(cu.pg);
     }
     const int i0 = cu.pg - cu.wbase;  // 0 .. 62
-    const uint32_t u0 = __builtin_amdgcn_readlane(cu.bt_w, i0);
-    row0 = static_cast<int64_t>(static_cast<uint64_t>(u0) * static_cast<uint32_t>(P)) + cu.off;
-    if (t0 + 16 >= end) {
-      row1 = row0;
-    } else if (cu.off + 16 < P) {
-      row1 = row0 + 16;
-    } else {  // the second tile opens the next page (off = P - 16)
-      const uint32_t u1 = __builtin_amdgcn_readlane(cu.bt_w, i0 + 1);
-      row1 = static_cast<int64_t>(static_cast<uint64_t>(u1) * static_cast<uint32_t>(P));
-    }
+    const uint32_t p16 = static_cast<uint32_t>(P >> 4);
+    t0 = __builtin_amdgcn_readlane(cu.bt_w, i0) * p16 + static_cast<uint32_t>(cu.off >> 4);
+    if (tok + 16 >= end)
+      d = 0u;
+    else if (cu.off + 16 < P)
+      d = 1u;
+    else  // the second tile opens the next page (off = P - 16)
+      d = __builtin_amdgcn_readlane(cu.bt_w, i0 + 1) * p16 - t0;
   };
 
-  // RING: on a partition of several pages the key cursor leaves each block's two tile rows
-  // in a 16-entry LDS ring slot (blk mod 16), and the value cursor reads them back. The key
+  // RING: on a partition of several pages the key cursor leaves each block's {t0, d} in a
+  // 16-entry LDS ring slot (blk mod 16), and the value cursor reads them back. The key
   // cursor is at most NBS + PF blocks ahead of the value cursor and one wave owns the ring,
   // whose DS instructions complete in program order: a slot is read after its block's key
   // lookup wrote it and before the key cursor reaches the block 16 further on.
-  __shared__ int64_t rows_s[RING ? 16 : 1][2];
-  auto key_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
-    tile_rows(cu, row0, row1);
+  __shared__ uint32_t ids_s[RING ? 16 : 1][2];
+  auto key_ids = [&](Cursor& cu, uint32_t& t0, uint32_t& d) {
+    tile_ids(cu, t0, d);
     if constexpr (RING) {
       if (!one_page) {
-        rows_s[cu.blk & 15][0] = row0;
-        rows_s[cu.blk & 15][1] = row1;
+        ids_s[cu.blk & 15][0] = t0;
+        ids_s[cu.blk & 15][1] = d;
       }
     }
   };
-  // a value load off the contiguous fast path: its tile rows, and the cursor step after it
-  auto value_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
+  // a value load off the contiguous fast path: its tiles, and the cursor step after it
+  auto value_ids = [&](Cursor& cu, uint32_t& t0, uint32_t& d) {
     if constexpr (RING) {
       if (!one_page) {
-        row0 = rows_s[cu.blk & 15][0];
-        row1 = rows_s[cu.blk & 15][1];
+        t0 = ids_s[cu.blk & 15][0];
+        d = ids_s[cu.blk & 15][1];
         return;
       }
     }
-    tile_rows(cu, row0, row1);
+    tile_ids(cu, t0, d);
+  };
+  // the same as token rows (narrow groups)
+  auto key_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
+    uint32_t t0, d;
+    key_ids(cu, t0, d);
+    row0 = static_cast<int64_t>(t0) << 4;
+    row1 = static_cast<int64_t>(t0 + d) << 4;
+  };
+  auto value_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
+    uint32_t t0, d;
+    value_ids(cu, t0, d);
+    row0 = static_cast<int64_t>(t0) << 4;
+    row1 = static_cast<int64_t>(t0 + d) << 4;
   };
   auto value_next = [&](Cursor& cu) {
     if constexpr (RING)
@@ -441,6 +455,14 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   const uint32_t kmoff = static_cast<uint32_t>(nQ * NG * 4);
   const uint32_t voff = static_cast<uint32_t>(q4 < 2 ? 0 : 16 * RB) + vc_lane;
   const uint32_t vmoff = static_cast<uint32_t>(q4 < 2 ? 0 : NG * 64) + vm_lane;
+  // Off the contiguous fast path a lane's tile is t0 + (mask & d), its second-tile lanes
+  // taking the mask: its address is one multiply-add from these per-lane bases.
+  const uint32_t hmK = nQ < 16 ? 0u : ~0u;  // key loads: token nQ lies in the second tile
+  const uint32_t hmV = q4 < 2 ? 0u : ~0u;   // value loads: tokens 8 q4 .. lie in the second tile
+  const uint8_t* const kc_l = c.kc + kc_lane;
+  const uint8_t* const km_l = reinterpret_cast<const uint8_t*>(c.km) + (nQ & 15) * NG * 4;
+  const uint8_t* const vc_l = c.vc + vc_lane;
+  const uint8_t* const vm_l = reinterpret_cast<const uint8_t*>(c.vm) + vm_lane;
   // Key and value streams are read once: non-temporal loads. V meta loads cover whole
   // cache lines only with 4 groups; with fewer they read half lines and stay cached.
   auto ld16 = [](const uint8_t* p) { return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)); };
@@ -510,11 +532,11 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       msrc = reinterpret_cast<const uint8_t*>(c.km) + r0 * (NG * 4) + kmoff;
       step_blk(cu);
     } else {
-      int64_t row0, row1;
-      key_rows(cu, row0, row1);
-      const int64_t trow = (nQ < 16) ? row0 : row1;
-      src = c.kc + trow * RB + kc_lane;
-      msrc = reinterpret_cast<const uint8_t*>(c.km + (trow + (nQ & 15)) * NG);
+      uint32_t t0, d;
+      key_ids(cu, t0, d);
+      const uint32_t ts = t0 + (hmK & d);  // this lane's tile
+      src = kc_l + static_cast<uint64_t>(ts) * (16 * RB);
+      msrc = km_l + static_cast<uint64_t>(ts) * (16 * NG * 4);
       advance(cu);
     }
     u32x4 x0 = {0u, 0u, 0u, 0u};
@@ -592,12 +614,12 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       brow = r0;
       step_blk(cu);
     } else {
-      int64_t row0, row1;
-      value_rows(cu, row0, row1);
-      const int64_t trow = (q4 < 2) ? row0 : row1;  // value tile of tokens 8q4..8q4+7
-      src = c.vc + trow * RB + vc_lane;
-      msrc = reinterpret_cast<const uint8_t*>(c.vm) + (trow / 16) * (NG * 64) + vm_lane;
-      brow = row0;
+      uint32_t t0, d;
+      value_ids(cu, t0, d);
+      const uint32_t ts = t0 + (hmV & d);  // value tile of tokens 8q4..8q4+7
+      src = vc_l + static_cast<uint64_t>(ts) * (16 * RB);
+      msrc = vm_l + static_cast<uint64_t>(ts) * (NG * 64);
+      brow = static_cast<int64_t>(t0) << 4;
       value_next(cu);
     }
     if (VT) {

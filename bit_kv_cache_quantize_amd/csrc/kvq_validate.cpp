@@ -64,8 +64,11 @@ kvq_status check_cache(const kvq_cache* c, bool planes, Geometry* g) {
 
 bool cache_supported(const Geometry& g) {
   if (g.d != 128) return false;
-  // the decode kernels index a page's rows of one kv head as page * Hkv + head in 32 bits
+  // the decode kernels index a page's rows of one kv head as page * Hkv + head, and a
+  // 16-token tile of one kv head as (page * Hkv + head) * page_size / 16 + offset / 16, in
+  // 32 bits: fewer than 2^32 tiles (2^32 tiles of INT2 codes alone would be 2 TiB)
   if (g.num_pages > 0xFFFFFFFFLL / g.hkv) return false;
+  if (g.num_pages * g.hkv > 0xFFFFFFFFLL / (g.page / kTile)) return false;
   if (g.group != 32 && g.group != 64 && g.group != 128) return false;
   if (g.hblock != 0 && (g.hblock < 2 || g.hblock > 128)) return false;
   return true;

@@ -287,6 +287,21 @@ def test_page_index_limit():
     assert L.kvq_decode_workspace_bytes(ctypes.byref(ok), 2, 32, 64, 0) > 0
 
 
+def test_tile_index_limit():
+    """The paged decode loads index a kv head's 16-token tiles as (page * Hkv + head) *
+    page_size / 16 + offset / 16 in 32 bits: a pool of 2^32 tiles or more is reported
+    unsupported before any launch, one tile fewer is accepted."""
+    L, v = kvq.lib(), ctypes.c_void_p
+    args = [v(FAKE), 2, 32, v(FAKE), 4, v(FAKE), 64, 0.0, 0, v(FAKE), 1 << 40, v(FAKE), None]
+    for page in (64, 256):
+        pages_at_limit = (1 << 32) // (8 * page // 16)  # x 8 kv heads x page / 16 tiles = 2^32
+        big = _desc(page_size=page, num_pages=pages_at_limit)
+        ok = _desc(page_size=page, num_pages=pages_at_limit - 1)
+        assert L.kvq_decode_attention(ctypes.byref(big), *args) == kvq.ERR_UNSUPPORTED, page
+        assert L.kvq_decode_workspace_bytes(ctypes.byref(big), 2, 32, 64, 0) == 0, page
+        assert L.kvq_decode_workspace_bytes(ctypes.byref(ok), 2, 32, 64, 0) > 0, page
+
+
 def _win(**kw):
     base = dict(sink=32, recent=128, batch=4, k=FAKE, v=FAKE, residual=0)
     base.update(kw)
