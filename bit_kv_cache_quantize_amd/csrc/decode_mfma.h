@@ -227,6 +227,8 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   constexpr int RB = 128 * BITS / 8;
   // one or two groups per head: int8 score MFMAs and merged value digits (see the top)
   constexpr bool NARROW = NG <= 2 && !PRUNE && !VT;
+  // paged instances with groups of 32 take their tiles a super-block at a time (SBT below)
+  constexpr bool SBT = RING && !NARROW;
   using VB = std::conditional_t<NARROW, VBlock<BITS, true, NG>, VBlock<BITS>>;
   const DevCache& c = a.c;
   const int lane = threadIdx.x;
@@ -373,9 +375,10 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   // the first tile t0 and the step d to the second (t0 + d; d = 0 when the second lies past
   // the partition end: the first tile again) are 32-bit. One window check per block keeps
   // both of its pages in the window.
+  const uint32_t p16 = static_cast<uint32_t>(P >> 4);  // tiles per page
   auto tile_ids = [&](Cursor& cu, uint32_t& t0, uint32_t& d) {
     const int tok = start + 32 * cu.blk;
-    if (one_page) {
+    if (one_page || SBT) {  // (SBT: only one-page partitions get here)
       t0 = static_cast<uint32_t>((row_base + tok) >> 4);
       d = tok + 16 < end ? 1u : 0u;
       return;
@@ -385,7 +388,6 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       cu.bt_w = window(cu.pg);
     }
     const int i0 = cu.pg - cu.wbase;  // 0 .. 62
-    const uint32_t p16 = static_cast<uint32_t>(P >> 4);
     t0 = __builtin_amdgcn_readlane(cu.bt_w, i0) * p16 + static_cast<uint32_t>(cu.off >> 4);
     if (tok + 16 >= end)
       d = 0u;
@@ -400,10 +402,10 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   // cursor is at most NBS + PF blocks ahead of the value cursor and one wave owns the ring,
   // whose DS instructions complete in program order: a slot is read after its block's key
   // lookup wrote it and before the key cursor reaches the block 16 further on.
-  __shared__ uint32_t ids_s[RING ? 16 : 1][2];
+  __shared__ uint32_t ids_s[RING && !SBT ? 16 : 1][2];
   auto key_ids = [&](Cursor& cu, uint32_t& t0, uint32_t& d) {
     tile_ids(cu, t0, d);
-    if constexpr (RING) {
+    if constexpr (RING && !SBT) {
       if (!one_page) {
         ids_s[cu.blk & 15][0] = t0;
         ids_s[cu.blk & 15][1] = d;
@@ -412,7 +414,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   };
   // a value load off the contiguous fast path: its tiles, and the cursor step after it
   auto value_ids = [&](Cursor& cu, uint32_t& t0, uint32_t& d) {
-    if constexpr (RING) {
+    if constexpr (RING && !SBT) {
       if (!one_page) {
         t0 = ids_s[cu.blk & 15][0];
         d = ids_s[cu.blk & 15][1];
@@ -433,6 +435,69 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     value_ids(cu, t0, d);
     row0 = static_cast<int64_t>(t0) << 4;
     row1 = static_cast<int64_t>(t0 + d) << 4;
+  };
+  // SBT (paged, groups of 32): the tiles of a whole super-block at a time. Lanes 0..15
+  // take the 16 tiles of its 8 blocks (lane 2j + h: tile h of block j; a block past the
+  // partition's last repeats the last, a tile past the partition end its block's first),
+  // divide their offset from the walk's page by the tiles per page, fetch the page's entry
+  // from the window of block-table entries with one cross-lane permute, and write the tile
+  // indices to a two-slot LDS table (slot = super-block mod 2) that both kinds' loads read
+  // per lane; lane 16 finds the next super-block's page and offset. A super-block's table
+  // is written before its first key load (the previous super-block's value pass, or the
+  // prologue) and read until the next one's value pass rewrites the other slot.
+  __shared__ __align__(8) uint32_t sbid_s[SBT ? 2 : 1][16];
+  struct SbWalk {
+    int blk, pg, off16, wbase;  // the super-block's first block, its page, tile offset in it
+    uint32_t bt_w;              // window of block-table entries from page wbase
+  };
+  const SbWalk walk0 = {0, pg_first, (start - pg_first * P) >> 4, pg_first, cur0.bt_w};
+  SbWalk walk = walk0;
+  // 1 / p16, for the lanes' quotients below: their offsets stay below p16 + 2 NBS + 1, so
+  // the fp32 estimate is within one of the quotient and one correction makes it exact
+  const float p16_rcp =
+      __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, 1.0f / static_cast<float>(p16))));
+  auto sb_ids = [&](SbWalk& w) {
+    // the lane index is re-read here, so that nothing derived from it stays live in a
+    // register between super-blocks
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    int x16;
+    if (ln < 16) {
+      const int j = min(ln >> 1, nblk - 1 - w.blk);
+      const int h = start + 32 * (w.blk + j) + 16 < end ? (ln & 1) : 0;
+      x16 = w.off16 + 2 * j + h;
+    } else {
+      x16 = w.off16 + 2 * NBS;
+    }
+    uint32_t q = static_cast<uint32_t>(static_cast<float>(x16) * p16_rcp);
+    int r = x16 - static_cast<int>(q * p16);
+    if (r < 0) {
+      --q;
+      r += static_cast<int>(p16);
+    } else if (r >= static_cast<int>(p16)) {
+      ++q;
+      r -= static_cast<int>(p16);
+    }
+    // pages w.pg .. w.pg + q(lane 15) hold the super-block (a cursor visits pages in
+    // increasing order; the window reaches at most pg_last)
+    const int qlast = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(static_cast<int>(q), 15));
+    if (w.pg + qlast - w.wbase >= 64) {
+      w.wbase = w.pg;
+      w.bt_w = window(w.pg);
+    }
+    const int wi = (w.pg + static_cast<int>(q) - w.wbase) & 63;
+    const uint32_t u = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * wi, static_cast<int>(w.bt_w)));
+    if (ln < 16) sbid_s[(w.blk >> 3) & 1][ln] = u * p16 + static_cast<uint32_t>(r);
+    w.blk += NBS;
+    w.pg += __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(static_cast<int>(q), 16));
+    w.off16 = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(static_cast<int>(r), 16));
+  };
+  // this lane's tile of the cursor block from the table (both tiles in one read; `second`:
+  // the lane reads the block's second tile)
+  auto sb_tile = [&](const Cursor& cu, bool second) -> uint32_t {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 t = *reinterpret_cast<const u32x2*>(&sbid_s[(cu.blk >> 3) & 1][2 * (cu.blk & 7)]);
+    return second ? t[1] : t[0];
   };
   auto value_next = [&](Cursor& cu) {
     if constexpr (RING)
@@ -531,6 +596,11 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       src = c.kc + r0 * RB + koff;
       msrc = reinterpret_cast<const uint8_t*>(c.km) + r0 * (NG * 4) + kmoff;
       step_blk(cu);
+    } else if (SBT && !one_page) {
+      const uint32_t ts = sb_tile(cu, nQ >= 16);
+      src = kc_l + static_cast<uint64_t>(ts) * (16 * RB);
+      msrc = km_l + static_cast<uint64_t>(ts) * (16 * NG * 4);
+      step_blk(cu);
     } else {
       uint32_t t0, d;
       key_ids(cu, t0, d);
@@ -613,6 +683,12 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (r0 / 16) * (NG * 64) + vmoff;
       brow = r0;
       step_blk(cu);
+    } else if (SBT && !one_page) {
+      const uint32_t ts = sb_tile(cu, q4 >= 2);  // value tile of tokens 8q4..8q4+7
+      src = vc_l + static_cast<uint64_t>(ts) * (16 * RB);
+      msrc = vm_l + static_cast<uint64_t>(ts) * (NG * 64);
+      brow = 0;  // (value token groups have no paged instances)
+      step_blk(cu);
     } else {
       uint32_t t0, d;
       value_ids(cu, t0, d);
@@ -669,6 +745,9 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   KBT kb[PF + 1];
   VB vb[PF + 1];
   Cursor kcur = cur0, vcur = cur0;
+  if constexpr (SBT) {
+    if (!one_page) sb_ids(walk);
+  }
 #pragma unroll
   for (int j = 0; j < PF; ++j) kb[j] = j < nblk ? load_k(kcur, std::false_type{}) : KBT{};
 
@@ -1224,6 +1303,9 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     }
     advance_max(bm0, bm1, check_big ? 8.0f : 0.0f);
     publish_p(lg, n, guard);
+    if constexpr (SBT && !GUARD && !LASTC) {  // the next super-block's tiles
+      if (!one_page) sb_ids(walk);
+    }
 #pragma unroll
     for (int j = 0; j < NBS; ++j) {
       if (j + PF < NBS)
@@ -1253,6 +1335,10 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     if (attempt > 0) {
       kcur = cur0;
       vcur = cur0;
+      if constexpr (SBT) {
+        walk = walk0;
+        if (!one_page) sb_ids(walk);
+      }
 #pragma unroll
       for (int j = 0; j < PF; ++j) kb[j] = j < nblk ? load_k(kcur, std::false_type{}) : KBT{};
     }

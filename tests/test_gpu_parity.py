@@ -123,7 +123,32 @@ DECODE_CASES = {
     "int2_g32_hb32": _small("c2", batch=2, context=190, bits=2, group_size=32, hadamard_block=32),
     # 48-token pages: a 32-token block's second tile often starts on the next page
     "paged48": _small("c5", batch=4, ragged=(40, 900), page_size=48),
+    # pages of 17 and 256 tiles: partitions cross page boundaries at other tile offsets
+    "paged272": _small("c5", batch=4, ragged=(300, 3000), page_size=272),
+    "paged4096": _small("c5", batch=3, ragged=(3000, 9000), page_size=4096),
+    "paged16_int2_g32": _small("c5", batch=4, ragged=(30, 700), bits=2, group_size=32),
 }
+
+
+LONG_PAGED_CASES = {f"p{page}_int{b}_splits{ns}": (page, b, ns)
+                    for page in (16, 48, 80) for b in (4, 2) for ns in (1, 2)}
+
+
+@pytest.mark.parametrize("name", list(LONG_PAGED_CASES))
+def test_decode_long_partitions_over_many_pages(name):
+    """Partitions spanning far more than the 64 block-table entries a wave keeps at a time
+    (one or two partitions per sequence of 3000-5200 tokens in 16-, 48- and 80-token
+    pages): the window of entries is refilled inside a partition, at every tile offset a
+    super-block can start on."""
+    page, bits, ns = LONG_PAGED_CASES[name]
+    w = _small("c5", batch=2, ragged=(3000, 5200), page_size=page, bits=bits, group_size=32, seed=page + bits)
+    print(f"[decode] long paged partitions {name}", flush=True)
+    p = make_pair(w, DEV)
+    got, want = decode_both(p, DEV, num_splits=ns)
+    err = max_err(got, want)
+    record(f"decode_long_paged/{name}", err)
+    assert np.all(np.isfinite(got))
+    assert err <= TOL
 
 
 @pytest.mark.parametrize("reference", [False, True], ids=["mfma", "reference"])
