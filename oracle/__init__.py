@@ -18,16 +18,16 @@ from dataclasses import dataclass
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "kvq_oracle.c")
+_SRC = os.path.join(_HERE, "kvq_oracle.cpp")
 _LIB = os.path.join(_HERE, "libkvq_oracle.so")
 
 # -ffp-contract=off: every fp32 operation of the contract is its own IEEE rounding.
-CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+CFLAGS = ["-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
 
 def build(src: str = _SRC, out: str = _LIB, extra: list[str] | None = None) -> str:
-    """Compile the oracle with gcc. Returns the path of the shared library."""
-    cmd = ["gcc", *CFLAGS, *(extra or []), src, "-o", out, "-lm"]
+    """Compile the oracle with g++. Returns the path of the shared library."""
+    cmd = ["g++", *CFLAGS, *(extra or []), src, "-o", out, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 

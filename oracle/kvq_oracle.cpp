@@ -1,7 +1,8 @@
 /*
  * kvq oracle: plain CPU reference. TEST INFRASTRUCTURE ONLY (see kvq_oracle.h).
  *
- * Build: gcc -std=c11 -O2 -ffp-contract=off -fno-fast-math -fPIC -shared kvq_oracle.c -lm
+ * Build: g++ -std=c++17 -O2 -ffp-contract=off -fno-fast-math -fPIC -shared kvq_oracle.cpp -lm
+ * (C-style C++: plain loops and arrays; the exported functions have C linkage.)
  * -ffp-contract=off keeps every fp32 operation a separate IEEE rounding, which the
  * arithmetic contract in kvq_oracle.h requires.
  */

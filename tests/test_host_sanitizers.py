@@ -2,7 +2,7 @@
 
 Two host-side parts are built with `-fsanitize=address,undefined -fno-sanitize-recover=all`
 and exercised:
-  - the oracle (oracle/kvq_oracle.c): every pin of tests/oracle_pins.py runs against the
+  - the oracle (oracle/kvq_oracle.cpp): every pin of tests/oracle_pins.py runs against the
     instrumented build in a child process with the ASan runtime preloaded;
   - the library's argument checks and size computations (csrc/kvq_validate.cpp, which
     needs no HIP): tests/native/validate_driver.cpp replays the documented statuses and
@@ -23,7 +23,7 @@ import pytest
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-ORACLE_SRC = os.path.join(ROOT, "oracle", "kvq_oracle.c")
+ORACLE_SRC = os.path.join(ROOT, "oracle", "kvq_oracle.cpp")
 SAN = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 RUNNER = r"""
@@ -60,7 +60,7 @@ def _run_pins(lib):
 
 
 def _build_oracle(src_text, tmp, name):
-    src = os.path.join(tmp, f"{name}.c")
+    src = os.path.join(tmp, f"{name}.cpp")
     with open(src, "w") as f:
         f.write(src_text)
     return oracle.build(src, os.path.join(tmp, f"lib{name}.so"), extra=SAN + [f"-I{os.path.dirname(ORACLE_SRC)}"])

@@ -2,7 +2,7 @@
 
 The mistakes are the plausible ones: a flipped sign, a wrong index, a dropped term,
 a transposed operand, a wrong rounding. Each mutant is compiled from a text-edited
-copy of oracle/kvq_oracle.c into a temporary directory and the pins of
+copy of oracle/kvq_oracle.cpp into a temporary directory and the pins of
 tests/oracle_pins.py run against it in a child process (so a mutant that crashes
 also counts as caught). Nothing here touches the real oracle build or a GPU.
 """
@@ -17,7 +17,7 @@ import pytest
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "oracle", "kvq_oracle.c")
+SRC = os.path.join(ROOT, "oracle", "kvq_oracle.cpp")
 
 # (name, original text, replacement)
 MUTANTS = [
@@ -94,7 +94,7 @@ def _run(name, old, new, tmp):
     src = open(SRC).read()
     # a pattern shared by the plain and the windowed decode is mutated in both
     assert src.count(old) >= 1, f"mutant {name}: pattern not found"
-    path = os.path.join(tmp, f"mut_{name}.c")
+    path = os.path.join(tmp, f"mut_{name}.cpp")
     with open(path, "w") as f:
         f.write(src.replace(old, new))
     # the mutant includes the oracle's header from the source tree
