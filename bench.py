@@ -102,6 +102,8 @@ def profile_key(args) -> str:
         key += "_hybrid"
     if args.hadamard_block >= 0:
         key += f"_hb{args.hadamard_block}"
+    if args.page_size >= 0:
+        key += f"_p{args.page_size}"
     if args.num_splits:
         key += f"_splits{args.num_splits}"
     if args.unfused:
@@ -202,6 +204,9 @@ def main():
     ap.add_argument("--hybrid", action="store_true", help="hybrid symmetric/asymmetric groups (quant_mode 1)")
     ap.add_argument("--hadamard-block", type=int, default=-1,
                     help="override the workload's rotation block (0 = no rotation), e.g. to time rotation on/off")
+    ap.add_argument("--page-size", type=int, default=-1,
+                    help="override the workload's page size (tokens, a multiple of 16; 0 = one page per sequence), "
+                         "e.g. to time a contiguous workload on paged caches")
     ap.add_argument("--vgroup", action="store_true",
                     help="values grouped along tokens (v_grouping 1) with a bf16 residual of one group")
     ap.add_argument("--prune", type=int, default=0,
@@ -233,6 +238,8 @@ def main():
     w = wl.get(args.workload)
     if args.hadamard_block >= 0:
         w = w.with_(hadamard_block=args.hadamard_block)
+    if args.page_size >= 0:
+        w = w.with_(page_size=args.page_size)
     if w.ragged is not None:
         lens = wl.seq_lens(w)
     else:

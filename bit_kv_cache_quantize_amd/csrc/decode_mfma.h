@@ -219,16 +219,17 @@ constexpr int PF = 3;   // blocks loaded ahead
 // of p), B = the codes), and each block's product C is folded per channel as
 // o += scale * (C_hi + C_lo) + zero * sum_t p, so the scale multiplies a finished partial
 // sum instead of every element.
-// RING (paged caches): the value cursor takes each block's tile rows from the key cursor
-// through a small LDS ring instead of repeating the block-table lookups.
-template <int BITS, int G, int R, bool PRUNE, bool VT, bool RING = false>
+// PAGED (caches whose sequences span pages): the tiles of a whole super-block are looked up
+// at once into a small LDS table that both kinds' loads read (SBT below), instead of a
+// block-table lookup per block and kind.
+template <int BITS, int G, int R, bool PRUNE, bool VT, bool PAGED = false>
 __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
   constexpr int NG = 128 / G;
   constexpr int RB = 128 * BITS / 8;
   // one or two groups per head: int8 score MFMAs and merged value digits (see the top)
   constexpr bool NARROW = NG <= 2 && !PRUNE && !VT;
-  // paged instances with groups of 32 take their tiles a super-block at a time (SBT below)
-  constexpr bool SBT = RING && !NARROW;
+  // paged instances take their tiles a super-block at a time (SBT below)
+  constexpr bool SBT = PAGED;
   using VB = std::conditional_t<NARROW, VBlock<BITS, true, NG>, VBlock<BITS>>;
   const DevCache& c = a.c;
   const int lane = threadIdx.x;
@@ -397,46 +398,14 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       d = __builtin_amdgcn_readlane(cu.bt_w, i0 + 1) * p16 - t0;
   };
 
-  // RING: on a partition of several pages the key cursor leaves each block's {t0, d} in a
-  // 16-entry LDS ring slot (blk mod 16), and the value cursor reads them back. The key
-  // cursor is at most NBS + PF blocks ahead of the value cursor and one wave owns the ring,
-  // whose DS instructions complete in program order: a slot is read after its block's key
-  // lookup wrote it and before the key cursor reaches the block 16 further on.
-  __shared__ uint32_t ids_s[RING && !SBT ? 16 : 1][2];
-  auto key_ids = [&](Cursor& cu, uint32_t& t0, uint32_t& d) {
-    tile_ids(cu, t0, d);
-    if constexpr (RING && !SBT) {
-      if (!one_page) {
-        ids_s[cu.blk & 15][0] = t0;
-        ids_s[cu.blk & 15][1] = d;
-      }
-    }
-  };
-  // a value load off the contiguous fast path: its tiles, and the cursor step after it
-  auto value_ids = [&](Cursor& cu, uint32_t& t0, uint32_t& d) {
-    if constexpr (RING && !SBT) {
-      if (!one_page) {
-        t0 = ids_s[cu.blk & 15][0];
-        d = ids_s[cu.blk & 15][1];
-        return;
-      }
-    }
-    tile_ids(cu, t0, d);
-  };
   // the same as token rows (narrow groups)
-  auto key_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
+  auto tile_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
     uint32_t t0, d;
-    key_ids(cu, t0, d);
+    tile_ids(cu, t0, d);
     row0 = static_cast<int64_t>(t0) << 4;
     row1 = static_cast<int64_t>(t0 + d) << 4;
   };
-  auto value_rows = [&](Cursor& cu, int64_t& row0, int64_t& row1) {
-    uint32_t t0, d;
-    value_ids(cu, t0, d);
-    row0 = static_cast<int64_t>(t0) << 4;
-    row1 = static_cast<int64_t>(t0 + d) << 4;
-  };
-  // SBT (paged, groups of 32): the tiles of a whole super-block at a time. Lanes 0..15
+  // SBT (paged instances): the tiles of a whole super-block at a time. Lanes 0..15
   // take the 16 tiles of its 8 blocks (lane 2j + h: tile h of block j; a block past the
   // partition's last repeats the last, a tile past the partition end its block's first),
   // divide their offset from the walk's page by the tiles per page, fetch the page's entry
@@ -499,9 +468,17 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
     const u32x2 t = *reinterpret_cast<const u32x2*>(&sbid_s[(cu.blk >> 3) & 1][2 * (cu.blk & 7)]);
     return second ? t[1] : t[0];
   };
+  // both tiles of the cursor block from the table, as token rows (a wave-uniform pair:
+  // the narrow-group key loads address one tile per instruction)
+  auto sb_rows = [&](const Cursor& cu, int64_t& row0, int64_t& row1) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 t = *reinterpret_cast<const u32x2*>(&sbid_s[(cu.blk >> 3) & 1][2 * (cu.blk & 7)]);
+    row0 = static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(t[0])))) << 4;
+    row1 = static_cast<int64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(t[1])))) << 4;
+  };
   auto value_next = [&](Cursor& cu) {
-    if constexpr (RING)
-      step_blk(cu);  // the ring is indexed by the block alone
+    if constexpr (PAGED)
+      step_blk(cu);  // only one-page partitions get here (the table serves the others)
     else
       advance(cu);
   };
@@ -551,8 +528,11 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       row0 = row_base + start + 32 * cu.blk;  // a multiple of 16
       row1 = row0 + 16;
       step_blk(cu);
+    } else if (SBT && !one_page) {
+      sb_rows(cu, row0, row1);
+      step_blk(cu);
     } else {
-      key_rows(cu, row0, row1);
+      tile_rows(cu, row0, row1);
       advance(cu);
     }
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -603,7 +583,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       step_blk(cu);
     } else {
       uint32_t t0, d;
-      key_ids(cu, t0, d);
+      tile_ids(cu, t0, d);
       const uint32_t ts = t0 + (hmK & d);  // this lane's tile
       src = kc_l + static_cast<uint64_t>(ts) * (16 * RB);
       msrc = km_l + static_cast<uint64_t>(ts) * (16 * NG * 4);
@@ -649,9 +629,14 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       src = c.vc + r0 * RB + voff;
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (r0 / 16 + (q4 >> 1)) * (NG * 64) + vmn_lane;
       step_blk(cu);
+    } else if (SBT && !one_page) {
+      const uint32_t ts = sb_tile(cu, q4 >= 2);  // value tile of tokens 8q4..8q4+7
+      src = vc_l + static_cast<uint64_t>(ts) * (16 * RB);
+      msrc = reinterpret_cast<const uint8_t*>(c.vm) + vmn_lane + static_cast<uint64_t>(ts) * (NG * 64);
+      step_blk(cu);
     } else {
       int64_t row0, row1;
-      value_rows(cu, row0, row1);
+      tile_rows(cu, row0, row1);
       const int64_t trow = (q4 < 2) ? row0 : row1;
       src = c.vc + trow * RB + vc_lane;
       msrc = reinterpret_cast<const uint8_t*>(c.vm) + (trow / 16) * (NG * 64) + vmn_lane;
@@ -691,7 +676,7 @@ __global__ __launch_bounds__(64) void decode_split_mfma_kernel(DecodeArgs a) {
       step_blk(cu);
     } else {
       uint32_t t0, d;
-      value_ids(cu, t0, d);
+      tile_ids(cu, t0, d);
       const uint32_t ts = t0 + (hmV & d);  // value tile of tokens 8q4..8q4+7
       src = vc_l + static_cast<uint64_t>(ts) * (16 * RB);
       msrc = vm_l + static_cast<uint64_t>(ts) * (NG * 64);

@@ -1,6 +1,7 @@
 // Split-K decode attention on the matrix cores for caches whose sequences span several
-// pages: the kernel (decode_mfma.h) with the value cursor reading the key cursor's tile
-// rows from an LDS ring, for every supported (bits, group, GQA ratio).
+// pages: the kernel (decode_mfma.h) with its PAGED form, which looks up the tiles of a
+// whole super-block at once into an LDS table, for every supported (bits, group, GQA
+// ratio).
 #include "decode_mfma.h"
 
 namespace kvq {

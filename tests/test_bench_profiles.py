@@ -12,7 +12,7 @@ import bench
 
 def _args(**kw):
     base = dict(workload="h1", prune=0, window="", vgroup=False, hybrid=False, hadamard_block=-1, num_splits=0,
-                unfused=False)
+                unfused=False, page_size=-1)
     base.update(kw)
     return argparse.Namespace(**base)
 
@@ -29,6 +29,7 @@ def test_profile_keys_name_every_variant():
     assert bench.profile_key(_args(prune=3, num_splits=16)) == "h1_prune3_splits16"
     assert bench.profile_key(_args(unfused=True)) == "h1_unfused"
     assert bench.profile_key(_args(workload="c2", unfused=True)) == "c2_unfused"
+    assert bench.profile_key(_args(workload="c4", page_size=16)) == "c4_p16"
 
 
 def test_traffic_only_from_matching_profiles():

@@ -517,12 +517,15 @@ def test_decode_long_paged_partitions(num_splits):
     assert err <= TOL
 
 
-def test_decode_large_value_scales():
+@pytest.mark.parametrize("page", [0, 16, 48])
+def test_decode_large_value_scales(page):
     """A few tokens with values in the thousands (value scales >= 128): the kernel's
     scaled f16 value weights would overflow, so it must fall back to unscaled weights
-    for the partition and still match the oracle."""
-    w = _small("c2", batch=2, context=700)
-    print("[decode] large value scales", flush=True)
+    for the partition and still match the oracle. Paged caches rewalk their pages for the
+    second pass (with one partition of 1500 tokens in 16-token pages, the window of
+    block-table entries is refilled in both passes)."""
+    w = _small("c2", batch=2, context=700 if page == 0 else 1500, page_size=page)
+    print(f"[decode] large value scales, page {page}", flush=True)
     lens = wl.seq_lens(w)
     geo = wl.geometry(w, lens=lens)
     gpu = kvq.KVCache.allocate(128, 8, 4, 32, 128, geo.page_size, geo.num_pages, device=DEV)
@@ -544,7 +547,7 @@ def test_decode_large_value_scales():
         got = out.cpu().numpy().astype(np.float64)
         want = ref.decode(wl.bf16_bits(q), geo.block_table.numpy(), lens.numpy())
         err = max_err(got, want)
-        record(f"large_value_scales/splits={ns}", err)
+        record(f"large_value_scales/page={page}/splits={ns}", err)
         print(f"  splits={ns}: max |o| {np.max(np.abs(want)):.1f}, max-abs err {err:.3e}", flush=True)
         assert np.all(np.isfinite(got)) and err <= TOL
 
