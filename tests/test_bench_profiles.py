@@ -44,8 +44,10 @@ def test_traffic_only_from_matching_profiles():
         want = t["hbm_bytes_per_launch"] if t["kernel_source_sha"] == sha else None
         assert bench.traffic_from_profile(key) == want
         if want is not None:
-            # counters within a few percent of the algorithmic bytes
-            assert 0.99 < t["traffic_over_algorithmic"] < 1.1, (key, t["traffic_over_algorithmic"])
+            # counters within a few percent of the algorithmic bytes; the widest case is
+            # INT2 g128 on 16-token pages (c4_p16), where a tile's 64-byte {scale, zero}
+            # block fills half a 128-byte line (8 B of 72 B per token read twice over)
+            assert 0.99 < t["traffic_over_algorithmic"] < 1.13, (key, t["traffic_over_algorithmic"])
     # a configuration without its own counter runs reports none (never another's figure)
     assert bench.traffic_from_profile("h1_prune1") is None
     assert bench.traffic_from_profile("h1_splits8") is None
