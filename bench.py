@@ -19,8 +19,8 @@ need some 50-100 ms of sustained load to settle.
 
   python bench.py [--steps K] [--warmup W] [--workload h1] [--gpus 1] [--window S,R] [--eager] [--unfused]
 
-The timed step is the K steps replayed from one HIP graph (after untimed replays for
---settle-s seconds, at least one);
+The timed step is the median of --repeats (5) timed replays of the K steps captured in one
+HIP graph (after untimed replays for --settle-s seconds, at least one);
 the eager host-launched K steps run first, and their per-launch events time the split
 kernel for the roofline. --eager reports the host-launched step time instead.
 
@@ -216,6 +216,8 @@ def main():
                     help="append and decode as two calls (default: kvq_decode_step where the cache allows it)")
     ap.add_argument("--eager", action="store_true",
                     help="time the steps as host launches (default: the K steps replayed from one HIP graph)")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="timed replays of the K-step graph; the step time is their median")
     ap.add_argument("--stream-gib", type=int, default=4, help="GiB read by the read-stream probe")
     ap.add_argument("--calibration-copy-mb", type=int, default=0,
                     help="run one plain elementwise copy (torch.neg, fp32) of this many MiB before timing, "
@@ -389,9 +391,9 @@ def main():
 
     # The same K steps replayed from one HIP graph: the three kernels of a step then run
     # back to back without host launches between them (short steps are otherwise paced by
-    # the host). The graph is replayed untimed (see below), then once timed; the last replayed
-    # step's output must equal the eager step's bit for bit. The split kernel's
-    # event-timed launches above give the roofline either way.
+    # the host). The graph is replayed untimed (see below), then timed --repeats times;
+    # the last replayed step's output must equal the eager step's bit for bit. The split
+    # kernel's event-timed launches above give the roofline either way.
     graph = None
     if not args.eager and not windowed and not args.reference:
         base = total_steps
@@ -407,7 +409,7 @@ def main():
             for j in range(args.steps):
                 step(base + j)
         # the capture leaves the GPU idle long enough for its clocks to drop: untimed
-        # replays for settle_s seconds (at least one) before the timed one; a short K
+        # replays for settle_s seconds (at least one) before the timed ones; a short K
         # (20 steps of h1 are ~9 ms) would otherwise be timed on unsettled clocks
         n_untimed = 0
         t_settle = time.perf_counter()
@@ -417,18 +419,22 @@ def main():
             torch.cuda.synchronize()
             if time.perf_counter() - t_settle >= args.settle_s:
                 break
+        # the timed replay, repeated: the step is the median of the repeats
         g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record()
-        g.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / args.steps
+        reps = []
+        for _ in range(max(1, args.repeats)):
+            g0.record()
+            g.replay()
+            g1.record()
+            torch.cuda.synchronize()
+            reps.append(g0.elapsed_time(g1) / args.steps)
+        graph_ms = float(np.median(reps))
         replayed = out.clone()
         step(base + args.steps - 1)
         torch.cuda.synchronize()
         graph = {"us_per_step": round(graph_ms * 1e3, 2), "steps": args.steps,
                  "matches_eager": bool(torch.equal(replayed, out)), "us_per_step_eager": round(ms * 1e3, 2),
-                 "untimed_replays": n_untimed}
+                 "untimed_replays": n_untimed, "repeats_us_per_step": [round(r * 1e3, 2) for r in reps]}
         if not graph["matches_eager"]:
             sys.exit("bench.py: the graph-replayed step differs from the eager step")
         ms = graph_ms
