@@ -49,6 +49,13 @@ CASES = {
     "boundaries_fixed": (_small("c2", batch=6, context=300), _lens(1, 33, 256, 257, 0, 32), 4, 0),
     # pages of 16 tokens: 17 opens a page, 48 closes one
     "boundaries_paged": (_small("c5", batch=4, ragged=(1, 100)), _lens(17, 48, 1, 97), 0, 0),
+    # paged narrow groups (the super-block tile table read as wave-uniform rows): INT2 g128
+    # and INT4 g64 in 16- and 48-token pages, one sequence in a single partition of 60+
+    # pages (the block-table window refilled after the append)
+    "paged_int2_g128": (_small("c5", batch=4, ragged=(1, 900), bits=2, group_size=128), None, 0, 0),
+    "paged48_int4_g64": (_small("c5", batch=3, ragged=(30, 700), page_size=48, group_size=64), None, 0, 0),
+    "paged_int2_g128_one_partition": (_small("c5", batch=2, ragged=(1100, 1500), bits=2, group_size=128),
+                                      None, 1, 0),
 }
 
 
