@@ -32,8 +32,8 @@
  *    hadamard_block 0 (off) or a power of two from 2 to 128; GQA ratio
  *    num_q_heads / num_kv_heads of 1, 2 or 4; page_size a multiple of 16;
  *    num_pages * num_kv_heads * page_size / 16 below 2^32 (the decode kernels index
- *    the 16-token tiles of one kv head in 32 bits); max_seq_len up to 2^30. Other well-formed descriptions
- *    return KVQ_ERR_UNSUPPORTED.
+ *    the 16-token tiles of one kv head in 32 bits); max_seq_len up to 2^30. Other
+ *    well-formed descriptions return KVQ_ERR_UNSUPPORTED.
  */
 #ifndef KVQ_H
 #define KVQ_H
