@@ -199,6 +199,8 @@ def main():
                     help="sequences in the oracle's one-thread timed sample (the multi-thread sample runs one "
                          "sequence per host thread)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-repeats", type=int, default=3,
+                    help="runs of the oracle's timed sample; the CPU baseline is their median")
     ap.add_argument("--parity-seqs", type=int, default=2, help="sequences checked against the oracle")
     ap.add_argument("--window", default="", help="S,R: bf16 sink and recent windows of S and R tokens")
     ap.add_argument("--hybrid", action="store_true", help="hybrid symmetric/asymmetric groups (quant_mode 1)")
@@ -611,19 +613,27 @@ def main():
             def step_bytes_of(b):
                 return int(lens[b]) * Hkv * per_tok_head + Hq * d * 6 + Hkv * (2 * d * 2 + per_tok_head)
 
+            # each timing is the median of cpu_repeats runs of the same steps (a repeat
+            # appends the same token to the same slot again, then decodes)
+            n_rep = 1 if args.no_cpu_baseline else max(1, args.cpu_repeats)
             # one thread, the first len(seqs1) jobs in turn
-            ts = time.perf_counter()
-            outs1 = [oracle_step(i) for i in range(len(seqs1))]
-            t1 = time.perf_counter() - ts
+            reps1 = []
+            for _ in range(n_rep):
+                ts = time.perf_counter()
+                outs1 = [oracle_step(i) for i in range(len(seqs1))]
+                reps1.append(time.perf_counter() - ts)
+            t1 = float(np.median(reps1))
             checked = list(zip(seqs1, outs1))
             # n_thr threads, one job each, all started together
-            tN, outsN = None, []
+            tN, outsN, repsN = None, [], []
             if seqsN:
                 idx = list(range(len(seqs1), len(jobs)))
-                ts = time.perf_counter()
-                with cf.ThreadPoolExecutor(max_workers=n_thr) as ex:
-                    outsN = list(ex.map(oracle_step, idx))
-                tN = time.perf_counter() - ts
+                for _ in range(n_rep):
+                    ts = time.perf_counter()
+                    with cf.ThreadPoolExecutor(max_workers=n_thr) as ex:
+                        outsN = list(ex.map(oracle_step, idx))
+                    repsN.append(time.perf_counter() - ts)
+                tN = float(np.median(repsN))
                 checked += list(zip(jobs[len(seqs1):], outsN))
             for b, o in checked:
                 worst = max(worst, float(np.max(np.abs(o - out_h[b]))))
@@ -634,7 +644,8 @@ def main():
                 T0 = int(lens[seqs1[0]])
                 bytes1 = sum(step_bytes_of(b) for b in seqs1)
                 one = {"value": round(bytes1 / t1 / 1e9, 6), "unit": "GB/s", "threads": 1,
-                       "sample": f"{len(seqs1)} sequences one after another, {t1:.1f}s"}
+                       "sample": f"{len(seqs1)} sequences one after another, {t1:.1f}s (median of "
+                                 f"{n_rep}: {', '.join(f'{x:.2f}' for x in reps1)} s)"}
                 cpu = {"value": one["value"], "unit": "GB/s", "cores": 1, "kind": "oracle",
                        "sample": f"{len(seqs1)} of {B} sequences ({Hkv} kv heads, {Hq} q heads, T={T0}): oracle "
                                  f"append of the step's token + fp64 decode of every query head, one after another; "
@@ -646,7 +657,8 @@ def main():
                                 "sample": f"{n_thr} sequence steps ({len(set(seqsN))} distinct of {B}; {Hkv} kv "
                                           f"heads, {Hq} q heads, T={T0}) on {n_thr} host threads at once, each the "
                                           f"unmodified oracle (append of the step's token + fp64 decode of every "
-                                          f"query head) on its own sequence; {tN:.1f}s timed, cache build "
+                                          f"query head) on its own sequence; {tN:.1f}s timed (median of {n_rep}: "
+                                          f"{', '.join(f'{x:.2f}' for x in repsN)} s), cache build "
                                           f"{t_build:.1f}s untimed"})
                 cpu.update(host_description())
 
