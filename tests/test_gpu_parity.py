@@ -130,6 +130,26 @@ DECODE_CASES = {
 }
 
 
+PAGE_SWEEP = [32, 80, 112, 144, 496, 1008, 2032]
+
+
+@pytest.mark.parametrize("page", PAGE_SWEEP)
+def test_decode_page_size_sweep(page):
+    """Page sizes of 2..127 tiles (the paged table walk divides tile offsets by the tiles
+    per page with a rounded reciprocal and one correction): one partition per sequence and
+    the balanced plan, INT4 g32 and INT2 g128 on alternate sizes, against the oracle."""
+    bits, G = (4, 32) if PAGE_SWEEP.index(page) % 2 == 0 else (2, 128)
+    w = _small("c5", batch=3, ragged=(900, 4100), page_size=page, bits=bits, group_size=G, seed=page)
+    print(f"[decode] page sweep {page} INT{bits} g{G}", flush=True)
+    p = make_pair(w, DEV)
+    for ns in (1, 0):
+        got, want = decode_both(p, DEV, num_splits=ns)
+        err = max_err(got, want)
+        record(f"decode_page_sweep/p{page}/splits={ns}", err)
+        assert np.all(np.isfinite(got))
+        assert err <= TOL, (page, ns, err)
+
+
 LONG_PAGED_CASES = {f"p{page}_int{b}_splits{ns}": (page, b, ns)
                     for page in (16, 48, 80) for b in (4, 2) for ns in (1, 2)}
 
