@@ -107,6 +107,12 @@ CASES = {
     # long spans through the split kernel, contiguous and paged
     "int4_g32_ragged": (_w("c2", batch=3, context=2000), 32, 128, [2000, 777, 161], 3),
     "paged16": (_w("c5", batch=3, ragged=None, context=3000), 64, 128, [3000, 1234, 300], 3),
+    # paged narrow groups: the split kernel's span starts at the sink (48 tokens, mid-page
+    # in 32-token pages) and its tiles come from the super-block table
+    "paged32_int2_g128": (_w("c5", batch=2, ragged=None, context=2600, bits=2, group_size=128, page_size=32),
+                          48, 64, [2600, 1000], 2),
+    "paged48_int4_g64": (_w("c5", batch=2, ragged=None, context=2200, group_size=64, page_size=48),
+                         16, 96, [2200, 700], 2),
     "no_sink": (_w("c2", batch=2, context=1500), 0, 96, [1500, 97], 3),
     "sink16_recent1": (_w("c2", batch=2, context=600), 16, 1, [600, 17], 3),
     "int2_g128": (_w("c4", batch=2, context=1200), 32, 128, [1200, 500], 2),
